@@ -1,0 +1,258 @@
+/*
+ * pagedkv.h — C ABI of libpagedkv.so, paged-KV attention for AMD MI355X (gfx950).
+ *
+ * What the library computes (sources are the pages' titles and sections):
+ *   - The KV cache is cut into fixed-size blocks of B token slots that live anywhere in a
+ *     shared pool and are found through a per-sequence block table
+ *     (「PagedAttention原理」 §从虚拟内存的启发, §实现一个虚拟内存).
+ *   - Attention of a query row over its sequence's cached keys and values,
+ *     o = softmax(scale · q Kᵀ) V, computed block by block
+ *     (「PagedAttention原理」 §为什么会有 KV cache and the block-wise equation for A_ij and o_i
+ *     in §实现一个虚拟内存).
+ *   - Reference-counted copy-on-write of shared blocks (「PagedAttention原理」 §解决COW).
+ *   - A ragged batch that mixes prefill chunks and decode rows, split per request only inside
+ *     attention (「Paged Attention&Orca Paper笔记与解读」 §Orca的Solution, selective batching).
+ *
+ * Conventions for every entry point
+ *   - Pointers documented as "device" are HIP device memory owned by the caller; the library
+ *     never allocates, frees or retains device memory. "host" pointers are ordinary CPU memory.
+ *   - Device work is enqueued asynchronously on `stream` (a hipStream_t; NULL = the default
+ *     stream). The return value only reports host-side validation and the launch itself; on
+ *     any error status nothing has been enqueued.
+ *   - Device-resident indices (block ids, slots, lengths) are trusted: the caller guarantees
+ *     they are in range. Host-visible scalars and shapes are validated.
+ *   - Ordering between calls is the caller's job: on one stream, copy_blocks for an append's
+ *     copy-on-write pairs, then kv_cache_write of the new tokens, then attention.
+ *   - All integers are int32 unless stated; a pool may hold at most 2^31-1 slots.
+ *
+ * KV pool layout (the contract tests decode independently)
+ *   K and V are two separate pools per layer with identical shape. With N = num_blocks,
+ *   H = num_kv_heads, B = block_size, D = head_dim, the element for (block b, kv head h,
+ *   slot o within the block, dim i) is at linear element index
+ *         ((b * H + h) * B + o) * D + i
+ *   i.e. [N][H][B][D], "head-major": one (block, kv head) tile of B×D elements is contiguous
+ *   and a whole block (all heads) is one contiguous region of H·B·D elements.
+ *   A slot number s addresses block s / B, offset s % B.
+ *
+ * Supported shapes: dtype f32 / f16 / bf16; B in {8, 16, 32}; D in {64, 128};
+ * num_q_heads / num_kv_heads in {1, 2, 4, 8}.
+ */
+#ifndef PAGEDKV_H
+#define PAGEDKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { PKV_F32 = 0, PKV_F16 = 1, PKV_BF16 = 2 } pkv_dtype;
+
+typedef enum {
+  PKV_OK = 0,
+  PKV_EINVAL = -1,      /* null pointer or out-of-range scalar argument */
+  PKV_EDTYPE = -2,      /* unsupported element type (or out dtype)       */
+  PKV_ESHAPE = -3,      /* unsupported block size, head dim or head ratio */
+  PKV_EWORKSPACE = -4,  /* workspace missing or smaller than required     */
+  PKV_ELAUNCH = -5,     /* the HIP launch itself failed                   */
+  PKV_ENOBLOCKS = -6,   /* block manager: pool exhausted (nothing changed) */
+  PKV_ENOSEQ = -7,      /* block manager: unknown sequence id             */
+  PKV_EEXIST = -8       /* block manager: sequence id already present     */
+} pkv_status;
+
+/* Shape of one layer's K and V pools. */
+typedef struct {
+  int32_t num_blocks;
+  int32_t block_size;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t dtype; /* a pkv_dtype */
+} pkv_cache_desc;
+
+/* Human-readable name of a status code (static storage). */
+const char* pkv_status_str(int32_t status);
+
+/* Library version string (static storage). */
+const char* pkv_version(void);
+
+/*
+ * kv_cache_write — store new tokens' keys and values into their slots.
+ *   k_cache[slot[t]] <- k[t], v_cache[slot[t]] <- v[t] for t < num_tokens, bit for bit.
+ *   Each decode step stores the new token's K/V; a prefill stores the whole prompt's
+ *   (「vllm」 §2.1 Prefill, §2.2 Decode).
+ *   k, v        device, [num_tokens][H][D] rows in the pool dtype; row t starts at element
+ *               t * k_token_stride (resp. v_token_stride); strides >= H*D, multiples of 8.
+ *   k_cache, v_cache  device pools (layout above).
+ *   slot_mapping      device int32 [num_tokens]; a negative slot means "skip this token".
+ *   Two tokens must not name the same slot in one call.
+ *   num_tokens == 0 is a no-op.
+ */
+int32_t pkv_kv_cache_write(const void* k, const void* v, void* k_cache, void* v_cache,
+                           const int32_t* slot_mapping, int32_t num_tokens,
+                           int64_t k_token_stride, int64_t v_token_stride,
+                           const pkv_cache_desc* cache, void* stream);
+
+/*
+ * copy_blocks — step (2) of copy-on-write: copy each shared block into its new block
+ *   (「PagedAttention原理」 §解决COW). For each pair i: the whole block dst_i <- block src_i,
+ *   all B slots, all kv heads, K and V pools, bit for bit.
+ *   block_pairs  device int32 [num_pairs][2] = (src, dst).
+ *   No block may appear both as a source and as a destination in one call, and destinations
+ *   must be distinct (the block manager's pair lists satisfy this). num_pairs == 0 is a no-op.
+ */
+int32_t pkv_copy_blocks(void* k_cache, void* v_cache, const int32_t* block_pairs,
+                        int32_t num_pairs, const pkv_cache_desc* cache, void* stream);
+
+/*
+ * Workspace of the decode attention: partial results of the split-context path and
+ * one completion counter per (sequence, kv head).
+ *   Returns the bytes needed for these arguments (0 on invalid arguments).
+ *   The workspace must be zero-filled once after allocation; every call leaves the counter
+ *   region zero again, so one workspace serves any later call that fits it. Calls that share
+ *   a workspace must not run concurrently.
+ */
+size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t max_context_len,
+                                  const pkv_cache_desc* cache);
+
+/* Tokens per context partition the decode kernel uses for these arguments
+ * (partition_size argument 0 of the _ex entry point). */
+int32_t pkv_decode_partition_size(int32_t num_seqs, int32_t num_q_heads, int32_t max_context_len,
+                                  const pkv_cache_desc* cache);
+
+/*
+ * paged_attention_decode — one query row per sequence (the newest token, whose K/V were
+ * already written) attending every cached token 0..context_lens[s]-1 of its sequence,
+ * reached through its block table (「PagedAttention原理」 §实现一个虚拟内存).
+ *   out[s][h][:] = softmax(scale · q[s][h] · K_sᵀ) V_s, K_s/V_s = kv head h / (Hq/Hkv).
+ *   out           device [num_seqs][num_q_heads][D], element type out_dtype (PKV_F32 or the
+ *                 pool dtype). Accumulation is in fp32.
+ *   q             device [num_seqs][num_q_heads][D] in the pool dtype.
+ *   block_tables  device int32 [num_seqs][max_blocks_per_seq]; entries past a sequence's
+ *                 last block are never read.
+ *   context_lens  device int32 [num_seqs], each in [0, max_context_len] and
+ *                 <= max_blocks_per_seq * B. A length of 0 gives an all-zero output row.
+ *   max_context_len  host upper bound of context_lens (sizes the split; not a limit check).
+ *   scale         multiplier of q·k (1/sqrt(D) for standard attention).
+ *   workspace     device, >= pkv_decode_workspace_bytes(...) bytes, zeroed once (see above).
+ *   Long contexts are cut into partitions that are processed independently and merged with
+ *   log-sum-exp weights; the result does not depend on which physical blocks hold the data.
+ */
+int32_t pkv_paged_attention_decode(void* out, int32_t out_dtype, const void* q,
+                                   const void* k_cache, const void* v_cache,
+                                   const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                   const int32_t* context_lens, int32_t num_seqs,
+                                   int32_t num_q_heads, float scale, int32_t max_context_len,
+                                   const pkv_cache_desc* cache, void* workspace,
+                                   size_t workspace_bytes, void* stream);
+
+/* As pkv_paged_attention_decode with an explicit partition size in tokens (0 = automatic;
+ * otherwise a multiple of 64 and of the block size, at most 1024). The workspace must then be
+ * sized with pkv_decode_workspace_bytes_ex. */
+int32_t pkv_paged_attention_decode_ex(void* out, int32_t out_dtype, const void* q,
+                                      const void* k_cache, const void* v_cache,
+                                      const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                      const int32_t* context_lens, int32_t num_seqs,
+                                      int32_t num_q_heads, float scale, int32_t max_context_len,
+                                      const pkv_cache_desc* cache, int32_t partition_size,
+                                      void* workspace, size_t workspace_bytes, void* stream);
+
+size_t pkv_decode_workspace_bytes_ex(int32_t num_seqs, int32_t num_q_heads,
+                                     int32_t max_context_len, const pkv_cache_desc* cache,
+                                     int32_t partition_size);
+
+/*
+ * paged_attention_ragged — one selective-batching step: a flattened batch of query rows
+ * from several sequences, some prefill chunks and some single decode rows
+ * (「Paged Attention&Orca Paper笔记与解读」 §Orca的Solution).
+ *   Sequence s owns query rows cu_seqlens_q[s] .. cu_seqlens_q[s+1]-1 (q_len_s rows). They
+ *   are the last q_len_s positions of its context: row t sits at position
+ *   context_lens[s] - q_len_s + t and attends keys 0..that position (causal), all read through
+ *   the block table after this step's K/V were written. q_len_s == 1 is a decode row.
+ *   out           device [num_tokens][num_q_heads][D], out_dtype PKV_F32 or the pool dtype.
+ *   q             device [num_tokens][num_q_heads][D] in the pool dtype.
+ *   cu_seqlens_q  device int32 [num_seqs+1], non-decreasing, cu[0] = 0,
+ *                 cu[num_seqs] = num_tokens.
+ *   context_lens  device int32 [num_seqs], context_lens[s] >= q_len_s.
+ *   max_q_len, max_context_len  host upper bounds (launch sizing only).
+ *   workspace     device, >= pkv_ragged_workspace_bytes(...) bytes, zeroed once; shared
+ *                 rules as for decode.
+ */
+size_t pkv_ragged_workspace_bytes(int32_t num_seqs, int32_t num_tokens, int32_t num_q_heads,
+                                  int32_t max_q_len, int32_t max_context_len,
+                                  const pkv_cache_desc* cache);
+
+int32_t pkv_paged_attention_ragged(void* out, int32_t out_dtype, const void* q,
+                                   const int32_t* cu_seqlens_q, const int32_t* context_lens,
+                                   const void* k_cache, const void* v_cache,
+                                   const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                   int32_t num_seqs, int32_t num_tokens, int32_t num_q_heads,
+                                   float scale, int32_t max_q_len, int32_t max_context_len,
+                                   const pkv_cache_desc* cache, void* workspace,
+                                   size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------------------------
+ * Host block manager (CPU only; touches no device memory). Deterministic:
+ *   - a sequence takes a new block only when its last block is full
+ *     (「PagedAttention原理」 §从虚拟内存的启发);
+ *   - the block table keeps the physical block of each logical block and the filled count
+ *     (「PagedAttention原理」 §实现一个虚拟内存);
+ *   - every physical block has a reference count; writing into a block with count 1 is in
+ *     place, otherwise: allocate a new block, record (old, new) for copy_blocks, remap the
+ *     logical block, drop the old count, and write into the new block
+ *     (「PagedAttention原理」 §解决COW);
+ *   - fork shares every block of the parent (count + 1 each); free drops counts and releases
+ *     blocks at zero (「Paged Attention&Orca Paper笔记与解读」 §PagedAttention的方法);
+ *   - an append is all-or-nothing: on PKV_ENOBLOCKS no state changes
+ *     (「PagedAttention原理」 §all-or-nothing 调度).
+ * Tie-breaks: free blocks are taken from the head of the creation-time order and released
+ * blocks join its tail in logical-block order; sequences of one append are served in the
+ * order given, tokens in position order.
+ * A pkv_bm object is not thread-safe.
+ * ------------------------------------------------------------------------------------------ */
+typedef struct pkv_bm pkv_bm;
+
+/* free_order: host int32 [num_blocks], a permutation of 0..num_blocks-1 (NULL = identity).
+ * Returns NULL on invalid arguments or allocation failure. */
+pkv_bm* pkv_bm_create(int32_t num_blocks, int32_t block_size, const int32_t* free_order);
+void pkv_bm_destroy(pkv_bm* bm);
+
+int32_t pkv_bm_add_seq(pkv_bm* bm, int64_t seq_id);
+int32_t pkv_bm_fork(pkv_bm* bm, int64_t parent_id, int64_t child_id);
+int32_t pkv_bm_free_seq(pkv_bm* bm, int64_t seq_id);
+
+/* Number of new blocks (fresh or copy-on-write) an append of these tokens would take
+ * (host arrays of n_seqs); negative status on error. */
+int64_t pkv_bm_blocks_needed(const pkv_bm* bm, const int64_t* seq_ids, const int32_t* n_tokens,
+                             int32_t n_seqs);
+
+/*
+ * Append n_tokens[i] positions to seq_ids[i] for i < n_seqs (host arrays).
+ *   slots_out      host int32 [sum n_tokens]: slot of every new token, in the order given.
+ *   cow_pairs_out  host int32 [2 * max_pairs]: (src, dst) per copy-on-write, in order.
+ *   num_pairs_out  host int32: number of pairs written.
+ *   max_pairs      capacity of cow_pairs_out in pairs; at most one pair per sequence per
+ *                  append can occur, so n_seqs always suffices.
+ * All or nothing: on any error status the manager is unchanged.
+ */
+int32_t pkv_bm_append(pkv_bm* bm, const int64_t* seq_ids, const int32_t* n_tokens, int32_t n_seqs,
+                      int32_t* slots_out, int32_t* cow_pairs_out, int32_t max_pairs,
+                      int32_t* num_pairs_out);
+
+/* Block tables and context lengths of n sequences into host arrays:
+ * tables_out [n][max_blocks] padded with -1; ctx_out [n] (may be NULL). */
+int32_t pkv_bm_block_tables(const pkv_bm* bm, const int64_t* seq_ids, int32_t n, int32_t max_blocks,
+                            int32_t* tables_out, int32_t* ctx_out);
+
+/* Table of one sequence: writes up to cap entries, returns its length in blocks (or error). */
+int32_t pkv_bm_seq_table(const pkv_bm* bm, int64_t seq_id, int32_t* table_out, int32_t cap);
+int32_t pkv_bm_context_len(const pkv_bm* bm, int64_t seq_id);
+int32_t pkv_bm_refcount(const pkv_bm* bm, int32_t block);
+int32_t pkv_bm_num_free(const pkv_bm* bm);
+/* Free list from head to tail into host out[cap]; returns its length. */
+int32_t pkv_bm_free_list(const pkv_bm* bm, int32_t* out, int32_t cap);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* PAGEDKV_H */

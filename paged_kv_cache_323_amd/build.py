@@ -1,0 +1,75 @@
+"""Build libpagedkv.so (HIP for gfx950) in-tree.
+
+    python -m paged_kv_cache_323_amd.build          # compile every source, link the library
+
+Every HIP source is compiled with packed-fp32 instruction selection disabled; the host-only
+block manager is compiled with the system C++ compiler.
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+from concurrent.futures import ThreadPoolExecutor
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+BUILD = os.path.join(ROOT, "_build")
+LIB = os.path.join(PKG, "libpagedkv.so")
+ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
+HIPCC = os.path.join(ROCM, "bin", "hipcc")
+ARCH = "gfx950"
+
+HIP_FLAGS = [
+    f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++17", "-I", INCLUDE, "-I", CSRC,
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wall", "-Wno-unused-function", "-Wno-unused-variable",
+]
+HOST_FLAGS = ["-O2", "-fPIC", "-std=c++17", "-Wall", "-I", INCLUDE]
+
+
+def _hip_sources():
+    return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip")) + [
+        os.path.join(CSRC, "api.cpp")]
+
+
+def _run(cmd):
+    p = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    out = "\n".join(line for line in p.stdout.splitlines()
+                    if "is not a recognized feature for this target" not in line)
+    if p.returncode != 0:
+        raise RuntimeError(f"command failed ({p.returncode}): {' '.join(cmd)}\n{out}")
+    return out
+
+
+def build(verbose: bool = False, jobs: int = 8) -> str:
+    if not os.path.exists(HIPCC):
+        raise RuntimeError(f"hipcc not found at {HIPCC}")
+    os.makedirs(BUILD, exist_ok=True)
+    jobs_list = []
+    objs = []
+    for src in _hip_sources():
+        obj = os.path.join(BUILD, os.path.basename(src) + ".o")
+        extra = ["-x", "hip"] if src.endswith(".cpp") else []
+        jobs_list.append([HIPCC, *HIP_FLAGS, *extra, "-c", src, "-o", obj])
+        objs.append(obj)
+    bm_src = os.path.join(CSRC, "block_manager.cpp")
+    bm_obj = os.path.join(BUILD, "block_manager.cpp.o")
+    cxx = shutil.which("g++") or "c++"
+    jobs_list.append([cxx, *HOST_FLAGS, "-c", bm_src, "-o", bm_obj])
+    objs.append(bm_obj)
+    with ThreadPoolExecutor(max(1, jobs)) as ex:
+        for out in ex.map(_run, jobs_list):
+            if verbose and out.strip():
+                print(out)
+    tmp = LIB + ".tmp"
+    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp])
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

@@ -1,0 +1,203 @@
+// C ABI of libpagedkv.so: argument validation, launch sizing and workspace carving.
+// The kernels live in cache_ops.hip, decode.hip and ragged.hip; the host block manager in
+// block_manager.cpp.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/pagedkv.h"
+#include "internal.hpp"
+
+namespace {
+
+constexpr size_t kAlign = 256;
+inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+int elem_bytes(int dt) { return dt == PKV_F32 ? 4 : (dt == PKV_F16 || dt == PKV_BF16) ? 2 : 0; }
+
+// Validates the pool description; returns PKV_OK or the status to report.
+int32_t check_cache(const pkv_cache_desc* c) {
+  if (!c) return PKV_EINVAL;
+  if (elem_bytes(c->dtype) == 0) return PKV_EDTYPE;
+  if (c->block_size != 8 && c->block_size != 16 && c->block_size != 32) return PKV_ESHAPE;
+  if (c->head_dim != 64 && c->head_dim != 128) return PKV_ESHAPE;
+  if (c->num_blocks <= 0 || c->num_kv_heads <= 0) return PKV_EINVAL;
+  if ((int64_t)c->num_blocks * c->block_size > INT32_MAX) return PKV_ESHAPE;
+  return PKV_OK;
+}
+
+int32_t check_heads(int32_t hq, const pkv_cache_desc* c) {
+  if (hq <= 0 || hq % c->num_kv_heads != 0) return PKV_ESHAPE;
+  const int g = hq / c->num_kv_heads;
+  if (g != 1 && g != 2 && g != 4 && g != 8) return PKV_ESHAPE;
+  return PKV_OK;
+}
+
+int32_t check_out_dtype(int32_t out_dt, const pkv_cache_desc* c) {
+  return (out_dt == PKV_F32 || out_dt == c->dtype) ? PKV_OK : PKV_EDTYPE;
+}
+
+int auto_partition(int32_t max_ctx) {
+  if (max_ctx <= 512) {
+    int p = ((max_ctx > 0 ? max_ctx : 1) + 63) / 64 * 64;
+    return p;
+  }
+  return 512;
+}
+
+bool valid_partition(int p, int bs) { return p >= 64 && p <= 512 && p % 64 == 0 && p % bs == 0; }
+
+struct DecodeWs {
+  size_t acc, ml, cnt, total;
+};
+
+DecodeWs decode_ws_layout(int32_t S, int32_t hq, int32_t hkv, int32_t head_dim, int max_parts) {
+  DecodeWs w{0, 0, 0, 0};
+  if (max_parts <= 1) return w;
+  const size_t items = (size_t)S * hkv * max_parts;
+  const int g = hq / hkv;
+  w.acc = 0;
+  w.ml = align_up(items * g * head_dim * sizeof(float));
+  w.cnt = w.ml + align_up(items * g * 2 * sizeof(float));
+  w.total = w.cnt + align_up((size_t)S * hkv * sizeof(int32_t));
+  return w;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pkv_status_str(int32_t s) {
+  switch (s) {
+    case PKV_OK: return "ok";
+    case PKV_EINVAL: return "invalid argument";
+    case PKV_EDTYPE: return "unsupported dtype";
+    case PKV_ESHAPE: return "unsupported shape";
+    case PKV_EWORKSPACE: return "workspace missing or too small";
+    case PKV_ELAUNCH: return "kernel launch failed";
+    case PKV_ENOBLOCKS: return "no free blocks";
+    case PKV_ENOSEQ: return "unknown sequence";
+    case PKV_EEXIST: return "sequence exists";
+  }
+  return "unknown status";
+}
+
+const char* pkv_version(void) { return "pagedkv 0.1 gfx950"; }
+
+int32_t pkv_kv_cache_write(const void* k, const void* v, void* k_cache, void* v_cache,
+                           const int32_t* slot_mapping, int32_t num_tokens, int64_t k_token_stride,
+                           int64_t v_token_stride, const pkv_cache_desc* c, void* stream) {
+  int32_t st = check_cache(c);
+  if (st != PKV_OK) return st;
+  if (num_tokens < 0) return PKV_EINVAL;
+  if (num_tokens == 0) return PKV_OK;
+  if (!k || !v || !k_cache || !v_cache || !slot_mapping) return PKV_EINVAL;
+  const int64_t row = (int64_t)c->num_kv_heads * c->head_dim;
+  if (k_token_stride < row || v_token_stride < row || k_token_stride % 8 || v_token_stride % 8)
+    return PKV_EINVAL;
+  const int es = elem_bytes(c->dtype);
+  if ((uint64_t)num_tokens * c->num_kv_heads * (c->head_dim * es / 16) > 0xffffffffull) return PKV_ESHAPE;
+  return pkv::launch_kv_cache_write(k, v, k_cache, v_cache, slot_mapping, num_tokens, k_token_stride * es,
+                                    v_token_stride * es, c->num_kv_heads, c->block_size, c->head_dim, es,
+                                    (hipStream_t)stream) == 0
+             ? PKV_OK
+             : PKV_ELAUNCH;
+}
+
+int32_t pkv_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs, int32_t num_pairs,
+                        const pkv_cache_desc* c, void* stream) {
+  int32_t st = check_cache(c);
+  if (st != PKV_OK) return st;
+  if (num_pairs < 0) return PKV_EINVAL;
+  if (num_pairs == 0) return PKV_OK;
+  if (!k_cache || !v_cache || !pairs) return PKV_EINVAL;
+  const int64_t block_bytes = (int64_t)c->num_kv_heads * c->block_size * c->head_dim * elem_bytes(c->dtype);
+  return pkv::launch_copy_blocks(k_cache, v_cache, pairs, num_pairs, block_bytes, (hipStream_t)stream) == 0
+             ? PKV_OK
+             : PKV_ELAUNCH;
+}
+
+int32_t pkv_decode_partition_size(int32_t num_seqs, int32_t num_q_heads, int32_t max_ctx,
+                                  const pkv_cache_desc* c) {
+  (void)num_seqs;
+  (void)num_q_heads;
+  if (check_cache(c) != PKV_OK || max_ctx < 0) return PKV_EINVAL;
+  int p = auto_partition(max_ctx);
+  while (p % c->block_size) p += 64;
+  return p;
+}
+
+size_t pkv_decode_workspace_bytes_ex(int32_t S, int32_t hq, int32_t max_ctx, const pkv_cache_desc* c,
+                                     int32_t partition) {
+  if (check_cache(c) != PKV_OK || check_heads(hq, c) != PKV_OK || S < 0 || max_ctx < 0) return 0;
+  const int p = partition > 0 ? partition : pkv_decode_partition_size(S, hq, max_ctx, c);
+  if (!valid_partition(p, c->block_size)) return 0;
+  const int max_parts = max_ctx > 0 ? (max_ctx + p - 1) / p : 1;
+  return decode_ws_layout(S, hq, c->num_kv_heads, c->head_dim, max_parts).total;
+}
+
+size_t pkv_decode_workspace_bytes(int32_t S, int32_t hq, int32_t max_ctx, const pkv_cache_desc* c) {
+  return pkv_decode_workspace_bytes_ex(S, hq, max_ctx, c, 0);
+}
+
+int32_t pkv_paged_attention_decode_ex(void* out, int32_t out_dtype, const void* q, const void* k_cache,
+                                      const void* v_cache, const int32_t* block_tables,
+                                      int32_t max_blocks_per_seq, const int32_t* context_lens,
+                                      int32_t num_seqs, int32_t num_q_heads, float scale,
+                                      int32_t max_context_len, const pkv_cache_desc* c,
+                                      int32_t partition_size, void* workspace, size_t workspace_bytes,
+                                      void* stream) {
+  int32_t st = check_cache(c);
+  if (st != PKV_OK) return st;
+  if ((st = check_heads(num_q_heads, c)) != PKV_OK) return st;
+  if ((st = check_out_dtype(out_dtype, c)) != PKV_OK) return st;
+  if (num_seqs < 0 || max_context_len < 0 || max_blocks_per_seq < 0) return PKV_EINVAL;
+  if (num_seqs == 0) return PKV_OK;
+  if (num_seqs > 65535) return PKV_ESHAPE;
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens) return PKV_EINVAL;
+  if ((int64_t)max_blocks_per_seq * c->block_size < max_context_len) return PKV_EINVAL;
+  if (!(scale == scale)) return PKV_EINVAL;
+  const int p = partition_size > 0 ? partition_size
+                                   : pkv_decode_partition_size(num_seqs, num_q_heads, max_context_len, c);
+  if (!valid_partition(p, c->block_size)) return PKV_EINVAL;
+  const int max_parts = max_context_len > 0 ? (max_context_len + p - 1) / p : 1;
+  if (max_parts > 65535) return PKV_ESHAPE;
+  const DecodeWs ws = decode_ws_layout(num_seqs, num_q_heads, c->num_kv_heads, c->head_dim, max_parts);
+  if (ws.total > 0 && (!workspace || workspace_bytes < ws.total)) return PKV_EWORKSPACE;
+
+  pkv::DecodeLaunch L;
+  L.out = out;
+  L.out_dt = out_dtype;
+  L.q = q;
+  L.kc = k_cache;
+  L.vc = v_cache;
+  L.tables = block_tables;
+  L.max_blocks = max_blocks_per_seq;
+  L.ctx_lens = context_lens;
+  L.num_seqs = num_seqs;
+  L.num_q_heads = num_q_heads;
+  L.num_kv_heads = c->num_kv_heads;
+  L.block_size = c->block_size;
+  L.head_dim = c->head_dim;
+  L.dt = c->dtype;
+  L.scale = scale;
+  L.partition = p;
+  L.max_parts = max_parts;
+  char* wb = static_cast<char*>(workspace);
+  L.ws_acc = ws.total ? reinterpret_cast<float*>(wb + ws.acc) : nullptr;
+  L.ws_ml = ws.total ? reinterpret_cast<float*>(wb + ws.ml) : nullptr;
+  L.ws_cnt = ws.total ? reinterpret_cast<int32_t*>(wb + ws.cnt) : nullptr;
+  return pkv::launch_decode(L, (hipStream_t)stream) == 0 ? PKV_OK : PKV_ELAUNCH;
+}
+
+int32_t pkv_paged_attention_decode(void* out, int32_t out_dtype, const void* q, const void* k_cache,
+                                   const void* v_cache, const int32_t* block_tables,
+                                   int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t num_seqs,
+                                   int32_t num_q_heads, float scale, int32_t max_context_len,
+                                   const pkv_cache_desc* c, void* workspace, size_t workspace_bytes,
+                                   void* stream) {
+  return pkv_paged_attention_decode_ex(out, out_dtype, q, k_cache, v_cache, block_tables, max_blocks_per_seq,
+                                       context_lens, num_seqs, num_q_heads, scale, max_context_len, c, 0,
+                                       workspace, workspace_bytes, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,115 @@
+// Device helpers shared by the paged-KV kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pkv {
+
+constexpr int kWave = 64;
+
+enum : int { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2 };
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+// Storage type of each element type (bf16 is kept as raw 16-bit patterns).
+template <int DT> struct Elem;
+template <> struct Elem<DT_F32> { using T = float; };
+template <> struct Elem<DT_F16> { using T = _Float16; };
+template <> struct Elem<DT_BF16> { using T = uint16_t; };
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
+
+// Round-to-nearest-even fp32 -> bf16 bits (finite inputs; NaN stays NaN).
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// Two packed 16-bit elements of one 32-bit word -> two floats.
+template <int DT> __device__ __forceinline__ void unpack2(uint32_t w, float& lo, float& hi);
+template <> __device__ __forceinline__ void unpack2<DT_BF16>(uint32_t w, float& lo, float& hi) {
+  lo = __uint_as_float(w << 16);
+  hi = __uint_as_float(w & 0xffff0000u);
+}
+template <> __device__ __forceinline__ void unpack2<DT_F16>(uint32_t w, float& lo, float& hi) {
+  f16x2 h = __builtin_bit_cast(f16x2, w);
+  lo = (float)h[0];
+  hi = (float)h[1];
+}
+
+// acc + a·b over the two packed elements of each 32-bit word (products exact in fp32).
+template <int DT> __device__ __forceinline__ float dot2_acc(uint32_t a, uint32_t b, float acc);
+template <> __device__ __forceinline__ float dot2_acc<DT_BF16>(uint32_t a, uint32_t b, float acc) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), acc, false);
+}
+template <> __device__ __forceinline__ float dot2_acc<DT_F16>(uint32_t a, uint32_t b, float acc) {
+  return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, a), __builtin_bit_cast(f16x2, b), acc, false);
+}
+
+// Dot product of two 16-byte chunks (8 x 16-bit or 4 x fp32 elements).
+template <int DT> __device__ __forceinline__ float dot16B(const u32x4& a, const u32x4& b, float acc) {
+  if constexpr (DT == DT_F32) {
+    acc = __builtin_fmaf(__uint_as_float(a[0]), __uint_as_float(b[0]), acc);
+    acc = __builtin_fmaf(__uint_as_float(a[1]), __uint_as_float(b[1]), acc);
+    acc = __builtin_fmaf(__uint_as_float(a[2]), __uint_as_float(b[2]), acc);
+    acc = __builtin_fmaf(__uint_as_float(a[3]), __uint_as_float(b[3]), acc);
+  } else {
+    acc = dot2_acc<DT>(a[0], b[0], acc);
+    acc = dot2_acc<DT>(a[1], b[1], acc);
+    acc = dot2_acc<DT>(a[2], b[2], acc);
+    acc = dot2_acc<DT>(a[3], b[3], acc);
+  }
+  return acc;
+}
+
+// ---- cross-lane reductions -------------------------------------------------------------------
+// DPP controls (gfx9 encoding).
+constexpr int kDppQuadXor1 = 0xB1;      // quad_perm [1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4E;      // quad_perm [2,3,0,1]
+constexpr int kDppRowHalfMirror = 0x141;
+constexpr int kDppRowMirror = 0x140;
+
+template <int CTRL> __device__ __forceinline__ float dpp(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over each aligned group of 8 lanes; every lane of the group gets the total.
+__device__ __forceinline__ float sum8(float x) {
+  x += dpp<kDppQuadXor1>(x);
+  x += dpp<kDppQuadXor2>(x);
+  x += dpp<kDppRowHalfMirror>(x);
+  return x;
+}
+
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, kWave));
+  return x;
+}
+
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, kWave);
+  return x;
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Store one fp32 value as the output element type.
+__device__ __forceinline__ void store_out(void* base, size_t idx, float v, int out_dt) {
+  if (out_dt == DT_F32) {
+    reinterpret_cast<float*>(base)[idx] = v;
+  } else if (out_dt == DT_F16) {
+    reinterpret_cast<_Float16*>(base)[idx] = (_Float16)v;
+  } else {
+    reinterpret_cast<uint16_t*>(base)[idx] = f32_to_bf16_bits(v);
+  }
+}
+
+}  // namespace pkv

@@ -1,0 +1,356 @@
+// Paged decode attention for gfx950.
+//
+// One workgroup (4 waves) per (kv head, sequence, context partition). The g = Hq/Hkv query
+// heads that share a kv head are served by the same workgroup, so every K/V tile is read from
+// HBM once per step. The partition's tokens are walked through the block table in units of 8
+// tokens (units never straddle a block, since B is a multiple of 8):
+//
+//   phase 1  scores: 8 lanes per token, each lane owns interleaved 16-byte chunks of the row;
+//            packed dot2 (bf16/f16) or fma (f32) against the query slices held in registers;
+//            an 8-lane DPP reduction; scores (pre-multiplied by scale·log2 e) go to LDS.
+//   softmax  per head over the partition: max, exp2, sum (one wave per head).
+//   phase 2  values: 16 lanes per token, each lane owns D/16 contiguous elements of the row;
+//            fp32 accumulators for all g heads; probabilities read from LDS.
+//   merge    lane groups and waves are summed through LDS.
+//
+// A sequence whose context fits one partition writes its normalised output directly. Longer
+// contexts write (max, sum, unnormalised output) per partition to the workspace; the last
+// workgroup of a (sequence, kv head) to finish merges them with log-sum-exp weights and resets
+// the completion counter. Any grouping of blocks gives the same softmax, which is what makes
+// the partitioning exact: the block-wise attention equation of 「PagedAttention原理」
+// §实现一个虚拟内存 sums exponentials block by block against one common denominator.
+#include "common.hpp"
+#include "internal.hpp"
+
+namespace pkv {
+
+constexpr int kDecThreads = 256;
+constexpr int kDecWaves = 4;
+constexpr int kMaxPartition = 512;
+
+struct DecodeArgs {
+  void* out;
+  const void* q;
+  const void* kc;
+  const void* vc;
+  const int32_t* tables;
+  const int32_t* ctx_lens;
+  float* ws_acc;
+  float2* ws_ml;
+  int32_t* ws_cnt;
+  int out_dt;
+  int max_blocks;
+  int hq;
+  int hkv;
+  int bs;
+  int log2_bs;
+  float scale_log2;
+  int partition;
+  int max_parts;
+};
+
+// Raw words of one lane's slice of a V row (PV mapping): 8, 16 or 32 bytes.
+template <int NWORDS> struct Words { uint32_t w[NWORDS]; };
+
+template <int NWORDS> __device__ __forceinline__ Words<NWORDS> load_words(const void* p) {
+  Words<NWORDS> r;
+  if constexpr (NWORDS == 2) {
+    const u32x2 x = *reinterpret_cast<const u32x2*>(p);
+    r.w[0] = x[0]; r.w[1] = x[1];
+  } else {
+#pragma unroll
+    for (int i = 0; i < NWORDS / 4; ++i) {
+      const u32x4 x = reinterpret_cast<const u32x4*>(p)[i];
+      r.w[4 * i] = x[0]; r.w[4 * i + 1] = x[1]; r.w[4 * i + 2] = x[2]; r.w[4 * i + 3] = x[3];
+    }
+  }
+  return r;
+}
+
+template <int DT, int NWORDS, int EPL> __device__ __forceinline__ void words_to_f32(const Words<NWORDS>& w, float (&f)[EPL]) {
+  if constexpr (DT == DT_F32) {
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) f[i] = __uint_as_float(w.w[i]);
+  } else {
+#pragma unroll
+    for (int i = 0; i < NWORDS; ++i) unpack2<DT>(w.w[i], f[2 * i], f[2 * i + 1]);
+  }
+}
+
+template <int DT, int D, int G>
+__global__ __launch_bounds__(kDecThreads) void paged_decode_kernel(DecodeArgs a) {
+  using T = typename Elem<DT>::T;
+  constexpr int ES = sizeof(T);
+  constexpr int VEC = 16 / ES;        // elements per 16-byte chunk
+  constexpr int NCH = D / (8 * VEC);  // 16-byte chunks per lane per token row (score mapping)
+  constexpr int EPL = D / 16;         // elements per lane per token row (value mapping)
+  constexpr int NWORDS = EPL * ES / 4;
+  static_assert(NCH >= 1 && EPL * ES % 8 == 0, "unsupported head dim");
+
+  __shared__ int32_t s_tab[kMaxPartition / 8];
+  __shared__ float s_p[kMaxPartition * G];  // [token][head]: scaled scores, then probabilities
+  __shared__ float s_red[kDecWaves * G * D];
+  __shared__ float s_m[G];
+  __shared__ float s_l[G];
+  __shared__ int s_last;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int kvh = blockIdx.x;
+  const int s = blockIdx.y;
+  const int part = blockIdx.z;
+
+  const int ctx = a.ctx_lens[s];
+  const int nparts = ctx > 0 ? (ctx + a.partition - 1) / a.partition : 1;
+  if (part >= nparts) return;  // uniform over the workgroup
+  const int t0 = part * a.partition;
+  const int n = min(a.partition, ctx - t0);  // tokens of this partition (0 iff ctx == 0)
+  const int nunits = (n + 7) >> 3;
+
+  // Block-table entries of this partition (the partition starts on a block boundary).
+  const int nblk = (n + a.bs - 1) >> a.log2_bs;
+  const int32_t* trow = a.tables + (size_t)s * a.max_blocks + (t0 >> a.log2_bs);
+  for (int i = tid; i < nblk; i += kDecThreads) s_tab[i] = trow[i];
+
+  // Query slices of the G heads in the score mapping.
+  const int c = lane & 7;   // 16-byte chunk column
+  const int r = lane >> 3;  // token row within a unit
+  const T* qb = static_cast<const T*>(a.q) + ((size_t)s * a.hq + (size_t)kvh * G) * D + c * VEC;
+  u32x4 qr[G][NCH];
+#pragma unroll
+  for (int g = 0; g < G; ++g)
+#pragma unroll
+    for (int ch = 0; ch < NCH; ++ch) qr[g][ch] = *reinterpret_cast<const u32x4*>(qb + g * D + ch * 8 * VEC);
+  __syncthreads();
+
+  const size_t head_off = (size_t)kvh * a.bs;  // in rows
+  const T* kbase = static_cast<const T*>(a.kc);
+  const T* vbase = static_cast<const T*>(a.vc);
+
+  // ---- phase 1: scores ----------------------------------------------------------------------
+  {
+    u32x4 kr[NCH];
+    int u = wave;
+    if (u < nunits) {
+      const int phys = s_tab[(u * 8) >> a.log2_bs];
+      const T* p = kbase + (((size_t)phys * a.hkv * a.bs + head_off + ((u * 8 + r) & (a.bs - 1))) * D) + c * VEC;
+#pragma unroll
+      for (int ch = 0; ch < NCH; ++ch) kr[ch] = *reinterpret_cast<const u32x4*>(p + ch * 8 * VEC);
+    }
+    for (; u < nunits; u += kDecWaves) {
+      const int un = u + kDecWaves;
+      u32x4 kn[NCH];
+      if (un < nunits) {
+        const int phys = s_tab[(un * 8) >> a.log2_bs];
+        const T* p = kbase + (((size_t)phys * a.hkv * a.bs + head_off + ((un * 8 + r) & (a.bs - 1))) * D) + c * VEC;
+#pragma unroll
+        for (int ch = 0; ch < NCH; ++ch) kn[ch] = *reinterpret_cast<const u32x4*>(p + ch * 8 * VEC);
+      }
+      float sc[G];
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        float acc = 0.f;
+#pragma unroll
+        for (int ch = 0; ch < NCH; ++ch) acc = dot16B<DT>(qr[g][ch], kr[ch], acc);
+        sc[g] = sum8(acc);
+      }
+      const int tl = u * 8 + r;
+      if (c < G) {
+        float mine = sc[0];
+#pragma unroll
+        for (int g = 1; g < G; ++g) mine = (c == g) ? sc[g] : mine;
+        s_p[tl * G + c] = tl < n ? mine * a.scale_log2 : -INFINITY;
+      }
+      if (un < nunits) {
+#pragma unroll
+        for (int ch = 0; ch < NCH; ++ch) kr[ch] = kn[ch];
+      }
+    }
+  }
+  __syncthreads();
+
+  // ---- softmax over the partition, one wave per head -----------------------------------------
+  for (int g = wave; g < G; g += kDecWaves) {
+    float m = -INFINITY;
+    for (int i = lane; i < n; i += kWave) m = fmaxf(m, s_p[i * G + g]);
+    m = wave_max(m);
+    float l = 0.f;
+    for (int i = lane; i < nunits * 8; i += kWave) {
+      const float p = i < n ? fast_exp2(s_p[i * G + g] - m) : 0.f;
+      s_p[i * G + g] = p;
+      l += p;
+    }
+    l = wave_sum(l);
+    if (lane == 0) {
+      s_m[g] = m;
+      s_l[g] = l;
+    }
+  }
+  __syncthreads();
+
+  // ---- phase 2: probability-weighted values ----------------------------------------------------
+  const int cv = lane & 15;  // column slice
+  const int rv = lane >> 4;  // token row within a pass of 4
+  float acc[G][EPL];
+#pragma unroll
+  for (int g = 0; g < G; ++g)
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[g][e] = 0.f;
+  {
+    Words<NWORDS> vr[2];
+    int u = wave;
+    if (u < nunits) {
+      const int phys = s_tab[(u * 8) >> a.log2_bs];
+      const T* p = vbase + ((size_t)phys * a.hkv * a.bs + head_off) * D + cv * EPL;
+#pragma unroll
+      for (int ps = 0; ps < 2; ++ps) vr[ps] = load_words<NWORDS>(p + (size_t)(((u * 8 + ps * 4 + rv) & (a.bs - 1)) * D));
+    }
+    for (; u < nunits; u += kDecWaves) {
+      const int un = u + kDecWaves;
+      Words<NWORDS> vn[2];
+      if (un < nunits) {
+        const int phys = s_tab[(un * 8) >> a.log2_bs];
+        const T* p = vbase + ((size_t)phys * a.hkv * a.bs + head_off) * D + cv * EPL;
+#pragma unroll
+        for (int ps = 0; ps < 2; ++ps) vn[ps] = load_words<NWORDS>(p + (size_t)(((un * 8 + ps * 4 + rv) & (a.bs - 1)) * D));
+      }
+#pragma unroll
+      for (int ps = 0; ps < 2; ++ps) {
+        const int tl = u * 8 + ps * 4 + rv;
+        const bool valid = tl < n;
+        float vf[EPL];
+        words_to_f32<DT, NWORDS, EPL>(vr[ps], vf);
+        float pg[G];
+#pragma unroll
+        for (int g = 0; g < G; ++g) pg[g] = s_p[tl * G + g];  // 0 past the context
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) {
+          const float x = valid ? vf[e] : 0.f;  // unwritten slots may hold anything
+#pragma unroll
+          for (int g = 0; g < G; ++g) acc[g][e] = __builtin_fmaf(pg[g], x, acc[g][e]);
+        }
+      }
+      if (un < nunits) {
+        vr[0] = vn[0];
+        vr[1] = vn[1];
+      }
+    }
+  }
+
+  // ---- merge the four token rows of each wave, then the four waves ------------------------------
+#pragma unroll
+  for (int g = 0; g < G; ++g)
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+      float x = acc[g][e];
+      x += __shfl_xor(x, 16, kWave);
+      x += __shfl_xor(x, 32, kWave);
+      acc[g][e] = x;
+    }
+  if (rv == 0) {
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) s_red[(wave * G + g) * D + cv * EPL + e] = acc[g][e];
+  }
+  __syncthreads();
+
+  const size_t out_row = (size_t)s * a.hq + (size_t)kvh * G;  // first of the G query heads
+  const size_t item = ((size_t)s * a.hkv + kvh) * a.max_parts;
+  for (int o = tid; o < G * D; o += kDecThreads) {
+    float v = 0.f;
+#pragma unroll
+    for (int w = 0; w < kDecWaves; ++w) v += s_red[w * G * D + o];
+    const int g = o / D;
+    if (nparts == 1) {
+      const float l = s_l[g];
+      store_out(a.out, out_row * D + o, l > 0.f ? v / l : 0.f, a.out_dt);
+    } else {
+      a.ws_acc[(item + part) * G * D + o] = v;
+      if (o % D == 0) a.ws_ml[(item + part) * G + g] = make_float2(s_m[g], s_l[g]);
+    }
+  }
+  if (nparts == 1) return;
+
+  // ---- split context: the last partition to finish merges all of them --------------------------
+  __threadfence();
+  __syncthreads();
+  if (tid == 0) {
+    const int prev = atomicAdd(&a.ws_cnt[(size_t)s * a.hkv + kvh], 1);
+    s_last = prev == nparts - 1;
+  }
+  __syncthreads();
+  if (!s_last) return;
+  __threadfence();
+  for (int o = tid; o < G * D; o += kDecThreads) {
+    const int g = o / D;
+    float mx = -INFINITY;
+    for (int p = 0; p < nparts; ++p) mx = fmaxf(mx, a.ws_ml[(item + p) * G + g].x);
+    float l = 0.f, v = 0.f;
+    for (int p = 0; p < nparts; ++p) {
+      const float2 ml = a.ws_ml[(item + p) * G + g];
+      const float w = fast_exp2(ml.x - mx);
+      l = __builtin_fmaf(w, ml.y, l);
+      v = __builtin_fmaf(w, a.ws_acc[(item + p) * G * D + o], v);
+    }
+    store_out(a.out, out_row * D + o, l > 0.f ? v / l : 0.f, a.out_dt);
+  }
+  if (tid == 0) a.ws_cnt[(size_t)s * a.hkv + kvh] = 0;
+}
+
+template <int DT, int D, int G>
+static int launch_decode_t(const DecodeLaunch& L, hipStream_t stream) {
+  DecodeArgs a;
+  a.out = L.out;
+  a.q = L.q;
+  a.kc = L.kc;
+  a.vc = L.vc;
+  a.tables = L.tables;
+  a.ctx_lens = L.ctx_lens;
+  a.ws_acc = L.ws_acc;
+  a.ws_ml = reinterpret_cast<float2*>(L.ws_ml);
+  a.ws_cnt = L.ws_cnt;
+  a.out_dt = L.out_dt;
+  a.max_blocks = L.max_blocks;
+  a.hq = L.num_q_heads;
+  a.hkv = L.num_kv_heads;
+  a.bs = L.block_size;
+  a.log2_bs = ilog2(L.block_size);
+  a.scale_log2 = L.scale * 1.4426950408889634f;
+  a.partition = L.partition;
+  a.max_parts = L.max_parts;
+  hipLaunchKernelGGL((paged_decode_kernel<DT, D, G>), dim3(L.num_kv_heads, L.num_seqs, L.max_parts),
+                     dim3(kDecThreads), 0, stream, a);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+template <int DT, int D>
+static int launch_decode_d(const DecodeLaunch& L, hipStream_t stream) {
+  switch (L.num_q_heads / L.num_kv_heads) {
+    case 1: return launch_decode_t<DT, D, 1>(L, stream);
+    case 2: return launch_decode_t<DT, D, 2>(L, stream);
+    case 4: return launch_decode_t<DT, D, 4>(L, stream);
+    case 8: return launch_decode_t<DT, D, 8>(L, stream);
+  }
+  return -1;
+}
+
+template <int DT>
+static int launch_decode_dt(const DecodeLaunch& L, hipStream_t stream) {
+  if (L.head_dim == 64) return launch_decode_d<DT, 64>(L, stream);
+  if (L.head_dim == 128) return launch_decode_d<DT, 128>(L, stream);
+  return -1;
+}
+
+int launch_decode(const DecodeLaunch& L, hipStream_t stream) {
+  if (L.partition > kMaxPartition || L.partition % 64 != 0) return -1;
+  switch (L.dt) {
+    case DT_F32: return launch_decode_dt<DT_F32>(L, stream);
+    case DT_F16: return launch_decode_dt<DT_F16>(L, stream);
+    case DT_BF16: return launch_decode_dt<DT_BF16>(L, stream);
+  }
+  return -1;
+}
+
+}  // namespace pkv

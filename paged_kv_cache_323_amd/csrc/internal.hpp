@@ -1,0 +1,48 @@
+// Internal launch interface between the C ABI (api.cpp) and the kernel translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pkv {
+
+inline int ilog2(int x) {
+  int r = 0;
+  while ((1 << r) < x) ++r;
+  return r;
+}
+
+// Launchers return 0 on success, -1 if the launch failed.
+int launch_kv_cache_write(const void* k, const void* v, void* kc, void* vc, const int32_t* slots,
+                          int num_tokens, int64_t k_stride_b, int64_t v_stride_b, int num_kv_heads,
+                          int block_size, int head_dim, int elem_bytes, hipStream_t stream);
+
+int launch_copy_blocks(void* kc, void* vc, const int32_t* pairs, int num_pairs, int64_t block_bytes,
+                       hipStream_t stream);
+
+struct DecodeLaunch {
+  void* out;
+  int out_dt;
+  const void* q;
+  const void* kc;
+  const void* vc;
+  const int32_t* tables;
+  int max_blocks;
+  const int32_t* ctx_lens;
+  int num_seqs;
+  int num_q_heads;
+  int num_kv_heads;
+  int block_size;
+  int head_dim;
+  int dt;
+  float scale;
+  int partition;   // tokens per partition
+  int max_parts;   // ceil(max_ctx / partition), >= 1
+  float* ws_acc;   // [S][Hkv][max_parts][G][D]   (only when max_parts > 1)
+  float* ws_ml;    // [S][Hkv][max_parts][G][2]
+  int32_t* ws_cnt; // [S][Hkv]
+};
+
+int launch_decode(const DecodeLaunch& a, hipStream_t stream);
+
+}  // namespace pkv

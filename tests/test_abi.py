@@ -1,0 +1,103 @@
+"""The C ABI: every declared symbol is exported, and host-side validation rejects bad
+arguments with the documented status before anything is launched (CPU only: no call here
+reaches a kernel launch)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pagedkv.h")
+
+pk = pytest.importorskip("paged_kv_cache_323_amd.native")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(pkv_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert len(names) >= 20
+    lib = ctypes.CDLL(pk.LIB_PATH)
+    missing = [n for n in names if not hasattr(lib, n)]
+    assert not missing, missing
+    out = subprocess.run(["nm", "-D", "--defined-only", pk.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r" T (pkv_\w+)", out))
+    assert set(names) <= exported, sorted(set(names) - exported)
+
+
+def test_binding_covers_every_declared_symbol():
+    assert set(declared_functions()) == set(pk.EXPORTED)
+
+
+def desc(**kw):
+    d = dict(num_blocks=64, block_size=16, num_kv_heads=4, head_dim=64, dtype=pk.F16)
+    d.update(kw)
+    return pk.CacheDesc(**d)
+
+
+L = pk._lib
+NULL = None
+
+
+def decode(c, hq=4, out_dt=None, S=2, max_ctx=100, ws=None, wsb=0, part=0, mb=8):
+    return L.pkv_paged_attention_decode_ex(ctypes.c_void_p(1), c.dtype if out_dt is None else out_dt,
+                                           ctypes.c_void_p(1), ctypes.c_void_p(1), ctypes.c_void_p(1),
+                                           ctypes.c_void_p(1), mb, ctypes.c_void_p(1), S, hq, 0.125, max_ctx,
+                                           ctypes.byref(c), part, ws, wsb, NULL)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(block_size=12), -3), (dict(block_size=64), -3), (dict(head_dim=96), -3),
+    (dict(dtype=7), -2), (dict(num_blocks=0), -1),
+])
+def test_decode_rejects_bad_cache(kw, status):
+    assert decode(desc(**kw)) == status
+
+
+def test_decode_rejects_bad_heads_and_dtypes():
+    assert decode(desc(), hq=6) == -3          # 6 % 4
+    assert decode(desc(), hq=64) == -3         # group 16 unsupported
+    assert decode(desc(), out_dt=pk.BF16) == -2  # f16 pool, bf16 out
+    assert decode(desc(), mb=2) == -1          # table cannot hold max_ctx
+
+
+def test_decode_workspace_validation():
+    c = desc()
+    need = L.pkv_decode_workspace_bytes(2, 4, 5000, ctypes.byref(c))
+    assert need > 0
+    assert decode(c, max_ctx=5000, mb=400) == -4
+    assert decode(c, max_ctx=5000, mb=400, ws=ctypes.c_void_p(1), wsb=need - 1) == -4
+    assert L.pkv_decode_workspace_bytes(2, 4, 300, ctypes.byref(c)) == 0  # one partition: none
+    assert decode(c, part=100) == -1      # not a multiple of 64
+    assert decode(c, part=1024) == -1     # too large
+
+
+def test_partition_size_rule():
+    c = desc()
+    assert L.pkv_decode_partition_size(1, 4, 100, ctypes.byref(c)) == 128
+    assert L.pkv_decode_partition_size(1, 4, 5000, ctypes.byref(c)) == 512
+    assert L.pkv_decode_partition_size(1, 4, 0, ctypes.byref(c)) == 64
+
+
+def test_write_and_copy_validation():
+    c = desc()
+    p = ctypes.c_void_p(1)
+    assert L.pkv_kv_cache_write(p, p, p, p, p, 0, 256, 256, ctypes.byref(c), NULL) == 0  # no-op
+    assert L.pkv_kv_cache_write(p, p, p, p, p, 3, 100, 256, ctypes.byref(c), NULL) == -1  # stride < H*D
+    assert L.pkv_kv_cache_write(NULL, p, p, p, p, 3, 256, 256, ctypes.byref(c), NULL) == -1
+    assert L.pkv_kv_cache_write(p, p, p, p, p, 3, 256, 256, ctypes.byref(desc(block_size=5)), NULL) == -3
+    assert L.pkv_copy_blocks(p, p, p, 0, ctypes.byref(c), NULL) == 0
+    assert L.pkv_copy_blocks(p, p, p, -1, ctypes.byref(c), NULL) == -1
+    assert L.pkv_copy_blocks(NULL, p, p, 2, ctypes.byref(c), NULL) == -1
+
+
+def test_status_strings():
+    for s in range(-8, 1):
+        assert L.pkv_status_str(s)
+    assert b"gfx950" in L.pkv_version()

@@ -13,6 +13,7 @@ from .synth import (  # noqa: F401
     ForkOp,
     FreeOp,
     make_workload,
+    make_decode_workload,
     CONFIG_NAMES,
     gen_kv,
     gen_q,

@@ -195,6 +195,20 @@ def _decode_script(seqs: List[int], ctx: List[int]) -> List[Op]:
     return ops
 
 
+def make_decode_workload(seed: int, ctx: List[int], hq: int, hkv: int, head_dim: int, dtype: str,
+                         block_size: int, slack: float = 1.5, name: str = "decode") -> Workload:
+    """A generic decode step: ctx-1 cached tokens per sequence, then the current one."""
+    need = sum(-(-c // block_size) if c > 0 else 0 for c in ctx)
+    nb = max(1, _pool_size(need, slack))
+    perm = _rng(seed, _S_PERM).permutation(nb).astype(np.int32)
+    seqs = list(range(len(ctx)))
+    ops: List[Op] = [AddOp(s) for s in seqs]
+    ops.append(AppendOp(list(seqs), [max(c - 1, 0) for c in ctx], tag=0))
+    ops.append(AppendOp(list(seqs), [1 if c > 0 else 0 for c in ctx], tag=1))
+    return Workload(name, seed, dtype, block_size, hq, hkv, head_dim, nb, perm, ops, seqs, [1] * len(ctx),
+                    list(ctx))
+
+
 def make_workload(name: str, size: str = "full", block_size: Optional[int] = None,
                   slack: float = 1.5) -> Workload:
     if size not in ("full", "small"):
