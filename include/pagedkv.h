@@ -105,12 +105,11 @@ int32_t pkv_copy_blocks(void* k_cache, void* v_cache, const int32_t* block_pairs
                         int32_t num_pairs, const pkv_cache_desc* cache, void* stream);
 
 /*
- * Workspace of the decode attention: partial results of the split-context path and
- * one completion counter per (sequence, kv head).
- *   Returns the bytes needed for these arguments (0 on invalid arguments).
- *   The workspace must be zero-filled once after allocation; every call leaves the counter
- *   region zero again, so one workspace serves any later call that fits it. Calls that share
- *   a workspace must not run concurrently.
+ * Workspace of the decode attention: per-partition partial results (running max, sum and
+ * unnormalised output, fp32) of sequences whose context spans more than one partition.
+ *   Returns the bytes needed for these arguments; 0 means no workspace is needed (every context
+ *   fits one partition) or the arguments are invalid. The contents need no initialisation and
+ *   are scratch between calls; calls that share a workspace must not run concurrently.
  */
 size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t max_context_len,
                                   const pkv_cache_desc* cache);
@@ -134,7 +133,7 @@ int32_t pkv_decode_partition_size(int32_t num_seqs, int32_t num_q_heads, int32_t
  *                 <= max_blocks_per_seq * B. A length of 0 gives an all-zero output row.
  *   max_context_len  host upper bound of context_lens (sizes the split; not a limit check).
  *   scale         multiplier of q·k (1/sqrt(D) for standard attention).
- *   workspace     device, >= pkv_decode_workspace_bytes(...) bytes, zeroed once (see above).
+ *   workspace     device, >= pkv_decode_workspace_bytes(...) bytes (may be NULL when that is 0).
  *   Long contexts are cut into partitions that are processed independently and merged with
  *   log-sum-exp weights; the result does not depend on which physical blocks hold the data.
  */
@@ -147,7 +146,7 @@ int32_t pkv_paged_attention_decode(void* out, int32_t out_dtype, const void* q,
                                    size_t workspace_bytes, void* stream);
 
 /* As pkv_paged_attention_decode with an explicit partition size in tokens (0 = automatic;
- * otherwise a multiple of 64 and of the block size, at most 1024). The workspace must then be
+ * otherwise a multiple of 64 and of the block size, at most 512). The workspace must then be
  * sized with pkv_decode_workspace_bytes_ex. */
 int32_t pkv_paged_attention_decode_ex(void* out, int32_t out_dtype, const void* q,
                                       const void* k_cache, const void* v_cache,
@@ -156,6 +155,28 @@ int32_t pkv_paged_attention_decode_ex(void* out, int32_t out_dtype, const void* 
                                       int32_t num_q_heads, float scale, int32_t max_context_len,
                                       const pkv_cache_desc* cache, int32_t partition_size,
                                       void* workspace, size_t workspace_bytes, void* stream);
+
+/* The two launches of pkv_paged_attention_decode_ex, for callers that time or schedule them
+ * separately. _partitions processes every (kv head, sequence, partition): sequences whose
+ * context fits one partition get their final output rows, the others leave partial results in
+ * the workspace. _merge then combines those partials with log-sum-exp weights into their output
+ * rows (it launches nothing when no context spans two partitions). Issued in that order on one
+ * stream with identical arguments they equal one call of pkv_paged_attention_decode_ex. */
+int32_t pkv_paged_attention_decode_partitions(void* out, int32_t out_dtype, const void* q,
+                                              const void* k_cache, const void* v_cache,
+                                              const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                              const int32_t* context_lens, int32_t num_seqs,
+                                              int32_t num_q_heads, float scale,
+                                              int32_t max_context_len, const pkv_cache_desc* cache,
+                                              int32_t partition_size, void* workspace,
+                                              size_t workspace_bytes, void* stream);
+int32_t pkv_paged_attention_decode_merge(void* out, int32_t out_dtype, const void* q,
+                                         const void* k_cache, const void* v_cache,
+                                         const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                         const int32_t* context_lens, int32_t num_seqs,
+                                         int32_t num_q_heads, float scale, int32_t max_context_len,
+                                         const pkv_cache_desc* cache, int32_t partition_size,
+                                         void* workspace, size_t workspace_bytes, void* stream);
 
 size_t pkv_decode_workspace_bytes_ex(int32_t num_seqs, int32_t num_q_heads,
                                      int32_t max_context_len, const pkv_cache_desc* cache,
@@ -175,8 +196,8 @@ size_t pkv_decode_workspace_bytes_ex(int32_t num_seqs, int32_t num_q_heads,
  *                 cu[num_seqs] = num_tokens.
  *   context_lens  device int32 [num_seqs], context_lens[s] >= q_len_s.
  *   max_q_len, max_context_len  host upper bounds (launch sizing only).
- *   workspace     device, >= pkv_ragged_workspace_bytes(...) bytes, zeroed once; shared
- *                 rules as for decode.
+ *   workspace     device, >= pkv_ragged_workspace_bytes(...) bytes (NULL when that is 0);
+ *                 scratch between calls, as for decode.
  */
 size_t pkv_ragged_workspace_bytes(int32_t num_seqs, int32_t num_tokens, int32_t num_q_heads,
                                   int32_t max_q_len, int32_t max_context_len,

@@ -47,18 +47,17 @@ int auto_partition(int32_t max_ctx) {
 bool valid_partition(int p, int bs) { return p >= 64 && p <= 512 && p % 64 == 0 && p % bs == 0; }
 
 struct DecodeWs {
-  size_t acc, ml, cnt, total;
+  size_t acc, ml, total;
 };
 
 DecodeWs decode_ws_layout(int32_t S, int32_t hq, int32_t hkv, int32_t head_dim, int max_parts) {
-  DecodeWs w{0, 0, 0, 0};
+  DecodeWs w{0, 0, 0};
   if (max_parts <= 1) return w;
   const size_t items = (size_t)S * hkv * max_parts;
   const int g = hq / hkv;
   w.acc = 0;
   w.ml = align_up(items * g * head_dim * sizeof(float));
-  w.cnt = w.ml + align_up(items * g * 2 * sizeof(float));
-  w.total = w.cnt + align_up((size_t)S * hkv * sizeof(int32_t));
+  w.total = w.ml + align_up(items * g * 2 * sizeof(float));
   return w;
 }
 
@@ -139,13 +138,11 @@ size_t pkv_decode_workspace_bytes(int32_t S, int32_t hq, int32_t max_ctx, const 
   return pkv_decode_workspace_bytes_ex(S, hq, max_ctx, c, 0);
 }
 
-int32_t pkv_paged_attention_decode_ex(void* out, int32_t out_dtype, const void* q, const void* k_cache,
-                                      const void* v_cache, const int32_t* block_tables,
-                                      int32_t max_blocks_per_seq, const int32_t* context_lens,
-                                      int32_t num_seqs, int32_t num_q_heads, float scale,
-                                      int32_t max_context_len, const pkv_cache_desc* c,
-                                      int32_t partition_size, void* workspace, size_t workspace_bytes,
-                                      void* stream) {
+static int32_t decode_common(void* out, int32_t out_dtype, const void* q, const void* k_cache,
+                             const void* v_cache, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                             const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads, float scale,
+                             int32_t max_context_len, const pkv_cache_desc* c, int32_t partition_size,
+                             void* workspace, size_t workspace_bytes, void* stream, int stage) {
   int32_t st = check_cache(c);
   if (st != PKV_OK) return st;
   if ((st = check_heads(num_q_heads, c)) != PKV_OK) return st;
@@ -185,8 +182,44 @@ int32_t pkv_paged_attention_decode_ex(void* out, int32_t out_dtype, const void* 
   char* wb = static_cast<char*>(workspace);
   L.ws_acc = ws.total ? reinterpret_cast<float*>(wb + ws.acc) : nullptr;
   L.ws_ml = ws.total ? reinterpret_cast<float*>(wb + ws.ml) : nullptr;
-  L.ws_cnt = ws.total ? reinterpret_cast<int32_t*>(wb + ws.cnt) : nullptr;
+  L.stage = stage;
   return pkv::launch_decode(L, (hipStream_t)stream) == 0 ? PKV_OK : PKV_ELAUNCH;
+}
+
+int32_t pkv_paged_attention_decode_ex(void* out, int32_t out_dtype, const void* q, const void* k_cache,
+                                      const void* v_cache, const int32_t* block_tables,
+                                      int32_t max_blocks_per_seq, const int32_t* context_lens,
+                                      int32_t num_seqs, int32_t num_q_heads, float scale,
+                                      int32_t max_context_len, const pkv_cache_desc* c,
+                                      int32_t partition_size, void* workspace, size_t workspace_bytes,
+                                      void* stream) {
+  return decode_common(out, out_dtype, q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens,
+                       num_seqs, num_q_heads, scale, max_context_len, c, partition_size, workspace,
+                       workspace_bytes, stream, 0);
+}
+
+int32_t pkv_paged_attention_decode_partitions(void* out, int32_t out_dtype, const void* q, const void* k_cache,
+                                              const void* v_cache, const int32_t* block_tables,
+                                              int32_t max_blocks_per_seq, const int32_t* context_lens,
+                                              int32_t num_seqs, int32_t num_q_heads, float scale,
+                                              int32_t max_context_len, const pkv_cache_desc* c,
+                                              int32_t partition_size, void* workspace, size_t workspace_bytes,
+                                              void* stream) {
+  return decode_common(out, out_dtype, q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens,
+                       num_seqs, num_q_heads, scale, max_context_len, c, partition_size, workspace,
+                       workspace_bytes, stream, 1);
+}
+
+int32_t pkv_paged_attention_decode_merge(void* out, int32_t out_dtype, const void* q, const void* k_cache,
+                                         const void* v_cache, const int32_t* block_tables,
+                                         int32_t max_blocks_per_seq, const int32_t* context_lens,
+                                         int32_t num_seqs, int32_t num_q_heads, float scale,
+                                         int32_t max_context_len, const pkv_cache_desc* c,
+                                         int32_t partition_size, void* workspace, size_t workspace_bytes,
+                                         void* stream) {
+  return decode_common(out, out_dtype, q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens,
+                       num_seqs, num_q_heads, scale, max_context_len, c, partition_size, workspace,
+                       workspace_bytes, stream, 2);
 }
 
 int32_t pkv_paged_attention_decode(void* out, int32_t out_dtype, const void* q, const void* k_cache,
@@ -195,9 +228,8 @@ int32_t pkv_paged_attention_decode(void* out, int32_t out_dtype, const void* q, 
                                    int32_t num_q_heads, float scale, int32_t max_context_len,
                                    const pkv_cache_desc* c, void* workspace, size_t workspace_bytes,
                                    void* stream) {
-  return pkv_paged_attention_decode_ex(out, out_dtype, q, k_cache, v_cache, block_tables, max_blocks_per_seq,
-                                       context_lens, num_seqs, num_q_heads, scale, max_context_len, c, 0,
-                                       workspace, workspace_bytes, stream);
+  return decode_common(out, out_dtype, q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens,
+                       num_seqs, num_q_heads, scale, max_context_len, c, 0, workspace, workspace_bytes, stream, 0);
 }
 
 }  // extern "C"

@@ -3,7 +3,8 @@
 // One workgroup (4 waves) per (kv head, sequence, context partition). The g = Hq/Hkv query
 // heads that share a kv head are served by the same workgroup, so every K/V tile is read from
 // HBM once per step. The partition's tokens are walked through the block table in units of 8
-// tokens (units never straddle a block, since B is a multiple of 8):
+// tokens (units never straddle a block, since B is a multiple of 8); unit u belongs to wave
+// u mod 4, and each wave keeps PF units of loads in flight:
 //
 //   phase 1  scores: 8 lanes per token, each lane owns interleaved 16-byte chunks of the row;
 //            packed dot2 (bf16/f16) or fma (f32) against the query slices held in registers;
@@ -14,11 +15,13 @@
 //   merge    lane groups and waves are summed through LDS.
 //
 // A sequence whose context fits one partition writes its normalised output directly. Longer
-// contexts write (max, sum, unnormalised output) per partition to the workspace; the last
-// workgroup of a (sequence, kv head) to finish merges them with log-sum-exp weights and resets
-// the completion counter. Any grouping of blocks gives the same softmax, which is what makes
-// the partitioning exact: the block-wise attention equation of 「PagedAttention原理」
-// §实现一个虚拟内存 sums exponentials block by block against one common denominator.
+// contexts write (max, sum, unnormalised output) per partition to the workspace, and a second
+// small kernel merges them with log-sum-exp weights. Any grouping of blocks gives the same
+// softmax, which is what makes the partitioning exact: the block-wise attention equation of
+// 「PagedAttention原理」 §实现一个虚拟内存 sums exponentials block by block against one common
+// denominator. The merge runs as its own launch so that no workgroup has to publish data to
+// another one inside a kernel (a device-scope fence per workgroup costs a full L2 write-back
+// and invalidate on this chip).
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -37,7 +40,6 @@ struct DecodeArgs {
   const int32_t* ctx_lens;
   float* ws_acc;
   float2* ws_ml;
-  int32_t* ws_cnt;
   int out_dt;
   int max_blocks;
   int hq;
@@ -77,7 +79,7 @@ template <int DT, int NWORDS, int EPL> __device__ __forceinline__ void words_to_
   }
 }
 
-template <int DT, int D, int G>
+template <int DT, int D, int G, int PF>
 __global__ __launch_bounds__(kDecThreads) void paged_decode_kernel(DecodeArgs a) {
   using T = typename Elem<DT>::T;
   constexpr int ES = sizeof(T);
@@ -88,11 +90,11 @@ __global__ __launch_bounds__(kDecThreads) void paged_decode_kernel(DecodeArgs a)
   static_assert(NCH >= 1 && EPL * ES % 8 == 0, "unsupported head dim");
 
   __shared__ int32_t s_tab[kMaxPartition / 8];
-  __shared__ float s_p[kMaxPartition * G];  // [token][head]: scaled scores, then probabilities
+  __shared__ float s_p[kMaxPartition * G + kWave];  // [token][head]: scaled scores, then probabilities;
+                                                    // the tail absorbs discarded writes
   __shared__ float s_red[kDecWaves * G * D];
   __shared__ float s_m[G];
   __shared__ float s_l[G];
-  __shared__ int s_last;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -107,6 +109,7 @@ __global__ __launch_bounds__(kDecThreads) void paged_decode_kernel(DecodeArgs a)
   const int t0 = part * a.partition;
   const int n = min(a.partition, ctx - t0);  // tokens of this partition (0 iff ctx == 0)
   const int nunits = (n + 7) >> 3;
+  const int nw = nunits > wave ? (nunits - wave + kDecWaves - 1) / kDecWaves : 0;  // this wave's units
 
   // Block-table entries of this partition (the partition starts on a block boundary).
   const int nblk = (n + a.bs - 1) >> a.log2_bs;
@@ -124,49 +127,67 @@ __global__ __launch_bounds__(kDecThreads) void paged_decode_kernel(DecodeArgs a)
     for (int ch = 0; ch < NCH; ++ch) qr[g][ch] = *reinterpret_cast<const u32x4*>(qb + g * D + ch * 8 * VEC);
   __syncthreads();
 
-  const size_t head_off = (size_t)kvh * a.bs;  // in rows
+  // Base of the (physical block, kv head) tile holding unit u; units never straddle blocks.
+  const size_t tile_rows = (size_t)a.hkv * a.bs;
+  const size_t head_rows = (size_t)kvh * a.bs;
+  auto tile = [&](const T* base, int u) -> const T* {
+    const int phys = s_tab[(u * 8) >> a.log2_bs];
+    return base + ((size_t)phys * tile_rows + head_rows) * D;
+  };
   const T* kbase = static_cast<const T*>(a.kc);
   const T* vbase = static_cast<const T*>(a.vc);
+  const int krow = r;                      // row offset of this lane within a unit
+  const int cv = lane & 15;                // value mapping: column slice
+  const int rv = lane >> 4;                // value mapping: token row within a pass of 4
 
-  // ---- phase 1: scores ----------------------------------------------------------------------
-  {
-    u32x4 kr[NCH];
-    int u = wave;
-    if (u < nunits) {
-      const int phys = s_tab[(u * 8) >> a.log2_bs];
-      const T* p = kbase + (((size_t)phys * a.hkv * a.bs + head_off + ((u * 8 + r) & (a.bs - 1))) * D) + c * VEC;
+  auto load_k = [&](int u, u32x4 (&dst)[NCH]) {
+    const T* p = tile(kbase, u) + (size_t)((u * 8 + krow) & (a.bs - 1)) * D + c * VEC;
 #pragma unroll
-      for (int ch = 0; ch < NCH; ++ch) kr[ch] = *reinterpret_cast<const u32x4*>(p + ch * 8 * VEC);
-    }
-    for (; u < nunits; u += kDecWaves) {
-      const int un = u + kDecWaves;
-      u32x4 kn[NCH];
-      if (un < nunits) {
-        const int phys = s_tab[(un * 8) >> a.log2_bs];
-        const T* p = kbase + (((size_t)phys * a.hkv * a.bs + head_off + ((un * 8 + r) & (a.bs - 1))) * D) + c * VEC;
+    for (int ch = 0; ch < NCH; ++ch) dst[ch] = *reinterpret_cast<const u32x4*>(p + ch * 8 * VEC);
+  };
+  auto load_v = [&](int u, Words<NWORDS> (&dst)[2]) {
+    const T* p = tile(vbase, u) + cv * EPL;
 #pragma unroll
-        for (int ch = 0; ch < NCH; ++ch) kn[ch] = *reinterpret_cast<const u32x4*>(p + ch * 8 * VEC);
-      }
-      float sc[G];
+    for (int ps = 0; ps < 2; ++ps) dst[ps] = load_words<NWORDS>(p + (size_t)((u * 8 + ps * 4 + rv) & (a.bs - 1)) * D);
+  };
+
+  // ---- phase 1: scores, PF units in flight per wave ---------------------------------------------
+  // Loads are unconditional (indices past the wave's last unit are clamped to it) so the wait
+  // counts inside the unrolled ring are static; results of padding iterations are discarded.
+  const int last = wave + kDecWaves * (nw > 0 ? nw - 1 : 0);
+  auto unit_of = [&](int i) { return min(wave + kDecWaves * i, last); };
+  const int nw_pad = (nw + PF - 1) / PF * PF;
+  Words<NWORDS> vb[PF][2];
+  if (nw > 0) {
+    u32x4 kb[PF][NCH];
 #pragma unroll
-      for (int g = 0; g < G; ++g) {
-        float acc = 0.f;
+    for (int j = 0; j < PF; ++j) load_k(unit_of(j), kb[j]);
+    for (int i0 = 0; i0 < nw_pad; i0 += PF) {
 #pragma unroll
-        for (int ch = 0; ch < NCH; ++ch) acc = dot16B<DT>(qr[g][ch], kr[ch], acc);
-        sc[g] = sum8(acc);
-      }
-      const int tl = u * 8 + r;
-      if (c < G) {
+      for (int j = 0; j < PF; ++j) {
+        const int i = i0 + j;
+        const int u = unit_of(i);
+        float sc[G];
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          float acc = 0.f;
+#pragma unroll
+          for (int ch = 0; ch < NCH; ++ch) acc = dot16B<DT>(qr[g][ch], kb[j][ch], acc);
+          sc[g] = sum8(acc);
+        }
+        load_k(unit_of(i + PF), kb[j]);
+        const int tl = u * 8 + r;
         float mine = sc[0];
 #pragma unroll
         for (int g = 1; g < G; ++g) mine = (c == g) ? sc[g] : mine;
-        s_p[tl * G + c] = tl < n ? mine * a.scale_log2 : -INFINITY;
-      }
-      if (un < nunits) {
-#pragma unroll
-        for (int ch = 0; ch < NCH; ++ch) kr[ch] = kn[ch];
+        // Branch-free store: lanes with nothing to keep write into the discard tail.
+        const int dst = (c < G && i < nw) ? tl * G + c : kMaxPartition * G + lane;
+        s_p[dst] = tl < n ? mine * a.scale_log2 : -INFINITY;
       }
     }
+    // Value loads of the first units go out before the softmax so they overlap it.
+#pragma unroll
+    for (int j = 0; j < PF; ++j) load_v(unit_of(j), vb[j]);
   }
   __syncthreads();
 
@@ -189,51 +210,36 @@ __global__ __launch_bounds__(kDecThreads) void paged_decode_kernel(DecodeArgs a)
   }
   __syncthreads();
 
-  // ---- phase 2: probability-weighted values ----------------------------------------------------
-  const int cv = lane & 15;  // column slice
-  const int rv = lane >> 4;  // token row within a pass of 4
+  // ---- phase 2: probability-weighted values, PF units in flight per wave ----------------------
   float acc[G][EPL];
 #pragma unroll
   for (int g = 0; g < G; ++g)
 #pragma unroll
     for (int e = 0; e < EPL; ++e) acc[g][e] = 0.f;
-  {
-    Words<NWORDS> vr[2];
-    int u = wave;
-    if (u < nunits) {
-      const int phys = s_tab[(u * 8) >> a.log2_bs];
-      const T* p = vbase + ((size_t)phys * a.hkv * a.bs + head_off) * D + cv * EPL;
+  if (nw > 0) {
+    for (int i0 = 0; i0 < nw_pad; i0 += PF) {
 #pragma unroll
-      for (int ps = 0; ps < 2; ++ps) vr[ps] = load_words<NWORDS>(p + (size_t)(((u * 8 + ps * 4 + rv) & (a.bs - 1)) * D));
-    }
-    for (; u < nunits; u += kDecWaves) {
-      const int un = u + kDecWaves;
-      Words<NWORDS> vn[2];
-      if (un < nunits) {
-        const int phys = s_tab[(un * 8) >> a.log2_bs];
-        const T* p = vbase + ((size_t)phys * a.hkv * a.bs + head_off) * D + cv * EPL;
+      for (int j = 0; j < PF; ++j) {
+        const int i = i0 + j;
+        const int u = unit_of(i);
+        float vf[2][EPL];
+        words_to_f32<DT, NWORDS, EPL>(vb[j][0], vf[0]);
+        words_to_f32<DT, NWORDS, EPL>(vb[j][1], vf[1]);
+        load_v(unit_of(i + PF), vb[j]);
 #pragma unroll
-        for (int ps = 0; ps < 2; ++ps) vn[ps] = load_words<NWORDS>(p + (size_t)(((un * 8 + ps * 4 + rv) & (a.bs - 1)) * D));
-      }
+        for (int ps = 0; ps < 2; ++ps) {
+          const int tl = u * 8 + ps * 4 + rv;
+          const bool valid = i < nw && tl < n;
+          float pg[G];
 #pragma unroll
-      for (int ps = 0; ps < 2; ++ps) {
-        const int tl = u * 8 + ps * 4 + rv;
-        const bool valid = tl < n;
-        float vf[EPL];
-        words_to_f32<DT, NWORDS, EPL>(vr[ps], vf);
-        float pg[G];
+          for (int g = 0; g < G; ++g) pg[g] = s_p[tl * G + g];  // 0 past the context
 #pragma unroll
-        for (int g = 0; g < G; ++g) pg[g] = s_p[tl * G + g];  // 0 past the context
+          for (int e = 0; e < EPL; ++e) {
+            const float x = valid ? vf[ps][e] : 0.f;  // unwritten slots may hold anything
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) {
-          const float x = valid ? vf[e] : 0.f;  // unwritten slots may hold anything
-#pragma unroll
-          for (int g = 0; g < G; ++g) acc[g][e] = __builtin_fmaf(pg[g], x, acc[g][e]);
+            for (int g = 0; g < G; ++g) acc[g][e] = __builtin_fmaf(pg[g], x, acc[g][e]);
+          }
         }
-      }
-      if (un < nunits) {
-        vr[0] = vn[0];
-        vr[1] = vn[1];
       }
     }
   }
@@ -257,7 +263,7 @@ __global__ __launch_bounds__(kDecThreads) void paged_decode_kernel(DecodeArgs a)
   __syncthreads();
 
   const size_t out_row = (size_t)s * a.hq + (size_t)kvh * G;  // first of the G query heads
-  const size_t item = ((size_t)s * a.hkv + kvh) * a.max_parts;
+  const size_t item = ((size_t)s * a.hkv + kvh) * a.max_parts + part;
   for (int o = tid; o < G * D; o += kDecThreads) {
     float v = 0.f;
 #pragma unroll
@@ -267,40 +273,39 @@ __global__ __launch_bounds__(kDecThreads) void paged_decode_kernel(DecodeArgs a)
       const float l = s_l[g];
       store_out(a.out, out_row * D + o, l > 0.f ? v / l : 0.f, a.out_dt);
     } else {
-      a.ws_acc[(item + part) * G * D + o] = v;
-      if (o % D == 0) a.ws_ml[(item + part) * G + g] = make_float2(s_m[g], s_l[g]);
+      a.ws_acc[item * G * D + o] = v;
+      if (o % D == 0) a.ws_ml[item * G + g] = make_float2(s_m[g], s_l[g]);
     }
   }
-  if (nparts == 1) return;
-
-  // ---- split context: the last partition to finish merges all of them --------------------------
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) {
-    const int prev = atomicAdd(&a.ws_cnt[(size_t)s * a.hkv + kvh], 1);
-    s_last = prev == nparts - 1;
-  }
-  __syncthreads();
-  if (!s_last) return;
-  __threadfence();
-  for (int o = tid; o < G * D; o += kDecThreads) {
-    const int g = o / D;
-    float mx = -INFINITY;
-    for (int p = 0; p < nparts; ++p) mx = fmaxf(mx, a.ws_ml[(item + p) * G + g].x);
-    float l = 0.f, v = 0.f;
-    for (int p = 0; p < nparts; ++p) {
-      const float2 ml = a.ws_ml[(item + p) * G + g];
-      const float w = fast_exp2(ml.x - mx);
-      l = __builtin_fmaf(w, ml.y, l);
-      v = __builtin_fmaf(w, a.ws_acc[(item + p) * G * D + o], v);
-    }
-    store_out(a.out, out_row * D + o, l > 0.f ? v / l : 0.f, a.out_dt);
-  }
-  if (tid == 0) a.ws_cnt[(size_t)s * a.hkv + kvh] = 0;
 }
 
-template <int DT, int D, int G>
-static int launch_decode_t(const DecodeLaunch& L, hipStream_t stream) {
+// Log-sum-exp merge of the partitions of every multi-partition sequence: one thread per output
+// element; single-partition sequences were finished by the partition kernel.
+__global__ __launch_bounds__(256) void paged_decode_merge_kernel(DecodeArgs a, int head_dim, int group) {
+  const int s = blockIdx.y;
+  const int o = blockIdx.x * 256 + threadIdx.x;
+  if (o >= a.hq * head_dim) return;
+  const int ctx = a.ctx_lens[s];
+  const int nparts = ctx > 0 ? (ctx + a.partition - 1) / a.partition : 1;
+  if (nparts <= 1) return;
+  const int h = o / head_dim;
+  const int kvh = h / group;
+  const int g = h - kvh * group;
+  const int d = o - h * head_dim;
+  const size_t item = ((size_t)s * a.hkv + kvh) * a.max_parts;
+  float mx = -INFINITY;
+  for (int p = 0; p < nparts; ++p) mx = fmaxf(mx, a.ws_ml[(item + p) * group + g].x);
+  float l = 0.f, v = 0.f;
+  for (int p = 0; p < nparts; ++p) {
+    const float2 ml = a.ws_ml[(item + p) * group + g];
+    const float w = fast_exp2(ml.x - mx);
+    l = __builtin_fmaf(w, ml.y, l);
+    v = __builtin_fmaf(w, a.ws_acc[((item + p) * group + g) * head_dim + d], v);
+  }
+  store_out(a.out, (size_t)s * a.hq * head_dim + o, l > 0.f ? v / l : 0.f, a.out_dt);
+}
+
+static DecodeArgs make_args(const DecodeLaunch& L) {
   DecodeArgs a;
   a.out = L.out;
   a.q = L.q;
@@ -310,7 +315,6 @@ static int launch_decode_t(const DecodeLaunch& L, hipStream_t stream) {
   a.ctx_lens = L.ctx_lens;
   a.ws_acc = L.ws_acc;
   a.ws_ml = reinterpret_cast<float2*>(L.ws_ml);
-  a.ws_cnt = L.ws_cnt;
   a.out_dt = L.out_dt;
   a.max_blocks = L.max_blocks;
   a.hq = L.num_q_heads;
@@ -320,9 +324,26 @@ static int launch_decode_t(const DecodeLaunch& L, hipStream_t stream) {
   a.scale_log2 = L.scale * 1.4426950408889634f;
   a.partition = L.partition;
   a.max_parts = L.max_parts;
-  hipLaunchKernelGGL((paged_decode_kernel<DT, D, G>), dim3(L.num_kv_heads, L.num_seqs, L.max_parts),
-                     dim3(kDecThreads), 0, stream, a);
-  return hipGetLastError() == hipSuccess ? 0 : -1;
+  return a;
+}
+
+constexpr int kPrefetch = 3;
+
+template <int DT, int D, int G>
+static int launch_decode_t(const DecodeLaunch& L, hipStream_t stream) {
+  const DecodeArgs a = make_args(L);
+  if (L.stage != 2) {
+    hipLaunchKernelGGL((paged_decode_kernel<DT, D, G, kPrefetch>), dim3(L.num_kv_heads, L.num_seqs, L.max_parts),
+                       dim3(kDecThreads), 0, stream, a);
+    if (hipGetLastError() != hipSuccess) return -1;
+  }
+  if (L.stage != 1 && L.max_parts > 1) {
+    const int outs = L.num_q_heads * D;
+    hipLaunchKernelGGL(paged_decode_merge_kernel, dim3((outs + 255) / 256, L.num_seqs), dim3(256), 0, stream, a, D,
+                       G);
+    if (hipGetLastError() != hipSuccess) return -1;
+  }
+  return 0;
 }
 
 template <int DT, int D>

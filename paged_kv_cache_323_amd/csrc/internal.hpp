@@ -40,7 +40,7 @@ struct DecodeLaunch {
   int max_parts;   // ceil(max_ctx / partition), >= 1
   float* ws_acc;   // [S][Hkv][max_parts][G][D]   (only when max_parts > 1)
   float* ws_ml;    // [S][Hkv][max_parts][G][2]
-  int32_t* ws_cnt; // [S][Hkv]
+  int stage;       // 0: partitions then merge; 1: partitions only; 2: merge only
 };
 
 int launch_decode(const DecodeLaunch& a, hipStream_t stream);

@@ -69,6 +69,10 @@ _SIGS = {
                                           _I32, _DESC, _P, _SZ, _P]),
     "pkv_paged_attention_decode_ex": (_I32, [_P, _I32, _P, _P, _P, _P, _I32, _P, _I32, _I32, ctypes.c_float,
                                              _I32, _DESC, _I32, _P, _SZ, _P]),
+    "pkv_paged_attention_decode_partitions": (_I32, [_P, _I32, _P, _P, _P, _P, _I32, _P, _I32, _I32,
+                                                     ctypes.c_float, _I32, _DESC, _I32, _P, _SZ, _P]),
+    "pkv_paged_attention_decode_merge": (_I32, [_P, _I32, _P, _P, _P, _P, _I32, _P, _I32, _I32, ctypes.c_float,
+                                                _I32, _DESC, _I32, _P, _SZ, _P]),
     "pkv_ragged_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32, _I32, _DESC]),
     "pkv_paged_attention_ragged": (_I32, [_P, _I32, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32,
                                           ctypes.c_float, _I32, _I32, _DESC, _P, _SZ, _P]),
@@ -177,22 +181,29 @@ def decode_partition_size(num_seqs: int, num_q_heads: int, max_context_len: int,
     return int(_lib.pkv_decode_partition_size(num_seqs, num_q_heads, max_context_len, ctypes.byref(desc)))
 
 
+_DECODE_STAGES = {"all": "pkv_paged_attention_decode_ex", "partitions": "pkv_paged_attention_decode_partitions",
+                  "merge": "pkv_paged_attention_decode_merge"}
+
+
 def paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_lens, scale: float,
                            max_context_len: int, desc: CacheDesc, workspace=None, partition_size: int = 0,
-                           stream=None) -> None:
-    """out[s, h] = attention of q[s, h] over sequence s's cached tokens (see include/pagedkv.h)."""
+                           stream=None, stage: str = "all") -> None:
+    """out[s, h] = attention of q[s, h] over sequence s's cached tokens (see include/pagedkv.h).
+
+    ``stage`` selects both launches ("all"), or only the partition or merge launch.
+    """
     torch = _torch()
     S, hq, d = q.shape
     if out.shape != q.shape or block_tables.dim() != 2 or block_tables.shape[0] != S:
         raise ValueError("shape mismatch")
     ws = _dev(workspace, "workspace") if workspace is not None else None
     wsb = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    st = _lib.pkv_paged_attention_decode_ex(
-        _dev(out, "out"), _tdtype_code(out), _dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
-        _dev(block_tables, "block_tables", torch.int32), int(block_tables.shape[1]),
-        _dev(context_lens, "context_lens", torch.int32), S, hq, float(scale), int(max_context_len),
-        ctypes.byref(desc), int(partition_size), ws, wsb, _stream(stream))
-    _check(st, "paged_attention_decode")
+    fn = getattr(_lib, _DECODE_STAGES[stage])
+    st = fn(_dev(out, "out"), _tdtype_code(out), _dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
+            _dev(block_tables, "block_tables", torch.int32), int(block_tables.shape[1]),
+            _dev(context_lens, "context_lens", torch.int32), S, hq, float(scale), int(max_context_len),
+            ctypes.byref(desc), int(partition_size), ws, wsb, _stream(stream))
+    _check(st, f"paged_attention_decode[{stage}]")
 
 
 def ragged_workspace_bytes(num_seqs: int, num_tokens: int, num_q_heads: int, max_q_len: int,
