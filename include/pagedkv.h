@@ -146,7 +146,7 @@ int32_t pkv_paged_attention_decode(void* out, int32_t out_dtype, const void* q,
                                    size_t workspace_bytes, void* stream);
 
 /* As pkv_paged_attention_decode with an explicit partition size in tokens (0 = automatic;
- * otherwise a multiple of 64 and of the block size, at most 512). The workspace must then be
+ * otherwise a multiple of 64 and of the block size, at most 1024). The workspace must then be
  * sized with pkv_decode_workspace_bytes_ex. */
 int32_t pkv_paged_attention_decode_ex(void* out, int32_t out_dtype, const void* q,
                                       const void* k_cache, const void* v_cache,

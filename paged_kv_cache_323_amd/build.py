@@ -45,30 +45,32 @@ def _run(cmd):
     return out
 
 
-def build(verbose: bool = False, jobs: int = 8) -> str:
+def build(verbose: bool = False, jobs: int = 8, defines=(), out: str = LIB, build_dir: str = BUILD) -> str:
+    """Compile and link; ``defines`` are extra -D macros (kernel tuning knobs)."""
     if not os.path.exists(HIPCC):
         raise RuntimeError(f"hipcc not found at {HIPCC}")
-    os.makedirs(BUILD, exist_ok=True)
+    os.makedirs(build_dir, exist_ok=True)
+    dflags = [f"-D{d}" for d in defines]
     jobs_list = []
     objs = []
     for src in _hip_sources():
-        obj = os.path.join(BUILD, os.path.basename(src) + ".o")
+        obj = os.path.join(build_dir, os.path.basename(src) + ".o")
         extra = ["-x", "hip"] if src.endswith(".cpp") else []
-        jobs_list.append([HIPCC, *HIP_FLAGS, *extra, "-c", src, "-o", obj])
+        jobs_list.append([HIPCC, *HIP_FLAGS, *dflags, *extra, "-c", src, "-o", obj])
         objs.append(obj)
     bm_src = os.path.join(CSRC, "block_manager.cpp")
-    bm_obj = os.path.join(BUILD, "block_manager.cpp.o")
+    bm_obj = os.path.join(build_dir, "block_manager.cpp.o")
     cxx = shutil.which("g++") or "c++"
     jobs_list.append([cxx, *HOST_FLAGS, "-c", bm_src, "-o", bm_obj])
     objs.append(bm_obj)
     with ThreadPoolExecutor(max(1, jobs)) as ex:
-        for out in ex.map(_run, jobs_list):
-            if verbose and out.strip():
-                print(out)
-    tmp = LIB + ".tmp"
+        for log in ex.map(_run, jobs_list):
+            if verbose and log.strip():
+                print(log)
+    tmp = out + ".tmp"
     _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp])
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

@@ -36,15 +36,21 @@ int32_t check_out_dtype(int32_t out_dt, const pkv_cache_desc* c) {
   return (out_dt == PKV_F32 || out_dt == c->dtype) ? PKV_OK : PKV_EDTYPE;
 }
 
+#ifndef PKV_AUTO_PARTITION
+#define PKV_AUTO_PARTITION 1024
+#endif
+
+// Contexts up to the automatic partition size take one partition (rounded up to 64 tokens);
+// longer ones are split into partitions of that size.
 int auto_partition(int32_t max_ctx) {
-  if (max_ctx <= 512) {
-    int p = ((max_ctx > 0 ? max_ctx : 1) + 63) / 64 * 64;
-    return p;
-  }
-  return 512;
+  constexpr int kAuto = PKV_AUTO_PARTITION <= pkv::kMaxPartition ? PKV_AUTO_PARTITION : pkv::kMaxPartition;
+  if (max_ctx <= kAuto) return ((max_ctx > 0 ? max_ctx : 1) + 63) / 64 * 64;
+  return kAuto;
 }
 
-bool valid_partition(int p, int bs) { return p >= 64 && p <= 512 && p % 64 == 0 && p % bs == 0; }
+bool valid_partition(int p, int bs) {
+  return p >= 64 && p <= pkv::kMaxPartition && p % 64 == 0 && p % bs == 0;
+}
 
 struct DecodeWs {
   size_t acc, ml, total;

@@ -4,7 +4,17 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#ifndef PKV_MAX_PARTITION
+#define PKV_MAX_PARTITION 1024
+#endif
+#ifndef PKV_DECODE_PREFETCH
+#define PKV_DECODE_PREFETCH 3
+#endif
+
 namespace pkv {
+
+// Largest decode partition in tokens (sizes the kernel's LDS score buffer).
+constexpr int kMaxPartition = PKV_MAX_PARTITION;
 
 inline int ilog2(int x) {
   int r = 0;

@@ -14,7 +14,8 @@ from typing import Optional, Sequence, Tuple
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libpagedkv.so")
+# PAGEDKV_LIB selects another build of the same library (e.g. a tuning variant).
+LIB_PATH = os.environ.get("PAGEDKV_LIB") or os.path.join(_HERE, "libpagedkv.so")
 
 F32, F16, BF16 = 0, 1, 2
 DTYPE_CODES = {"f32": F32, "f16": F16, "bf16": BF16}

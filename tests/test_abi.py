@@ -73,15 +73,16 @@ def test_decode_workspace_validation():
     assert need > 0
     assert decode(c, max_ctx=5000, mb=400) == -4
     assert decode(c, max_ctx=5000, mb=400, ws=ctypes.c_void_p(1), wsb=need - 1) == -4
-    assert L.pkv_decode_workspace_bytes(2, 4, 300, ctypes.byref(c)) == 0  # one partition: none
+    assert L.pkv_decode_workspace_bytes(2, 4, 1000, ctypes.byref(c)) == 0  # one partition: none
     assert decode(c, part=100) == -1      # not a multiple of 64
-    assert decode(c, part=1024) == -1     # too large
+    assert decode(c, part=2048) == -1     # too large
 
 
 def test_partition_size_rule():
     c = desc()
     assert L.pkv_decode_partition_size(1, 4, 100, ctypes.byref(c)) == 128
-    assert L.pkv_decode_partition_size(1, 4, 5000, ctypes.byref(c)) == 512
+    assert L.pkv_decode_partition_size(1, 4, 5000, ctypes.byref(c)) == 1024
+    assert L.pkv_decode_partition_size(1, 4, 1000, ctypes.byref(c)) == 1024
     assert L.pkv_decode_partition_size(1, 4, 0, ctypes.byref(c)) == 64
 
 
