@@ -144,11 +144,12 @@ size_t pkv_decode_workspace_bytes(int32_t S, int32_t hq, int32_t max_ctx, const 
   return pkv_decode_workspace_bytes_ex(S, hq, max_ctx, c, 0);
 }
 
-static int32_t decode_common(void* out, int32_t out_dtype, const void* q, const void* k_cache,
-                             const void* v_cache, const int32_t* block_tables, int32_t max_blocks_per_seq,
-                             const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads, float scale,
-                             int32_t max_context_len, const pkv_cache_desc* c, int32_t partition_size,
-                             void* workspace, size_t workspace_bytes, void* stream, int stage) {
+static int32_t decode_common_cu(void* out, int32_t out_dtype, const void* q, const void* k_cache,
+                                const void* v_cache, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads, float scale,
+                                int32_t max_context_len, const pkv_cache_desc* c, int32_t partition_size,
+                                void* workspace, size_t workspace_bytes, void* stream, const int32_t* cu,
+                                int stage = 0) {
   int32_t st = check_cache(c);
   if (st != PKV_OK) return st;
   if ((st = check_heads(num_q_heads, c)) != PKV_OK) return st;
@@ -189,7 +190,18 @@ static int32_t decode_common(void* out, int32_t out_dtype, const void* q, const 
   L.ws_acc = ws.total ? reinterpret_cast<float*>(wb + ws.acc) : nullptr;
   L.ws_ml = ws.total ? reinterpret_cast<float*>(wb + ws.ml) : nullptr;
   L.stage = stage;
+  L.cu = cu;
   return pkv::launch_decode(L, (hipStream_t)stream) == 0 ? PKV_OK : PKV_ELAUNCH;
+}
+
+static int32_t decode_common(void* out, int32_t out_dtype, const void* q, const void* k_cache,
+                             const void* v_cache, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                             const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads, float scale,
+                             int32_t max_context_len, const pkv_cache_desc* c, int32_t partition_size,
+                             void* workspace, size_t workspace_bytes, void* stream, int stage) {
+  return decode_common_cu(out, out_dtype, q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens,
+                          num_seqs, num_q_heads, scale, max_context_len, c, partition_size, workspace,
+                          workspace_bytes, stream, nullptr, stage);
 }
 
 int32_t pkv_paged_attention_decode_ex(void* out, int32_t out_dtype, const void* q, const void* k_cache,
@@ -226,6 +238,56 @@ int32_t pkv_paged_attention_decode_merge(void* out, int32_t out_dtype, const voi
   return decode_common(out, out_dtype, q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens,
                        num_seqs, num_q_heads, scale, max_context_len, c, partition_size, workspace,
                        workspace_bytes, stream, 2);
+}
+
+size_t pkv_ragged_workspace_bytes(int32_t num_seqs, int32_t num_tokens, int32_t num_q_heads, int32_t max_q_len,
+                                  int32_t max_context_len, const pkv_cache_desc* c) {
+  (void)num_tokens;
+  (void)max_q_len;
+  return pkv_decode_workspace_bytes_ex(num_seqs, num_q_heads, max_context_len, c, 0);
+}
+
+int32_t pkv_paged_attention_ragged(void* out, int32_t out_dtype, const void* q, const int32_t* cu_seqlens_q,
+                                   const int32_t* context_lens, const void* k_cache, const void* v_cache,
+                                   const int32_t* block_tables, int32_t max_blocks_per_seq, int32_t num_seqs,
+                                   int32_t num_tokens, int32_t num_q_heads, float scale, int32_t max_q_len,
+                                   int32_t max_context_len, const pkv_cache_desc* c, void* workspace,
+                                   size_t workspace_bytes, void* stream) {
+  int32_t st = check_cache(c);
+  if (st != PKV_OK) return st;
+  if ((st = check_heads(num_q_heads, c)) != PKV_OK) return st;
+  if ((st = check_out_dtype(out_dtype, c)) != PKV_OK) return st;
+  if (num_seqs < 0 || num_tokens < 0 || max_q_len < 0 || max_context_len < 0 || max_blocks_per_seq < 0)
+    return PKV_EINVAL;
+  if (num_seqs == 0 || num_tokens == 0) return PKV_OK;
+  if (max_q_len > max_context_len || max_q_len > num_tokens) return PKV_EINVAL;
+  // Prefill rows run on 16-bit MFMA; fp32 pools are served only for decode-only batches.
+  if (max_q_len > 1 && c->dtype == PKV_F32) return PKV_EDTYPE;
+  if (!out || !q || !cu_seqlens_q || !context_lens || !k_cache || !v_cache || !block_tables) return PKV_EINVAL;
+  // decode rows (q_len == 1) through the decode kernels with row indirection
+  st = decode_common_cu(out, out_dtype, q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens,
+                        num_seqs, num_q_heads, scale, max_context_len, c, 0, workspace, workspace_bytes, stream,
+                        cu_seqlens_q);
+  if (st != PKV_OK || max_q_len <= 1) return st;
+  pkv::PrefillLaunch P;
+  P.out = out;
+  P.out_dt = out_dtype;
+  P.q = q;
+  P.kc = k_cache;
+  P.vc = v_cache;
+  P.tables = block_tables;
+  P.max_blocks = max_blocks_per_seq;
+  P.cu = cu_seqlens_q;
+  P.ctx_lens = context_lens;
+  P.num_seqs = num_seqs;
+  P.num_tokens = num_tokens;
+  P.num_q_heads = num_q_heads;
+  P.num_kv_heads = c->num_kv_heads;
+  P.block_size = c->block_size;
+  P.head_dim = c->head_dim;
+  P.dt = c->dtype;
+  P.scale = scale;
+  return pkv::launch_ragged_prefill(P, (hipStream_t)stream) == 0 ? PKV_OK : PKV_ELAUNCH;
 }
 
 int32_t pkv_paged_attention_decode(void* out, int32_t out_dtype, const void* q, const void* k_cache,

@@ -37,6 +37,7 @@ struct DecodeArgs {
   const void* vc;
   const int32_t* tables;
   const int32_t* ctx_lens;
+  const int32_t* cu;  // ragged batches: query rows of sequence s are cu[s]..cu[s+1]-1 (else row s)
   float* ws_acc;
   float2* ws_ml;
   int out_dt;
@@ -117,6 +118,12 @@ __global__ __launch_bounds__(kDecThreads) void paged_decode_kernel(DecodeArgs a)
   // full, while partition 0 of every sequence (often partial) fills the tail of the launch.
   const int part = (int)gridDim.z - 1 - (int)blockIdx.z;
 
+  // In a ragged batch only single-row (decode) sequences are handled here.
+  int row = s;
+  if (a.cu) {
+    row = a.cu[s];
+    if (a.cu[s + 1] - row != 1) return;
+  }
   const int ctx = a.ctx_lens[s];
   const int nparts = ctx > 0 ? (ctx + a.partition - 1) / a.partition : 1;
   if (part >= nparts) return;  // uniform over the workgroup
@@ -133,7 +140,7 @@ __global__ __launch_bounds__(kDecThreads) void paged_decode_kernel(DecodeArgs a)
   // Query slices of the G heads in the score mapping.
   const int c = lane & 7;   // 16-byte chunk column
   const int r = lane >> 3;  // token row within a unit
-  const T* qb = static_cast<const T*>(a.q) + ((size_t)s * a.hq + (size_t)kvh * G) * D + c * VEC;
+  const T* qb = static_cast<const T*>(a.q) + ((size_t)row * a.hq + (size_t)kvh * G) * D + c * VEC;
   u32x4 qr[G][NCH];
 #pragma unroll
   for (int g = 0; g < G; ++g)
@@ -276,7 +283,7 @@ __global__ __launch_bounds__(kDecThreads) void paged_decode_kernel(DecodeArgs a)
   }
   __syncthreads();
 
-  const size_t out_row = (size_t)s * a.hq + (size_t)kvh * G;  // first of the G query heads
+  const size_t out_row = (size_t)row * a.hq + (size_t)kvh * G;  // first of the G query heads
   const size_t item = ((size_t)s * a.hkv + kvh) * a.max_parts + part;
   for (int o = tid; o < G * D; o += kDecThreads) {
     float v = 0.f;
@@ -299,6 +306,11 @@ __global__ __launch_bounds__(256) void paged_decode_merge_kernel(DecodeArgs a, i
   const int s = blockIdx.y;
   const int o = blockIdx.x * 256 + threadIdx.x;
   if (o >= a.hq * head_dim) return;
+  int row = s;
+  if (a.cu) {
+    row = a.cu[s];
+    if (a.cu[s + 1] - row != 1) return;
+  }
   const int ctx = a.ctx_lens[s];
   const int nparts = ctx > 0 ? (ctx + a.partition - 1) / a.partition : 1;
   if (nparts <= 1) return;
@@ -316,7 +328,7 @@ __global__ __launch_bounds__(256) void paged_decode_merge_kernel(DecodeArgs a, i
     l = __builtin_fmaf(w, ml.y, l);
     v = __builtin_fmaf(w, a.ws_acc[((item + p) * group + g) * head_dim + d], v);
   }
-  store_out(a.out, (size_t)s * a.hq * head_dim + o, l > 0.f ? v / l : 0.f, a.out_dt);
+  store_out(a.out, (size_t)row * a.hq * head_dim + o, l > 0.f ? v / l : 0.f, a.out_dt);
 }
 
 static DecodeArgs make_args(const DecodeLaunch& L) {
@@ -327,6 +339,7 @@ static DecodeArgs make_args(const DecodeLaunch& L) {
   a.vc = L.vc;
   a.tables = L.tables;
   a.ctx_lens = L.ctx_lens;
+  a.cu = L.cu;
   a.ws_acc = L.ws_acc;
   a.ws_ml = reinterpret_cast<float2*>(L.ws_ml);
   a.out_dt = L.out_dt;

@@ -39,6 +39,7 @@ struct DecodeLaunch {
   const int32_t* tables;
   int max_blocks;
   const int32_t* ctx_lens;
+  const int32_t* cu = nullptr;  // ragged batches: per-sequence query row offsets (decode rows only)
   int num_seqs;
   int num_q_heads;
   int num_kv_heads;
@@ -54,5 +55,29 @@ struct DecodeLaunch {
 };
 
 int launch_decode(const DecodeLaunch& a, hipStream_t stream);
+
+struct PrefillLaunch {
+  void* out;
+  int out_dt;
+  const void* q;
+  const void* kc;
+  const void* vc;
+  const int32_t* tables;
+  int max_blocks;
+  const int32_t* cu;
+  const int32_t* ctx_lens;
+  int num_seqs;
+  int num_tokens;
+  int num_q_heads;
+  int num_kv_heads;
+  int block_size;
+  int head_dim;
+  int dt;
+  float scale;
+};
+
+// Causal attention of every multi-row (prefill) sequence of a ragged batch; rows of
+// single-row sequences are left untouched.
+int launch_ragged_prefill(const PrefillLaunch& a, hipStream_t stream);
 
 }  // namespace pkv

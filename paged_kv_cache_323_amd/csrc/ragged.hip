@@ -1,13 +1,346 @@
-// Ragged mixed prefill + decode attention (selective batching). Placeholder until the kernel
-// lands: the entry points validate nothing and report an unsupported shape.
-#include <hip/hip_runtime.h>
-#include "../../include/pagedkv.h"
+// Prefill part of the ragged mixed step: causal attention of multi-row sequences over the paged
+// cache, on MFMA (v_mfma_f32_16x16x32_{bf16,f16}).
+//
+// Selective batching flattens every request's new tokens into one batch and splits it per
+// request only inside attention, where each request's phase decides whether it reads cached
+// keys (「Paged Attention&Orca Paper笔记与解读」 §Orca的Solution). Here a workgroup takes a tile of
+// 128 query rows of one prefill sequence for one query head; its four waves own 32 rows each.
+// Keys and values are read through the block table in tiles of 64 (a tile spans 2-8 blocks) and
+// staged in LDS: K row-major, V transposed (d-major) so both feed MFMA A-operands with plain
+// 16- or 8-byte reads. Per key tile and wave:
+//   Sᵀ = K·Qᵀ            (M = 64 keys, N = 32 rows, K = head_dim)   -> lane holds 4 keys x 1 row
+//   online softmax        (row max across the 4 lane groups; fp32; exp2 on log2-scaled scores)
+//   Oᵀ += Vᵀ·Pᵀ          (M = head_dim, N = 32 rows, K = 64 keys)    -> lane holds 4 dims x 1 row
+// The P operand comes straight from the Sᵀ accumulators: MFMA sums over k, so any fixed order of
+// the 32 keys of a k-step works as long as the Vᵀ operand uses the same order. P is split into
+// a 16-bit high part and a 16-bit remainder, each multiplied by V, so the products keep about
+// 16 significant bits (a single 16-bit P would cost up to ~1e-2 relative on short rows).
+// A query row at position p sees keys 0..p (the block-wise equation's ⌈i/B⌉ limit,
+// 「PagedAttention原理」 §实现一个虚拟内存).
+#include "common.hpp"
+#include "internal.hpp"
 
-extern "C" {
-size_t pkv_ragged_workspace_bytes(int32_t, int32_t, int32_t, int32_t, int32_t, const pkv_cache_desc*) { return 0; }
-int32_t pkv_paged_attention_ragged(void*, int32_t, const void*, const int32_t*, const int32_t*, const void*,
-                                   const void*, const int32_t*, int32_t, int32_t, int32_t, int32_t, float,
-                                   int32_t, int32_t, const pkv_cache_desc*, void*, size_t, void*) {
-  return PKV_ESHAPE;
+namespace pkv {
+
+constexpr int kPfThreads = 256;
+constexpr int kPfRows = 128;  // query rows per workgroup (4 waves x 32)
+constexpr int kPfKeys = 64;   // keys per tile
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+template <int DT> struct Mfma;
+template <> struct Mfma<DT_BF16> {
+  using V8 = bf16x8;
+  using S = __bf16;
+  static __device__ __forceinline__ f32x4 mma(const V8& a, const V8& b, const f32x4& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+};
+template <> struct Mfma<DT_F16> {
+  using V8 = f16x8;
+  using S = _Float16;
+  static __device__ __forceinline__ f32x4 mma(const V8& a, const V8& b, const f32x4& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+  }
+};
+
+struct PrefillArgs {
+  void* out;
+  const uint16_t* q;
+  const uint16_t* kc;
+  const uint16_t* vc;
+  const int32_t* tables;
+  const int32_t* cu;
+  const int32_t* ctx_lens;
+  int out_dt;
+  int max_blocks;
+  int num_seqs;
+  int hq;
+  int hkv;
+  int bs;
+  int log2_bs;
+  float scale_log2;
+};
+
+template <int DT, int D>
+__global__ __launch_bounds__(kPfThreads) void ragged_prefill_kernel(PrefillArgs a) {
+  using M = Mfma<DT>;
+  using V8 = typename M::V8;
+  constexpr int KS = D / 32;         // k-steps of Sᵀ = K·Qᵀ
+  constexpr int DT16 = D / 16;       // 16-row tiles of the head dim (M-tiles of Oᵀ)
+  constexpr int KLD = D + 8;         // LDS row stride of the K tile (elements)
+  constexpr int VLD = kPfKeys + 8;   // LDS row stride of the transposed V tile (elements)
+  constexpr int CPR = D / 8;         // 16-byte chunks per K/V row
+
+  __shared__ __attribute__((aligned(16))) uint16_t sK[kPfKeys * KLD];
+  __shared__ __attribute__((aligned(16))) uint16_t sVt[D * VLD];
+  __shared__ int s_scan[kPfThreads];
+  __shared__ int s_seq, s_tile;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int h = blockIdx.y;
+  const int kvh = h / (a.hq / a.hkv);
+
+  // ---- which (sequence, row tile) this workgroup owns: scan of per-sequence tile counts ----
+  if (tid == 0) s_seq = -1;
+  {
+    int base = 0;
+    for (int c0 = 0; c0 < a.num_seqs; c0 += kPfThreads) {
+      const int sq = c0 + tid;
+      int nt = 0;
+      if (sq < a.num_seqs) {
+        const int ql = a.cu[sq + 1] - a.cu[sq];
+        nt = ql > 1 ? (ql + kPfRows - 1) / kPfRows : 0;
+      }
+      s_scan[tid] = nt;
+      __syncthreads();
+      for (int off = 1; off < kPfThreads; off <<= 1) {
+        const int v = tid >= off ? s_scan[tid - off] : 0;
+        __syncthreads();
+        s_scan[tid] += v;
+        __syncthreads();
+      }
+      const int total = s_scan[kPfThreads - 1];
+      const int target = (int)blockIdx.x - base;
+      if (target < total) {
+        if (nt > 0 && s_scan[tid] > target && s_scan[tid] - nt <= target) {
+          s_seq = sq;
+          s_tile = target - (s_scan[tid] - nt);
+        }
+        __syncthreads();
+        break;
+      }
+      base += total;
+      __syncthreads();
+    }
+  }
+  __syncthreads();
+  const int s = s_seq;
+  if (s < 0) return;  // uniform: this slot of the launch has no tile
+  const int q0 = a.cu[s];
+  const int ql = a.cu[s + 1] - q0;
+  const int ctx = a.ctx_lens[s];
+  const int row0 = s_tile * kPfRows;
+  const int nrows = min(kPfRows, ql - row0);
+  const int pos0 = ctx - ql + row0;      // position of the tile's first query row
+  const int kend = pos0 + nrows;         // keys 0..kend-1 are visible to some row of the tile
+  const int nkt = (kend + kPfKeys - 1) / kPfKeys;
+
+  const int g = lane >> 4;   // lane group: k-slice of an operand / 4-row slice of a result
+  const int lr = lane & 15;  // row (operand) or column (result) within a 16-tile
+
+  // Q as the B operand of Sᵀ = K·Qᵀ: rows wave*32 + 16*nt + lr, dims 32*ks + 8*g .. +7.
+  V8 qb[2][KS];
+  int qpos[2];
+  bool qvalid[2];
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) {
+    const int r = wave * 32 + nt * 16 + lr;  // row within the tile
+    qvalid[nt] = r < nrows;
+    qpos[nt] = pos0 + r;
+    const uint16_t* qp = a.q + ((size_t)(q0 + row0 + (qvalid[nt] ? r : 0)) * a.hq + h) * D + 8 * g;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      u32x4 w = *reinterpret_cast<const u32x4*>(qp + 32 * ks);
+      if (!qvalid[nt]) w = u32x4{0, 0, 0, 0};
+      qb[nt][ks] = __builtin_bit_cast(V8, w);
+    }
+  }
+
+  f32x4 oacc[DT16][2];
+#pragma unroll
+  for (int dt = 0; dt < DT16; ++dt)
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) oacc[dt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run[2] = {-INFINITY, -INFINITY};
+  float l_part[2] = {0.f, 0.f};  // this lane's share of the row sum (its 4-key slices)
+
+  const int32_t* trow = a.tables + (size_t)s * a.max_blocks;
+  const size_t tile_rows = (size_t)a.hkv * a.bs;
+  const size_t head_rows = (size_t)kvh * a.bs;
+
+  for (int kt = 0; kt < nkt; ++kt) {
+    const int k0 = kt * kPfKeys;
+    // ---- stage K (row-major) and V (transposed) of keys k0..k0+63; keys >= kend are zeros ----
+#pragma unroll
+    for (int it = 0; it < kPfKeys * CPR / kPfThreads; ++it) {
+      const int idx = it * kPfThreads + tid;
+      const int key = idx / CPR;
+      const int ch = idx - key * CPR;
+      const int kk = k0 + key;
+      u32x4 w = u32x4{0, 0, 0, 0};
+      if (kk < kend) {
+        const int phys = trow[kk >> a.log2_bs];
+        const size_t row = (size_t)phys * tile_rows + head_rows + (kk & (a.bs - 1));
+        w = *reinterpret_cast<const u32x4*>(a.kc + row * D + ch * 8);
+      }
+      *reinterpret_cast<u32x4*>(&sK[key * KLD + ch * 8]) = w;
+    }
+#pragma unroll
+    for (int it = 0; it < (kPfKeys / 2) * CPR / kPfThreads; ++it) {
+      const int idx = it * kPfThreads + tid;
+      const int kp = idx & (kPfKeys / 2 - 1);  // key pair
+      const int ch = idx / (kPfKeys / 2);       // 8-dim chunk
+      u32x4 w0 = u32x4{0, 0, 0, 0}, w1 = u32x4{0, 0, 0, 0};
+      const int kk = k0 + 2 * kp;
+      if (kk < kend) {
+        const int phys = trow[kk >> a.log2_bs];
+        const size_t row = (size_t)phys * tile_rows + head_rows + (kk & (a.bs - 1));
+        w0 = *reinterpret_cast<const u32x4*>(a.vc + row * D + ch * 8);
+      }
+      if (kk + 1 < kend) {
+        const int phys = trow[(kk + 1) >> a.log2_bs];
+        const size_t row = (size_t)phys * tile_rows + head_rows + ((kk + 1) & (a.bs - 1));
+        w1 = *reinterpret_cast<const u32x4*>(a.vc + row * D + ch * 8);
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        // dims ch*8 + 2e and ch*8 + 2e + 1; each LDS word packs (key 2kp, key 2kp+1)
+        const uint32_t lo = (w0[e] & 0xffffu) | (w1[e] << 16);
+        const uint32_t hi = (w0[e] >> 16) | (w1[e] & 0xffff0000u);
+        *reinterpret_cast<uint32_t*>(&sVt[(ch * 8 + 2 * e) * VLD + 2 * kp]) = lo;
+        *reinterpret_cast<uint32_t*>(&sVt[(ch * 8 + 2 * e + 1) * VLD + 2 * kp]) = hi;
+      }
+    }
+    __syncthreads();
+
+    // ---- Sᵀ = K·Qᵀ: 4 key tiles x 2 row tiles -------------------------------------------------
+    f32x4 sacc[4][2];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) sacc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const V8 ka = __builtin_bit_cast(V8, *reinterpret_cast<const u32x4*>(&sK[(16 * mt + lr) * KLD + 32 * ks + 8 * g]));
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) sacc[mt][nt] = M::mma(ka, qb[nt][ks], sacc[mt][nt]);
+      }
+    }
+
+    // ---- causal mask and online softmax (per query row = per lane column) ----------------------
+    V8 phi[2][2], plo[2][2];  // [row tile][k-step of 32 keys]
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      float sv[4][4];
+      float mx = -INFINITY;
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int kk = k0 + 16 * mt + 4 * g + i;
+          const float v = kk <= qpos[nt] ? sacc[mt][nt][i] * a.scale_log2 : -INFINITY;
+          sv[mt][i] = v;
+          mx = fmaxf(mx, v);
+        }
+      mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
+      mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+      const float m_new = fmaxf(m_run[nt], mx);
+      // Row with no visible key yet (only possible for padding rows): keep everything at zero.
+      const float m_use = m_new == -INFINITY ? 0.f : m_new;
+      const float alpha = fast_exp2(m_run[nt] - m_use);
+      m_run[nt] = m_new;
+      float lsum = 0.f;
+      float p[4][4];
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          p[mt][i] = fast_exp2(sv[mt][i] - m_use);
+          lsum += p[mt][i];
+        }
+      l_part[nt] = l_part[nt] * alpha + lsum;
+#pragma unroll
+      for (int dt = 0; dt < DT16; ++dt) oacc[dt][nt] *= alpha;
+      // B operand of k-step j: keys 32j + 4g + (0..3) then 32j + 16 + 4g + (0..3).
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        V8 hi, lo;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float x = p[2 * j + (e >> 2)][e & 3];
+          const typename M::S xh = (typename M::S)x;
+          hi[e] = xh;
+          lo[e] = (typename M::S)(x - (float)xh);
+        }
+        phi[nt][j] = hi;
+        plo[nt][j] = lo;
+      }
+    }
+
+    // ---- Oᵀ += Vᵀ·Pᵀ with the same key order in both operands ---------------------------------
+#pragma unroll
+    for (int dt = 0; dt < DT16; ++dt) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const uint16_t* vrow = &sVt[(16 * dt + lr) * VLD + 32 * j + 4 * g];
+        const u32x2 x0 = *reinterpret_cast<const u32x2*>(vrow);
+        const u32x2 x1 = *reinterpret_cast<const u32x2*>(vrow + 16);
+        const V8 va = __builtin_bit_cast(V8, u32x4{x0[0], x0[1], x1[0], x1[1]});
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) {
+          oacc[dt][nt] = M::mma(va, phi[nt][j], oacc[dt][nt]);
+          oacc[dt][nt] = M::mma(va, plo[nt][j], oacc[dt][nt]);
+        }
+      }
+    }
+    __syncthreads();  // the next tile overwrites sK / sVt
+  }
+
+  // ---- normalise and store: lane writes dims 16*dt + 4*g .. +3 of its row ----------------------
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) {
+    float l = l_part[nt];
+    l += __shfl_xor(l, 16, kWave);
+    l += __shfl_xor(l, 32, kWave);
+    if (!qvalid[nt]) continue;
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    const size_t orow = ((size_t)(q0 + wave * 32 + nt * 16 + lr + row0) * a.hq + h) * D;
+#pragma unroll
+    for (int dt = 0; dt < DT16; ++dt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) store_out(a.out, orow + 16 * dt + 4 * g + i, oacc[dt][nt][i] * inv, a.out_dt);
+  }
 }
+
+template <int DT>
+static int launch_prefill_dt(const PrefillLaunch& L, hipStream_t stream) {
+  PrefillArgs a;
+  a.out = L.out;
+  a.q = static_cast<const uint16_t*>(L.q);
+  a.kc = static_cast<const uint16_t*>(L.kc);
+  a.vc = static_cast<const uint16_t*>(L.vc);
+  a.tables = L.tables;
+  a.cu = L.cu;
+  a.ctx_lens = L.ctx_lens;
+  a.out_dt = L.out_dt;
+  a.max_blocks = L.max_blocks;
+  a.num_seqs = L.num_seqs;
+  a.hq = L.num_q_heads;
+  a.hkv = L.num_kv_heads;
+  a.bs = L.block_size;
+  a.log2_bs = ilog2(L.block_size);
+  a.scale_log2 = L.scale * 1.4426950408889634f;
+  // Row tiles: sum over sequences of ceil(q_len / 128) <= T / 128 + (number of prefill
+  // sequences); slots past the real count exit at once.
+  const long long slots = (L.num_tokens + kPfRows - 1) / kPfRows + (L.num_seqs < L.num_tokens / 2 ? L.num_seqs : L.num_tokens / 2);
+  if (slots <= 0) return 0;
+  if (slots > 0x7fffffffLL || L.num_q_heads > 65535) return -1;
+  if (L.head_dim == 128)
+    hipLaunchKernelGGL((ragged_prefill_kernel<DT, 128>), dim3((unsigned)slots, L.num_q_heads), dim3(kPfThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL((ragged_prefill_kernel<DT, 64>), dim3((unsigned)slots, L.num_q_heads), dim3(kPfThreads), 0, stream, a);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
 }
+
+int launch_ragged_prefill(const PrefillLaunch& L, hipStream_t stream) {
+  if (L.dt == DT_BF16) return launch_prefill_dt<DT_BF16>(L, stream);
+  if (L.dt == DT_F16) return launch_prefill_dt<DT_F16>(L, stream);
+  return -1;
+}
+
+}  // namespace pkv

@@ -14,6 +14,7 @@ from .synth import (  # noqa: F401
     FreeOp,
     make_workload,
     make_decode_workload,
+    make_ragged_workload,
     CONFIG_NAMES,
     gen_kv,
     gen_q,

@@ -209,6 +209,22 @@ def make_decode_workload(seed: int, ctx: List[int], hq: int, hkv: int, head_dim:
                     list(ctx))
 
 
+def make_ragged_workload(seed: int, q_lens: List[int], ctx: List[int], hq: int, hkv: int, head_dim: int,
+                         dtype: str, block_size: int, slack: float = 1.5, name: str = "ragged") -> Workload:
+    """A generic selective-batching step: sequence s has ctx[s] - q_lens[s] cached tokens, then
+    appends q_lens[s] new tokens whose rows are queried (q_len 1 = decode, more = prefill chunk)."""
+    assert all(0 <= q <= c for q, c in zip(q_lens, ctx))
+    need = sum(-(-c // block_size) for c in ctx)
+    nb = max(1, _pool_size(need, slack))
+    perm = _rng(seed, _S_PERM).permutation(nb).astype(np.int32)
+    seqs = list(range(len(ctx)))
+    ops: List[Op] = [AddOp(s) for s in seqs]
+    ops.append(AppendOp(list(seqs), [c - q for c, q in zip(ctx, q_lens)], tag=0))
+    ops.append(AppendOp(list(seqs), list(q_lens), tag=1))
+    return Workload(name, seed, dtype, block_size, hq, hkv, head_dim, nb, perm, ops, seqs, list(q_lens),
+                    list(ctx))
+
+
 def make_workload(name: str, size: str = "full", block_size: Optional[int] = None,
                   slack: float = 1.5) -> Workload:
     if size not in ("full", "small"):
