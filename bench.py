@@ -6,7 +6,8 @@ at 8192, physical blocks in a seeded random order):
 
   1. host block manager: append one token to every sequence -> slots, copy-on-write pairs,
      block tables (C++ inside libpagedkv.so);
-  2. one pinned-memory upload of slots, context lengths and block tables;
+  2. one pinned-memory upload of slots, context lengths and block tables (on a copy stream, so
+     it overlaps the previous step's kernels);
   3. copy_blocks for any copy-on-write pairs (none in this workload);
   4. kv_cache_write of the 256 new tokens;
   5. paged decode attention of the 256 query rows over their whole contexts.
@@ -69,14 +70,16 @@ class DecodeLoop:
         self.max_ctx_final = max(w.context_lens) + steps_total
         self.max_blocks = -(-self.max_ctx_final // w.block_size)
         # one pinned staging area per parity of the step: [slots S | ctx S | tables S*MB]
+        # Two staging sets (host pinned + device) so that the upload of step k+1 runs on a copy
+        # stream while step k's kernels still read their own device copy.
         n = 2 * self.S + self.S * self.max_blocks
         self.host = [torch.empty(n, dtype=torch.int32).pin_memory() for _ in range(2)]
         self.host_np = [h.numpy() for h in self.host]
-        self.uploaded = [None, None]
-        self.dev = torch.empty(n, dtype=torch.int32, device=device)
-        self.slots_d = self.dev[: self.S]
-        self.ctx_d = self.dev[self.S: 2 * self.S]
-        self.tab_d = self.dev[2 * self.S:].view(self.S, self.max_blocks)
+        self.dev = [torch.empty(n, dtype=torch.int32, device=device) for _ in range(2)]
+        self.uploaded = [None, None]      # copy-stream event: upload of set i finished
+        self.consumed = [None, None]      # main-stream event: kernels reading set i finished
+        self.copy_stream = torch.cuda.Stream()
+        self._views(0)
         self.q = R.to_device(w.queries(), w.dtype, device)
         # new-token K/V for the steps (fixed values; only their placement changes per step)
         r = np.random.default_rng([w.seed, 77])
@@ -92,20 +95,37 @@ class DecodeLoop:
         self.ctx_history = []
         self.pairs_total = 0
 
+    def _views(self, i):
+        d = self.dev[i]
+        self.slots_d = d[: self.S]
+        self.ctx_d = d[self.S: 2 * self.S]
+        self.tab_d = d[2 * self.S:].view(self.S, self.max_blocks)
+
+    def repeat_attention(self, n):
+        for _ in range(n):
+            self.pk.paged_attention_decode(self.out, self.q, self.st.k_cache, self.st.v_cache, self.tab_d,
+                                           self.ctx_d, self.w.scale, self.max_ctx_final, self.st.desc, self.ws)
+
     def step(self, ev=None):
         torch, pk, w = self.torch, self.pk, self.w
         buf = self.step_idx & 1
         if self.uploaded[buf] is not None:
-            self.uploaded[buf].synchronize()       # the H2D that last read this buffer is done
+            self.uploaded[buf].synchronize()       # the H2D that last read this host buffer is done
         hn = self.host_np[buf]
         slots, pairs = self.st.bm.append(self.seqs, np.ones(self.S, dtype=np.int32))
         hn[: self.S] = slots
         tab = hn[2 * self.S:].reshape(self.S, self.max_blocks)
         self.st.bm.block_tables(self.seqs, self.max_blocks, out=tab, ctx_out=hn[self.S: 2 * self.S])
-        self.dev.copy_(self.host[buf], non_blocking=True)
-        e = torch.cuda.Event()
-        e.record()
+        main = torch.cuda.current_stream()
+        with torch.cuda.stream(self.copy_stream):
+            if self.consumed[buf] is not None:
+                self.copy_stream.wait_event(self.consumed[buf])
+            self.dev[buf].copy_(self.host[buf], non_blocking=True)
+            e = torch.cuda.Event()
+            e.record(self.copy_stream)
         self.uploaded[buf] = e
+        main.wait_event(e)
+        self._views(buf)
         if len(pairs):
             self.pairs_total += len(pairs)
             pk.copy_blocks(self.st.k_cache, self.st.v_cache,
@@ -121,6 +141,9 @@ class DecodeLoop:
         pk.paged_attention_decode(*args, stage="merge")
         if ev is not None:
             ev[2].record()
+        done = torch.cuda.Event()
+        done.record(main)
+        self.consumed[buf] = done
         self.ctx_history.append(hn[self.S: 2 * self.S].copy())
         self.step_idx += 1
 
@@ -129,18 +152,16 @@ def run_headline(args):
     import torch
     from workloads import make_workload
     w = make_workload("gqa", "full", block_size=args.block_size)
-    ramp_max = 100
-    loop = DecodeLoop(w, args.warmup + args.steps + ramp_max)
+    ramp_repeats = 400
+    loop = DecodeLoop(w, args.warmup + args.steps)
     for _ in range(args.warmup):
         loop.step()
     torch.cuda.synchronize()
-    # keep the GPU busy for a moment so clocks have ramped before the timed steps
-    t_ramp = time.perf_counter()
-    for _ in range(ramp_max):
-        if time.perf_counter() - t_ramp > 0.1:
-            break
-        loop.step()
-        torch.cuda.synchronize()
+    # Keep the GPU busy for a moment so clocks have ramped before the timed steps: repeat the
+    # last step's attention without advancing the state (a fixed count, so every run of this
+    # command times the same launches).
+    loop.repeat_attention(ramp_repeats)
+    torch.cuda.synchronize()
     loop.ctx_history.clear()
     evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(args.steps)]
     torch.cuda.synchronize()
@@ -171,6 +192,171 @@ def run_headline(args):
         kern_kv_gbs=kv_per_step / kern_avg_s / 1e9, partition=loop.partition,
         mean_ctx=float(np.mean([c.mean() for c in loop.ctx_history])),
         merge_avg_us=float(np.mean(merge_ms)) * 1e3)
+
+
+def _time_events(fn, reps=20, warm=3):
+    """Median and mean duration (us) of fn() measured with HIP events on the current stream."""
+    import torch
+    for _ in range(warm):
+        fn()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for a, b in evs:
+        a.record()
+        fn()
+        b.record()
+    torch.cuda.synchronize()
+    ms = [a.elapsed_time(b) for a, b in evs]
+    return float(np.median(ms)) * 1e3, float(np.mean(ms)) * 1e3
+
+
+def run_decode_config(name, block_size=None, steps=30, warmup=5):
+    """Decode-step loop for another configuration; returns partition-launch and step figures."""
+    import torch
+    from workloads import make_workload
+    w = make_workload(name, "full", block_size=block_size)
+    loop = DecodeLoop(w, warmup + steps + 2)
+    for _ in range(warmup):
+        loop.step()
+    torch.cuda.synchronize()
+    loop.ctx_history.clear()
+    evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        loop.step(evs[i])
+    torch.cuda.synchronize()
+    el = (time.perf_counter() - t0) / steps
+    kern = float(np.mean([a.elapsed_time(b) for a, b, _ in evs])) * 1e-3
+    merge = float(np.mean([b.elapsed_time(c) for _, b, c in evs])) * 1e-3
+    kv = float(np.mean([decode_algorithmic_bytes(c, w, 2)[0] for c in loop.ctx_history]))
+    res = {"workload": w.name, "seqs": len(w.query_seqs), "step_us": round(el * 1e6, 1),
+           "seqs_per_s": round(len(w.query_seqs) / el, 1), "kv_gbs_step": round(kv / el / 1e9, 1),
+           "partition_launch_us": round(kern * 1e6, 1), "merge_launch_us": round(merge * 1e6, 1),
+           "kv_gbs_partition_launch": round(kv / kern / 1e9, 1),
+           "pct_hbm_partition_launch": round(100 * kv / kern / 1e9 / HBM_PEAK_GBS, 1)}
+    del loop
+    torch.cuda.empty_cache()
+    return res
+
+
+def run_shared_prefix():
+    """Copy-on-write copies at the first generated token and decode over shared blocks."""
+    import torch
+    from paged_kv_cache_323_amd import native as pk
+    from paged_kv_cache_323_amd import runner as R
+    from workloads import make_workload
+    w = make_workload("shared_prefix", "full")
+    st = R.play_script(w, threads=16)
+    pairs = st.pairs_per_append[-2]               # the first generated token's COW pairs
+    pd = torch.from_numpy(np.ascontiguousarray(pairs)).cuda()
+    blk_bytes = w.num_kv_heads * w.block_size * w.head_dim * 2
+    med, _ = _time_events(lambda: pk.copy_blocks(st.k_cache, st.v_cache, pd, st.desc), reps=50)
+    res = {"workload": w.name, "cow_pairs": int(len(pairs)), "copy_us": round(med, 2),
+           "copy_gbs": round(2 * 2 * len(pairs) * blk_bytes / med / 1e3, 1)}
+    # decode at the final state
+    out, inp = R.attention(w, st, w.dtype)
+    bt, cl, q, ws = inp["block_tables"], inp["context_lens"], inp["q"], inp["workspace"]
+    mx = int(inp["lens_host"].max())
+    med, _ = _time_events(lambda: pk.paged_attention_decode(out, q, st.k_cache, st.v_cache, bt, cl, w.scale, mx,
+                                                            st.desc, ws), reps=30)
+    lens = inp["lens_host"]
+    tables = inp["tables_host"]
+    logical = int(lens.sum()) * w.kv_bytes_per_token()
+    fill = {}
+    for t, L in zip(tables, lens):
+        for j in range(-(-int(L) // w.block_size)):
+            fill[int(t[j])] = max(fill.get(int(t[j]), 0), min(w.block_size, int(L) - j * w.block_size))
+    unique = sum(fill.values()) * w.kv_bytes_per_token()
+    res.update({"decode_us": round(med, 1), "decode_logical_gbs": round(logical / med / 1e3, 1),
+                "decode_unique_gbs": round(unique / med / 1e3, 1), "seqs_per_s": round(len(lens) / med * 1e6, 1)})
+    del st
+    torch.cuda.empty_cache()
+    # bandwidth-scale copy: 4096 pairs over a separate pool of the same block shape
+    nb = 8192
+    kc = torch.empty((nb, w.num_kv_heads, w.block_size, w.head_dim), dtype=torch.float16, device="cuda")
+    vc = torch.empty_like(kc)
+    kc.normal_()
+    vc.normal_()
+    desc = pk.CacheDesc.make(nb, w.block_size, w.num_kv_heads, w.head_dim, "f16")
+    perm = np.random.default_rng(4).permutation(nb).astype(np.int32)
+    big = torch.from_numpy(np.ascontiguousarray(perm.reshape(2, -1).T)).cuda()
+    med, _ = _time_events(lambda: pk.copy_blocks(kc, vc, big, desc), reps=20)
+    res["copy_4096_pairs_us"] = round(med, 1)
+    res["copy_4096_pairs_gbs"] = round(2 * 2 * 4096 * blk_bytes / med / 1e3, 1)
+    del kc, vc
+    torch.cuda.empty_cache()
+    return res
+
+
+def prefill_flops(q_lens, ctx, hq, d):
+    """4·d·Hq per causal (query, key) pair: query at position p sees p+1 keys."""
+    tot = 0
+    for ql, c in zip(q_lens, ctx):
+        if ql <= 1:
+            continue
+        first = c - ql  # position of the first query row
+        tot += sum(int(first) + t + 1 for t in range(int(ql)))
+    return 4 * int(d) * int(hq) * int(tot)
+
+
+def run_mixed():
+    """Selective-batching mixed step (8 prefills + 248 decodes, 40 heads, bf16): the step's
+    cache write plus the ragged attention, and a prefill-only call for MFMA utilisation."""
+    import torch
+    from paged_kv_cache_323_amd import native as pk
+    from paged_kv_cache_323_amd import runner as R
+    from workloads import make_workload
+    w = make_workload("mixed", "full")
+    t = time.perf_counter()
+    st = R.play_script(w, threads=16)
+    torch.cuda.synchronize()
+    log(f"setup {w.name}: wrote {sum(w.context_lens)} tokens in {time.perf_counter() - t:.1f}s")
+    step_op = w.ops[-1]
+    k, v = w.append_values(step_op, threads=16)
+    kd, vd = R.to_device(k, w.dtype), R.to_device(v, w.dtype)
+    slots = torch.from_numpy(np.ascontiguousarray(st.slots_per_append[-1])).cuda()
+    q = R.to_device(w.queries(), w.dtype)
+    out = torch.empty_like(q)
+    tables, lens = st.bm.block_tables(w.query_seqs, w.max_blocks_per_seq())
+    bt, cl = torch.from_numpy(tables).cuda(), torch.from_numpy(lens).cuda()
+    cu = torch.from_numpy(w.cu_seqlens()).cuda()
+    mx, mq = int(lens.max()), int(max(w.q_lens))
+    ws = torch.zeros(max(pk.ragged_workspace_bytes(len(lens), q.shape[0], w.num_q_heads, mq, mx, st.desc), 1),
+                     dtype=torch.uint8, device="cuda")
+
+    def step():
+        pk.kv_cache_write(kd, vd, st.k_cache, st.v_cache, slots, st.desc)
+        pk.paged_attention_ragged(out, q, cu, cl, st.k_cache, st.v_cache, bt, w.scale, mq, mx, st.desc, ws)
+
+    step_us, _ = _time_events(step, reps=20)
+    att_us, _ = _time_events(lambda: pk.paged_attention_ragged(out, q, cu, cl, st.k_cache, st.v_cache, bt, w.scale,
+                                                               mq, mx, st.desc, ws), reps=20)
+    n_pre = sum(1 for x in w.q_lens if x > 1)
+    # prefill-only call: the 8 prompt sequences alone
+    cu_p = torch.from_numpy(w.cu_seqlens()[: n_pre + 1].copy()).cuda()
+    T_p = int(w.cu_seqlens()[n_pre])
+    ql_p, ctx_p = w.q_lens[:n_pre], list(lens[:n_pre])
+    mx_p = int(max(ctx_p))
+    pre_us, _ = _time_events(lambda: pk.paged_attention_ragged(out[:T_p], q[:T_p], cu_p, cl[:n_pre], st.k_cache,
+                                                               st.v_cache, bt[:n_pre], w.scale, mq, mx_p, st.desc,
+                                                               ws), reps=20)
+    flops = prefill_flops(ql_p, ctx_p, w.num_q_heads, w.head_dim)
+    dec_kv = int(sum(int(c) for c, ql in zip(lens, w.q_lens) if ql == 1)) * w.kv_bytes_per_token()
+    write_bytes = 2 * 2 * int(q.shape[0]) * w.num_kv_heads * w.head_dim * 2
+    res = {"workload": w.name, "tokens": int(q.shape[0]), "prefill_seqs": n_pre,
+           "decode_seqs": len(lens) - n_pre, "step_us": round(step_us, 1),
+           "seqs_per_s": round(len(lens) / step_us * 1e6, 1), "attention_us": round(att_us, 1),
+           "decode_kv_gb": round(dec_kv / 1e9, 3), "prefill_only_us": round(pre_us, 1),
+           "prefill_gflop": round(flops / 1e9, 2), "prefill_tflops": round(flops / pre_us / 1e6, 1),
+           "prefill_mfma_util": round(flops / pre_us / 1e6 / MFMA_BF16_PEAK_TFLOPS, 4),
+           "kv_cache_write_bytes": write_bytes}
+    # cache write alone at the step's size
+    w_us, _ = _time_events(lambda: pk.kv_cache_write(kd, vd, st.k_cache, st.v_cache, slots, st.desc), reps=20)
+    res["kv_cache_write_us"] = round(w_us, 1)
+    res["kv_cache_write_gbs"] = round(write_bytes / w_us / 1e3, 1)
+    del st
+    torch.cuda.empty_cache()
+    return res
 
 
 def cpu_baseline(w, budget_s=20.0):
@@ -208,6 +394,52 @@ def cpu_baseline(w, budget_s=20.0):
                       f"sum ctx {int(np.sum(lens))}, median of {len(times)} runs, 1 BLAS thread"}
 
 
+def source_digest() -> str:
+    """Digest of the decode kernel source: counter-derived figures are only valid for it."""
+    import hashlib
+    src = os.path.join(ROOT, "paged_kv_cache_323_amd", "csrc", "decode.hip")
+    with open(src, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def load_traffic(block_size: int):
+    """HBM bytes per decode partition launch from the committed counter summary, or None when
+    that summary was taken on a different kernel source or workload."""
+    path = os.path.join(ROOT, "profiles", f"decode_gqa_B{block_size}_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as f:
+        for line in f:
+            if "=" in line and not line.startswith("#"):
+                k, v = line.strip().split("=", 1)
+                kv[k.strip()] = v.strip()
+    if kv.get("source_digest") != source_digest():
+        return None
+    try:
+        return float(kv["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def profile_copy(reps: int = 10):
+    """Calibration for HBM counters: copy_blocks of 4096 whole blocks (f16, 32 heads x 16 slots
+    x 128 dims), 1 GiB read and 1 GiB written per launch."""
+    import torch
+    from paged_kv_cache_323_amd import native as pk
+    nb, H, B, D = 8192, 32, 16, 128
+    kc = torch.empty((nb, H, B, D), dtype=torch.float16, device="cuda").normal_()
+    vc = torch.empty_like(kc).normal_()
+    desc = pk.CacheDesc.make(nb, B, H, D, "f16")
+    perm = np.random.default_rng(4).permutation(nb).astype(np.int32)
+    pairs = torch.from_numpy(np.ascontiguousarray(perm.reshape(2, -1).T)).cuda()
+    for _ in range(reps):
+        pk.copy_blocks(kc, vc, pairs, desc)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_blocks_pairs": 4096, "bytes_read_per_launch": 2 * 4096 * H * B * D * 2,
+                      "bytes_written_per_launch": 2 * 4096 * H * B * D * 2, "launches": reps}))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -216,6 +448,8 @@ def main():
     ap.add_argument("--block-size", type=int, default=16)
     ap.add_argument("--no-extra", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--profile-copy", action="store_true",
+                    help="only run the copy kernel used to calibrate HBM byte counters")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the path has no "
@@ -226,6 +460,9 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
     torch.cuda.set_device(0)
+    if args.profile_copy:
+        profile_copy()
+        return
     h = run_headline(args)
     w = h["w"]
     log(f"decode kernel avg {h['kern_avg_us']:.1f} us (median {h['kern_med_us']:.1f}), "
@@ -252,12 +489,24 @@ def main():
         "seqs_per_s": round(h["seqs_per_s"], 1),
         "pct_hbm_peak_step": round(100 * h["kv_gbs"] / HBM_PEAK_GBS, 2),
         "roofline": {"bound": "hbm", "achieved": round(h["achieved"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(h["achieved"] / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(h["achieved"] / HBM_PEAK_GBS, 4), "traffic": load_traffic(w.block_size),
                      "kernel": "paged_decode_kernel<bf16,128,4> (partition launch)",
                      "kernel_avg_us": round(h["kern_avg_us"], 2),
                      "merge_launch_avg_us": round(h["merge_avg_us"], 2),
                      "algorithmic_bytes_per_launch": int(h["alg_per_launch"])},
     }
+    if not args.no_extra:
+        extra = {}
+        for key, fn in (("gqa_B32", lambda: run_decode_config("gqa", 32)),
+                        ("llama7b", lambda: run_decode_config("llama7b")),
+                        ("shared_prefix", run_shared_prefix),
+                        ("mixed", run_mixed)):
+            log(f"extra: {key}")
+            try:
+                extra[key] = fn()
+            except Exception as e:  # keep the headline line even if a side measurement fails
+                extra[key] = {"error": repr(e)}
+        result["extra"] = extra
     if not args.no_cpu:
         log("timing the oracle on the host CPU")
         result["cpu_baseline"] = cpu_baseline(w)

@@ -64,6 +64,8 @@ struct PrefillArgs {
   float scale_log2;
 };
 
+constexpr int kPfTab = 1024;  // block-table entries cached in LDS at a time
+
 template <int DT, int D>
 __global__ __launch_bounds__(kPfThreads) void ragged_prefill_kernel(PrefillArgs a) {
   using M = Mfma<DT>;
@@ -73,23 +75,46 @@ __global__ __launch_bounds__(kPfThreads) void ragged_prefill_kernel(PrefillArgs 
   constexpr int KLD = D + 8;         // LDS row stride of the K tile (elements)
   constexpr int VLD = kPfKeys + 8;   // LDS row stride of the transposed V tile (elements)
   constexpr int CPR = D / 8;         // 16-byte chunks per K/V row
+  constexpr int KIT = kPfKeys * CPR / kPfThreads;        // K chunks staged per thread
+  constexpr int VIT = (kPfKeys / 2) * CPR / kPfThreads;  // V key-pair chunks staged per thread
 
   __shared__ __attribute__((aligned(16))) uint16_t sK[kPfKeys * KLD];
   __shared__ __attribute__((aligned(16))) uint16_t sVt[D * VLD];
+  __shared__ int s_tab[kPfTab];
   __shared__ int s_scan[kPfThreads];
   __shared__ int s_seq, s_tile;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int h = blockIdx.y;
+  const int h = blockIdx.x;
   const int kvh = h / (a.hq / a.hkv);
 
-  // ---- which (sequence, row tile) this workgroup owns: scan of per-sequence tile counts ----
+  // ---- which (sequence, row tile) this workgroup owns ----------------------------------------
+  // Slots are numbered from the end: the last row tiles of the last sequences (the longest
+  // causal rows, hence the most key tiles) are dispatched first, short ones fill the tail.
   if (tid == 0) s_seq = -1;
   {
-    int base = 0;
+    int total_all = 0;  // total tiles, needed to reverse the slot order
     for (int c0 = 0; c0 < a.num_seqs; c0 += kPfThreads) {
+      const int sq = c0 + tid;
+      int nt = 0;
+      if (sq < a.num_seqs) {
+        const int ql = a.cu[sq + 1] - a.cu[sq];
+        nt = ql > 1 ? (ql + kPfRows - 1) / kPfRows : 0;
+      }
+      s_scan[tid] = nt;
+      __syncthreads();
+      for (int off = kPfThreads / 2; off > 0; off >>= 1) {
+        if (tid < off) s_scan[tid] += s_scan[tid + off];
+        __syncthreads();
+      }
+      total_all += s_scan[0];
+      __syncthreads();
+    }
+    const int slot = total_all - 1 - (int)blockIdx.y;
+    int base = 0;
+    for (int c0 = 0; slot >= 0 && c0 < a.num_seqs; c0 += kPfThreads) {
       const int sq = c0 + tid;
       int nt = 0;
       if (sq < a.num_seqs) {
@@ -105,7 +130,7 @@ __global__ __launch_bounds__(kPfThreads) void ragged_prefill_kernel(PrefillArgs 
         __syncthreads();
       }
       const int total = s_scan[kPfThreads - 1];
-      const int target = (int)blockIdx.x - base;
+      const int target = slot - base;
       if (target < total) {
         if (nt > 0 && s_scan[tid] > target && s_scan[tid] - nt <= target) {
           s_seq = sq;
@@ -162,44 +187,75 @@ __global__ __launch_bounds__(kPfThreads) void ragged_prefill_kernel(PrefillArgs 
   const int32_t* trow = a.tables + (size_t)s * a.max_blocks;
   const size_t tile_rows = (size_t)a.hkv * a.bs;
   const size_t head_rows = (size_t)kvh * a.bs;
+  const int nblk = (kend + a.bs - 1) >> a.log2_bs;
+  int tab_base = -kPfTab;  // first table entry held in s_tab
 
-  for (int kt = 0; kt < nkt; ++kt) {
+  // Global -> register staging of one key tile (keys >= kend are zeros). Table entries come
+  // from the LDS cache, which covers every key of the tile (refreshed between tiles).
+  u32x4 kreg[KIT];
+  u32x4 vreg[VIT][2];
+  auto fetch = [&](int kt) {
     const int k0 = kt * kPfKeys;
-    // ---- stage K (row-major) and V (transposed) of keys k0..k0+63; keys >= kend are zeros ----
 #pragma unroll
-    for (int it = 0; it < kPfKeys * CPR / kPfThreads; ++it) {
+    for (int it = 0; it < KIT; ++it) {
       const int idx = it * kPfThreads + tid;
       const int key = idx / CPR;
       const int ch = idx - key * CPR;
       const int kk = k0 + key;
-      u32x4 w = u32x4{0, 0, 0, 0};
+      kreg[it] = u32x4{0, 0, 0, 0};
       if (kk < kend) {
-        const int phys = trow[kk >> a.log2_bs];
+        const int phys = s_tab[(kk >> a.log2_bs) - tab_base];
         const size_t row = (size_t)phys * tile_rows + head_rows + (kk & (a.bs - 1));
-        w = *reinterpret_cast<const u32x4*>(a.kc + row * D + ch * 8);
+        kreg[it] = *reinterpret_cast<const u32x4*>(a.kc + row * D + ch * 8);
       }
-      *reinterpret_cast<u32x4*>(&sK[key * KLD + ch * 8]) = w;
     }
 #pragma unroll
-    for (int it = 0; it < (kPfKeys / 2) * CPR / kPfThreads; ++it) {
+    for (int it = 0; it < VIT; ++it) {
       const int idx = it * kPfThreads + tid;
-      const int kp = idx & (kPfKeys / 2 - 1);  // key pair
-      const int ch = idx / (kPfKeys / 2);       // 8-dim chunk
-      u32x4 w0 = u32x4{0, 0, 0, 0}, w1 = u32x4{0, 0, 0, 0};
-      const int kk = k0 + 2 * kp;
+      const int kp = idx & (kPfKeys / 2 - 1);
+      const int ch = idx / (kPfKeys / 2);
+      const int kk = k0 + 2 * kp;  // kk and kk+1 share a block (B is even)
+      vreg[it][0] = u32x4{0, 0, 0, 0};
+      vreg[it][1] = u32x4{0, 0, 0, 0};
       if (kk < kend) {
-        const int phys = trow[kk >> a.log2_bs];
+        const int phys = s_tab[(kk >> a.log2_bs) - tab_base];
         const size_t row = (size_t)phys * tile_rows + head_rows + (kk & (a.bs - 1));
-        w0 = *reinterpret_cast<const u32x4*>(a.vc + row * D + ch * 8);
+        vreg[it][0] = *reinterpret_cast<const u32x4*>(a.vc + row * D + ch * 8);
+        if (kk + 1 < kend) vreg[it][1] = *reinterpret_cast<const u32x4*>(a.vc + (row + 1) * D + ch * 8);
       }
-      if (kk + 1 < kend) {
-        const int phys = trow[(kk + 1) >> a.log2_bs];
-        const size_t row = (size_t)phys * tile_rows + head_rows + ((kk + 1) & (a.bs - 1));
-        w1 = *reinterpret_cast<const u32x4*>(a.vc + row * D + ch * 8);
-      }
+    }
+  };
+  // Makes s_tab hold the entries of key tiles kt (and kt+1 when it is in range). Uniform.
+  auto ensure_table = [&](int kt) {
+    const int jlo = (kt * kPfKeys) >> a.log2_bs;
+    const int jhi = min(nblk, (min(kt + 2, nkt) * kPfKeys + a.bs - 1) >> a.log2_bs);
+    if (jlo >= tab_base && jhi <= tab_base + kPfTab) return;
+    __syncthreads();  // nobody still reads the old entries
+    tab_base = jlo;
+    for (int i = tid; i < kPfTab && jlo + i < nblk; i += kPfThreads) s_tab[i] = trow[jlo + i];
+    __syncthreads();
+  };
+
+  ensure_table(0);
+  fetch(0);
+  for (int kt = 0; kt < nkt; ++kt) {
+    const int k0 = kt * kPfKeys;
+    // ---- registers of tile kt -> LDS: K row-major, V transposed (word = two adjacent keys) ----
+#pragma unroll
+    for (int it = 0; it < KIT; ++it) {
+      const int idx = it * kPfThreads + tid;
+      const int key = idx / CPR;
+      const int ch = idx - key * CPR;
+      *reinterpret_cast<u32x4*>(&sK[key * KLD + ch * 8]) = kreg[it];
+    }
+#pragma unroll
+    for (int it = 0; it < VIT; ++it) {
+      const int idx = it * kPfThreads + tid;
+      const int kp = idx & (kPfKeys / 2 - 1);
+      const int ch = idx / (kPfKeys / 2);
+      const u32x4 w0 = vreg[it][0], w1 = vreg[it][1];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        // dims ch*8 + 2e and ch*8 + 2e + 1; each LDS word packs (key 2kp, key 2kp+1)
         const uint32_t lo = (w0[e] & 0xffffu) | (w1[e] << 16);
         const uint32_t hi = (w0[e] >> 16) | (w1[e] & 0xffff0000u);
         *reinterpret_cast<uint32_t*>(&sVt[(ch * 8 + 2 * e) * VLD + 2 * kp]) = lo;
@@ -207,6 +263,11 @@ __global__ __launch_bounds__(kPfThreads) void ragged_prefill_kernel(PrefillArgs 
       }
     }
     __syncthreads();
+    // ---- next tile's loads go out now and land while this tile computes ----
+    if (kt + 1 < nkt) {
+      ensure_table(kt + 1);
+      fetch(kt + 1);
+    }
 
     // ---- Sᵀ = K·Qᵀ: 4 key tiles x 2 row tiles -------------------------------------------------
     f32x4 sacc[4][2];
@@ -329,11 +390,12 @@ static int launch_prefill_dt(const PrefillLaunch& L, hipStream_t stream) {
   // sequences); slots past the real count exit at once.
   const long long slots = (L.num_tokens + kPfRows - 1) / kPfRows + (L.num_seqs < L.num_tokens / 2 ? L.num_seqs : L.num_tokens / 2);
   if (slots <= 0) return 0;
-  if (slots > 0x7fffffffLL || L.num_q_heads > 65535) return -1;
+  if (slots > 65535 || L.num_q_heads > 0x7fffffff) return -1;
+  // Heads are the fast grid dimension so the heaviest row tiles of every head go out first.
   if (L.head_dim == 128)
-    hipLaunchKernelGGL((ragged_prefill_kernel<DT, 128>), dim3((unsigned)slots, L.num_q_heads), dim3(kPfThreads), 0, stream, a);
+    hipLaunchKernelGGL((ragged_prefill_kernel<DT, 128>), dim3(L.num_q_heads, (unsigned)slots), dim3(kPfThreads), 0, stream, a);
   else
-    hipLaunchKernelGGL((ragged_prefill_kernel<DT, 64>), dim3((unsigned)slots, L.num_q_heads), dim3(kPfThreads), 0, stream, a);
+    hipLaunchKernelGGL((ragged_prefill_kernel<DT, 64>), dim3(L.num_q_heads, (unsigned)slots), dim3(kPfThreads), 0, stream, a);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
