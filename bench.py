@@ -154,6 +154,7 @@ def run_headline(args):
     w = make_workload("gqa", "full", block_size=args.block_size)
     ramp_repeats = 400
     loop = DecodeLoop(w, args.warmup + args.steps)
+    util = kv_utilisation(w, loop.st.bm, MAX_LEN["gqa"])
     for _ in range(args.warmup):
         loop.step()
     torch.cuda.synchronize()
@@ -190,7 +191,7 @@ def run_headline(args):
         kv_gbs=kv_per_step / (elapsed / K) / 1e9, kern_avg_us=kern_avg_s * 1e6, kern_med_us=float(np.median(kern_ms)) * 1e3,
         achieved=achieved, alg_per_launch=alg_per_launch, kv_per_step=kv_per_step,
         kern_kv_gbs=kv_per_step / kern_avg_s / 1e9, partition=loop.partition,
-        mean_ctx=float(np.mean([c.mean() for c in loop.ctx_history])),
+        mean_ctx=float(np.mean([c.mean() for c in loop.ctx_history])), util=util,
         merge_avg_us=float(np.mean(merge_ms)) * 1e3)
 
 
@@ -210,12 +211,28 @@ def _time_events(fn, reps=20, warm=3):
     return float(np.median(ms)) * 1e3, float(np.mean(ms)) * 1e3
 
 
+# Longest length a request of each workload may reach: what max-length preallocation reserves.
+MAX_LEN = {"gqa": 8192, "llama7b": 2048, "shared_prefix": 1000 + 512, "mixed": 4096}
+
+
+def kv_utilisation(w, bm, max_len, stored_tokens=None):
+    """KV memory actually holding tokens, paged vs max-length preallocation (the pages quote
+    20-40 % for the latter). Paged: tokens stored / slots of the blocks in use; preallocation:
+    every sequence reserves max_len slots and shares nothing."""
+    used = w.num_blocks - bm.num_free()
+    tokens = int(sum(w.context_lens)) if stored_tokens is None else int(stored_tokens)
+    return {"paged": round(tokens / (used * w.block_size), 4),
+            "max_len_prealloc": round(int(sum(w.context_lens)) / (len(w.context_lens) * max_len), 4),
+            "max_len": max_len, "blocks_in_use": int(used)}
+
+
 def run_decode_config(name, block_size=None, steps=30, warmup=5):
     """Decode-step loop for another configuration; returns partition-launch and step figures."""
     import torch
     from workloads import make_workload
     w = make_workload(name, "full", block_size=block_size)
     loop = DecodeLoop(w, warmup + steps + 2)
+    util = kv_utilisation(w, loop.st.bm, MAX_LEN[name])
     for _ in range(warmup):
         loop.step()
     torch.cuda.synchronize()
@@ -233,7 +250,8 @@ def run_decode_config(name, block_size=None, steps=30, warmup=5):
            "seqs_per_s": round(len(w.query_seqs) / el, 1), "kv_gbs_step": round(kv / el / 1e9, 1),
            "partition_launch_us": round(kern * 1e6, 1), "merge_launch_us": round(merge * 1e6, 1),
            "kv_gbs_partition_launch": round(kv / kern / 1e9, 1),
-           "pct_hbm_partition_launch": round(100 * kv / kern / 1e9 / HBM_PEAK_GBS, 1)}
+           "pct_hbm_partition_launch": round(100 * kv / kern / 1e9 / HBM_PEAK_GBS, 1),
+           "kv_memory_utilisation": util}
     del loop
     torch.cuda.empty_cache()
     return res
@@ -267,6 +285,7 @@ def run_shared_prefix():
         for j in range(-(-int(L) // w.block_size)):
             fill[int(t[j])] = max(fill.get(int(t[j]), 0), min(w.block_size, int(L) - j * w.block_size))
     unique = sum(fill.values()) * w.kv_bytes_per_token()
+    res["kv_memory_utilisation"] = kv_utilisation(w, st.bm, MAX_LEN["shared_prefix"], sum(fill.values()))
     res.update({"decode_us": round(med, 1), "decode_logical_gbs": round(logical / med / 1e3, 1),
                 "decode_unique_gbs": round(unique / med / 1e3, 1), "seqs_per_s": round(len(lens) / med * 1e6, 1)})
     del st
@@ -311,6 +330,7 @@ def run_mixed():
     st = R.play_script(w, threads=16)
     torch.cuda.synchronize()
     log(f"setup {w.name}: wrote {sum(w.context_lens)} tokens in {time.perf_counter() - t:.1f}s")
+    util = kv_utilisation(w, st.bm, MAX_LEN["mixed"])
     step_op = w.ops[-1]
     k, v = w.append_values(step_op, threads=16)
     kd, vd = R.to_device(k, w.dtype), R.to_device(v, w.dtype)
@@ -349,7 +369,7 @@ def run_mixed():
            "decode_kv_gb": round(dec_kv / 1e9, 3), "prefill_only_us": round(pre_us, 1),
            "prefill_gflop": round(flops / 1e9, 2), "prefill_tflops": round(flops / pre_us / 1e6, 1),
            "prefill_mfma_util": round(flops / pre_us / 1e6 / MFMA_BF16_PEAK_TFLOPS, 4),
-           "kv_cache_write_bytes": write_bytes}
+           "kv_cache_write_bytes": write_bytes, "kv_memory_utilisation": util}
     # cache write alone at the step's size
     w_us, _ = _time_events(lambda: pk.kv_cache_write(kd, vd, st.k_cache, st.v_cache, slots, st.desc), reps=20)
     res["kv_cache_write_us"] = round(w_us, 1)
@@ -487,6 +507,7 @@ def main():
                    "sum_ctx_first_step": int(sum(w.context_lens)) + len(w.context_lens),
                    "partition_tokens": h["partition"], "mean_ctx_timed": round(h["mean_ctx"], 1)},
         "seqs_per_s": round(h["seqs_per_s"], 1),
+        "kv_memory_utilisation": h["util"],
         "pct_hbm_peak_step": round(100 * h["kv_gbs"] / HBM_PEAK_GBS, 2),
         "roofline": {"bound": "hbm", "achieved": round(h["achieved"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(h["achieved"] / HBM_PEAK_GBS, 4), "traffic": load_traffic(w.block_size),
@@ -498,6 +519,7 @@ def main():
     if not args.no_extra:
         extra = {}
         for key, fn in (("gqa_B32", lambda: run_decode_config("gqa", 32)),
+                        ("gqa_B8", lambda: run_decode_config("gqa", 8)),
                         ("llama7b", lambda: run_decode_config("llama7b")),
                         ("shared_prefix", run_shared_prefix),
                         ("mixed", run_mixed)):

@@ -130,9 +130,11 @@ int32_t pkv_decode_partition_size(int32_t num_seqs, int32_t num_q_heads, int32_t
  *   block_tables  device int32 [num_seqs][max_blocks_per_seq]; entries past a sequence's
  *                 last block are never read.
  *   context_lens  device int32 [num_seqs], each in [0, max_context_len] and
- *                 <= max_blocks_per_seq * B. A length of 0 gives an all-zero output row.
+ *                 <= max_blocks_per_seq * B. A length of 0 gives an all-zero output row. A length
+ *                 outside that range is a caller error: the kernels clamp it to stay in bounds,
+ *                 so the row is then computed over the clamped context.
  *   max_context_len  host upper bound of context_lens (sizes the split; not a limit check).
- *   scale         multiplier of q·k (1/sqrt(D) for standard attention).
+ *   scale         multiplier of q·k, positive and finite (1/sqrt(D) for standard attention).
  *   workspace     device, >= pkv_decode_workspace_bytes(...) bytes (may be NULL when that is 0).
  *   Long contexts are cut into partitions that are processed independently and merged with
  *   log-sum-exp weights; the result does not depend on which physical blocks hold the data.
@@ -196,6 +198,9 @@ size_t pkv_decode_workspace_bytes_ex(int32_t num_seqs, int32_t num_q_heads,
  *                 cu[num_seqs] = num_tokens.
  *   context_lens  device int32 [num_seqs], context_lens[s] >= q_len_s.
  *   max_q_len, max_context_len  host upper bounds (launch sizing only).
+ *   scale         multiplier of q·k, positive and finite.
+ *   Rows of prefill chunks (q_len > 1) need an f16 or bf16 pool (PKV_EDTYPE for f32); rows of
+ *   decode sequences work for every dtype.
  *   workspace     device, >= pkv_ragged_workspace_bytes(...) bytes (NULL when that is 0);
  *                 scratch between calls, as for decode.
  */

@@ -2,6 +2,7 @@
 // The kernels live in cache_ops.hip, decode.hip and ragged.hip; the host block manager in
 // block_manager.cpp.
 #include <hip/hip_runtime.h>
+#include <math.h>
 #include <stdint.h>
 
 #include "../../include/pagedkv.h"
@@ -159,7 +160,7 @@ static int32_t decode_common_cu(void* out, int32_t out_dtype, const void* q, con
   if (num_seqs > 65535) return PKV_ESHAPE;
   if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens) return PKV_EINVAL;
   if ((int64_t)max_blocks_per_seq * c->block_size < max_context_len) return PKV_EINVAL;
-  if (!(scale == scale)) return PKV_EINVAL;
+  if (!(scale > 0.f) || !(scale < INFINITY)) return PKV_EINVAL;  // a positive, finite multiplier
   const int p = partition_size > 0 ? partition_size
                                    : pkv_decode_partition_size(num_seqs, num_q_heads, max_context_len, c);
   if (!valid_partition(p, c->block_size)) return PKV_EINVAL;

@@ -112,4 +112,20 @@ __device__ __forceinline__ void store_out(void* base, size_t idx, float v, int o
   }
 }
 
+// Store four consecutive fp32 values (idx a multiple of 4) as the output element type.
+__device__ __forceinline__ void store_out4(void* base, size_t idx, float __attribute__((ext_vector_type(4))) v,
+                                           int out_dt) {
+  if (out_dt == DT_F32) {
+    *reinterpret_cast<float __attribute__((ext_vector_type(4)))*>(reinterpret_cast<float*>(base) + idx) = v;
+  } else if (out_dt == DT_F16) {
+    const uint32_t lo = __builtin_bit_cast(uint32_t, f16x2{(_Float16)v[0], (_Float16)v[1]});
+    const uint32_t hi = __builtin_bit_cast(uint32_t, f16x2{(_Float16)v[2], (_Float16)v[3]});
+    *reinterpret_cast<u32x2*>(reinterpret_cast<_Float16*>(base) + idx) = u32x2{lo, hi};
+  } else {
+    const uint32_t lo = f32_to_bf16_bits(v[0]) | ((uint32_t)f32_to_bf16_bits(v[1]) << 16);
+    const uint32_t hi = f32_to_bf16_bits(v[2]) | ((uint32_t)f32_to_bf16_bits(v[3]) << 16);
+    *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(base) + idx) = u32x2{lo, hi};
+  }
+}
+
 }  // namespace pkv

@@ -124,7 +124,9 @@ __global__ __launch_bounds__(kDecThreads) void paged_decode_kernel(DecodeArgs a)
     row = a.cu[s];
     if (a.cu[s + 1] - row != 1) return;
   }
-  const int ctx = a.ctx_lens[s];
+  // A length beyond the table or the launch's partitions breaks the caller's contract; clamping
+  // keeps every access inside the table and the workspace.
+  const int ctx = min(a.ctx_lens[s], min(a.max_blocks * a.bs, a.max_parts * a.partition));
   const int nparts = ctx > 0 ? (ctx + a.partition - 1) / a.partition : 1;
   if (part >= nparts) return;  // uniform over the workgroup
   const int t0 = part * a.partition;
@@ -311,7 +313,7 @@ __global__ __launch_bounds__(256) void paged_decode_merge_kernel(DecodeArgs a, i
     row = a.cu[s];
     if (a.cu[s + 1] - row != 1) return;
   }
-  const int ctx = a.ctx_lens[s];
+  const int ctx = min(a.ctx_lens[s], min(a.max_blocks * a.bs, a.max_parts * a.partition));
   const int nparts = ctx > 0 ? (ctx + a.partition - 1) / a.partition : 1;
   if (nparts <= 1) return;
   const int h = o / head_dim;

@@ -67,13 +67,17 @@ struct PrefillArgs {
 constexpr int kPfTab = 1024;  // block-table entries cached in LDS at a time
 
 template <int DT, int D>
-__global__ __launch_bounds__(kPfThreads) void ragged_prefill_kernel(PrefillArgs a) {
+// Two workgroups per CU: the register budget is capped at 256 per lane so that one wave's MFMA
+// work overlaps the other's softmax and staging.
+__global__ __launch_bounds__(kPfThreads, 2) void ragged_prefill_kernel(PrefillArgs a) {
   using M = Mfma<DT>;
   using V8 = typename M::V8;
   constexpr int KS = D / 32;         // k-steps of Sᵀ = K·Qᵀ
   constexpr int DT16 = D / 16;       // 16-row tiles of the head dim (M-tiles of Oᵀ)
   constexpr int KLD = D + 8;         // LDS row stride of the K tile (elements)
-  constexpr int VLD = kPfKeys + 8;   // LDS row stride of the transposed V tile (elements)
+  // LDS row stride of the transposed V tile: 34 dwords, so the 16 rows one operand read touches
+  // land on distinct bank pairs.
+  constexpr int VLD = kPfKeys + 4;
   constexpr int CPR = D / 8;         // 16-byte chunks per K/V row
   constexpr int KIT = kPfKeys * CPR / kPfThreads;        // K chunks staged per thread
   constexpr int VIT = (kPfKeys / 2) * CPR / kPfThreads;  // V key-pair chunks staged per thread
@@ -148,7 +152,7 @@ __global__ __launch_bounds__(kPfThreads) void ragged_prefill_kernel(PrefillArgs 
   if (s < 0) return;  // uniform: this slot of the launch has no tile
   const int q0 = a.cu[s];
   const int ql = a.cu[s + 1] - q0;
-  const int ctx = a.ctx_lens[s];
+  const int ctx = min(a.ctx_lens[s], a.max_blocks * a.bs);  // contract: ctx fits the table
   const int row0 = s_tile * kPfRows;
   const int nrows = min(kPfRows, ql - row0);
   const int pos0 = ctx - ql + row0;      // position of the tile's first query row
@@ -284,39 +288,46 @@ __global__ __launch_bounds__(kPfThreads) void ragged_prefill_kernel(PrefillArgs 
     }
 
     // ---- causal mask and online softmax (per query row = per lane column) ----------------------
+    // Scores stay unscaled here; exp2((s - m)·scale·log2 e) is one FMA per score. Only tiles that
+    // reach past a wave's first row need the causal mask (a wave-uniform test).
+    const bool need_mask = k0 + kPfKeys - 1 > pos0 + wave * 32;
     V8 phi[2][2], plo[2][2];  // [row tile][k-step of 32 keys]
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
-      float sv[4][4];
+      if (need_mask) {
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (k0 + 16 * mt + 4 * g + i > qpos[nt]) sacc[mt][nt][i] = -INFINITY;
+      }
       float mx = -INFINITY;
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int kk = k0 + 16 * mt + 4 * g + i;
-          const float v = kk <= qpos[nt] ? sacc[mt][nt][i] * a.scale_log2 : -INFINITY;
-          sv[mt][i] = v;
-          mx = fmaxf(mx, v);
-        }
+        mx = fmaxf(fmaxf(mx, fmaxf(sacc[mt][nt][0], sacc[mt][nt][1])), fmaxf(sacc[mt][nt][2], sacc[mt][nt][3]));
       mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
       mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
       const float m_new = fmaxf(m_run[nt], mx);
       // Row with no visible key yet (only possible for padding rows): keep everything at zero.
       const float m_use = m_new == -INFINITY ? 0.f : m_new;
-      const float alpha = fast_exp2(m_run[nt] - m_use);
+      const float alpha = fast_exp2((m_run[nt] - m_use) * a.scale_log2);
       m_run[nt] = m_new;
+      const float off = -m_use * a.scale_log2;
       float lsum = 0.f;
       float p[4][4];
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          p[mt][i] = fast_exp2(sv[mt][i] - m_use);
+          p[mt][i] = fast_exp2(__builtin_fmaf(sacc[mt][nt][i], a.scale_log2, off));
           lsum += p[mt][i];
         }
       l_part[nt] = l_part[nt] * alpha + lsum;
+      // Rescale the running output only when some row's max moved (rare after the first tiles).
+      if (__builtin_amdgcn_read_exec() & __ballot(alpha != 1.f)) {
 #pragma unroll
-      for (int dt = 0; dt < DT16; ++dt) oacc[dt][nt] *= alpha;
+        for (int dt = 0; dt < DT16; ++dt) oacc[dt][nt] *= alpha;
+      }
       // B operand of k-step j: keys 32j + 4g + (0..3) then 32j + 16 + 4g + (0..3).
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
@@ -362,9 +373,7 @@ __global__ __launch_bounds__(kPfThreads) void ragged_prefill_kernel(PrefillArgs 
     const float inv = l > 0.f ? 1.f / l : 0.f;
     const size_t orow = ((size_t)(q0 + wave * 32 + nt * 16 + lr + row0) * a.hq + h) * D;
 #pragma unroll
-    for (int dt = 0; dt < DT16; ++dt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) store_out(a.out, orow + 16 * dt + 4 * g + i, oacc[dt][nt][i] * inv, a.out_dt);
+    for (int dt = 0; dt < DT16; ++dt) store_out4(a.out, orow + 16 * dt + 4 * g, oacc[dt][nt] * inv, a.out_dt);
   }
 }
 

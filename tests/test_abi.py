@@ -45,10 +45,10 @@ L = pk._lib
 NULL = None
 
 
-def decode(c, hq=4, out_dt=None, S=2, max_ctx=100, ws=None, wsb=0, part=0, mb=8):
+def decode(c, hq=4, out_dt=None, S=2, max_ctx=100, ws=None, wsb=0, part=0, mb=8, scale=0.125):
     return L.pkv_paged_attention_decode_ex(ctypes.c_void_p(1), c.dtype if out_dt is None else out_dt,
                                            ctypes.c_void_p(1), ctypes.c_void_p(1), ctypes.c_void_p(1),
-                                           ctypes.c_void_p(1), mb, ctypes.c_void_p(1), S, hq, 0.125, max_ctx,
+                                           ctypes.c_void_p(1), mb, ctypes.c_void_p(1), S, hq, scale, max_ctx,
                                            ctypes.byref(c), part, ws, wsb, NULL)
 
 
@@ -65,6 +65,10 @@ def test_decode_rejects_bad_heads_and_dtypes():
     assert decode(desc(), hq=64) == -3         # group 16 unsupported
     assert decode(desc(), out_dt=pk.BF16) == -2  # f16 pool, bf16 out
     assert decode(desc(), mb=2) == -1          # table cannot hold max_ctx
+    assert decode(desc(), scale=0.0) == -1
+    assert decode(desc(), scale=-0.125) == -1
+    assert decode(desc(), scale=float("nan")) == -1
+    assert decode(desc(), scale=float("inf")) == -1
 
 
 def test_decode_workspace_validation():
@@ -102,3 +106,17 @@ def test_status_strings():
     for s in range(-8, 1):
         assert L.pkv_status_str(s)
     assert b"gfx950" in L.pkv_version()
+
+
+def ragged(c, hq=4, out_dt=None, S=2, T=5, max_q=3, max_ctx=100, mb=8):
+    p = ctypes.c_void_p(1)
+    return L.pkv_paged_attention_ragged(p, c.dtype if out_dt is None else out_dt, p, p, p, p, p, p, mb, S, T, hq,
+                                        0.125, max_q, max_ctx, ctypes.byref(c), NULL, 0, NULL)
+
+
+def test_ragged_validation():
+    assert ragged(desc(dtype=pk.F32), max_q=3) == -2     # prefill rows need a 16-bit pool
+    assert ragged(desc(), max_q=200, max_ctx=100) == -1  # q_len cannot exceed the context
+    assert ragged(desc(), max_q=6, T=5) == -1            # nor the token count
+    assert ragged(desc(), hq=6) == -3
+    assert ragged(desc(), S=0) == 0 and ragged(desc(), T=0) == 0

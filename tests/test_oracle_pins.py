@@ -68,3 +68,11 @@ def test_shared_prefix_small_pairs():
     st, _ = oracle.run_workload(w, attend=False)
     n_req = len(w.query_seqs) // 4
     assert len(st.pairs_per_append[-2]) == n_req * 3
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_oracle_matches_sdpa_on_churn(seed):
+    """Beam-search-like fork/append/free churn: the paged oracle still equals SDPA over each
+    live sequence's contiguous history."""
+    from workloads import make_churn_workload
+    P.pin_sdpa(make_churn_workload(seed, 8, 4, 2, 64, "f16"))

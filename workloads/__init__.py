@@ -15,6 +15,7 @@ from .synth import (  # noqa: F401
     make_workload,
     make_decode_workload,
     make_ragged_workload,
+    make_churn_workload,
     CONFIG_NAMES,
     gen_kv,
     gen_q,

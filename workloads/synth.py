@@ -225,6 +225,47 @@ def make_ragged_workload(seed: int, q_lens: List[int], ctx: List[int], hq: int, 
                     list(ctx))
 
 
+def make_churn_workload(seed: int, block_size: int, hq: int, hkv: int, head_dim: int, dtype: str,
+                        n_ops: int = 150, max_live: int = 10, slack: float = 1.25,
+                        name: str = "churn") -> Workload:
+    """Beam-search-like churn: sequences are added, forked at arbitrary points, extended in
+    batches and freed, so blocks are shared, copied on write and released repeatedly. The final
+    query is one decode row for every live sequence with a non-empty context.
+
+    The pool is sized from an upper bound (every live sequence's own blocks, as if nothing were
+    shared), so no append can run out of blocks.
+    """
+    r = _rng(seed, _S_LENGTHS)
+    ops: List[Op] = []
+    lens = {}
+    nxt = 0
+    peak = 0
+    for i in range(n_ops):
+        x = r.random()
+        live = sorted(lens)
+        if not live or (x < 0.12 and len(live) < max_live):
+            ops.append(AddOp(nxt)); lens[nxt] = 0; nxt += 1
+        elif x < 0.35 and len(live) < max_live:
+            p = int(live[r.integers(len(live))])
+            ops.append(ForkOp(p, nxt)); lens[nxt] = lens[p]; nxt += 1
+        elif x < 0.45 and len(live) > 2:
+            sq = int(live[r.integers(len(live))])
+            ops.append(FreeOp(sq)); del lens[sq]
+        else:
+            k = int(r.integers(1, min(len(live), 4) + 1))
+            pick = [int(v) for v in r.choice(live, size=k, replace=False)]
+            ns = [int(r.integers(0, 3 * block_size)) for _ in pick]
+            ops.append(AppendOp(pick, ns, tag=100 + i))
+            for sq, n in zip(pick, ns):
+                lens[sq] += n
+        peak = max(peak, sum(-(-v // block_size) for v in lens.values()))
+    q = [sq for sq in sorted(lens) if lens[sq] > 0]
+    nb = max(1, int(math.ceil(slack * peak)) + 4)
+    perm = _rng(seed, _S_PERM).permutation(nb).astype(np.int32)
+    return Workload(name, seed, dtype, block_size, hq, hkv, head_dim, nb, perm, ops, q, [1] * len(q),
+                    [lens[sq] for sq in q])
+
+
 def make_workload(name: str, size: str = "full", block_size: Optional[int] = None,
                   slack: float = 1.5) -> Workload:
     if size not in ("full", "small"):
