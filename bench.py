@@ -307,6 +307,32 @@ def run_shared_prefix():
     return res
 
 
+def run_swap():
+    """Preemption traffic: whole GQA-shaped blocks (8 kv heads x 16 slots x 128 dims, bf16) moved
+    between the GPU pool and a pinned host swap pool by pkv_swap_blocks, both directions."""
+    import torch
+    from paged_kv_cache_323_amd import native as pk
+    nb, H, B, D = 8192, 8, 16, 128
+    dk = torch.empty((nb, H, B, D), dtype=torch.bfloat16, device="cuda").normal_()
+    dv = torch.empty_like(dk).normal_()
+    hk = torch.empty((nb, H, B, D), dtype=torch.bfloat16, pin_memory=True)
+    hv = torch.empty_like(hk, pin_memory=True)
+    desc = pk.CacheDesc.make(nb, B, H, D, "bf16")
+    n = 4096
+    perm = np.random.default_rng(9).permutation(nb).astype(np.int32)
+    out_pairs = torch.from_numpy(np.ascontiguousarray(np.stack([perm[:n], perm[n:2 * n]], 1))).cuda()
+    in_pairs = torch.from_numpy(np.ascontiguousarray(np.stack([perm[n:2 * n], perm[:n]], 1))).cuda()
+    out_us, _ = _time_events(lambda: pk.swap_blocks(hk, hv, dk, dv, out_pairs, desc), reps=10)
+    in_us, _ = _time_events(lambda: pk.swap_blocks(dk, dv, hk, hv, in_pairs, desc), reps=10)
+    moved = 2 * n * H * B * D * 2
+    res = {"blocks": n, "bytes_per_direction": moved, "swap_out_us": round(out_us, 1),
+           "swap_out_gbs": round(moved / out_us / 1e3, 1), "swap_in_us": round(in_us, 1),
+           "swap_in_gbs": round(moved / in_us / 1e3, 1)}
+    del dk, dv, hk, hv
+    torch.cuda.empty_cache()
+    return res
+
+
 def prefill_flops(q_lens, ctx, hq, d):
     """4·d·Hq per causal (query, key) pair: query at position p sees p+1 keys."""
     tot = 0
@@ -522,6 +548,7 @@ def main():
                         ("gqa_B8", lambda: run_decode_config("gqa", 8)),
                         ("llama7b", lambda: run_decode_config("llama7b")),
                         ("shared_prefix", run_shared_prefix),
+                        ("swap", run_swap),
                         ("mixed", run_mixed)):
             log(f"extra: {key}")
             try:

@@ -58,7 +58,8 @@ typedef enum {
   PKV_ELAUNCH = -5,     /* the HIP launch itself failed                   */
   PKV_ENOBLOCKS = -6,   /* block manager: pool exhausted (nothing changed) */
   PKV_ENOSEQ = -7,      /* block manager: unknown sequence id             */
-  PKV_EEXIST = -8       /* block manager: sequence id already present     */
+  PKV_EEXIST = -8,      /* block manager: sequence id already present     */
+  PKV_ENOTRESIDENT = -9 /* block manager: sequence is (or is not) swapped out as required */
 } pkv_status;
 
 /* Shape of one layer's K and V pools. */
@@ -217,6 +218,21 @@ int32_t pkv_paged_attention_ragged(void* out, int32_t out_dtype, const void* q,
                                    const pkv_cache_desc* cache, void* workspace,
                                    size_t workspace_bytes, void* stream);
 
+/*
+ * swap_blocks — move whole blocks between a GPU pool and a host swap pool for preemption and
+ *   restore (「PagedAttention原理」 §抢占与恢复 / §swap). For each pair i: block dst_i of
+ *   (dst_k, dst_v) <- block src_i of (src_k, src_v), all B slots, all kv heads, bit for bit.
+ *   Either side may be device memory or pinned host memory that the device can address (e.g.
+ *   hipHostMalloc); both use the pool layout above with the same block shape (num_blocks of the
+ *   descriptor is not used). The copy runs as a kernel on `stream`, so it is ordered with the
+ *   attention and cache writes around it.
+ *   block_pairs  device (or device-addressable) int32 [num_pairs][2] = (src, dst); destinations
+ *                distinct. num_pairs == 0 is a no-op.
+ */
+int32_t pkv_swap_blocks(void* dst_k, void* dst_v, const void* src_k, const void* src_v,
+                        const int32_t* block_pairs, int32_t num_pairs, const pkv_cache_desc* cache,
+                        void* stream);
+
 /* ------------------------------------------------------------------------------------------
  * Host block manager (CPU only; touches no device memory). Deterministic:
  *   - a sequence takes a new block only when its last block is full
@@ -231,9 +247,15 @@ int32_t pkv_paged_attention_ragged(void* out, int32_t out_dtype, const void* q,
  *     blocks at zero (「Paged Attention&Orca Paper笔记与解读」 §PagedAttention的方法);
  *   - an append is all-or-nothing: on PKV_ENOBLOCKS no state changes
  *     (「PagedAttention原理」 §all-or-nothing 调度).
+ *   - preemption: a set of sequences is swapped to a host swap pool and back as a whole or not
+ *     at all; while swapped out a sequence cannot be appended to, forked or attended
+ *     (PKV_ENOTRESIDENT). A block also referenced by a sequence outside the set is copied
+ *     (its count drops by the set's references) instead of moved, so the swap space never holds
+ *     more blocks than the GPU pool (「PagedAttention原理」 §抢占与恢复, §swap;
+ *     「Paged Attention&Orca Paper笔记与解读」 §PagedAttention的方法).
  * Tie-breaks: free blocks are taken from the head of the creation-time order and released
  * blocks join its tail in logical-block order; sequences of one append are served in the
- * order given, tokens in position order.
+ * order given, tokens in position order; swaps take destinations in first-reference order.
  * A pkv_bm object is not thread-safe.
  * ------------------------------------------------------------------------------------------ */
 typedef struct pkv_bm pkv_bm;
@@ -265,7 +287,7 @@ int32_t pkv_bm_append(pkv_bm* bm, const int64_t* seq_ids, const int32_t* n_token
                       int32_t* slots_out, int32_t* cow_pairs_out, int32_t max_pairs,
                       int32_t* num_pairs_out);
 
-/* Block tables and context lengths of n sequences into host arrays:
+/* Block tables and context lengths of n resident sequences into host arrays:
  * tables_out [n][max_blocks] padded with -1; ctx_out [n] (may be NULL). */
 int32_t pkv_bm_block_tables(const pkv_bm* bm, const int64_t* seq_ids, int32_t n, int32_t max_blocks,
                             int32_t* tables_out, int32_t* ctx_out);
@@ -277,6 +299,24 @@ int32_t pkv_bm_refcount(const pkv_bm* bm, int32_t block);
 int32_t pkv_bm_num_free(const pkv_bm* bm);
 /* Free list from head to tail into host out[cap]; returns its length. */
 int32_t pkv_bm_free_list(const pkv_bm* bm, int32_t* out, int32_t cap);
+
+/* Gives the manager a host swap pool of num_host_blocks blocks (ids 0..n-1; free_order a
+ * permutation or NULL for the identity). Once per manager. */
+int32_t pkv_bm_attach_host_pool(pkv_bm* bm, int32_t num_host_blocks, const int32_t* free_order);
+
+/* Swap out (resp. in) the n sequences seq_ids (host array, distinct, all resident (resp. all
+ * swapped out)). pairs_out receives (src, dst) block pairs to copy with pkv_swap_blocks BEFORE
+ * any later write reuses a released block: (GPU block, host block) for swap_out, (host block,
+ * GPU block) for swap_in; at most one pair per distinct block of the set, max_pairs is the
+ * capacity. All or nothing: PKV_ENOBLOCKS (target pool short) leaves the manager unchanged. */
+int32_t pkv_bm_swap_out(pkv_bm* bm, const int64_t* seq_ids, int32_t n, int32_t* pairs_out,
+                        int32_t max_pairs, int32_t* num_pairs_out);
+int32_t pkv_bm_swap_in(pkv_bm* bm, const int64_t* seq_ids, int32_t n, int32_t* pairs_out,
+                       int32_t max_pairs, int32_t* num_pairs_out);
+/* 1 if resident on the GPU, 0 if swapped out, negative status on error. */
+int32_t pkv_bm_is_resident(const pkv_bm* bm, int64_t seq_id);
+int32_t pkv_bm_host_refcount(const pkv_bm* bm, int32_t host_block);
+int32_t pkv_bm_host_free_list(const pkv_bm* bm, int32_t* out, int32_t cap);
 
 #ifdef __cplusplus
 }

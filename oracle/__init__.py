@@ -32,6 +32,6 @@ from .attention import (  # noqa: F401
     paged_decode,
     paged_ragged,
 )
-from .block_manager import BlockManager, NoFreeBlocks  # noqa: F401
-from .pool import new_pool, write_slots, copy_blocks  # noqa: F401
+from .block_manager import BlockManager, NoFreeBlocks, NotResident  # noqa: F401
+from .pool import new_pool, write_slots, copy_blocks, copy_between  # noqa: F401
 from .run import run_workload, OracleState  # noqa: F401

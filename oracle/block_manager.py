@@ -21,6 +21,12 @@ Rules followed, in the pages' terms:
     its count; freeing drops counts and releases blocks that reach zero.
   * 「PagedAttention原理」 §all-or-nothing 调度: a batch append either succeeds for
     every sequence or changes nothing (raises ``NoFreeBlocks``).
+  * 「PagedAttention原理」 §抢占与恢复 / §swap and 「Paged Attention&Orca Paper笔记与解读」
+    §PagedAttention的方法 (eviction to CPU memory): a group of sequences is preempted or
+    restored as a whole: every block the group references moves between the GPU pool and a
+    host swap pool, or nothing happens. A sequence runs only while all its blocks are on the
+    GPU. A block that some sequence outside the group still references is copied instead of
+    moved, so the swap space never holds more than the GPU blocks the group used.
 
 Choices where the pages leave freedom (any choice is valid; this one is the
 deterministic contract the device-side block manager must reproduce):
@@ -40,6 +46,10 @@ class NoFreeBlocks(RuntimeError):
     pass
 
 
+class NotResident(RuntimeError):
+    pass
+
+
 class BlockManager:
     def __init__(self, num_blocks: int, block_size: int, free_order: Sequence[int]):
         if sorted(int(b) for b in free_order) != list(range(num_blocks)):
@@ -50,6 +60,19 @@ class BlockManager:
         self.rc: List[int] = [0] * num_blocks
         self.tables: Dict[int, List[int]] = {}
         self.lens: Dict[int, int] = {}
+        self.on_host: Dict[int, bool] = {}
+        self.host_free = deque()
+        self.host_rc: List[int] = []
+        self.num_host_blocks = 0
+
+    def attach_host_pool(self, num_host_blocks: int, free_order: Sequence[int]) -> None:
+        if self.num_host_blocks:
+            raise ValueError("host pool already attached")
+        if sorted(int(b) for b in free_order) != list(range(num_host_blocks)):
+            raise ValueError("free_order must be a permutation of the host block ids")
+        self.num_host_blocks = int(num_host_blocks)
+        self.host_free = deque(int(b) for b in free_order)
+        self.host_rc = [0] * num_host_blocks
 
     # ---- sequences -------------------------------------------------------------------------
     def add_seq(self, seq: int) -> None:
@@ -57,21 +80,76 @@ class BlockManager:
             raise KeyError(f"sequence {seq} exists")
         self.tables[seq] = []
         self.lens[seq] = 0
+        self.on_host[seq] = False
+
+    def _resident(self, seq: int) -> None:
+        if self.on_host.get(seq):
+            raise NotResident(f"sequence {seq} is swapped out")
 
     def fork(self, parent: int, child: int) -> None:
         if child in self.tables:
             raise KeyError(f"sequence {child} exists")
+        self._resident(parent)
+        self.on_host[child] = False
         self.tables[child] = list(self.tables[parent])
         self.lens[child] = self.lens[parent]
         for b in self.tables[child]:
             self.rc[b] += 1
 
     def free_seq(self, seq: int) -> None:
+        host = self.on_host.pop(seq)
+        rc, free = (self.host_rc, self.host_free) if host else (self.rc, self.free)
         for b in self.tables.pop(seq):
-            self.rc[b] -= 1
-            if self.rc[b] == 0:
-                self.free.append(b)
+            rc[b] -= 1
+            if rc[b] == 0:
+                free.append(b)
         del self.lens[seq]
+
+    # ---- swap ------------------------------------------------------------------------------
+    def _move(self, seqs, to_host: bool):
+        """Move (or copy, when referenced outside ``seqs``) every block of ``seqs`` to the
+        other pool. Returns [(src_block, dst_block)] in first-reference order."""
+        seqs = [int(s) for s in seqs]
+        if len(set(seqs)) != len(seqs):
+            raise ValueError("duplicate sequence")
+        for s in seqs:
+            if s not in self.tables:
+                raise KeyError(f"unknown sequence {s}")
+            if self.on_host[s] == to_host:
+                raise NotResident(f"sequence {s} is already {'on the host' if to_host else 'resident'}")
+        src_rc, src_free = (self.rc, self.free) if to_host else (self.host_rc, self.host_free)
+        dst_rc, dst_free = (self.host_rc, self.host_free) if to_host else (self.rc, self.free)
+        order, refs = [], {}
+        for s in seqs:
+            for b in self.tables[s]:
+                if b not in refs:
+                    order.append(b)
+                    refs[b] = 0
+                refs[b] += 1
+        if len(order) > len(dst_free):
+            raise NoFreeBlocks("swap pool exhausted" if to_host else "pool exhausted")
+        mapping, pairs = {}, []
+        for b in order:
+            nb = dst_free.popleft()
+            dst_rc[nb] = refs[b]
+            mapping[b] = nb
+            pairs.append((b, nb))
+        for s in seqs:
+            self.tables[s] = [mapping[b] for b in self.tables[s]]
+            self.on_host[s] = to_host
+        for b in order:
+            src_rc[b] -= refs[b]
+            if src_rc[b] == 0:
+                src_free.append(b)
+        return pairs
+
+    def swap_out(self, seqs):
+        """Preempt ``seqs`` to the host pool; returns [(gpu_block, host_block)] to copy first."""
+        return self._move(seqs, True)
+
+    def swap_in(self, seqs):
+        """Restore ``seqs`` to the GPU pool; returns [(host_block, gpu_block)] to copy first."""
+        return self._move(seqs, False)
 
     # ---- appends ---------------------------------------------------------------------------
     def _take(self) -> int:
@@ -109,6 +187,7 @@ class BlockManager:
             for s, n in zip(seqs, n_tokens):
                 if s not in self.tables:
                     raise KeyError(f"unknown sequence {s}")
+                self._resident(s)
                 for _ in range(int(n)):
                     self._append_one(int(s), slots, pairs)
         except Exception:
@@ -131,6 +210,15 @@ class BlockManager:
 
     def free_list(self) -> List[int]:
         return list(self.free)
+
+    def host_refcount(self, block: int) -> int:
+        return self.host_rc[block]
+
+    def host_free_list(self) -> List[int]:
+        return list(self.host_free)
+
+    def is_resident(self, seq: int) -> bool:
+        return not self.on_host[seq]
 
     def padded_tables(self, seqs: Sequence[int], max_blocks: int):
         import numpy as np

@@ -48,3 +48,11 @@ def copy_blocks(pool_k: np.ndarray, pool_v: np.ndarray, pairs) -> None:
     for src, dst in pairs:
         pool_k[int(dst)] = pool_k[int(src)]
         pool_v[int(dst)] = pool_v[int(src)]
+
+
+def copy_between(dst_k: np.ndarray, dst_v: np.ndarray, src_k: np.ndarray, src_v: np.ndarray, pairs) -> None:
+    """dst[d] <- src[s] for every (s, d): whole blocks between two pools (GPU pool and host
+    swap pool), bit for bit (「PagedAttention原理」 §swap)."""
+    for s_, d_ in pairs:
+        dst_k[int(d_)] = src_k[int(s_)]
+        dst_v[int(d_)] = src_v[int(s_)]

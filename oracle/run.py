@@ -14,7 +14,7 @@ import numpy as np
 
 from .attention import paged_ragged
 from .block_manager import BlockManager
-from .pool import copy_blocks, new_pool, write_slots
+from .pool import copy_between, copy_blocks, new_pool, write_slots
 
 
 @dataclass
@@ -22,6 +22,8 @@ class OracleState:
     bm: BlockManager
     pool_k: np.ndarray
     pool_v: np.ndarray
+    host_k: np.ndarray = None
+    host_v: np.ndarray = None
     slots_per_append: List[List[int]] = field(default_factory=list)
     pairs_per_append: List[List[Tuple[int, int]]] = field(default_factory=list)
 
@@ -52,9 +54,21 @@ def run_workload(w, only_seqs: Optional[Sequence[int]] = None, attend: bool = Tr
     pk = new_pool(w.num_blocks, w.block_size, w.num_kv_heads, w.head_dim, w.dtype)
     pv = new_pool(w.num_blocks, w.block_size, w.num_kv_heads, w.head_dim, w.dtype)
     st = OracleState(bm, pk, pv)
+    if getattr(w, "num_host_blocks", 0):
+        bm.attach_host_pool(w.num_host_blocks, w.host_free_order)
+        st.host_k = new_pool(w.num_host_blocks, w.block_size, w.num_kv_heads, w.head_dim, w.dtype)
+        st.host_v = new_pool(w.num_host_blocks, w.block_size, w.num_kv_heads, w.head_dim, w.dtype)
     for op in w.ops:
         kind = type(op).__name__
-        if kind == "AddOp":
+        if kind == "SwapOutOp":
+            pairs = bm.swap_out(op.seqs)
+            st.pairs_per_append.append(pairs)
+            copy_between(st.host_k, st.host_v, pk, pv, pairs)
+        elif kind == "SwapInOp":
+            pairs = bm.swap_in(op.seqs)
+            st.pairs_per_append.append(pairs)
+            copy_between(pk, pv, st.host_k, st.host_v, pairs)
+        elif kind == "AddOp":
             bm.add_seq(op.seq)
         elif kind == "ForkOp":
             bm.fork(op.parent, op.child)

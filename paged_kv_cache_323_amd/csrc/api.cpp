@@ -83,6 +83,7 @@ const char* pkv_status_str(int32_t s) {
     case PKV_ENOBLOCKS: return "no free blocks";
     case PKV_ENOSEQ: return "unknown sequence";
     case PKV_EEXIST: return "sequence exists";
+    case PKV_ENOTRESIDENT: return "sequence not in the required pool (swapped out or resident)";
   }
   return "unknown status";
 }
@@ -118,6 +119,20 @@ int32_t pkv_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs, int3
   if (!k_cache || !v_cache || !pairs) return PKV_EINVAL;
   const int64_t block_bytes = (int64_t)c->num_kv_heads * c->block_size * c->head_dim * elem_bytes(c->dtype);
   return pkv::launch_copy_blocks(k_cache, v_cache, pairs, num_pairs, block_bytes, (hipStream_t)stream) == 0
+             ? PKV_OK
+             : PKV_ELAUNCH;
+}
+
+int32_t pkv_swap_blocks(void* dst_k, void* dst_v, const void* src_k, const void* src_v, const int32_t* pairs,
+                        int32_t num_pairs, const pkv_cache_desc* c, void* stream) {
+  int32_t st = check_cache(c);
+  if (st != PKV_OK) return st;
+  if (num_pairs < 0) return PKV_EINVAL;
+  if (num_pairs == 0) return PKV_OK;
+  if (!dst_k || !dst_v || !src_k || !src_v || !pairs) return PKV_EINVAL;
+  const int64_t block_bytes = (int64_t)c->num_kv_heads * c->block_size * c->head_dim * elem_bytes(c->dtype);
+  return pkv::launch_copy_between(dst_k, dst_v, src_k, src_v, pairs, num_pairs, block_bytes,
+                                  (hipStream_t)stream) == 0
              ? PKV_OK
              : PKV_ELAUNCH;
 }

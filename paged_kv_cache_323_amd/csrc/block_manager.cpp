@@ -12,7 +12,12 @@
 //   - 「Paged Attention&Orca Paper笔记与解读」 §PagedAttention的方法: fork shares every block of
 //     the parent (count + 1); free drops counts and releases blocks that reach zero;
 //   - 「PagedAttention原理」 §all-or-nothing 调度: an append either succeeds for every sequence of
-//     the batch or changes nothing.
+//     the batch or changes nothing;
+//   - 「PagedAttention原理」 §抢占与恢复 / §swap, 「Paged Attention&Orca Paper笔记与解读」
+//     §PagedAttention的方法 (eviction to CPU memory): a set of sequences is swapped between the GPU
+//     pool and a host swap pool as a whole or not at all; a swapped-out sequence cannot run, grow
+//     or be forked. A block also referenced by a sequence outside the set is copied (its count
+//     drops by the set's references) instead of moved.
 // Tie-breaks (any choice is valid; this one is the documented, reproducible contract): free
 // blocks come from the head of the creation-time order, released blocks join its tail in
 // logical-block order, sequences are served in the order given.
@@ -28,8 +33,9 @@
 namespace {
 
 struct Seq {
-  std::vector<int32_t> table;
+  std::vector<int32_t> table;  // GPU block ids, or host block ids while swapped out
   int32_t len = 0;
+  bool on_host = false;
 };
 
 }  // namespace
@@ -40,6 +46,63 @@ struct pkv_bm {
   std::deque<int32_t> free_list;
   std::vector<int32_t> rc;
   std::unordered_map<int64_t, Seq> seqs;
+  int32_t num_host_blocks = 0;
+  std::deque<int32_t> host_free;
+  std::vector<int32_t> host_rc;
+
+  // Moves the blocks of a set of sequences to the other pool (see the file comment). On
+  // success writes (src, dst) pairs in first-reference order.
+  int32_t move(const int64_t* ids, int32_t count, bool to_host, int32_t* pairs_out, int32_t max_pairs,
+               int32_t* num_pairs_out) {
+    if (count < 0 || (count > 0 && !ids)) return PKV_EINVAL;
+    std::vector<Seq*> set;
+    set.reserve(count);
+    for (int32_t i = 0; i < count; ++i) {
+      auto it = seqs.find(ids[i]);
+      if (it == seqs.end()) return PKV_ENOSEQ;
+      if (it->second.on_host == to_host) return PKV_ENOTRESIDENT;
+      for (int32_t k = 0; k < i; ++k)
+        if (ids[k] == ids[i]) return PKV_EINVAL;
+      set.push_back(&it->second);
+    }
+    std::vector<int32_t>& src_rc = to_host ? rc : host_rc;
+    std::deque<int32_t>& src_free = to_host ? free_list : host_free;
+    std::vector<int32_t>& dst_rc = to_host ? host_rc : rc;
+    std::deque<int32_t>& dst_free = to_host ? host_free : free_list;
+    std::vector<int32_t> order;
+    std::unordered_map<int32_t, int32_t> refs;
+    for (Seq* sq : set)
+      for (int32_t b : sq->table) {
+        auto r = refs.find(b);
+        if (r == refs.end()) {
+          refs.emplace(b, 1);
+          order.push_back(b);
+        } else {
+          ++r->second;
+        }
+      }
+    if ((int64_t)order.size() > (int64_t)dst_free.size()) return PKV_ENOBLOCKS;
+    if (!order.empty() && (!pairs_out || (int64_t)order.size() > max_pairs)) return PKV_EINVAL;
+    std::unordered_map<int32_t, int32_t> mapping;
+    for (size_t i = 0; i < order.size(); ++i) {
+      const int32_t nb = dst_free.front();
+      dst_free.pop_front();
+      dst_rc[nb] = refs[order[i]];
+      mapping[order[i]] = nb;
+      pairs_out[2 * i] = order[i];
+      pairs_out[2 * i + 1] = nb;
+    }
+    for (Seq* sq : set) {
+      for (int32_t& b : sq->table) b = mapping[b];
+      sq->on_host = to_host;
+    }
+    for (int32_t b : order) {
+      src_rc[b] -= refs[b];
+      if (src_rc[b] == 0) src_free.push_back(b);
+    }
+    if (num_pairs_out) *num_pairs_out = (int32_t)order.size();
+    return PKV_OK;
+  }
 
   int32_t take() {
     const int32_t b = free_list.front();
@@ -59,6 +122,7 @@ struct pkv_bm {
       auto it = seqs.find(ids[i]);
       if (it == seqs.end()) return PKV_ENOSEQ;
       if (n[i] < 0) return PKV_EINVAL;
+      if (it->second.on_host) return PKV_ENOTRESIDENT;
       if (n[i] == 0) continue;
       const Seq& sq = it->second;
       auto ls = sim_len.find(ids[i]);
@@ -123,6 +187,7 @@ int32_t pkv_bm_fork(pkv_bm* bm, int64_t parent, int64_t child) {
   if (!bm) return PKV_EINVAL;
   auto it = bm->seqs.find(parent);
   if (it == bm->seqs.end()) return PKV_ENOSEQ;
+  if (it->second.on_host) return PKV_ENOTRESIDENT;
   if (bm->seqs.count(child)) return PKV_EEXIST;
   Seq c = it->second;  // copy before emplace may rehash
   for (int32_t b : c.table) bm->rc[b] += 1;
@@ -134,8 +199,10 @@ int32_t pkv_bm_free_seq(pkv_bm* bm, int64_t id) {
   if (!bm) return PKV_EINVAL;
   auto it = bm->seqs.find(id);
   if (it == bm->seqs.end()) return PKV_ENOSEQ;
+  std::vector<int32_t>& rc = it->second.on_host ? bm->host_rc : bm->rc;
+  std::deque<int32_t>& fl = it->second.on_host ? bm->host_free : bm->free_list;
   for (int32_t b : it->second.table) {
-    if (--bm->rc[b] == 0) bm->free_list.push_back(b);
+    if (--rc[b] == 0) fl.push_back(b);
   }
   bm->seqs.erase(it);
   return PKV_OK;
@@ -192,6 +259,7 @@ int32_t pkv_bm_block_tables(const pkv_bm* bm, const int64_t* ids, int32_t count,
   for (int32_t i = 0; i < count; ++i) {
     auto it = bm->seqs.find(ids[i]);
     if (it == bm->seqs.end()) return PKV_ENOSEQ;
+    if (it->second.on_host) return PKV_ENOTRESIDENT;
     if ((int32_t)it->second.table.size() > max_blocks) return PKV_ESHAPE;
   }
   for (int32_t i = 0; i < count; ++i) {
@@ -225,6 +293,55 @@ int32_t pkv_bm_refcount(const pkv_bm* bm, int32_t block) {
 }
 
 int32_t pkv_bm_num_free(const pkv_bm* bm) { return bm ? (int32_t)bm->free_list.size() : PKV_EINVAL; }
+
+int32_t pkv_bm_attach_host_pool(pkv_bm* bm, int32_t num_host_blocks, const int32_t* free_order) {
+  if (!bm || num_host_blocks <= 0 || bm->num_host_blocks) return PKV_EINVAL;
+  std::vector<char> seen(num_host_blocks, 0);
+  std::deque<int32_t> fl;
+  for (int32_t i = 0; i < num_host_blocks; ++i) {
+    const int32_t b = free_order ? free_order[i] : i;
+    if (b < 0 || b >= num_host_blocks || seen[b]) return PKV_EINVAL;
+    seen[b] = 1;
+    fl.push_back(b);
+  }
+  bm->num_host_blocks = num_host_blocks;
+  bm->host_free.swap(fl);
+  bm->host_rc.assign(num_host_blocks, 0);
+  return PKV_OK;
+}
+
+int32_t pkv_bm_swap_out(pkv_bm* bm, const int64_t* seq_ids, int32_t n, int32_t* pairs_out, int32_t max_pairs,
+                        int32_t* num_pairs_out) {
+  if (!bm || !bm->num_host_blocks) return PKV_EINVAL;
+  return bm->move(seq_ids, n, true, pairs_out, max_pairs, num_pairs_out);
+}
+
+int32_t pkv_bm_swap_in(pkv_bm* bm, const int64_t* seq_ids, int32_t n, int32_t* pairs_out, int32_t max_pairs,
+                       int32_t* num_pairs_out) {
+  if (!bm || !bm->num_host_blocks) return PKV_EINVAL;
+  return bm->move(seq_ids, n, false, pairs_out, max_pairs, num_pairs_out);
+}
+
+int32_t pkv_bm_is_resident(const pkv_bm* bm, int64_t id) {
+  if (!bm) return PKV_EINVAL;
+  auto it = bm->seqs.find(id);
+  return it == bm->seqs.end() ? PKV_ENOSEQ : (it->second.on_host ? 0 : 1);
+}
+
+int32_t pkv_bm_host_refcount(const pkv_bm* bm, int32_t block) {
+  if (!bm || block < 0 || block >= bm->num_host_blocks) return PKV_EINVAL;
+  return bm->host_rc[block];
+}
+
+int32_t pkv_bm_host_free_list(const pkv_bm* bm, int32_t* out, int32_t cap) {
+  if (!bm) return PKV_EINVAL;
+  int32_t i = 0;
+  for (int32_t b : bm->host_free) {
+    if (i < cap) out[i] = b;
+    ++i;
+  }
+  return i;
+}
 
 int32_t pkv_bm_free_list(const pkv_bm* bm, int32_t* out, int32_t cap) {
   if (!bm) return PKV_EINVAL;

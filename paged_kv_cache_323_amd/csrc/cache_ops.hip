@@ -33,20 +33,21 @@ __global__ __launch_bounds__(256) void kv_cache_write_kernel(
   }
 }
 
-// Whole-block copies for copy-on-write: block dst <- block src in both pools. A block of
-// the head-major layout is one contiguous region, so each pair is two flat copies.
-__global__ __launch_bounds__(256) void copy_blocks_kernel(char* __restrict__ kc, char* __restrict__ vc,
-                                                          const int32_t* __restrict__ pairs,
-                                                          int64_t block_bytes) {
+// Whole-block copies: block dst <- block src for K and V. A block of the head-major layout is one
+// contiguous region, so each pair is two flat copies. Copy-on-write copies within one pool; swap
+// copies between a GPU pool and a host swap pool (device-addressable pinned memory).
+__global__ __launch_bounds__(256) void copy_blocks_kernel(char* __restrict__ dk, char* __restrict__ dv,
+                                                          const char* __restrict__ sk, const char* __restrict__ sv,
+                                                          const int32_t* __restrict__ pairs, int64_t block_bytes) {
   const int p = blockIdx.y;
   const int64_t src = (int64_t)pairs[2 * p] * block_bytes;
   const int64_t dst = (int64_t)pairs[2 * p + 1] * block_bytes;
   const int64_t step = (int64_t)gridDim.x * blockDim.x * 16;
   for (int64_t off = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 16; off < block_bytes; off += step) {
-    const u32x4 a = *reinterpret_cast<const u32x4*>(kc + src + off);
-    const u32x4 b = *reinterpret_cast<const u32x4*>(vc + src + off);
-    *reinterpret_cast<u32x4*>(kc + dst + off) = a;
-    *reinterpret_cast<u32x4*>(vc + dst + off) = b;
+    const u32x4 a = *reinterpret_cast<const u32x4*>(sk + src + off);
+    const u32x4 b = *reinterpret_cast<const u32x4*>(sv + src + off);
+    *reinterpret_cast<u32x4*>(dk + dst + off) = a;
+    *reinterpret_cast<u32x4*>(dv + dst + off) = b;
   }
 }
 
@@ -68,19 +69,24 @@ int launch_kv_cache_write(const void* k, const void* v, void* kc, void* vc, cons
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
-int launch_copy_blocks(void* kc, void* vc, const int32_t* pairs, int num_pairs, int64_t block_bytes,
-                       hipStream_t stream) {
+int launch_copy_between(void* dk, void* dv, const void* sk, const void* sv, const int32_t* pairs, int num_pairs,
+                        int64_t block_bytes, hipStream_t stream) {
   int64_t gx = (block_bytes + 256 * 16 * 4 - 1) / (256 * 16 * 4);  // ~4 chunks per thread
   if (gx < 1) gx = 1;
   if (gx > 256) gx = 256;
   for (int first = 0; first < num_pairs; first += 65535) {  // grid.y limit
     const int n = num_pairs - first < 65535 ? num_pairs - first : 65535;
     hipLaunchKernelGGL(copy_blocks_kernel, dim3((unsigned)gx, (unsigned)n), dim3(256), 0, stream,
-                       static_cast<char*>(kc), static_cast<char*>(vc), pairs + 2 * (int64_t)first,
-                       block_bytes);
+                       static_cast<char*>(dk), static_cast<char*>(dv), static_cast<const char*>(sk),
+                       static_cast<const char*>(sv), pairs + 2 * (int64_t)first, block_bytes);
     if (hipGetLastError() != hipSuccess) return -1;
   }
   return 0;
+}
+
+int launch_copy_blocks(void* kc, void* vc, const int32_t* pairs, int num_pairs, int64_t block_bytes,
+                       hipStream_t stream) {
+  return launch_copy_between(kc, vc, kc, vc, pairs, num_pairs, block_bytes, stream);
 }
 
 }  // namespace pkv

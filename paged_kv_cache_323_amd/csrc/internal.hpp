@@ -30,6 +30,10 @@ int launch_kv_cache_write(const void* k, const void* v, void* kc, void* vc, cons
 int launch_copy_blocks(void* kc, void* vc, const int32_t* pairs, int num_pairs, int64_t block_bytes,
                        hipStream_t stream);
 
+// Whole-block copies from (src_k, src_v) to (dst_k, dst_v); either may be pinned host memory.
+int launch_copy_between(void* dst_k, void* dst_v, const void* src_k, const void* src_v, const int32_t* pairs,
+                        int num_pairs, int64_t block_bytes, hipStream_t stream);
+
 struct DecodeLaunch {
   void* out;
   int out_dt;

@@ -21,7 +21,7 @@ F32, F16, BF16 = 0, 1, 2
 DTYPE_CODES = {"f32": F32, "f16": F16, "bf16": BF16}
 
 STATUS = {0: "PKV_OK", -1: "PKV_EINVAL", -2: "PKV_EDTYPE", -3: "PKV_ESHAPE", -4: "PKV_EWORKSPACE",
-          -5: "PKV_ELAUNCH", -6: "PKV_ENOBLOCKS", -7: "PKV_ENOSEQ", -8: "PKV_EEXIST"}
+          -5: "PKV_ELAUNCH", -6: "PKV_ENOBLOCKS", -7: "PKV_ENOSEQ", -8: "PKV_EEXIST", -9: "PKV_ENOTRESIDENT"}
 
 
 class PagedKVError(RuntimeError):
@@ -31,6 +31,10 @@ class PagedKVError(RuntimeError):
 
 
 class NoFreeBlocksError(PagedKVError):
+    pass
+
+
+class NotResidentError(PagedKVError):
     pass
 
 
@@ -63,6 +67,7 @@ _SIGS = {
     "pkv_version": (ctypes.c_char_p, []),
     "pkv_kv_cache_write": (_I32, [_P, _P, _P, _P, _P, _I32, _I64, _I64, _DESC, _P]),
     "pkv_copy_blocks": (_I32, [_P, _P, _P, _I32, _DESC, _P]),
+    "pkv_swap_blocks": (_I32, [_P, _P, _P, _P, _P, _I32, _DESC, _P]),
     "pkv_decode_workspace_bytes": (_SZ, [_I32, _I32, _I32, _DESC]),
     "pkv_decode_workspace_bytes_ex": (_SZ, [_I32, _I32, _I32, _DESC, _I32]),
     "pkv_decode_partition_size": (_I32, [_I32, _I32, _I32, _DESC]),
@@ -90,6 +95,12 @@ _SIGS = {
     "pkv_bm_refcount": (_I32, [_P, _I32]),
     "pkv_bm_num_free": (_I32, [_P]),
     "pkv_bm_free_list": (_I32, [_P, _I32P, _I32]),
+    "pkv_bm_attach_host_pool": (_I32, [_P, _I32, _I32P]),
+    "pkv_bm_swap_out": (_I32, [_P, _I64P, _I32, _I32P, _I32, _I32P]),
+    "pkv_bm_swap_in": (_I32, [_P, _I64P, _I32, _I32P, _I32, _I32P]),
+    "pkv_bm_is_resident": (_I32, [_P, _I64]),
+    "pkv_bm_host_refcount": (_I32, [_P, _I32]),
+    "pkv_bm_host_free_list": (_I32, [_P, _I32P, _I32]),
 }
 for _name, (_res, _args) in _SIGS.items():
     _fn = getattr(_lib, _name)
@@ -107,6 +118,8 @@ def _check(status: int, where: str) -> None:
     if status != 0:
         if status == -6:
             raise NoFreeBlocksError(status, where)
+        if status == -9:
+            raise NotResidentError(status, where)
         raise PagedKVError(status, where)
 
 
@@ -170,6 +183,42 @@ def copy_blocks(k_cache, v_cache, block_pairs, desc: CacheDesc, stream=None) -> 
                               _dev(block_pairs, "block_pairs", torch.int32), n, ctypes.byref(desc),
                               _stream(stream))
     _check(st, "copy_blocks")
+
+
+_hip = None
+
+
+def _device_address(t, name: str) -> ctypes.c_void_p:
+    """Device-addressable pointer of a device tensor or of a pinned host tensor."""
+    global _hip
+    if t.is_cuda:
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+        return ctypes.c_void_p(t.data_ptr())
+    if not t.is_pinned():
+        raise ValueError(f"{name} must be a device tensor or pinned host memory")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if _hip is None:
+        _hip = ctypes.CDLL("libamdhip64.so")
+        _hip.hipHostGetDevicePointer.restype = ctypes.c_int
+        _hip.hipHostGetDevicePointer.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_void_p, ctypes.c_uint]
+    dptr = ctypes.c_void_p()
+    if _hip.hipHostGetDevicePointer(ctypes.byref(dptr), ctypes.c_void_p(t.data_ptr()), 0) != 0:
+        raise ValueError(f"{name}: host memory is not device-addressable")
+    return dptr
+
+
+def swap_blocks(dst_k, dst_v, src_k, src_v, block_pairs, desc: CacheDesc, stream=None) -> None:
+    """Whole-block copies src -> dst between a GPU pool and a pinned host swap pool (either way)."""
+    torch = _torch()
+    n = int(block_pairs.shape[0]) if block_pairs is not None else 0
+    if n == 0:
+        return
+    st = _lib.pkv_swap_blocks(_device_address(dst_k, "dst_k"), _device_address(dst_v, "dst_v"),
+                              _device_address(src_k, "src_k"), _device_address(src_v, "src_v"),
+                              _dev(block_pairs, "block_pairs", torch.int32), n, ctypes.byref(desc), _stream(stream))
+    _check(st, "swap_blocks")
 
 
 def decode_workspace_bytes(num_seqs: int, num_q_heads: int, max_context_len: int, desc: CacheDesc,
@@ -324,4 +373,45 @@ class BlockManager:
     def free_list(self):
         buf = np.empty(self.num_blocks, dtype=np.int32)
         n = _lib.pkv_bm_free_list(self._h, _i32p(buf), self.num_blocks)
+        return [int(x) for x in buf[:n]]
+
+    # ---- swap (preemption to a host swap pool) ----
+    def attach_host_pool(self, num_host_blocks: int, free_order: Optional[Sequence[int]] = None) -> None:
+        fo = None if free_order is None else np.ascontiguousarray(free_order, dtype=np.int32)
+        _check(_lib.pkv_bm_attach_host_pool(self._h, int(num_host_blocks), None if fo is None else _i32p(fo)),
+               "bm_attach_host_pool")
+        self.num_host_blocks = int(num_host_blocks)
+
+    def _swap(self, fn, seqs):
+        ids = np.ascontiguousarray(seqs, dtype=np.int64)
+        cap = max(1, (self.num_blocks + getattr(self, "num_host_blocks", 0)))
+        pairs = np.empty((cap, 2), dtype=np.int32)
+        n = ctypes.c_int32(0)
+        _check(fn(self._h, _i64p(ids), len(ids), _i32p(pairs), cap, ctypes.byref(n)), fn.__name__)
+        return pairs[: n.value]
+
+    def swap_out(self, seqs) -> np.ndarray:
+        """Returns (gpu_block, host_block) pairs to copy before any released block is reused."""
+        return self._swap(_lib.pkv_bm_swap_out, seqs)
+
+    def swap_in(self, seqs) -> np.ndarray:
+        """Returns (host_block, gpu_block) pairs to copy before the sequences run."""
+        return self._swap(_lib.pkv_bm_swap_in, seqs)
+
+    def is_resident(self, seq: int) -> bool:
+        r = _lib.pkv_bm_is_resident(self._h, int(seq))
+        if r < 0:
+            _check(r, "bm_is_resident")
+        return bool(r)
+
+    def host_refcount(self, block: int) -> int:
+        r = _lib.pkv_bm_host_refcount(self._h, int(block))
+        if r < 0:
+            _check(r, "bm_host_refcount")
+        return int(r)
+
+    def host_free_list(self):
+        cap = max(1, getattr(self, "num_host_blocks", 0))
+        buf = np.empty(cap, dtype=np.int32)
+        n = _lib.pkv_bm_host_free_list(self._h, _i32p(buf), cap)
         return [int(x) for x in buf[:n]]

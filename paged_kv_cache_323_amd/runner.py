@@ -48,6 +48,8 @@ class DeviceState:
     v_cache: torch.Tensor
     slots_per_append: List[np.ndarray] = field(default_factory=list)
     pairs_per_append: List[np.ndarray] = field(default_factory=list)
+    host_k: Optional[torch.Tensor] = None  # pinned host swap pool
+    host_v: Optional[torch.Tensor] = None
 
 
 def make_pools(w, device="cuda", fill_nan=True):
@@ -66,9 +68,27 @@ def play_script(w, device="cuda", threads: int = 8, fill_nan: bool = True, chunk
     desc = pk.CacheDesc.make(w.num_blocks, w.block_size, w.num_kv_heads, w.head_dim, w.dtype)
     bm = pk.BlockManager(w.num_blocks, w.block_size, w.free_order)
     st = DeviceState(bm, desc, kc, vc)
+    if getattr(w, "num_host_blocks", 0):
+        bm.attach_host_pool(w.num_host_blocks, w.host_free_order)
+        hshape = (w.num_host_blocks, w.num_kv_heads, w.block_size, w.head_dim)
+        st.host_k = torch.empty(hshape, dtype=TORCH_DTYPE[w.dtype], pin_memory=True)
+        st.host_v = torch.empty(hshape, dtype=TORCH_DTYPE[w.dtype], pin_memory=True)
+        if fill_nan:
+            st.host_k.fill_(float("nan"))
+            st.host_v.fill_(float("nan"))
     for op in w.ops:
         kind = type(op).__name__
-        if kind == "AddOp":
+        if kind in ("SwapOutOp", "SwapInOp"):
+            out = kind == "SwapOutOp"
+            pairs = bm.swap_out(op.seqs) if out else bm.swap_in(op.seqs)
+            st.pairs_per_append.append(pairs)
+            if len(pairs):
+                pd = torch.from_numpy(np.ascontiguousarray(pairs)).to(device)
+                if out:
+                    pk.swap_blocks(st.host_k, st.host_v, kc, vc, pd, desc)
+                else:
+                    pk.swap_blocks(kc, vc, st.host_k, st.host_v, pd, desc)
+        elif kind == "AddOp":
             bm.add_seq(op.seq)
         elif kind == "ForkOp":
             bm.fork(op.parent, op.child)

@@ -220,12 +220,26 @@ def pin_closed_forms():
 # Block-manager pins
 # ---------------------------------------------------------------------------------------------
 def play_trace(make_bm, trace):
-    """Run golden/cow_trace.json against a block-manager object with the oracle's API."""
+    """Run a golden block-manager trace against an object with the oracle's API."""
     bm = make_bm(trace["num_blocks"], trace["block_size"], trace["free_order"])
+    if "num_host_blocks" in trace:
+        bm.attach_host_pool(trace["num_host_blocks"], trace["host_free_order"])
     for i, st in enumerate(trace["steps"]):
         op = st["op"]
         exp = st["expect"]
-        if op == "add":
+        if op in ("swap_out", "swap_in"):
+            fn = getattr(bm, op)
+            if st.get("fails"):
+                try:
+                    fn(st["seqs"])
+                except oracle.NoFreeBlocks:
+                    pass
+                else:
+                    raise AssertionError(f"step {i}: {op} should have failed")
+            else:
+                pairs = fn(st["seqs"])
+                assert [list(p) for p in pairs] == exp["pairs"], (i, pairs, exp["pairs"])
+        elif op == "add":
             bm.add_seq(st["seq"])
         elif op == "fork":
             bm.fork(st["parent"], st["child"])
@@ -251,10 +265,18 @@ def play_trace(make_bm, trace):
             assert bm.refcount(int(b)) == r, (i, b, bm.refcount(int(b)), r)
         if "free" in exp:
             assert bm.free_list() == exp["free"], (i, bm.free_list(), exp["free"])
+        for b, r in exp.get("host_rc", {}).items():
+            assert bm.host_refcount(int(b)) == r, (i, b, bm.host_refcount(int(b)), r)
+        if "host_free" in exp:
+            assert bm.host_free_list() == exp["host_free"], (i, bm.host_free_list(), exp["host_free"])
 
 
 def pin_cow_trace(make_bm=None):
     play_trace(make_bm or oracle.BlockManager, golden("cow_trace.json"))
+
+
+def pin_swap_trace(make_bm=None):
+    play_trace(make_bm or oracle.BlockManager, golden("swap_trace.json"))
 
 
 def pin_fragmentation(make_bm=None):
@@ -354,11 +376,16 @@ def pin_cow_contents():
         assert np.array_equal(pv[b, :L % B], before_v[:L % B])
 
 
-def random_script(rng: random.Random, num_blocks: int, B: int, n_ops: int = 200):
-    """A random add / append / fork / free script (beam-search-like sharing churn)."""
+def random_script(rng: random.Random, num_blocks: int, B: int, n_ops: int = 200, swap: bool = False):
+    """A random add / append / fork / free script (beam-search-like sharing churn), optionally
+    with swap-out / swap-in of random groups."""
     ops, live, nxt = [], [], 0
     for _ in range(n_ops):
         r = rng.random()
+        if swap and live and r > 0.85:
+            ss = rng.sample(live, k=min(len(live), rng.randint(1, 3)))
+            ops.append(("swap_out" if r > 0.925 else "swap_in", ss))
+            continue
         if not live or r < 0.1:
             ops.append(("add", nxt)); live.append(nxt); nxt += 1
         elif r < 0.3:
@@ -373,50 +400,87 @@ def random_script(rng: random.Random, num_blocks: int, B: int, n_ops: int = 200)
     return ops
 
 
-def pin_invariants(make_bm=None, seeds=range(6), num_blocks=48, B=4):
-    """Under random fork / append / free churn: every count equals the number of table
-    entries naming the block; free + referenced = all blocks, disjointly; each table holds
-    ⌈len/B⌉ blocks; a failed append changes nothing; each COW pair's source is still
-    referenced by someone else and its destination is fresh."""
+def pin_invariants(make_bm=None, seeds=range(6), num_blocks=48, B=4, swap=False, host_blocks=24):
+    """Under random fork / append / free (and swap) churn: every count equals the number of
+    table entries naming the block; free + referenced = all blocks, disjointly, in each pool;
+    each table holds ⌈len/B⌉ blocks; a failed append or swap changes nothing; each COW pair's
+    source is still referenced by someone else and its destination is fresh; the host swap
+    space never holds more blocks than the GPU pool has."""
     make_bm = make_bm or oracle.BlockManager
     for seed in seeds:
         rng = random.Random(seed)
         order = list(range(num_blocks))
         rng.shuffle(order)
         bm = make_bm(num_blocks, B, order)
+        if swap:
+            horder = list(range(host_blocks))
+            rng.shuffle(horder)
+            bm.attach_host_pool(host_blocks, horder)
         lens = {}
-        for op in random_script(rng, num_blocks, B):
-            if op[0] == "add":
+        on_host = set()
+
+        def state():
+            return ({s: bm.block_table(s) for s in lens}, bm.free_list(),
+                    [bm.refcount(b) for b in range(num_blocks)],
+                    bm.host_free_list() if swap else None)
+
+        for op in random_script(rng, num_blocks, B, swap=swap):
+            # ops on sequences whose creation was skipped (fork of a swapped-out parent) are skipped
+            named = [op[1]] if op[0] in ("free", "fork") else (list(op[1]) if op[0] != "add" else [])
+            if any(x not in lens for x in named):
+                continue
+            if op[0] in ("swap_out", "swap_in"):
+                want_host = op[0] == "swap_out"
+                if any((s in on_host) == want_host for s in op[1]):
+                    continue  # only valid moves are exercised here
+                snap = state()
+                try:
+                    pairs = getattr(bm, op[0])(op[1])
+                except oracle.NoFreeBlocks:
+                    assert state() == snap, "failed swap changed state"
+                    continue
+                for s in op[1]:
+                    (on_host.add if want_host else on_host.discard)(s)
+                assert len(pairs) == len({b for s in op[1] for b in bm.block_table(s)})
+            elif op[0] == "add":
                 bm.add_seq(op[1]); lens[op[1]] = 0
             elif op[0] == "fork":
+                if op[1] in on_host:
+                    continue
                 bm.fork(op[1], op[2]); lens[op[2]] = lens[op[1]]
             elif op[0] == "free":
-                bm.free_seq(op[1]); lens.pop(op[1])
+                bm.free_seq(op[1]); lens.pop(op[1]); on_host.discard(op[1])
             else:
-                snap = ({s: bm.block_table(s) for s in lens}, bm.free_list(),
-                        [bm.refcount(b) for b in range(num_blocks)])
+                if any(s in on_host for s in op[1]):
+                    continue
+                snap = state()
                 try:
                     free_before = set(bm.free_list())
                     slots, pairs = bm.append(op[1], op[2])
                 except oracle.NoFreeBlocks:
-                    after = ({s: bm.block_table(s) for s in lens}, bm.free_list(),
-                             [bm.refcount(b) for b in range(num_blocks)])
-                    assert after == snap, "failed append changed state"
+                    assert state() == snap, "failed append changed state"
                     continue
                 for s, n in zip(op[1], op[2]):
                     lens[s] += n
                 for src, dst in pairs:
                     assert dst in free_before and bm.refcount(src) >= 1
                 assert len(slots) == sum(op[2])
-            refs = {}
+            refs, hrefs = {}, {}
             for s in lens:
                 t = bm.block_table(s)
                 assert len(t) == -(-lens[s] // B), (s, len(t), lens[s])
                 assert bm.context_len(s) == lens[s]
                 for b in t:
-                    refs[b] = refs.get(b, 0) + 1
+                    d = hrefs if s in on_host else refs
+                    d[b] = d.get(b, 0) + 1
             for b in range(num_blocks):
                 assert bm.refcount(b) == refs.get(b, 0), (b, bm.refcount(b), refs.get(b, 0))
             fl = bm.free_list()
             assert len(fl) == len(set(fl)) and not (set(fl) & set(refs))
             assert len(fl) + len(refs) == num_blocks
+            if swap:
+                for b in range(host_blocks):
+                    assert bm.host_refcount(b) == hrefs.get(b, 0)
+                hfl = bm.host_free_list()
+                assert len(hfl) + len(hrefs) == host_blocks and not (set(hfl) & set(hrefs))
+                assert len(hrefs) <= num_blocks

@@ -47,9 +47,109 @@ class NativeBM:
     def free_list(self):
         return self.bm.free_list()
 
+    def attach_host_pool(self, n, order):
+        self.bm.attach_host_pool(n, order)
+
+    def swap_out(self, seqs):
+        try:
+            return [(int(a), int(b)) for a, b in self.bm.swap_out(seqs)]
+        except pk.NoFreeBlocksError as e:
+            raise oracle.NoFreeBlocks(str(e))
+
+    def swap_in(self, seqs):
+        try:
+            return [(int(a), int(b)) for a, b in self.bm.swap_in(seqs)]
+        except pk.NoFreeBlocksError as e:
+            raise oracle.NoFreeBlocks(str(e))
+
+    def host_refcount(self, b):
+        return self.bm.host_refcount(b)
+
+    def host_free_list(self):
+        return self.bm.host_free_list()
+
 
 def test_native_cow_trace():
     P.pin_cow_trace(NativeBM)
+
+
+def test_native_swap_trace():
+    P.pin_swap_trace(NativeBM)
+
+
+def test_native_swap_invariants():
+    P.pin_invariants(NativeBM, swap=True, seeds=range(10))
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_native_swap_equals_oracle_on_random_scripts(seed):
+    """Random churn with swaps: slots, COW pairs, swap pairs, tables, both pools' counts and
+    free lists bit-exact vs the oracle's manager."""
+    rng = random.Random(5000 + seed)
+    nb, hb, B = 40, 24, rng.choice([4, 8])
+    order = list(range(nb)); rng.shuffle(order)
+    horder = list(range(hb)); rng.shuffle(horder)
+    a = oracle.BlockManager(nb, B, order); a.attach_host_pool(hb, horder)
+    b = NativeBM(nb, B, order); b.attach_host_pool(hb, horder)
+    live, on_host = [], set()
+    for op in P.random_script(rng, nb, B, n_ops=300, swap=True):
+        named = [op[1]] if op[0] in ("free", "fork") else (list(op[1]) if op[0] != "add" else [])
+        if any(x not in live for x in named):
+            continue
+        if op[0] in ("swap_out", "swap_in"):
+            want = op[0] == "swap_out"
+            if any((s in on_host) == want for s in op[1]):
+                continue
+            res = []
+            for m in (a, b):
+                try:
+                    res.append([tuple(int(v) for v in p) for p in getattr(m, op[0])(op[1])])
+                except oracle.NoFreeBlocks:
+                    res.append("fail")
+            assert res[0] == res[1], (op, res)
+            if res[0] != "fail":
+                for s in op[1]:
+                    (on_host.add if want else on_host.discard)(s)
+        elif op[0] == "add":
+            a.add_seq(op[1]); b.add_seq(op[1]); live.append(op[1])
+        elif op[0] == "fork":
+            if op[1] in on_host:
+                continue
+            a.fork(op[1], op[2]); b.fork(op[1], op[2]); live.append(op[2])
+        elif op[0] == "free":
+            a.free_seq(op[1]); b.free_seq(op[1]); live.remove(op[1]); on_host.discard(op[1])
+        else:
+            if any(s in on_host for s in op[1]):
+                continue
+            ra = rb = "fail"
+            try:
+                ra = a.append(op[1], op[2])
+            except oracle.NoFreeBlocks:
+                pass
+            try:
+                rb = b.append(op[1], op[2])
+            except oracle.NoFreeBlocks:
+                pass
+            assert (ra == "fail") == (rb == "fail")
+            if ra != "fail":
+                assert list(ra[0]) == list(rb[0]) and [tuple(p) for p in ra[1]] == [tuple(p) for p in rb[1]]
+        for s in live:
+            assert a.block_table(s) == b.block_table(s) and a.context_len(s) == b.context_len(s)
+        assert a.free_list() == b.free_list() and a.host_free_list() == b.host_free_list()
+
+
+def test_native_swapped_out_sequence_cannot_run():
+    bm = pk.BlockManager(16, 4, None)
+    bm.attach_host_pool(8)
+    bm.add_seq(1); bm.append([1], [5])
+    pairs = bm.swap_out([1])
+    assert len(pairs) == 2 and not bm.is_resident(1)
+    for call in (lambda: bm.append([1], [1]), lambda: bm.fork(1, 2), lambda: bm.block_tables([1], 4),
+                 lambda: bm.swap_out([1])):
+        with pytest.raises(pk.NotResidentError):
+            call()
+    bm.swap_in([1])
+    assert bm.is_resident(1) and bm.num_free() == 14
 
 
 def test_native_fragmentation():

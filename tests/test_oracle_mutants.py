@@ -59,6 +59,11 @@ def _bm_pins():
     P.pin_sdpa(make_workload("shared_prefix", "small"))
 
 
+def _swap_pins():
+    P.pin_swap_trace()
+    P.pin_invariants(swap=True, seeds=range(10))
+
+
 def _pool_pins():
     P.pin_cow_contents()
     P.pin_sdpa(make_workload("shared_prefix", "small"))
@@ -83,10 +88,14 @@ MUTANTS = [
     # block manager
     ("block_manager", "            self.rc[old] -= 1 ", "            pass; ", _bm_pins),
     ("block_manager", "elif self.rc[table[j]] > 1:", "elif self.rc[table[j]] >= 1:", _bm_pins),
-    ("block_manager", "self.free.append(b)", "self.free.appendleft(b)", _bm_pins),
+    ("block_manager", "                free.append(b)\n        del self.lens[seq]", "                free.appendleft(b)\n        del self.lens[seq]", _bm_pins),
     ("block_manager", "            self.rc[b] += 1", "            pass", _bm_pins),
     ("block_manager", "self.free, self.rc, self.tables, self.lens = saved", "pass", _bm_pins),
     ("block_manager", "b = self.free.popleft()", "b = self.free.pop()", _bm_pins),
+    # swap
+    ("block_manager", "            src_rc[b] -= refs[b]", "            src_rc[b] = 0", _swap_pins),
+    ("block_manager", "            dst_rc[nb] = refs[b]", "            dst_rc[nb] = 1", _swap_pins),
+    ("block_manager", "        if len(order) > len(dst_free):", "        if len(order) > len(dst_free) + 1:", _swap_pins),
     # pool
     ("pool", "pool_v[int(dst)] = pool_v[int(src)]", "pass", _pool_pins),
     ("pool", "b, o = divmod(s, B)", "o, b = divmod(s, B)", _pool_pins),

@@ -45,6 +45,10 @@ def test_block_manager_cow_trace():
     P.pin_cow_trace()
 
 
+def test_block_manager_swap_trace():
+    P.pin_swap_trace()
+
+
 def test_block_manager_fragmentation():
     P.pin_fragmentation()
 
@@ -59,6 +63,10 @@ def test_cow_contents():
 
 def test_block_manager_invariants():
     P.pin_invariants()
+
+
+def test_block_manager_swap_invariants():
+    P.pin_invariants(swap=True, seeds=range(10))
 
 
 def test_shared_prefix_small_pairs():
@@ -76,3 +84,20 @@ def test_oracle_matches_sdpa_on_churn(seed):
     live sequence's contiguous history."""
     from workloads import make_churn_workload
     P.pin_sdpa(make_churn_workload(seed, 8, 4, 2, 64, "f16"))
+
+
+@pytest.mark.parametrize("seed,B", [(0, 8), (1, 16), (2, 32)])
+def test_oracle_swap_round_trip(seed, B):
+    """Swapping groups out to the host pool and back (with their GPU blocks reused meanwhile)
+    leaves every attention output bit-identical to the same script without swaps, and SDPA
+    over the contiguous histories still agrees."""
+    import dataclasses
+    import numpy as np
+    import oracle
+    from workloads import make_swap_workload
+    w = make_swap_workload(seed, B, 4, 2, 64, "bf16")
+    _, out = oracle.run_workload(w)
+    twin = dataclasses.replace(w, ops=[op for op in w.ops if type(op).__name__ not in ("SwapOutOp", "SwapInOp")])
+    _, out2 = oracle.run_workload(twin)
+    assert np.array_equal(out, out2)
+    P.pin_sdpa(w)

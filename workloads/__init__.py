@@ -12,6 +12,9 @@ from .synth import (  # noqa: F401
     AppendOp,
     ForkOp,
     FreeOp,
+    SwapOutOp,
+    SwapInOp,
+    make_swap_workload,
     make_workload,
     make_decode_workload,
     make_ragged_workload,

@@ -96,7 +96,17 @@ class FreeOp:
     seq: int
 
 
-Op = Union[AddOp, AppendOp, ForkOp, FreeOp]
+@dataclass
+class SwapOutOp:
+    seqs: List[int]
+
+
+@dataclass
+class SwapInOp:
+    seqs: List[int]
+
+
+Op = Union[AddOp, AppendOp, ForkOp, FreeOp, SwapOutOp, SwapInOp]
 
 
 @dataclass
@@ -118,6 +128,8 @@ class Workload:
     context_lens: List[int]  # inclusive of the rows being queried
     scale: float = field(default=0.0)
     notes: str = ""
+    num_host_blocks: int = 0               # host swap pool (0: none)
+    host_free_order: Optional[np.ndarray] = None
 
     def __post_init__(self):
         if not self.scale:
@@ -264,6 +276,63 @@ def make_churn_workload(seed: int, block_size: int, hq: int, hkv: int, head_dim:
     perm = _rng(seed, _S_PERM).permutation(nb).astype(np.int32)
     return Workload(name, seed, dtype, block_size, hq, hkv, head_dim, nb, perm, ops, q, [1] * len(q),
                     [lens[sq] for sq in q])
+
+
+def make_swap_workload(seed: int, block_size: int, hq: int, hkv: int, head_dim: int, dtype: str,
+                       groups: int = 4, samples: int = 3, prompt: int = 70, gen: int = 20,
+                       name: str = "swap") -> Workload:
+    """Preemption and restore of sequence groups: parallel-sampling groups are built, one whole
+    group is swapped to the host and its GPU blocks are reused by a newcomer, two samples of
+    another group are swapped out while their siblings keep running (shared blocks are copied,
+    not moved), then everything is swapped back in, extended and decoded."""
+    r = _rng(seed, _S_LENGTHS)
+    ops: List[Op] = []
+    lens = {}
+    gid = lambda g, i: g * samples + i
+    tag = 0
+    for g in range(groups):
+        p = gid(g, 0)
+        ops.append(AddOp(p))
+        L = prompt + int(r.integers(0, block_size))
+        ops.append(AppendOp([p], [L], tag=tag)); tag += 1
+        lens[p] = L
+        for i in range(1, samples):
+            ops.append(ForkOp(p, gid(g, i)))
+            lens[gid(g, i)] = L
+    seqs = sorted(lens)
+    first = [int(r.integers(1, gen)) for _ in seqs]
+    ops.append(AppendOp(seqs, first, tag=tag)); tag += 1
+    for sq, n in zip(seqs, first):
+        lens[sq] += n
+    g0 = [gid(0, i) for i in range(samples)]
+    ops.append(SwapOutOp(g0))                          # whole group preempted
+    newcomer = groups * samples
+    ops.append(AddOp(newcomer))
+    ops.append(AppendOp([newcomer], [prompt * 2], tag=tag)); tag += 1   # reuses the freed GPU blocks
+    lens[newcomer] = prompt * 2
+    part = [gid(1, 0), gid(1, 1)]
+    ops.append(SwapOutOp(part))                        # shares blocks with gid(1, 2..): copies
+    rest = [sq for sq in seqs if sq not in g0 and sq not in part]
+    more = [int(r.integers(1, gen)) for _ in rest]
+    ops.append(AppendOp(rest, more, tag=tag)); tag += 1
+    for sq, n in zip(rest, more):
+        lens[sq] += n
+    ops.append(FreeOp(newcomer))
+    del lens[newcomer]
+    ops.append(SwapInOp(part))
+    ops.append(SwapInOp(g0))
+    live = sorted(lens)
+    last = [1] * len(live)
+    ops.append(AppendOp(live, last, tag=tag)); tag += 1
+    for sq in live:
+        lens[sq] += 1
+    total = sum(-(-v // block_size) for v in lens.values()) + 2 * prompt // block_size + 8
+    nb = _pool_size(total, 1.2)
+    perm = _rng(seed, _S_PERM).permutation(nb).astype(np.int32)
+    hb = nb
+    hperm = _rng(seed, _S_PERM, 1).permutation(hb).astype(np.int32)
+    return Workload(name, seed, dtype, block_size, hq, hkv, head_dim, nb, perm, ops, live, [1] * len(live),
+                    [lens[sq] for sq in live], num_host_blocks=hb, host_free_order=hperm)
 
 
 def make_workload(name: str, size: str = "full", block_size: Optional[int] = None,
