@@ -1,0 +1,301 @@
+"""Iteration-level continuous batching over the paged KV cache.
+
+A small driver, not a serving system: requests carry a prompt length and a number of tokens to
+generate, there is no model, and the new tokens' q/k/v come from a value provider (the seeded
+generator for parity runs, device random numbers for throughput runs). What it exercises is the
+hot path as an engine drives it, step after step with changing tables:
+
+  * scheduling is per model step: finished requests leave and waiting ones join
+    (「Paged Attention&Orca Paper笔记与解读」 §Orca的Solution, iteration-level scheduling); requests
+    move through waiting -> prefilling -> decoding -> finished, admitted first come first served
+    while fewer than ``max_num_seqs`` are in flight (the scheduler of the koas-w.github.io
+    continuous-batching post, "Continous Batching的相关代码");
+  * each step is one selective-batching call: every new prompt's tokens plus one token per
+    decoding request, flattened, written to the cache, then attended in one ragged launch pair
+    (「Paged Attention&Orca Paper笔记与解读」 §Orca的Solution, selective batching);
+  * when the pool cannot hold the next step, the most recently admitted requests are preempted
+    whole, their blocks swapped to the host pool, and they are resumed (swapped back in) before
+    new requests are admitted (「PagedAttention原理」 §all-or-nothing 调度, §抢占与恢复 / §swap;
+    「Paged Attention&Orca Paper笔记与解读」 §PagedAttention的方法: no new admissions while
+    preempted requests wait).
+
+Every block-manager operation is recorded as a script op (the same ops the synthetic workloads
+use), so any step can be replayed elsewhere.
+"""
+from __future__ import annotations
+
+from collections import deque
+from dataclasses import dataclass, field
+from typing import Deque, Dict, List, Optional
+
+import numpy as np
+import torch
+
+from . import native as pk
+from .runner import TORCH_DTYPE, to_device
+
+WAITING, PREFILL, DECODING, SWAPPED, FINISHED = "waiting", "prefill", "decoding", "swapped", "finished"
+
+
+@dataclass
+class Request:
+    seq: int
+    prompt_len: int
+    max_new_tokens: int
+    generated: int = 0
+    state: str = WAITING
+    admitted_step: int = -1
+
+
+@dataclass
+class StepRecord:
+    step: int
+    seqs: List[int]
+    q_lens: List[int]
+    context_lens: List[int]
+    ops_end: int                  # number of ops in the log up to and including this step's append
+    out: Optional[torch.Tensor] = None
+
+
+@dataclass
+class EngineStats:
+    steps: int = 0
+    prefill_tokens: int = 0
+    decode_tokens: int = 0
+    finished: int = 0
+    preemptions: int = 0
+    resumptions: int = 0
+
+
+class Engine:
+    def __init__(self, num_blocks: int, block_size: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
+                 dtype: str, max_num_seqs: int = 64, max_step_tokens: int = 8192, num_host_blocks: int = 0,
+                 seed: int = 0, values: str = "generator", keep_outputs: bool = False, device: str = "cuda"):
+        self.B, self.hq, self.hkv, self.d, self.dtype = block_size, num_q_heads, num_kv_heads, head_dim, dtype
+        self.max_num_seqs, self.max_step_tokens = max_num_seqs, max_step_tokens
+        self.seed, self.values, self.keep_outputs, self.device = seed, values, keep_outputs, device
+        rng = np.random.default_rng([seed, 1])
+        self.free_order = rng.permutation(num_blocks).astype(np.int32)
+        self.num_blocks = num_blocks
+        self.bm = pk.BlockManager(num_blocks, block_size, self.free_order)
+        self.desc = pk.CacheDesc.make(num_blocks, block_size, num_kv_heads, head_dim, dtype)
+        shape = (num_blocks, num_kv_heads, block_size, head_dim)
+        tdt = TORCH_DTYPE[dtype]
+        self.k_cache = torch.empty(shape, dtype=tdt, device=device).fill_(float("nan"))
+        self.v_cache = torch.empty(shape, dtype=tdt, device=device).fill_(float("nan"))
+        self.num_host_blocks = num_host_blocks
+        self.host_free_order = None
+        if num_host_blocks:
+            self.host_free_order = np.random.default_rng([seed, 2]).permutation(num_host_blocks).astype(np.int32)
+            self.bm.attach_host_pool(num_host_blocks, self.host_free_order)
+            hshape = (num_host_blocks, num_kv_heads, block_size, head_dim)
+            self.host_k = torch.empty(hshape, dtype=tdt, pin_memory=True)
+            self.host_v = torch.empty(hshape, dtype=tdt, pin_memory=True)
+        self.requests: Dict[int, Request] = {}
+        self.waiting: Deque[int] = deque()
+        self.running: List[int] = []      # admission order
+        self.swapped: Deque[int] = deque()
+        self.finished: List[int] = []
+        self.ops: list = []
+        self.records: List[StepRecord] = []
+        self.stats = EngineStats()
+        self.step_idx = 0
+        self._next_seq = 0
+        self.ws = torch.zeros(1, dtype=torch.uint8, device=device)
+        self.scale = float(np.float32(1.0 / np.sqrt(head_dim)))
+
+    # ---- requests -------------------------------------------------------------------------------
+    def add_request(self, prompt_len: int, max_new_tokens: int) -> int:
+        seq = self._next_seq
+        self._next_seq += 1
+        self.requests[seq] = Request(seq, int(prompt_len), int(max_new_tokens))
+        self.waiting.append(seq)
+        return seq
+
+    def has_work(self) -> bool:
+        return bool(self.waiting or self.running or self.swapped)
+
+    # ---- scheduling -----------------------------------------------------------------------------
+    def _ops_add(self, op):
+        self.ops.append(op)
+
+    def _preempt_one(self) -> bool:
+        """Make room: a request admitted this step (no cache yet) goes back to the head of the
+        queue; otherwise the most recently admitted running request is swapped out whole."""
+        if not self.running:
+            return False
+        victim = self.running[-1]
+        from workloads import FreeOp, SwapOutOp
+        if self.requests[victim].state == PREFILL:
+            self.bm.free_seq(victim)
+            self._ops_add(FreeOp(victim))
+            self.running.pop()
+            self.requests[victim].state = WAITING
+            self.waiting.appendleft(victim)
+            return True
+        if not self.num_host_blocks:
+            return False
+        try:
+            pairs = self.bm.swap_out([victim])
+        except pk.NoFreeBlocksError:
+            return False
+        self._ops_add(SwapOutOp([victim]))
+        if len(pairs):
+            pk.swap_blocks(self.host_k, self.host_v, self.k_cache, self.v_cache,
+                           torch.from_numpy(np.ascontiguousarray(pairs)).to(self.device), self.desc)
+        self.running.pop()
+        self.requests[victim].state = SWAPPED
+        self.swapped.appendleft(victim)
+        self.stats.preemptions += 1
+        return True
+
+    def _resume(self) -> None:
+        from workloads import SwapInOp
+        while self.swapped and len(self.running) < self.max_num_seqs:
+            seq = self.swapped[0]
+            try:
+                pairs = self.bm.swap_in([seq])
+            except pk.NoFreeBlocksError:
+                return
+            self._ops_add(SwapInOp([seq]))
+            if len(pairs):
+                pk.swap_blocks(self.k_cache, self.v_cache, self.host_k, self.host_v,
+                               torch.from_numpy(np.ascontiguousarray(pairs)).to(self.device), self.desc)
+            self.swapped.popleft()
+            self.requests[seq].state = DECODING
+            self.running.append(seq)
+            self.stats.resumptions += 1
+
+    def _schedule(self):
+        """Returns (seqs, n_tokens) of this step's batch (prompts first, then decodes)."""
+        from workloads import AddOp
+        # retire
+        for seq in [s for s in self.running if self.requests[s].state == FINISHED]:
+            self.running.remove(seq)
+        self._resume()
+        # admit first come first served (none while preempted requests wait)
+        budget = self.max_step_tokens - sum(1 for s in self.running if self.requests[s].state == DECODING)
+        while (self.waiting and not self.swapped and len(self.running) < self.max_num_seqs):
+            req = self.requests[self.waiting[0]]
+            if req.prompt_len > budget:
+                break
+            self.waiting.popleft()
+            self.bm.add_seq(req.seq)
+            self._ops_add(AddOp(req.seq))
+            req.state = PREFILL
+            req.admitted_step = self.step_idx
+            self.running.append(req.seq)
+            budget -= req.prompt_len
+        # make room: preempt the newest until the batch fits the pool
+        while True:
+            seqs, ns = self._batch()
+            if not seqs:
+                return seqs, ns
+            if self.bm.blocks_needed(seqs, ns) <= self.bm.num_free():
+                return seqs, ns
+            if not self._preempt_one():
+                raise RuntimeError("pool exhausted and nothing can be preempted")
+
+    def _batch(self):
+        pre = [s for s in self.running if self.requests[s].state == PREFILL]
+        dec = [s for s in self.running if self.requests[s].state == DECODING]
+        seqs = pre + dec
+        ns = [self.requests[s].prompt_len for s in pre] + [1] * len(dec)
+        return seqs, ns
+
+    # ---- values ---------------------------------------------------------------------------------
+    def _kv(self, seqs, ns, tag):
+        if self.values == "generator":
+            from workloads import AppendOp
+            from workloads.synth import Workload
+            w = self._workload_stub()
+            k, v = w.append_values(AppendOp(list(seqs), list(ns), tag), threads=8)
+            return to_device(k, self.dtype, self.device), to_device(v, self.dtype, self.device)
+        T = int(sum(ns))
+        k, v, _ = self._device_values(T)
+        return k, v
+
+    def _q(self, seqs, ns):
+        if self.values == "generator":
+            from workloads import gen_q
+            parts = [gen_q(self.seed, s, n, self.hq, self.d, self.dtype) for s, n in zip(seqs, ns)]
+            return to_device(np.concatenate(parts), self.dtype, self.device)
+        T = int(sum(ns))
+        return self._device_values(T)[2]
+
+    def _device_values(self, T):
+        """Throughput runs: rows of a fixed random device buffer stand in for the model's new
+        q/k/v (their values do not change the work)."""
+        cap = getattr(self, "_vals_cap", 0)
+        if T > cap:
+            cap = max(T, 2 * cap, 1024)
+            g = torch.Generator(device=self.device)
+            g.manual_seed(self.seed)
+            tdt = TORCH_DTYPE[self.dtype]
+            self._vals = tuple(torch.randn((cap, h, self.d), device=self.device, generator=g).to(tdt)
+                               for h in (self.hkv, self.hkv, self.hq))
+            self._vals_cap = cap
+        return tuple(x[:T] for x in self._vals)
+
+    def _workload_stub(self, query=None):
+        from workloads.synth import Workload
+        seqs, ql, ctx = query if query is not None else ([], [], [])
+        return Workload("engine", self.seed, self.dtype, self.B, self.hq, self.hkv, self.d, self.num_blocks,
+                        self.free_order, list(self.ops), list(seqs), list(ql), list(ctx),
+                        num_host_blocks=self.num_host_blocks, host_free_order=self.host_free_order)
+
+    def replay_workload(self, rec: StepRecord):
+        """The script of steps up to ``rec`` with ``rec``'s rows as the query (for the oracle)."""
+        from workloads.synth import Workload
+        w = self._workload_stub((rec.seqs, rec.q_lens, rec.context_lens))
+        w.ops = list(self.ops[: rec.ops_end])
+        return w
+
+    # ---- one model step -------------------------------------------------------------------------
+    def step(self) -> Optional[StepRecord]:
+        from workloads import AppendOp, FreeOp
+        seqs, ns = self._schedule()
+        if not seqs:
+            return None
+        tag = 1000 + self.step_idx
+        slots, pairs = self.bm.append(seqs, ns)
+        self._ops_add(AppendOp(list(seqs), list(ns), tag))
+        if len(pairs):
+            pk.copy_blocks(self.k_cache, self.v_cache, torch.from_numpy(np.ascontiguousarray(pairs)).to(self.device),
+                           self.desc)
+        k, v = self._kv(seqs, ns, tag)
+        sd = torch.from_numpy(np.ascontiguousarray(slots)).to(self.device)
+        pk.kv_cache_write(k, v, self.k_cache, self.v_cache, sd, self.desc)
+        max_blocks = max(len(self.bm.block_table(s)) for s in seqs)
+        tables, lens = self.bm.block_tables(seqs, max_blocks)
+        cu = np.concatenate([[0], np.cumsum(ns)]).astype(np.int32)
+        q = self._q(seqs, ns)
+        out = torch.empty(q.shape, dtype=torch.float32 if self.keep_outputs else q.dtype, device=self.device)
+        max_ctx, max_q = int(lens.max()), int(max(ns))
+        nbytes = pk.ragged_workspace_bytes(len(seqs), int(cu[-1]), self.hq, max_q, max_ctx, self.desc)
+        if self.ws.numel() < nbytes:
+            self.ws = torch.zeros(nbytes, dtype=torch.uint8, device=self.device)
+        pk.paged_attention_ragged(out, q, torch.from_numpy(cu).to(self.device), torch.from_numpy(lens).to(self.device),
+                                  self.k_cache, self.v_cache, torch.from_numpy(tables).to(self.device), self.scale,
+                                  max_q, max_ctx, self.desc, self.ws)
+        rec = StepRecord(self.step_idx, list(seqs), list(ns), [int(x) for x in lens], len(self.ops),
+                         out if self.keep_outputs else None)
+        self.records.append(rec)
+        # every row group yields one generated token (the prompt's last row, or the decode row)
+        for s, n in zip(seqs, ns):
+            req = self.requests[s]
+            if req.state == PREFILL:
+                self.stats.prefill_tokens += n
+                req.state = DECODING
+            else:
+                self.stats.decode_tokens += 1
+            req.generated += 1
+            if req.generated >= req.max_new_tokens:
+                req.state = FINISHED
+                self.bm.free_seq(s)
+                self._ops_add(FreeOp(s))
+                self.finished.append(s)
+                self.stats.finished += 1
+        self.stats.steps += 1
+        self.step_idx += 1
+        return rec
