@@ -77,6 +77,12 @@ const char* pkv_status_str(int32_t status);
 /* Library version string (static storage). */
 const char* pkv_version(void);
 
+/* Name of the HIP status ("hipSuccess", "hipErrorInvalidConfiguration", ...) of the most recent
+ * kernel launch made by a device entry point on the calling thread; static storage. After an
+ * entry point returns PKV_ELAUNCH it names the launch's own error, not one left behind by an
+ * unrelated HIP call. */
+const char* pkv_last_launch_error(void);
+
 /*
  * kv_cache_write — store new tokens' keys and values into their slots.
  *   k_cache[slot[t]] <- k[t], v_cache[slot[t]] <- v[t] for t < num_tokens, bit for bit.

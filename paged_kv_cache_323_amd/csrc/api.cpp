@@ -68,9 +68,19 @@ DecodeWs decode_ws_layout(int32_t S, int32_t hq, int32_t hkv, int32_t head_dim, 
   return w;
 }
 
+// HIP status of the most recent kernel launch made by an entry point on this thread.
+thread_local hipError_t g_last_launch = hipSuccess;
+
+int32_t launched(hipError_t e) {
+  g_last_launch = e;
+  return e == hipSuccess ? PKV_OK : PKV_ELAUNCH;
+}
+
 }  // namespace
 
 extern "C" {
+
+const char* pkv_last_launch_error(void) { return hipGetErrorName(g_last_launch); }
 
 const char* pkv_status_str(int32_t s) {
   switch (s) {
@@ -103,11 +113,9 @@ int32_t pkv_kv_cache_write(const void* k, const void* v, void* k_cache, void* v_
     return PKV_EINVAL;
   const int es = elem_bytes(c->dtype);
   if ((uint64_t)num_tokens * c->num_kv_heads * (c->head_dim * es / 16) > 0xffffffffull) return PKV_ESHAPE;
-  return pkv::launch_kv_cache_write(k, v, k_cache, v_cache, slot_mapping, num_tokens, k_token_stride * es,
-                                    v_token_stride * es, c->num_kv_heads, c->block_size, c->head_dim, es,
-                                    (hipStream_t)stream) == 0
-             ? PKV_OK
-             : PKV_ELAUNCH;
+  return launched(pkv::launch_kv_cache_write(k, v, k_cache, v_cache, slot_mapping, num_tokens,
+                                             k_token_stride * es, v_token_stride * es, c->num_kv_heads,
+                                             c->block_size, c->head_dim, es, (hipStream_t)stream));
 }
 
 int32_t pkv_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs, int32_t num_pairs,
@@ -118,9 +126,7 @@ int32_t pkv_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs, int3
   if (num_pairs == 0) return PKV_OK;
   if (!k_cache || !v_cache || !pairs) return PKV_EINVAL;
   const int64_t block_bytes = (int64_t)c->num_kv_heads * c->block_size * c->head_dim * elem_bytes(c->dtype);
-  return pkv::launch_copy_blocks(k_cache, v_cache, pairs, num_pairs, block_bytes, (hipStream_t)stream) == 0
-             ? PKV_OK
-             : PKV_ELAUNCH;
+  return launched(pkv::launch_copy_blocks(k_cache, v_cache, pairs, num_pairs, block_bytes, (hipStream_t)stream));
 }
 
 int32_t pkv_swap_blocks(void* dst_k, void* dst_v, const void* src_k, const void* src_v, const int32_t* pairs,
@@ -131,10 +137,8 @@ int32_t pkv_swap_blocks(void* dst_k, void* dst_v, const void* src_k, const void*
   if (num_pairs == 0) return PKV_OK;
   if (!dst_k || !dst_v || !src_k || !src_v || !pairs) return PKV_EINVAL;
   const int64_t block_bytes = (int64_t)c->num_kv_heads * c->block_size * c->head_dim * elem_bytes(c->dtype);
-  return pkv::launch_copy_between(dst_k, dst_v, src_k, src_v, pairs, num_pairs, block_bytes,
-                                  (hipStream_t)stream) == 0
-             ? PKV_OK
-             : PKV_ELAUNCH;
+  return launched(
+      pkv::launch_copy_between(dst_k, dst_v, src_k, src_v, pairs, num_pairs, block_bytes, (hipStream_t)stream));
 }
 
 int32_t pkv_decode_partition_size(int32_t num_seqs, int32_t num_q_heads, int32_t max_ctx,
@@ -207,7 +211,7 @@ static int32_t decode_common_cu(void* out, int32_t out_dtype, const void* q, con
   L.ws_ml = ws.total ? reinterpret_cast<float*>(wb + ws.ml) : nullptr;
   L.stage = stage;
   L.cu = cu;
-  return pkv::launch_decode(L, (hipStream_t)stream) == 0 ? PKV_OK : PKV_ELAUNCH;
+  return launched(pkv::launch_decode(L, (hipStream_t)stream));
 }
 
 static int32_t decode_common(void* out, int32_t out_dtype, const void* q, const void* k_cache,
@@ -303,7 +307,7 @@ int32_t pkv_paged_attention_ragged(void* out, int32_t out_dtype, const void* q, 
   P.head_dim = c->head_dim;
   P.dt = c->dtype;
   P.scale = scale;
-  return pkv::launch_ragged_prefill(P, (hipStream_t)stream) == 0 ? PKV_OK : PKV_ELAUNCH;
+  return launched(pkv::launch_ragged_prefill(P, (hipStream_t)stream));
 }
 
 int32_t pkv_paged_attention_decode(void* out, int32_t out_dtype, const void* q, const void* k_cache,

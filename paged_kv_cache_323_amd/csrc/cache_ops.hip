@@ -51,40 +51,40 @@ __global__ __launch_bounds__(256) void copy_blocks_kernel(char* __restrict__ dk,
   }
 }
 
-int launch_kv_cache_write(const void* k, const void* v, void* kc, void* vc, const int32_t* slots,
+hipError_t launch_kv_cache_write(const void* k, const void* v, void* kc, void* vc, const int32_t* slots,
                           int num_tokens, int64_t k_stride_b, int64_t v_stride_b, int num_kv_heads,
                           int block_size, int head_dim, int elem_bytes, hipStream_t stream) {
   const int row_bytes = head_dim * elem_bytes;
   const uint32_t cpr = row_bytes / 16;
   const uint32_t cpt = cpr * num_kv_heads;
   const uint64_t total = (uint64_t)cpt * num_tokens;
-  if (total == 0) return 0;
-  if (total > 0xffffffffull) return -1;
+  if (total == 0) return hipSuccess;
+  if (total > 0xffffffffull) return hipErrorInvalidConfiguration;
   const uint64_t want = (total + 255) / 256;
   const unsigned grid = (unsigned)(want < 65536 ? want : 65536);
-  hipLaunchKernelGGL(kv_cache_write_kernel, dim3(grid), dim3(256), 0, stream,
-                     static_cast<const char*>(k), static_cast<const char*>(v), static_cast<char*>(kc),
-                     static_cast<char*>(vc), slots, (uint32_t)total, cpt, cpr, k_stride_b, v_stride_b,
-                     num_kv_heads, block_size, ilog2(block_size), row_bytes);
-  return hipGetLastError() == hipSuccess ? 0 : -1;
+  return launch_kernel(kv_cache_write_kernel, dim3(grid), dim3(256), stream, static_cast<const char*>(k),
+                       static_cast<const char*>(v), static_cast<char*>(kc), static_cast<char*>(vc), slots,
+                       (uint32_t)total, cpt, cpr, k_stride_b, v_stride_b, num_kv_heads, block_size,
+                       ilog2(block_size), row_bytes);
 }
 
-int launch_copy_between(void* dk, void* dv, const void* sk, const void* sv, const int32_t* pairs, int num_pairs,
+hipError_t launch_copy_between(void* dk, void* dv, const void* sk, const void* sv, const int32_t* pairs, int num_pairs,
                         int64_t block_bytes, hipStream_t stream) {
   int64_t gx = (block_bytes + 256 * 16 * 4 - 1) / (256 * 16 * 4);  // ~4 chunks per thread
   if (gx < 1) gx = 1;
   if (gx > 256) gx = 256;
   for (int first = 0; first < num_pairs; first += 65535) {  // grid.y limit
     const int n = num_pairs - first < 65535 ? num_pairs - first : 65535;
-    hipLaunchKernelGGL(copy_blocks_kernel, dim3((unsigned)gx, (unsigned)n), dim3(256), 0, stream,
-                       static_cast<char*>(dk), static_cast<char*>(dv), static_cast<const char*>(sk),
-                       static_cast<const char*>(sv), pairs + 2 * (int64_t)first, block_bytes);
-    if (hipGetLastError() != hipSuccess) return -1;
+    const hipError_t e =
+        launch_kernel(copy_blocks_kernel, dim3((unsigned)gx, (unsigned)n), dim3(256), stream, static_cast<char*>(dk),
+                      static_cast<char*>(dv), static_cast<const char*>(sk), static_cast<const char*>(sv),
+                      pairs + 2 * (int64_t)first, block_bytes);
+    if (e != hipSuccess) return e;
   }
-  return 0;
+  return hipSuccess;
 }
 
-int launch_copy_blocks(void* kc, void* vc, const int32_t* pairs, int num_pairs, int64_t block_bytes,
+hipError_t launch_copy_blocks(void* kc, void* vc, const int32_t* pairs, int num_pairs, int64_t block_bytes,
                        hipStream_t stream) {
   return launch_copy_between(kc, vc, kc, vc, pairs, num_pairs, block_bytes, stream);
 }

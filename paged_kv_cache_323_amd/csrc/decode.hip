@@ -92,8 +92,12 @@ template <int DT, int NWORDS, int EPL> __device__ __forceinline__ void words_to_
   }
 }
 
+#ifndef PKV_DECODE_MIN_WG
+#define PKV_DECODE_MIN_WG 1
+#endif
+
 template <int DT, int D, int G, int PF>
-__global__ __launch_bounds__(kDecThreads) void paged_decode_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(kDecThreads, PKV_DECODE_MIN_WG) void paged_decode_kernel(DecodeArgs a) {
   using T = typename Elem<DT>::T;
   constexpr int ES = sizeof(T);
   constexpr int VEC = 16 / ES;        // elements per 16-byte chunk
@@ -129,12 +133,15 @@ __global__ __launch_bounds__(kDecThreads) void paged_decode_kernel(DecodeArgs a)
   const int ctx = min(a.ctx_lens[s], min(a.max_blocks * a.bs, a.max_parts * a.partition));
   const int nparts = ctx > 0 ? (ctx + a.partition - 1) / a.partition : 1;
   if (part >= nparts) return;  // uniform over the workgroup
-  const int t0 = part * a.partition;
-  const int n = min(a.partition, ctx - t0);  // tokens of this partition (0 iff ctx == 0)
+  // Balanced split: the sequence's partitions get equal sizes (a multiple of 64 tokens, so each
+  // starts on a block boundary) instead of leaving a short last partition.
+  const int psz = min(a.partition, (((ctx + nparts - 1) / nparts) + 63) & ~63);
+  const int t0 = part * psz;
+  const int n = max(0, min(psz, ctx - t0));  // tokens of this partition (0 iff ctx == 0)
   const int nunits = (n + 7) >> 3;
   const int nw = nunits > wave ? (nunits - wave + kDecWaves - 1) / kDecWaves : 0;  // this wave's units
 
-  // Block-table entries of this partition (the partition starts on a block boundary).
+  // Block-table entries of this partition.
   const int nblk = (n + a.bs - 1) >> a.log2_bs;
   const int32_t* trow = a.tables + (size_t)s * a.max_blocks + (t0 >> a.log2_bs);
   for (int i = tid; i < nblk; i += kDecThreads) s_tab[i] = trow[i];
@@ -321,14 +328,35 @@ __global__ __launch_bounds__(256) void paged_decode_merge_kernel(DecodeArgs a, i
   const int g = h - kvh * group;
   const int d = o - h * head_dim;
   const size_t item = ((size_t)s * a.hkv + kvh) * a.max_parts;
-  float mx = -INFINITY;
-  for (int p = 0; p < nparts; ++p) mx = fmaxf(mx, a.ws_ml[(item + p) * group + g].x);
-  float l = 0.f, v = 0.f;
-  for (int p = 0; p < nparts; ++p) {
-    const float2 ml = a.ws_ml[(item + p) * group + g];
-    const float w = fast_exp2(ml.x - mx);
-    l = __builtin_fmaf(w, ml.y, l);
-    v = __builtin_fmaf(w, a.ws_acc[((item + p) * group + g) * head_dim + d], v);
+  // Partials are read in chunks of 8 whose loads are all issued before any is used, and merged
+  // with a running log-sum-exp.
+  constexpr int kChunk = 8;
+  float mx = -INFINITY, l = 0.f, v = 0.f;
+  for (int p0 = 0; p0 < nparts; p0 += kChunk) {
+    float2 ml[kChunk];
+    float av[kChunk];
+#pragma unroll
+    for (int j = 0; j < kChunk; ++j) {
+      const int p = min(p0 + j, nparts - 1);  // padding lanes re-read the last partial; dropped below
+      ml[j] = a.ws_ml[(item + p) * group + g];
+      av[j] = a.ws_acc[((item + p) * group + g) * head_dim + d];
+    }
+    float cm = mx;
+#pragma unroll
+    for (int j = 0; j < kChunk; ++j)
+      if (p0 + j < nparts) cm = fmaxf(cm, ml[j].x);
+    const float r = fast_exp2(mx - cm);  // rescale what was merged so far (0 on the first chunk)
+    l *= r;
+    v *= r;
+#pragma unroll
+    for (int j = 0; j < kChunk; ++j) {
+      if (p0 + j < nparts) {
+        const float w = fast_exp2(ml[j].x - cm);
+        l = __builtin_fmaf(w, ml[j].y, l);
+        v = __builtin_fmaf(w, av[j], v);
+      }
+    }
+    mx = cm;
   }
   store_out(a.out, (size_t)row * a.hq * head_dim + o, l > 0.f ? v / l : 0.f, a.out_dt);
 }
@@ -359,48 +387,46 @@ static DecodeArgs make_args(const DecodeLaunch& L) {
 constexpr int kPrefetch = PKV_DECODE_PREFETCH;
 
 template <int DT, int D, int G>
-static int launch_decode_t(const DecodeLaunch& L, hipStream_t stream) {
+static hipError_t launch_decode_t(const DecodeLaunch& L, hipStream_t stream) {
   const DecodeArgs a = make_args(L);
   if (L.stage != 2) {
-    hipLaunchKernelGGL((paged_decode_kernel<DT, D, G, kPrefetch>), dim3(L.num_kv_heads, L.num_seqs, L.max_parts),
-                       dim3(kDecThreads), 0, stream, a);
-    if (hipGetLastError() != hipSuccess) return -1;
+    const hipError_t e = launch_kernel(paged_decode_kernel<DT, D, G, kPrefetch>,
+                                       dim3(L.num_kv_heads, L.num_seqs, L.max_parts), dim3(kDecThreads), stream, a);
+    if (e != hipSuccess) return e;
   }
   if (L.stage != 1 && L.max_parts > 1) {
     const int outs = L.num_q_heads * D;
-    hipLaunchKernelGGL(paged_decode_merge_kernel, dim3((outs + 255) / 256, L.num_seqs), dim3(256), 0, stream, a, D,
-                       G);
-    if (hipGetLastError() != hipSuccess) return -1;
+    return launch_kernel(paged_decode_merge_kernel, dim3((outs + 255) / 256, L.num_seqs), dim3(256), stream, a, D, G);
   }
-  return 0;
+  return hipSuccess;
 }
 
 template <int DT, int D>
-static int launch_decode_d(const DecodeLaunch& L, hipStream_t stream) {
+static hipError_t launch_decode_d(const DecodeLaunch& L, hipStream_t stream) {
   switch (L.num_q_heads / L.num_kv_heads) {
     case 1: return launch_decode_t<DT, D, 1>(L, stream);
     case 2: return launch_decode_t<DT, D, 2>(L, stream);
     case 4: return launch_decode_t<DT, D, 4>(L, stream);
     case 8: return launch_decode_t<DT, D, 8>(L, stream);
   }
-  return -1;
+  return hipErrorInvalidConfiguration;
 }
 
 template <int DT>
-static int launch_decode_dt(const DecodeLaunch& L, hipStream_t stream) {
+static hipError_t launch_decode_dt(const DecodeLaunch& L, hipStream_t stream) {
   if (L.head_dim == 64) return launch_decode_d<DT, 64>(L, stream);
   if (L.head_dim == 128) return launch_decode_d<DT, 128>(L, stream);
-  return -1;
+  return hipErrorInvalidConfiguration;
 }
 
-int launch_decode(const DecodeLaunch& L, hipStream_t stream) {
-  if (L.partition > kMaxPartition || L.partition % 64 != 0) return -1;
+hipError_t launch_decode(const DecodeLaunch& L, hipStream_t stream) {
+  if (L.partition > kMaxPartition || L.partition % 64 != 0) return hipErrorInvalidConfiguration;
   switch (L.dt) {
     case DT_F32: return launch_decode_dt<DT_F32>(L, stream);
     case DT_F16: return launch_decode_dt<DT_F16>(L, stream);
     case DT_BF16: return launch_decode_dt<DT_BF16>(L, stream);
   }
-  return -1;
+  return hipErrorInvalidConfiguration;
 }
 
 }  // namespace pkv

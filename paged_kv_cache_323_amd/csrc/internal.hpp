@@ -22,16 +22,28 @@ inline int ilog2(int x) {
   return r;
 }
 
-// Launchers return 0 on success, -1 if the launch failed.
-int launch_kv_cache_write(const void* k, const void* v, void* kc, void* vc, const int32_t* slots,
+template <class T> struct NonDeduced { using type = T; };
+
+// Enqueue kernel<<<grid, block, 0, stream>>>(args...) and return the status of this launch
+// alone: an error left behind by an earlier, unrelated HIP call on the thread does not leak in.
+template <typename... P>
+inline hipError_t launch_kernel(void (*kernel)(P...), dim3 grid, dim3 block, hipStream_t stream,
+                                typename NonDeduced<P>::type... args) {
+  void* argv[] = {static_cast<void*>(&args)..., nullptr};
+  return hipLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, argv, 0, stream);
+}
+
+// Launchers return hipSuccess, the failed launch's hipError_t, or hipErrorInvalidConfiguration
+// for a shape they do not handle.
+hipError_t launch_kv_cache_write(const void* k, const void* v, void* kc, void* vc, const int32_t* slots,
                           int num_tokens, int64_t k_stride_b, int64_t v_stride_b, int num_kv_heads,
                           int block_size, int head_dim, int elem_bytes, hipStream_t stream);
 
-int launch_copy_blocks(void* kc, void* vc, const int32_t* pairs, int num_pairs, int64_t block_bytes,
+hipError_t launch_copy_blocks(void* kc, void* vc, const int32_t* pairs, int num_pairs, int64_t block_bytes,
                        hipStream_t stream);
 
 // Whole-block copies from (src_k, src_v) to (dst_k, dst_v); either may be pinned host memory.
-int launch_copy_between(void* dst_k, void* dst_v, const void* src_k, const void* src_v, const int32_t* pairs,
+hipError_t launch_copy_between(void* dst_k, void* dst_v, const void* src_k, const void* src_v, const int32_t* pairs,
                         int num_pairs, int64_t block_bytes, hipStream_t stream);
 
 struct DecodeLaunch {
@@ -58,7 +70,7 @@ struct DecodeLaunch {
   int stage;       // 0: partitions then merge; 1: partitions only; 2: merge only
 };
 
-int launch_decode(const DecodeLaunch& a, hipStream_t stream);
+hipError_t launch_decode(const DecodeLaunch& a, hipStream_t stream);
 
 struct PrefillLaunch {
   void* out;
@@ -82,6 +94,6 @@ struct PrefillLaunch {
 
 // Causal attention of every multi-row (prefill) sequence of a ragged batch; rows of
 // single-row sequences are left untouched.
-int launch_ragged_prefill(const PrefillLaunch& a, hipStream_t stream);
+hipError_t launch_ragged_prefill(const PrefillLaunch& a, hipStream_t stream);
 
 }  // namespace pkv

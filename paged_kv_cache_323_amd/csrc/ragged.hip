@@ -378,7 +378,7 @@ __global__ __launch_bounds__(kPfThreads, 2) void ragged_prefill_kernel(PrefillAr
 }
 
 template <int DT>
-static int launch_prefill_dt(const PrefillLaunch& L, hipStream_t stream) {
+static hipError_t launch_prefill_dt(const PrefillLaunch& L, hipStream_t stream) {
   PrefillArgs a;
   a.out = L.out;
   a.q = static_cast<const uint16_t*>(L.q);
@@ -398,20 +398,18 @@ static int launch_prefill_dt(const PrefillLaunch& L, hipStream_t stream) {
   // Row tiles: sum over sequences of ceil(q_len / 128) <= T / 128 + (number of prefill
   // sequences); slots past the real count exit at once.
   const long long slots = (L.num_tokens + kPfRows - 1) / kPfRows + (L.num_seqs < L.num_tokens / 2 ? L.num_seqs : L.num_tokens / 2);
-  if (slots <= 0) return 0;
-  if (slots > 65535 || L.num_q_heads > 0x7fffffff) return -1;
+  if (slots <= 0) return hipSuccess;
+  if (slots > 65535 || L.num_q_heads > 0x7fffffff) return hipErrorInvalidConfiguration;
   // Heads are the fast grid dimension so the heaviest row tiles of every head go out first.
-  if (L.head_dim == 128)
-    hipLaunchKernelGGL((ragged_prefill_kernel<DT, 128>), dim3(L.num_q_heads, (unsigned)slots), dim3(kPfThreads), 0, stream, a);
-  else
-    hipLaunchKernelGGL((ragged_prefill_kernel<DT, 64>), dim3(L.num_q_heads, (unsigned)slots), dim3(kPfThreads), 0, stream, a);
-  return hipGetLastError() == hipSuccess ? 0 : -1;
+  const dim3 grid(L.num_q_heads, (unsigned)slots);
+  if (L.head_dim == 128) return launch_kernel(ragged_prefill_kernel<DT, 128>, grid, dim3(kPfThreads), stream, a);
+  return launch_kernel(ragged_prefill_kernel<DT, 64>, grid, dim3(kPfThreads), stream, a);
 }
 
-int launch_ragged_prefill(const PrefillLaunch& L, hipStream_t stream) {
+hipError_t launch_ragged_prefill(const PrefillLaunch& L, hipStream_t stream) {
   if (L.dt == DT_BF16) return launch_prefill_dt<DT_BF16>(L, stream);
   if (L.dt == DT_F16) return launch_prefill_dt<DT_F16>(L, stream);
-  return -1;
+  return hipErrorInvalidConfiguration;
 }
 
 }  // namespace pkv

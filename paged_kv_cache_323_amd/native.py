@@ -13,6 +13,13 @@ from typing import Optional, Sequence, Tuple
 
 import numpy as np
 
+# The library's HIP calls must reach the same HIP runtime as torch's allocations and streams.
+# torch ships its own libamdhip64 under the same soname; importing torch first makes the dynamic
+# loader bind libpagedkv.so to that copy. Loaded the other way round, the process would map two
+# runtimes, and the second one may not see the device at all (its launches fail with
+# hipErrorNoDevice).
+import torch  # noqa: F401  (imported for its side effect on symbol binding)
+
 _HERE = os.path.dirname(os.path.abspath(__file__))
 # PAGEDKV_LIB selects another build of the same library (e.g. a tuning variant).
 LIB_PATH = os.environ.get("PAGEDKV_LIB") or os.path.join(_HERE, "libpagedkv.so")
@@ -27,7 +34,10 @@ STATUS = {0: "PKV_OK", -1: "PKV_EINVAL", -2: "PKV_EDTYPE", -3: "PKV_ESHAPE", -4:
 class PagedKVError(RuntimeError):
     def __init__(self, status: int, where: str):
         self.status = status
-        super().__init__(f"{where}: {STATUS.get(status, status)} ({_lib.pkv_status_str(status).decode()})")
+        msg = f"{where}: {STATUS.get(status, status)} ({_lib.pkv_status_str(status).decode()})"
+        if status == -5:  # PKV_ELAUNCH
+            msg += f" [{_lib.pkv_last_launch_error().decode()}]"
+        super().__init__(msg)
 
 
 class NoFreeBlocksError(PagedKVError):
@@ -42,6 +52,21 @@ if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is missing: build it with `python -m paged_kv_cache_323_amd.build`")
 
 _lib = ctypes.CDLL(LIB_PATH)
+
+
+def _hip_runtimes():
+    """Distinct libamdhip64 files mapped into this process."""
+    try:
+        with open("/proc/self/maps") as f:
+            return sorted({os.path.realpath(ln.split()[-1]) for ln in f
+                           if len(ln.split()) >= 6 and "libamdhip64" in ln.split()[-1]})
+    except OSError:
+        return []
+
+
+if len(_hip_runtimes()) > 1:
+    raise ImportError(f"two HIP runtimes are mapped into this process ({', '.join(_hip_runtimes())}); "
+                      "libpagedkv.so must share torch's: import torch before loading it")
 
 
 class CacheDesc(ctypes.Structure):
@@ -65,6 +90,7 @@ _I64P = ctypes.POINTER(ctypes.c_int64)
 _SIGS = {
     "pkv_status_str": (ctypes.c_char_p, [_I32]),
     "pkv_version": (ctypes.c_char_p, []),
+    "pkv_last_launch_error": (ctypes.c_char_p, []),
     "pkv_kv_cache_write": (_I32, [_P, _P, _P, _P, _P, _I32, _I64, _I64, _DESC, _P]),
     "pkv_copy_blocks": (_I32, [_P, _P, _P, _I32, _DESC, _P]),
     "pkv_swap_blocks": (_I32, [_P, _P, _P, _P, _P, _I32, _DESC, _P]),
@@ -200,7 +226,7 @@ def _device_address(t, name: str) -> ctypes.c_void_p:
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
     if _hip is None:
-        _hip = ctypes.CDLL("libamdhip64.so")
+        _hip = ctypes.CDLL(_hip_runtimes()[0] if _hip_runtimes() else "libamdhip64.so.7")
         _hip.hipHostGetDevicePointer.restype = ctypes.c_int
         _hip.hipHostGetDevicePointer.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_void_p, ctypes.c_uint]
     dptr = ctypes.c_void_p()
@@ -305,7 +331,7 @@ class BlockManager:
 
     def __del__(self):
         h = getattr(self, "_h", None)
-        if h:
+        if h and _lib is not None:  # at interpreter shutdown the module may already be torn down
             _lib.pkv_bm_destroy(h)
             self._h = None
 

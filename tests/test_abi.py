@@ -5,6 +5,7 @@ import ctypes
 import os
 import re
 import subprocess
+import sys
 
 import pytest
 
@@ -120,3 +121,14 @@ def test_ragged_validation():
     assert ragged(desc(), max_q=6, T=5) == -1            # nor the token count
     assert ragged(desc(), hq=6) == -3
     assert ragged(desc(), S=0) == 0 and ragged(desc(), T=0) == 0
+
+
+def test_single_hip_runtime_when_binding_is_imported_before_torch():
+    # Loaded before torch, the library would bind to a second libamdhip64 that may not see
+    # the device; the binding imports torch first so every HIP call shares torch's runtime.
+    code = ("import paged_kv_cache_323_amd.native as n, torch, os\n"
+            "maps = [l.split()[-1] for l in open('/proc/self/maps') if 'libamdhip64' in l]\n"
+            "print(len({os.path.realpath(m) for m in maps}))\n")
+    out = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True, timeout=300)
+    assert out.returncode == 0, out.stderr
+    assert out.stdout.strip().splitlines()[-1] == "1"
