@@ -46,6 +46,24 @@ template <> struct Mfma<DT_F16> {
   }
 };
 
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// Split two probabilities x = hi + lo into 16-bit high parts and 16-bit remainders, each pair
+// packed into one 32-bit operand word (element 0 in the low half). hi is truncated, the
+// remainder carries the rest, so hi + lo keeps about 16 significant bits.
+template <int DT> __device__ __forceinline__ void split_pair(float x0, float x1, uint32_t& hi, uint32_t& lo);
+template <> __device__ __forceinline__ void split_pair<DT_BF16>(float x0, float x1, uint32_t& hi, uint32_t& lo) {
+  const uint32_t u0 = __float_as_uint(x0), u1 = __float_as_uint(x1);
+  hi = __builtin_amdgcn_perm(u1, u0, 0x07060302u);  // upper halves: bf16 truncation of both
+  const f32x2 r = {x0 - __uint_as_float(u0 & 0xffff0000u), x1 - __uint_as_float(u1 & 0xffff0000u)};
+  lo = __builtin_bit_cast(uint32_t, __builtin_convertvector(r, bf16x2));
+}
+template <> __device__ __forceinline__ void split_pair<DT_F16>(float x0, float x1, uint32_t& hi, uint32_t& lo) {
+  const auto h = __builtin_amdgcn_cvt_pkrtz(x0, x1);  // round toward zero; the remainder is exact
+  hi = __builtin_bit_cast(uint32_t, h);
+  lo = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(x0 - (float)h[0], x1 - (float)h[1]));
+}
+
 struct PrefillArgs {
   void* out;
   const uint16_t* q;
@@ -66,6 +84,21 @@ struct PrefillArgs {
 
 constexpr int kPfTab = 1024;  // block-table entries cached in LDS at a time
 
+// Max / sum over the four 16-lane rows of a wave (lanes l, l^16, l^32, l^48), all in VALU: a
+// row swap with itself leaves the two partners' values in the two results.
+__device__ __forceinline__ float rows_max(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  const auto t = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(t[0]), __uint_as_float(t[1]));
+}
+__device__ __forceinline__ float rows_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  const auto t = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(t[0]) + __uint_as_float(t[1]);
+}
+
 template <int DT, int D>
 // Two workgroups per CU: the register budget is capped at 256 per lane so that one wave's MFMA
 // work overlaps the other's softmax and staging.
@@ -82,8 +115,10 @@ __global__ __launch_bounds__(kPfThreads, 2) void ragged_prefill_kernel(PrefillAr
   constexpr int KIT = kPfKeys * CPR / kPfThreads;        // K chunks staged per thread
   constexpr int VIT = (kPfKeys / 2) * CPR / kPfThreads;  // V key-pair chunks staged per thread
 
-  __shared__ __attribute__((aligned(16))) uint16_t sK[kPfKeys * KLD];
-  __shared__ __attribute__((aligned(16))) uint16_t sVt[D * VLD];
+  constexpr int KBUF = kPfKeys * KLD;  // elements of one K buffer
+  constexpr int VBUF = D * VLD;        // elements of one transposed-V buffer
+  __shared__ __attribute__((aligned(16))) uint16_t sK[2 * KBUF];
+  __shared__ __attribute__((aligned(16))) uint16_t sVt[2 * VBUF];
   __shared__ int s_tab[kPfTab];
   __shared__ int s_scan[kPfThreads];
   __shared__ int s_seq, s_tile;
@@ -185,47 +220,71 @@ __global__ __launch_bounds__(kPfThreads, 2) void ragged_prefill_kernel(PrefillAr
   for (int dt = 0; dt < DT16; ++dt)
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) oacc[dt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run[2] = {-INFINITY, -INFINITY};
+  float m_run[2] = {-INFINITY, -INFINITY};    // reference max of each row (raw score units)
+  const float lazy_thr = 8.f / a.scale_log2;  // 2^8 in probability terms, in raw score units
   float l_part[2] = {0.f, 0.f};  // this lane's share of the row sum (its 4-key slices)
 
   const int32_t* trow = a.tables + (size_t)s * a.max_blocks;
-  const size_t tile_rows = (size_t)a.hkv * a.bs;
-  const size_t head_rows = (size_t)kvh * a.bs;
+  const uint32_t blk_elems = (uint32_t)(a.hkv * a.bs * D);  // elements of one pool block
+  const uint32_t head_off = (uint32_t)(kvh * a.bs * D);      // this kv head's rows in a block
   const int nblk = (kend + a.bs - 1) >> a.log2_bs;
   int tab_base = -kPfTab;  // first table entry held in s_tab
 
-  // Global -> register staging of one key tile (keys >= kend are zeros). Table entries come
-  // from the LDS cache, which covers every key of the tile (refreshed between tiles).
+  // Global -> register staging of one key tile. Keys past kend are clamped to key kend-1 (a
+  // written row, so finite): such keys are masked for every row that is stored, and their V
+  // rows meet a zero probability. All loads are unconditional, so their table lookups and
+  // addresses are computed together and the loads issue back to back.
   u32x4 kreg[KIT];
   u32x4 vreg[VIT][2];
   auto fetch = [&](int kt) {
     const int k0 = kt * kPfKeys;
+    uint32_t inner[KIT], phys[KIT];
+#pragma unroll
+    for (int it = 0; it < KIT; ++it) {
+      const int kk = min(k0 + (it * kPfThreads + tid) / CPR, kend - 1);
+      phys[it] = (uint32_t)s_tab[(kk >> a.log2_bs) - tab_base];
+      inner[it] = head_off + (uint32_t)(kk & (a.bs - 1)) * D + ((it * kPfThreads + tid) % CPR) * 8;
+    }
+    // Every V chunk of this thread covers the same key pair (kp = tid mod 32); the pair shares
+    // a block because B is even.
+    const int kv0 = min(k0 + 2 * (tid & (kPfKeys / 2 - 1)), kend - 1);
+    const int kv1 = min(k0 + 2 * (tid & (kPfKeys / 2 - 1)) + 1, kend - 1);
+    const uint32_t vphys = (uint32_t)s_tab[(kv0 >> a.log2_bs) - tab_base];
+    const uint64_t vbase = (uint64_t)vphys * blk_elems + head_off;
+    const uint32_t v0 = (uint32_t)(kv0 & (a.bs - 1)) * D, v1 = (uint32_t)(kv1 & (a.bs - 1)) * D;
+#pragma unroll
+    for (int it = 0; it < KIT; ++it)
+      kreg[it] = *reinterpret_cast<const u32x4*>(a.kc + ((uint64_t)phys[it] * blk_elems + inner[it]));
+#pragma unroll
+    for (int it = 0; it < VIT; ++it) {
+      const uint32_t ch8 = ((it * kPfThreads + tid) / (kPfKeys / 2)) * 8;
+      vreg[it][0] = *reinterpret_cast<const u32x4*>(a.vc + (vbase + v0 + ch8));
+      vreg[it][1] = *reinterpret_cast<const u32x4*>(a.vc + (vbase + v1 + ch8));
+    }
+  };
+  // Registers -> LDS buffer b: K row-major, V transposed (word = two adjacent keys).
+  auto stage = [&](int b) {
+    uint16_t* k_dst = sK + b * KBUF;
+    uint16_t* v_dst = sVt + b * VBUF;
 #pragma unroll
     for (int it = 0; it < KIT; ++it) {
       const int idx = it * kPfThreads + tid;
       const int key = idx / CPR;
       const int ch = idx - key * CPR;
-      const int kk = k0 + key;
-      kreg[it] = u32x4{0, 0, 0, 0};
-      if (kk < kend) {
-        const int phys = s_tab[(kk >> a.log2_bs) - tab_base];
-        const size_t row = (size_t)phys * tile_rows + head_rows + (kk & (a.bs - 1));
-        kreg[it] = *reinterpret_cast<const u32x4*>(a.kc + row * D + ch * 8);
-      }
+      *reinterpret_cast<u32x4*>(&k_dst[key * KLD + ch * 8]) = kreg[it];
     }
 #pragma unroll
     for (int it = 0; it < VIT; ++it) {
       const int idx = it * kPfThreads + tid;
       const int kp = idx & (kPfKeys / 2 - 1);
       const int ch = idx / (kPfKeys / 2);
-      const int kk = k0 + 2 * kp;  // kk and kk+1 share a block (B is even)
-      vreg[it][0] = u32x4{0, 0, 0, 0};
-      vreg[it][1] = u32x4{0, 0, 0, 0};
-      if (kk < kend) {
-        const int phys = s_tab[(kk >> a.log2_bs) - tab_base];
-        const size_t row = (size_t)phys * tile_rows + head_rows + (kk & (a.bs - 1));
-        vreg[it][0] = *reinterpret_cast<const u32x4*>(a.vc + row * D + ch * 8);
-        if (kk + 1 < kend) vreg[it][1] = *reinterpret_cast<const u32x4*>(a.vc + (row + 1) * D + ch * 8);
+      const u32x4 w0 = vreg[it][0], w1 = vreg[it][1];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t lo = __builtin_amdgcn_perm(w1[e], w0[e], 0x05040100u);  // low halves
+        const uint32_t hi = __builtin_amdgcn_perm(w1[e], w0[e], 0x07060302u);  // high halves
+        *reinterpret_cast<uint32_t*>(&v_dst[(ch * 8 + 2 * e) * VLD + 2 * kp]) = lo;
+        *reinterpret_cast<uint32_t*>(&v_dst[(ch * 8 + 2 * e + 1) * VLD + 2 * kp]) = hi;
       }
     }
   };
@@ -240,38 +299,20 @@ __global__ __launch_bounds__(kPfThreads, 2) void ragged_prefill_kernel(PrefillAr
     __syncthreads();
   };
 
-  ensure_table(0);
-  fetch(0);
+  // Two LDS buffers: tile kt is computed from buffer kt&1 while tile kt+1 (loaded into registers
+  // during the previous tile) is staged into the other one and tile kt+2's loads go out. One
+  // barrier per tile separates a buffer's last reads from its next writes.
+  if (nkt > 0) {  // nkt <= 0 only when a context is shorter than its query rows: nothing to read
+    ensure_table(0);
+    fetch(0);
+    stage(0);
+  }
+  __syncthreads();
+  if (nkt > 1) fetch(1);
   for (int kt = 0; kt < nkt; ++kt) {
     const int k0 = kt * kPfKeys;
-    // ---- registers of tile kt -> LDS: K row-major, V transposed (word = two adjacent keys) ----
-#pragma unroll
-    for (int it = 0; it < KIT; ++it) {
-      const int idx = it * kPfThreads + tid;
-      const int key = idx / CPR;
-      const int ch = idx - key * CPR;
-      *reinterpret_cast<u32x4*>(&sK[key * KLD + ch * 8]) = kreg[it];
-    }
-#pragma unroll
-    for (int it = 0; it < VIT; ++it) {
-      const int idx = it * kPfThreads + tid;
-      const int kp = idx & (kPfKeys / 2 - 1);
-      const int ch = idx / (kPfKeys / 2);
-      const u32x4 w0 = vreg[it][0], w1 = vreg[it][1];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint32_t lo = (w0[e] & 0xffffu) | (w1[e] << 16);
-        const uint32_t hi = (w0[e] >> 16) | (w1[e] & 0xffff0000u);
-        *reinterpret_cast<uint32_t*>(&sVt[(ch * 8 + 2 * e) * VLD + 2 * kp]) = lo;
-        *reinterpret_cast<uint32_t*>(&sVt[(ch * 8 + 2 * e + 1) * VLD + 2 * kp]) = hi;
-      }
-    }
-    __syncthreads();
-    // ---- next tile's loads go out now and land while this tile computes ----
-    if (kt + 1 < nkt) {
-      ensure_table(kt + 1);
-      fetch(kt + 1);
-    }
+    const uint16_t* cK = sK + (kt & 1) * KBUF;
+    const uint16_t* cV = sVt + (kt & 1) * VBUF;
 
     // ---- Sᵀ = K·Qᵀ: 4 key tiles x 2 row tiles -------------------------------------------------
     f32x4 sacc[4][2];
@@ -281,7 +322,7 @@ __global__ __launch_bounds__(kPfThreads, 2) void ragged_prefill_kernel(PrefillAr
       for (int nt = 0; nt < 2; ++nt) sacc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const V8 ka = __builtin_bit_cast(V8, *reinterpret_cast<const u32x4*>(&sK[(16 * mt + lr) * KLD + 32 * ks + 8 * g]));
+        const V8 ka = __builtin_bit_cast(V8, *reinterpret_cast<const u32x4*>(&cK[(16 * mt + lr) * KLD + 32 * ks + 8 * g]));
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) sacc[mt][nt] = M::mma(ka, qb[nt][ks], sacc[mt][nt]);
       }
@@ -305,14 +346,21 @@ __global__ __launch_bounds__(kPfThreads, 2) void ragged_prefill_kernel(PrefillAr
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
         mx = fmaxf(fmaxf(mx, fmaxf(sacc[mt][nt][0], sacc[mt][nt][1])), fmaxf(sacc[mt][nt][2], sacc[mt][nt][3]));
-      mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
-      mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
-      const float m_new = fmaxf(m_run[nt], mx);
-      // Row with no visible key yet (only possible for padding rows): keep everything at zero.
-      const float m_use = m_new == -INFINITY ? 0.f : m_new;
-      const float alpha = fast_exp2((m_run[nt] - m_use) * a.scale_log2);
-      m_run[nt] = m_new;
-      const float off = -m_use * a.scale_log2;
+      mx = rows_max(mx);
+      // Lazy rescaling: the reference max m_run only moves when some row's tile max exceeds it by
+      // more than 2^8 in probability terms; until then probabilities may reach 2^8, which fp32
+      // sums and the 16-bit split represent as well as values below 1. A row with no visible key
+      // yet keeps m_run = -inf (its probabilities are exactly 0).
+      const bool grow = mx > m_run[nt] + lazy_thr;
+      if (__builtin_amdgcn_read_exec() & __ballot(grow)) {  // wave-uniform
+        const float m_new = fmaxf(m_run[nt], mx);
+        const float alpha = m_run[nt] == -INFINITY ? 0.f : fast_exp2((m_run[nt] - m_new) * a.scale_log2);
+        m_run[nt] = m_new;
+        l_part[nt] *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < DT16; ++dt) oacc[dt][nt] *= alpha;
+      }
+      const float off = -(m_run[nt] == -INFINITY ? 0.f : m_run[nt]) * a.scale_log2;
       float lsum = 0.f;
       float p[4][4];
 #pragma unroll
@@ -322,25 +370,31 @@ __global__ __launch_bounds__(kPfThreads, 2) void ragged_prefill_kernel(PrefillAr
           p[mt][i] = fast_exp2(__builtin_fmaf(sacc[mt][nt][i], a.scale_log2, off));
           lsum += p[mt][i];
         }
-      l_part[nt] = l_part[nt] * alpha + lsum;
-      // Rescale the running output only when some row's max moved (rare after the first tiles).
-      if (__builtin_amdgcn_read_exec() & __ballot(alpha != 1.f)) {
-#pragma unroll
-        for (int dt = 0; dt < DT16; ++dt) oacc[dt][nt] *= alpha;
-      }
-      // B operand of k-step j: keys 32j + 4g + (0..3) then 32j + 16 + 4g + (0..3).
+      l_part[nt] += lsum;
+      // B operand of k-step j: keys 32j + 4g + (0..3) then 32j + 16 + 4g + (0..3); element e of
+      // the operand is the low (e even) or high half of word e/2.
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
-        V8 hi, lo;
+        u32x4 hw, lw;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float x = p[2 * j + (e >> 2)][e & 3];
-          const typename M::S xh = (typename M::S)x;
-          hi[e] = xh;
-          lo[e] = (typename M::S)(x - (float)xh);
+        for (int w = 0; w < 4; ++w) {
+          const int e = 2 * w;
+          uint32_t h, l;
+          split_pair<DT>(p[2 * j + (e >> 2)][e & 3], p[2 * j + (e >> 2)][(e & 3) + 1], h, l);
+          hw[w] = h;
+          lw[w] = l;
         }
-        phi[nt][j] = hi;
-        plo[nt][j] = lo;
+        phi[nt][j] = __builtin_bit_cast(V8, hw);
+        plo[nt][j] = __builtin_bit_cast(V8, lw);
+      }
+    }
+
+    // ---- the next tile goes to the other buffer; the one after it starts loading ---------------
+    if (kt + 1 < nkt) {
+      stage((kt + 1) & 1);
+      if (kt + 2 < nkt) {
+        ensure_table(kt + 2);
+        fetch(kt + 2);
       }
     }
 
@@ -349,7 +403,7 @@ __global__ __launch_bounds__(kPfThreads, 2) void ragged_prefill_kernel(PrefillAr
     for (int dt = 0; dt < DT16; ++dt) {
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
-        const uint16_t* vrow = &sVt[(16 * dt + lr) * VLD + 32 * j + 4 * g];
+        const uint16_t* vrow = &cV[(16 * dt + lr) * VLD + 32 * j + 4 * g];
         const u32x2 x0 = *reinterpret_cast<const u32x2*>(vrow);
         const u32x2 x1 = *reinterpret_cast<const u32x2*>(vrow + 16);
         const V8 va = __builtin_bit_cast(V8, u32x4{x0[0], x0[1], x1[0], x1[1]});
@@ -360,15 +414,13 @@ __global__ __launch_bounds__(kPfThreads, 2) void ragged_prefill_kernel(PrefillAr
         }
       }
     }
-    __syncthreads();  // the next tile overwrites sK / sVt
+    __syncthreads();  // buffer kt&1 is free for tile kt+2; buffer (kt+1)&1 is complete
   }
 
   // ---- normalise and store: lane writes dims 16*dt + 4*g .. +3 of its row ----------------------
 #pragma unroll
   for (int nt = 0; nt < 2; ++nt) {
-    float l = l_part[nt];
-    l += __shfl_xor(l, 16, kWave);
-    l += __shfl_xor(l, 32, kWave);
+    const float l = rows_sum(l_part[nt]);
     if (!qvalid[nt]) continue;
     const float inv = l > 0.f ? 1.f / l : 0.f;
     const size_t orow = ((size_t)(q0 + wave * 32 + nt * 16 + lr + row0) * a.hq + h) * D;
