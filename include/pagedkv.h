@@ -84,6 +84,29 @@ const char* pkv_version(void);
 const char* pkv_last_launch_error(void);
 
 /*
+ * Debug builds. Device-resident indices (slots, block-table entries, copy pairs, ragged row
+ * offsets) are trusted by the release library. libpagedkv_debug.so, the same sources compiled
+ * with PKV_DEBUG_CHECKS, checks each one in the kernel before using it:
+ *   - a slot >= num_blocks * block_size is skipped                      (flag bit 0, PKV_DBG_SLOT)
+ *   - a block-table entry outside [0, num_blocks) is read as block 0     (bit 1, PKV_DBG_BLOCK)
+ *   - ragged row offsets that are negative, decreasing or past num_tokens make that sequence
+ *     empty (and a decode row outside the batch is skipped)              (bit 2, PKV_DBG_RAGGED)
+ *   - a copy pair with a negative index, or (copy_blocks) one >= num_blocks, is skipped;
+ *     pkv_swap_blocks checks non-negativity only, as it does not know the host pool's size
+ *                                                                        (bit 3, PKV_DBG_PAIR)
+ * so a bad index yields wrong values instead of an out-of-bounds access. Results are otherwise
+ * identical to the release build.
+ *
+ * pkv_debug_checks_enabled: 1 in a debug build, 0 in a release build.
+ * pkv_debug_flags: waits for all work on the current device, writes the OR of the flag bits raised
+ *   on it since the last clear into *flags, and clears them if clear != 0. Always 0 in a release
+ *   build. Returns PKV_EINVAL for a null flags pointer, PKV_ELAUNCH if a HIP call fails.
+ */
+enum { PKV_DBG_SLOT = 1, PKV_DBG_BLOCK = 2, PKV_DBG_RAGGED = 4, PKV_DBG_PAIR = 8 };
+int32_t pkv_debug_checks_enabled(void);
+int32_t pkv_debug_flags(uint32_t* flags, int32_t clear);
+
+/*
  * kv_cache_write — store new tokens' keys and values into their slots.
  *   k_cache[slot[t]] <- k[t], v_cache[slot[t]] <- v[t] for t < num_tokens, bit for bit.
  *   Each decode step stores the new token's K/V; a prefill stores the whole prompt's

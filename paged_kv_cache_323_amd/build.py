@@ -19,6 +19,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libpagedkv.so")
+# The same sources with bounds checks of device-resident indices (PKV_DEBUG_CHECKS).
+DEBUG_LIB = os.path.join(PKG, "libpagedkv_debug.so")
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 HIPCC = os.path.join(ROCM, "bin", "hipcc")
 ARCH = "gfx950"
@@ -78,5 +80,12 @@ def build(verbose: bool = False, jobs: int = 8, defines=(), out: str = LIB, buil
     return out
 
 
+def build_all(verbose: bool = False):
+    """The release library and the debug (bounds-checked) library."""
+    return [build(verbose=verbose),
+            build(verbose=verbose, defines=("PKV_DEBUG_CHECKS",), out=DEBUG_LIB,
+                  build_dir=os.path.join(BUILD, "debug"))]
+
+
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    print("\n".join(build_all(verbose="-v" in sys.argv)))

@@ -6,6 +6,7 @@
 #include <stdint.h>
 
 #include "../../include/pagedkv.h"
+#include "common.hpp"
 #include "internal.hpp"
 
 namespace {
@@ -82,6 +83,22 @@ extern "C" {
 
 const char* pkv_last_launch_error(void) { return hipGetErrorName(g_last_launch); }
 
+int32_t pkv_debug_checks_enabled(void) { return pkv::kDebugChecks ? 1 : 0; }
+
+int32_t pkv_debug_flags(uint32_t* flags, int32_t clear) {
+  if (!flags) return PKV_EINVAL;
+  uint32_t w[3][pkv::DBG_WORDS];
+  if (pkv::debug_words_cache_ops(w[0], clear != 0) || pkv::debug_words_decode(w[1], clear != 0) ||
+      pkv::debug_words_ragged(w[2], clear != 0))
+    return PKV_ELAUNCH;
+  uint32_t bits = 0;
+  for (int u = 0; u < 3; ++u)
+    for (int i = 0; i < pkv::DBG_WORDS; ++i)
+      if (w[u][i]) bits |= 1u << i;
+  *flags = bits;
+  return PKV_OK;
+}
+
 const char* pkv_status_str(int32_t s) {
   switch (s) {
     case PKV_OK: return "ok";
@@ -115,7 +132,7 @@ int32_t pkv_kv_cache_write(const void* k, const void* v, void* k_cache, void* v_
   if ((uint64_t)num_tokens * c->num_kv_heads * (c->head_dim * es / 16) > 0xffffffffull) return PKV_ESHAPE;
   return launched(pkv::launch_kv_cache_write(k, v, k_cache, v_cache, slot_mapping, num_tokens,
                                              k_token_stride * es, v_token_stride * es, c->num_kv_heads,
-                                             c->block_size, c->head_dim, es, (hipStream_t)stream));
+                                             c->block_size, c->head_dim, es, c->num_blocks, (hipStream_t)stream));
 }
 
 int32_t pkv_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs, int32_t num_pairs,
@@ -126,7 +143,8 @@ int32_t pkv_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs, int3
   if (num_pairs == 0) return PKV_OK;
   if (!k_cache || !v_cache || !pairs) return PKV_EINVAL;
   const int64_t block_bytes = (int64_t)c->num_kv_heads * c->block_size * c->head_dim * elem_bytes(c->dtype);
-  return launched(pkv::launch_copy_blocks(k_cache, v_cache, pairs, num_pairs, block_bytes, (hipStream_t)stream));
+  return launched(
+      pkv::launch_copy_blocks(k_cache, v_cache, pairs, num_pairs, block_bytes, c->num_blocks, (hipStream_t)stream));
 }
 
 int32_t pkv_swap_blocks(void* dst_k, void* dst_v, const void* src_k, const void* src_v, const int32_t* pairs,
@@ -138,7 +156,7 @@ int32_t pkv_swap_blocks(void* dst_k, void* dst_v, const void* src_k, const void*
   if (!dst_k || !dst_v || !src_k || !src_v || !pairs) return PKV_EINVAL;
   const int64_t block_bytes = (int64_t)c->num_kv_heads * c->block_size * c->head_dim * elem_bytes(c->dtype);
   return launched(
-      pkv::launch_copy_between(dst_k, dst_v, src_k, src_v, pairs, num_pairs, block_bytes, (hipStream_t)stream));
+      pkv::launch_copy_between(dst_k, dst_v, src_k, src_v, pairs, num_pairs, block_bytes, 0, 0, (hipStream_t)stream));
 }
 
 int32_t pkv_decode_partition_size(int32_t num_seqs, int32_t num_q_heads, int32_t max_ctx,
@@ -169,7 +187,7 @@ static int32_t decode_common_cu(void* out, int32_t out_dtype, const void* q, con
                                 const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads, float scale,
                                 int32_t max_context_len, const pkv_cache_desc* c, int32_t partition_size,
                                 void* workspace, size_t workspace_bytes, void* stream, const int32_t* cu,
-                                int stage = 0) {
+                                int stage = 0, int32_t num_rows = -1) {
   int32_t st = check_cache(c);
   if (st != PKV_OK) return st;
   if ((st = check_heads(num_q_heads, c)) != PKV_OK) return st;
@@ -211,6 +229,8 @@ static int32_t decode_common_cu(void* out, int32_t out_dtype, const void* q, con
   L.ws_ml = ws.total ? reinterpret_cast<float*>(wb + ws.ml) : nullptr;
   L.stage = stage;
   L.cu = cu;
+  L.num_blocks = c->num_blocks;
+  L.num_rows = num_rows >= 0 ? num_rows : num_seqs;
   return launched(pkv::launch_decode(L, (hipStream_t)stream));
 }
 
@@ -287,7 +307,7 @@ int32_t pkv_paged_attention_ragged(void* out, int32_t out_dtype, const void* q, 
   // decode rows (q_len == 1) through the decode kernels with row indirection
   st = decode_common_cu(out, out_dtype, q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens,
                         num_seqs, num_q_heads, scale, max_context_len, c, 0, workspace, workspace_bytes, stream,
-                        cu_seqlens_q);
+                        cu_seqlens_q, 0, num_tokens);
   if (st != PKV_OK || max_q_len <= 1) return st;
   pkv::PrefillLaunch P;
   P.out = out;
@@ -307,6 +327,7 @@ int32_t pkv_paged_attention_ragged(void* out, int32_t out_dtype, const void* q, 
   P.head_dim = c->head_dim;
   P.dt = c->dtype;
   P.scale = scale;
+  P.num_blocks = c->num_blocks;
   return launched(pkv::launch_ragged_prefill(P, (hipStream_t)stream));
 }
 

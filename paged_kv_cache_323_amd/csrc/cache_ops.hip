@@ -7,13 +7,15 @@
 
 namespace pkv {
 
+PKV_DEBUG_UNIT(cache_ops)
+
 // pool[slot[t]] <- (k[t], v[t]): one thread per 16-byte chunk of one (token, kv head) row.
 // A slot addresses block slot/B, offset slot%B; the device layout is [N][H][B][D].
 __global__ __launch_bounds__(256) void kv_cache_write_kernel(
     const char* __restrict__ k, const char* __restrict__ v, char* __restrict__ kc,
     char* __restrict__ vc, const int32_t* __restrict__ slots, uint32_t total_chunks,
     uint32_t chunks_per_token, uint32_t chunks_per_row, int64_t k_stride_b, int64_t v_stride_b,
-    int num_kv_heads, int block_size, int log2_block, int row_bytes) {
+    int num_kv_heads, int block_size, int log2_block, int row_bytes, int64_t num_slots) {
   const uint32_t step = gridDim.x * blockDim.x;
   for (uint32_t i = blockIdx.x * blockDim.x + threadIdx.x; i < total_chunks; i += step) {
     const uint32_t t = i / chunks_per_token;
@@ -22,6 +24,10 @@ __global__ __launch_bounds__(256) void kv_cache_write_kernel(
     const uint32_t ch = rem - h * chunks_per_row;
     const int32_t slot = slots[t];
     if (slot < 0) continue;
+    if (kDebugChecks && slot >= num_slots) {
+      debug_flag(DBG_SLOT);
+      continue;
+    }
     const int64_t blk = slot >> log2_block;
     const int64_t off = slot & (block_size - 1);
     const int64_t dst = ((blk * num_kv_heads + h) * block_size + off) * row_bytes + ch * 16;
@@ -38,10 +44,17 @@ __global__ __launch_bounds__(256) void kv_cache_write_kernel(
 // copies between a GPU pool and a host swap pool (device-addressable pinned memory).
 __global__ __launch_bounds__(256) void copy_blocks_kernel(char* __restrict__ dk, char* __restrict__ dv,
                                                           const char* __restrict__ sk, const char* __restrict__ sv,
-                                                          const int32_t* __restrict__ pairs, int64_t block_bytes) {
+                                                          const int32_t* __restrict__ pairs, int64_t block_bytes,
+                                                          int src_blocks, int dst_blocks) {
   const int p = blockIdx.y;
-  const int64_t src = (int64_t)pairs[2 * p] * block_bytes;
-  const int64_t dst = (int64_t)pairs[2 * p + 1] * block_bytes;
+  const int32_t si = pairs[2 * p], di = pairs[2 * p + 1];
+  if (kDebugChecks &&
+      (si < 0 || di < 0 || (src_blocks > 0 && si >= src_blocks) || (dst_blocks > 0 && di >= dst_blocks))) {
+    if (blockIdx.x == 0 && threadIdx.x == 0) debug_flag(DBG_PAIR);
+    return;  // uniform over the workgroup
+  }
+  const int64_t src = (int64_t)si * block_bytes;
+  const int64_t dst = (int64_t)di * block_bytes;
   const int64_t step = (int64_t)gridDim.x * blockDim.x * 16;
   for (int64_t off = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 16; off < block_bytes; off += step) {
     const u32x4 a = *reinterpret_cast<const u32x4*>(sk + src + off);
@@ -52,8 +65,8 @@ __global__ __launch_bounds__(256) void copy_blocks_kernel(char* __restrict__ dk,
 }
 
 hipError_t launch_kv_cache_write(const void* k, const void* v, void* kc, void* vc, const int32_t* slots,
-                          int num_tokens, int64_t k_stride_b, int64_t v_stride_b, int num_kv_heads,
-                          int block_size, int head_dim, int elem_bytes, hipStream_t stream) {
+                                 int num_tokens, int64_t k_stride_b, int64_t v_stride_b, int num_kv_heads,
+                                 int block_size, int head_dim, int elem_bytes, int num_blocks, hipStream_t stream) {
   const int row_bytes = head_dim * elem_bytes;
   const uint32_t cpr = row_bytes / 16;
   const uint32_t cpt = cpr * num_kv_heads;
@@ -65,11 +78,11 @@ hipError_t launch_kv_cache_write(const void* k, const void* v, void* kc, void* v
   return launch_kernel(kv_cache_write_kernel, dim3(grid), dim3(256), stream, static_cast<const char*>(k),
                        static_cast<const char*>(v), static_cast<char*>(kc), static_cast<char*>(vc), slots,
                        (uint32_t)total, cpt, cpr, k_stride_b, v_stride_b, num_kv_heads, block_size,
-                       ilog2(block_size), row_bytes);
+                       ilog2(block_size), row_bytes, (int64_t)num_blocks * block_size);
 }
 
 hipError_t launch_copy_between(void* dk, void* dv, const void* sk, const void* sv, const int32_t* pairs, int num_pairs,
-                        int64_t block_bytes, hipStream_t stream) {
+                               int64_t block_bytes, int src_blocks, int dst_blocks, hipStream_t stream) {
   int64_t gx = (block_bytes + 256 * 16 * 4 - 1) / (256 * 16 * 4);  // ~4 chunks per thread
   if (gx < 1) gx = 1;
   if (gx > 256) gx = 256;
@@ -78,15 +91,15 @@ hipError_t launch_copy_between(void* dk, void* dv, const void* sk, const void* s
     const hipError_t e =
         launch_kernel(copy_blocks_kernel, dim3((unsigned)gx, (unsigned)n), dim3(256), stream, static_cast<char*>(dk),
                       static_cast<char*>(dv), static_cast<const char*>(sk), static_cast<const char*>(sv),
-                      pairs + 2 * (int64_t)first, block_bytes);
+                      pairs + 2 * (int64_t)first, block_bytes, src_blocks, dst_blocks);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
 }
 
 hipError_t launch_copy_blocks(void* kc, void* vc, const int32_t* pairs, int num_pairs, int64_t block_bytes,
-                       hipStream_t stream) {
-  return launch_copy_between(kc, vc, kc, vc, pairs, num_pairs, block_bytes, stream);
+                              int num_blocks, hipStream_t stream) {
+  return launch_copy_between(kc, vc, kc, vc, pairs, num_pairs, block_bytes, num_blocks, num_blocks, stream);
 }
 
 }  // namespace pkv

@@ -15,6 +15,46 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
+// ---- debug builds: bounds checks of device-resident indices ----------------------------------
+// Built with PKV_DEBUG_CHECKS, the kernels check every index they take from device memory (slots,
+// block ids, copy pairs, ragged row offsets) before using it. A bad index is skipped or replaced
+// by a safe one, and the kernel stores 1 into the matching error word of its translation unit
+// (plain stores: concurrent writers store the same value). Release builds compile the checks out.
+enum : int { DBG_SLOT = 0, DBG_BLOCK = 1, DBG_RAGGED = 2, DBG_PAIR = 3, DBG_WORDS = 4 };
+#ifdef PKV_DEBUG_CHECKS
+constexpr bool kDebugChecks = true;
+#else
+constexpr bool kDebugChecks = false;
+#endif
+
+// Defines the translation unit's error words, debug_flag(word), and the host accessor
+// debug_words_<unit> (declared in internal.hpp).
+#ifdef PKV_DEBUG_CHECKS
+#define PKV_DEBUG_UNIT(unit)                                                                        \
+  static __device__ uint32_t g_debug_words[DBG_WORDS];                                              \
+  static __device__ __forceinline__ void debug_flag(int w) { g_debug_words[w] = 1u; }               \
+  int debug_words_##unit(uint32_t* out, bool clear) {                                               \
+    if (hipDeviceSynchronize() != hipSuccess) return -1;                                            \
+    if (hipMemcpyFromSymbol(out, HIP_SYMBOL(g_debug_words), sizeof(uint32_t) * DBG_WORDS, 0,        \
+                            hipMemcpyDeviceToHost) != hipSuccess)                                   \
+      return -1;                                                                                    \
+    if (clear) {                                                                                    \
+      const uint32_t zero[DBG_WORDS] = {0, 0, 0, 0};                                                \
+      if (hipMemcpyToSymbol(HIP_SYMBOL(g_debug_words), zero, sizeof(zero), 0,                       \
+                            hipMemcpyHostToDevice) != hipSuccess)                                   \
+        return -1;                                                                                  \
+    }                                                                                               \
+    return 0;                                                                                       \
+  }
+#else
+#define PKV_DEBUG_UNIT(unit)                                                                        \
+  static __device__ __forceinline__ void debug_flag(int) {}                                         \
+  int debug_words_##unit(uint32_t* out, bool) {                                                     \
+    for (int i = 0; i < DBG_WORDS; ++i) out[i] = 0;                                                 \
+    return 0;                                                                                       \
+  }
+#endif
+
 // Storage type of each element type (bf16 is kept as raw 16-bit patterns).
 template <int DT> struct Elem;
 template <> struct Elem<DT_F32> { using T = float; };

@@ -27,6 +27,8 @@
 
 namespace pkv {
 
+PKV_DEBUG_UNIT(decode)
+
 constexpr int kDecThreads = 256;
 constexpr int kDecWaves = 4;
 
@@ -49,6 +51,8 @@ struct DecodeArgs {
   float scale_log2;
   int partition;
   int max_parts;
+  int num_blocks;  // pool blocks (debug builds check table entries)
+  int num_rows;    // rows of q / out (debug builds check ragged row offsets)
 };
 
 // Raw words of one lane's slice of a V row (PV mapping): 8, 16 or 32 bytes.
@@ -127,6 +131,10 @@ __global__ __launch_bounds__(kDecThreads, PKV_DECODE_MIN_WG) void paged_decode_k
   if (a.cu) {
     row = a.cu[s];
     if (a.cu[s + 1] - row != 1) return;
+    if (kDebugChecks && (row < 0 || row >= a.num_rows)) {
+      if (tid == 0) debug_flag(DBG_RAGGED);
+      return;  // uniform over the workgroup
+    }
   }
   // A length beyond the table or the launch's partitions breaks the caller's contract; clamping
   // keeps every access inside the table and the workspace.
@@ -144,7 +152,14 @@ __global__ __launch_bounds__(kDecThreads, PKV_DECODE_MIN_WG) void paged_decode_k
   // Block-table entries of this partition.
   const int nblk = (n + a.bs - 1) >> a.log2_bs;
   const int32_t* trow = a.tables + (size_t)s * a.max_blocks + (t0 >> a.log2_bs);
-  for (int i = tid; i < nblk; i += kDecThreads) s_tab[i] = trow[i];
+  for (int i = tid; i < nblk; i += kDecThreads) {
+    int b = trow[i];
+    if (kDebugChecks && (b < 0 || b >= a.num_blocks)) {
+      debug_flag(DBG_BLOCK);
+      b = 0;
+    }
+    s_tab[i] = b;
+  }
 
   // Query slices of the G heads in the score mapping.
   const int c = lane & 7;   // 16-byte chunk column
@@ -319,6 +334,7 @@ __global__ __launch_bounds__(256) void paged_decode_merge_kernel(DecodeArgs a, i
   if (a.cu) {
     row = a.cu[s];
     if (a.cu[s + 1] - row != 1) return;
+    if (kDebugChecks && (row < 0 || row >= a.num_rows)) return;  // flagged by the partition kernel
   }
   const int ctx = min(a.ctx_lens[s], min(a.max_blocks * a.bs, a.max_parts * a.partition));
   const int nparts = ctx > 0 ? (ctx + a.partition - 1) / a.partition : 1;
@@ -381,6 +397,8 @@ static DecodeArgs make_args(const DecodeLaunch& L) {
   a.scale_log2 = L.scale * 1.4426950408889634f;
   a.partition = L.partition;
   a.max_parts = L.max_parts;
+  a.num_blocks = L.num_blocks;
+  a.num_rows = L.num_rows;
   return a;
 }
 

@@ -35,16 +35,25 @@ inline hipError_t launch_kernel(void (*kernel)(P...), dim3 grid, dim3 block, hip
 
 // Launchers return hipSuccess, the failed launch's hipError_t, or hipErrorInvalidConfiguration
 // for a shape they do not handle.
+// num_blocks: blocks of the pool (debug builds reject slots beyond it).
 hipError_t launch_kv_cache_write(const void* k, const void* v, void* kc, void* vc, const int32_t* slots,
-                          int num_tokens, int64_t k_stride_b, int64_t v_stride_b, int num_kv_heads,
-                          int block_size, int head_dim, int elem_bytes, hipStream_t stream);
+                                 int num_tokens, int64_t k_stride_b, int64_t v_stride_b, int num_kv_heads,
+                                 int block_size, int head_dim, int elem_bytes, int num_blocks, hipStream_t stream);
 
 hipError_t launch_copy_blocks(void* kc, void* vc, const int32_t* pairs, int num_pairs, int64_t block_bytes,
-                       hipStream_t stream);
+                              int num_blocks, hipStream_t stream);
 
 // Whole-block copies from (src_k, src_v) to (dst_k, dst_v); either may be pinned host memory.
+// src_blocks / dst_blocks bound the pair indices in debug builds (0: no upper bound known).
 hipError_t launch_copy_between(void* dst_k, void* dst_v, const void* src_k, const void* src_v, const int32_t* pairs,
-                        int num_pairs, int64_t block_bytes, hipStream_t stream);
+                               int num_pairs, int64_t block_bytes, int src_blocks, int dst_blocks,
+                               hipStream_t stream);
+
+// Debug builds: copy the translation unit's error words to out[DBG_WORDS] (after a device-wide
+// wait) and clear them when clear is set. Release builds write zeros.
+int debug_words_cache_ops(uint32_t* out, bool clear);
+int debug_words_decode(uint32_t* out, bool clear);
+int debug_words_ragged(uint32_t* out, bool clear);
 
 struct DecodeLaunch {
   void* out;
@@ -68,6 +77,8 @@ struct DecodeLaunch {
   float* ws_acc;   // [S][Hkv][max_parts][G][D]   (only when max_parts > 1)
   float* ws_ml;    // [S][Hkv][max_parts][G][2]
   int stage;       // 0: partitions then merge; 1: partitions only; 2: merge only
+  int num_blocks;  // pool blocks (debug builds check table entries against it)
+  int num_rows;    // rows of q / out (debug builds check ragged row offsets against it)
 };
 
 hipError_t launch_decode(const DecodeLaunch& a, hipStream_t stream);
@@ -90,6 +101,7 @@ struct PrefillLaunch {
   int head_dim;
   int dt;
   float scale;
+  int num_blocks;  // pool blocks (debug builds check table entries against it)
 };
 
 // Causal attention of every multi-row (prefill) sequence of a ragged batch; rows of

@@ -22,6 +22,8 @@
 
 namespace pkv {
 
+PKV_DEBUG_UNIT(ragged)
+
 constexpr int kPfThreads = 256;
 constexpr int kPfRows = 128;  // query rows per workgroup (4 waves x 32)
 constexpr int kPfKeys = 64;   // keys per tile
@@ -80,6 +82,8 @@ struct PrefillArgs {
   int bs;
   int log2_bs;
   float scale_log2;
+  int num_tokens;  // rows of q / out (debug builds check cu_seqlens against it)
+  int num_blocks;  // pool blocks (debug builds check table entries)
 };
 
 constexpr int kPfTab = 1024;  // block-table entries cached in LDS at a time
@@ -128,6 +132,17 @@ __global__ __launch_bounds__(kPfThreads, 2) void ragged_prefill_kernel(PrefillAr
   const int wave = tid >> 6;
   const int h = blockIdx.x;
   const int kvh = h / (a.hq / a.hkv);
+  // Row tiles of sequence sq (0 for decode rows). Debug builds reject row offsets that are
+  // negative, decreasing or past the batch, and treat such a sequence as empty.
+  auto tiles_of = [&](int sq) {
+    const int c0 = a.cu[sq], c1 = a.cu[sq + 1];
+    if (kDebugChecks && (c0 < 0 || c1 < c0 || c1 > a.num_tokens)) {
+      debug_flag(DBG_RAGGED);
+      return 0;
+    }
+    const int ql = c1 - c0;
+    return ql > 1 ? (ql + kPfRows - 1) / kPfRows : 0;
+  };
 
   // ---- which (sequence, row tile) this workgroup owns ----------------------------------------
   // Slots are numbered from the end: the last row tiles of the last sequences (the longest
@@ -137,11 +152,7 @@ __global__ __launch_bounds__(kPfThreads, 2) void ragged_prefill_kernel(PrefillAr
     int total_all = 0;  // total tiles, needed to reverse the slot order
     for (int c0 = 0; c0 < a.num_seqs; c0 += kPfThreads) {
       const int sq = c0 + tid;
-      int nt = 0;
-      if (sq < a.num_seqs) {
-        const int ql = a.cu[sq + 1] - a.cu[sq];
-        nt = ql > 1 ? (ql + kPfRows - 1) / kPfRows : 0;
-      }
+      const int nt = sq < a.num_seqs ? tiles_of(sq) : 0;
       s_scan[tid] = nt;
       __syncthreads();
       for (int off = kPfThreads / 2; off > 0; off >>= 1) {
@@ -155,11 +166,7 @@ __global__ __launch_bounds__(kPfThreads, 2) void ragged_prefill_kernel(PrefillAr
     int base = 0;
     for (int c0 = 0; slot >= 0 && c0 < a.num_seqs; c0 += kPfThreads) {
       const int sq = c0 + tid;
-      int nt = 0;
-      if (sq < a.num_seqs) {
-        const int ql = a.cu[sq + 1] - a.cu[sq];
-        nt = ql > 1 ? (ql + kPfRows - 1) / kPfRows : 0;
-      }
+      const int nt = sq < a.num_seqs ? tiles_of(sq) : 0;
       s_scan[tid] = nt;
       __syncthreads();
       for (int off = 1; off < kPfThreads; off <<= 1) {
@@ -295,7 +302,14 @@ __global__ __launch_bounds__(kPfThreads, 2) void ragged_prefill_kernel(PrefillAr
     if (jlo >= tab_base && jhi <= tab_base + kPfTab) return;
     __syncthreads();  // nobody still reads the old entries
     tab_base = jlo;
-    for (int i = tid; i < kPfTab && jlo + i < nblk; i += kPfThreads) s_tab[i] = trow[jlo + i];
+    for (int i = tid; i < kPfTab && jlo + i < nblk; i += kPfThreads) {
+      int b = trow[jlo + i];
+      if (kDebugChecks && (b < 0 || b >= a.num_blocks)) {
+        debug_flag(DBG_BLOCK);
+        b = 0;
+      }
+      s_tab[i] = b;
+    }
     __syncthreads();
   };
 
@@ -447,6 +461,8 @@ static hipError_t launch_prefill_dt(const PrefillLaunch& L, hipStream_t stream) 
   a.bs = L.block_size;
   a.log2_bs = ilog2(L.block_size);
   a.scale_log2 = L.scale * 1.4426950408889634f;
+  a.num_tokens = L.num_tokens;
+  a.num_blocks = L.num_blocks;
   // Row tiles: sum over sequences of ceil(q_len / 128) <= T / 128 + (number of prefill
   // sequences); slots past the real count exit at once.
   const long long slots = (L.num_tokens + kPfRows - 1) / kPfRows + (L.num_seqs < L.num_tokens / 2 ? L.num_seqs : L.num_tokens / 2);

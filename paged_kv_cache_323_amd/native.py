@@ -91,6 +91,8 @@ _SIGS = {
     "pkv_status_str": (ctypes.c_char_p, [_I32]),
     "pkv_version": (ctypes.c_char_p, []),
     "pkv_last_launch_error": (ctypes.c_char_p, []),
+    "pkv_debug_checks_enabled": (_I32, []),
+    "pkv_debug_flags": (_I32, [ctypes.POINTER(ctypes.c_uint32), _I32]),
     "pkv_kv_cache_write": (_I32, [_P, _P, _P, _P, _P, _I32, _I64, _I64, _DESC, _P]),
     "pkv_copy_blocks": (_I32, [_P, _P, _P, _I32, _DESC, _P]),
     "pkv_swap_blocks": (_I32, [_P, _P, _P, _P, _P, _I32, _DESC, _P]),
@@ -138,6 +140,21 @@ EXPORTED = tuple(_SIGS)
 
 def version() -> str:
     return _lib.pkv_version().decode()
+
+
+# Debug builds (libpagedkv_debug.so, selected with PAGEDKV_LIB) bounds-check device-resident indices.
+DEBUG_SLOT, DEBUG_BLOCK, DEBUG_RAGGED, DEBUG_PAIR = 1, 2, 4, 8
+
+
+def debug_checks_enabled() -> bool:
+    return bool(_lib.pkv_debug_checks_enabled())
+
+
+def debug_flags(clear: bool = True) -> int:
+    """Flag bits raised by the debug checks on the current device (waits for the device)."""
+    v = ctypes.c_uint32(0)
+    _check(_lib.pkv_debug_flags(ctypes.byref(v), int(clear)), "debug_flags")
+    return int(v.value)
 
 
 def _check(status: int, where: str) -> None:

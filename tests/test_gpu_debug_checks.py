@@ -1,0 +1,106 @@
+"""The bounds-checked debug build (libpagedkv_debug.so): identical results on valid input, and a
+flag instead of an out-of-bounds access when a device-resident index is bad.
+
+Every bad index below is one the debug kernels check before using it (slots against the pool,
+copy pairs against the pool, block-table entries against the pool, ragged row offsets against
+the batch), so each call stays in bounds. The cases run in one child process that loads the
+debug library through PAGEDKV_LIB.
+"""
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+TESTS = os.path.join(ROOT, "tests")
+DEBUG_LIB = os.path.join(ROOT, "paged_kv_cache_323_amd", "libpagedkv_debug.so")
+
+CHILD = r'''
+import json, sys
+sys.path[:0] = [ROOT, TESTS]
+import numpy as np, torch
+import oracle
+from paged_kv_cache_323_amd import native as pk, runner as R
+from workloads import make_workload, make_ragged_workload
+
+def say(msg):
+    print("[case] " + msg, file=sys.stderr, flush=True)
+
+res = {"enabled": pk.debug_checks_enabled()}
+pk.debug_flags(clear=True)
+
+say("tiny decode parity")
+w = make_workload("tiny")
+st = R.play_script(w)
+out, inp = R.attention(w, st, "f32")
+_, ref = oracle.run_workload(w)
+res["parity_err"] = float(np.max(np.abs(out.cpu().numpy().astype(np.float64) - ref)))
+res["flags_clean"] = pk.debug_flags()
+kc, vc, desc = st.k_cache, st.v_cache, st.desc
+N, B = w.num_blocks, w.block_size
+
+say("slots past the pool")
+k0, v0 = kc.clone(), vc.clone()
+T = 3
+kk = torch.randn(T, w.num_kv_heads, w.head_dim, device="cuda").to(kc.dtype)
+slots = torch.tensor([N * B, N * B + 7, 2**31 - 1], dtype=torch.int32, device="cuda")
+pk.kv_cache_write(kk, kk.clone(), kc, vc, slots, desc)
+res["slot_flags"] = pk.debug_flags()
+res["slot_pool_unchanged"] = bool(torch.equal(kc.view(torch.int32), k0.view(torch.int32))
+                                  and torch.equal(vc.view(torch.int32), v0.view(torch.int32)))
+
+say("copy pairs past the pool")
+pairs = torch.tensor([[0, N], [N + 3, 1], [-1, 2]], dtype=torch.int32, device="cuda")
+pk.copy_blocks(kc, vc, pairs, desc)
+res["pair_flags"] = pk.debug_flags()
+res["pair_pool_unchanged"] = bool(torch.equal(kc.view(torch.int32), k0.view(torch.int32))
+                                  and torch.equal(vc.view(torch.int32), v0.view(torch.int32)))
+
+say("block-table entries past the pool")
+bt = inp["block_tables"].clone()
+bt[0, 0] = N + 5
+bt[1, 0] = -7
+cl = inp["context_lens"]
+max_ctx = int(inp["lens_host"].max())
+out2 = torch.empty_like(out)
+ws = torch.zeros(max(1, pk.decode_workspace_bytes(bt.shape[0], w.num_q_heads, max_ctx, desc)), dtype=torch.uint8,
+                 device="cuda")
+pk.paged_attention_decode(out2, inp["q"], kc, vc, bt, cl, w.scale, max_ctx, desc, ws)
+res["block_flags"] = pk.debug_flags()
+# sequences whose tables were left intact still match the oracle
+res["block_intact_err"] = float(np.max(np.abs(out2[2:].cpu().numpy().astype(np.float64) - ref[2:])))
+
+say("ragged row offsets out of order")
+wr = make_ragged_workload(7, [1, 20, 1, 40], [30, 20, 50, 40], 4, 2, 64, "bf16", 16, name="dbg-ragged")
+sr = R.play_script(wr)
+outr, inr = R.attention(wr, sr, "f32")
+pk.debug_flags(clear=True)
+cu_bad = torch.tensor([0, 1, 21, 15, 62], dtype=torch.int32, device="cuda")  # sequence 2 decreases
+outb = torch.empty_like(outr)
+pk.paged_attention_ragged(outb, inr["q"], cu_bad, inr["context_lens"], sr.k_cache, sr.v_cache,
+                          inr["block_tables"], wr.scale, 40, int(inr["lens_host"].max()), sr.desc, inr["workspace"])
+res["ragged_flags"] = pk.debug_flags()
+torch.cuda.synchronize()
+print(json.dumps(res), flush=True)
+'''
+
+
+@pytest.mark.gpu
+def test_debug_build_checks_device_indices():
+    if not os.path.exists(DEBUG_LIB):
+        pytest.fail(f"{DEBUG_LIB} is missing: build it with `python -m paged_kv_cache_323_amd.build`")
+    code = f"ROOT = {ROOT!r}\nTESTS = {TESTS!r}\n" + CHILD
+    env = dict(os.environ, PAGEDKV_LIB=DEBUG_LIB)
+    print("[case] debug build, child process", flush=True)
+    # the child's progress lines go straight to this process's stderr
+    p = subprocess.run([sys.executable, "-c", code], env=env, stdout=subprocess.PIPE, text=True, timeout=240)
+    assert p.returncode == 0, p.stdout[-2000:]
+    res = json.loads([ln for ln in p.stdout.splitlines() if ln.startswith("{")][-1])
+    assert res["enabled"] is True
+    assert res["parity_err"] <= 1e-5 and res["flags_clean"] == 0
+    assert res["slot_flags"] == 1 and res["slot_pool_unchanged"]
+    assert res["pair_flags"] == 8 and res["pair_pool_unchanged"]
+    assert res["block_flags"] == 2 and res["block_intact_err"] <= 1e-5
+    assert res["ragged_flags"] == 4
