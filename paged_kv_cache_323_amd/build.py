@@ -80,11 +80,24 @@ def build(verbose: bool = False, jobs: int = 8, defines=(), out: str = LIB, buil
     return out
 
 
+PROBE_SRC = os.path.join(CSRC, "probe", "stream_read.hip")
+PROBE_LIB = os.path.join(PKG, "libpkv_probe.so")
+
+
+def build_probe() -> str:
+    """The benchmark's streaming-read probe (its own small library, outside libpagedkv)."""
+    tmp = PROBE_LIB + ".tmp"
+    _run([HIPCC, *HIP_FLAGS, "-shared", PROBE_SRC, "-o", tmp])
+    os.replace(tmp, PROBE_LIB)
+    return PROBE_LIB
+
+
 def build_all(verbose: bool = False):
-    """The release library and the debug (bounds-checked) library."""
+    """The release library, the debug (bounds-checked) library and the benchmark's probe."""
     return [build(verbose=verbose),
             build(verbose=verbose, defines=("PKV_DEBUG_CHECKS",), out=DEBUG_LIB,
-                  build_dir=os.path.join(BUILD, "debug"))]
+                  build_dir=os.path.join(BUILD, "debug")),
+            build_probe()]
 
 
 if __name__ == "__main__":
