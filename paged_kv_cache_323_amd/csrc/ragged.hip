@@ -88,6 +88,14 @@ struct PrefillArgs {
 
 constexpr int kPfTab = 1024;  // block-table entries cached in LDS at a time
 
+#ifndef PF_LOOKAHEAD
+#define PF_LOOKAHEAD 2
+#endif
+#ifndef PF_SCHED
+#define PF_SCHED 1
+#endif
+constexpr int kPfLookahead = PF_LOOKAHEAD;  // MFMA operand reads issued this many steps ahead
+
 // Max / sum over the four 16-lane rows of a wave (lanes l, l^16, l^32, l^48), all in VALU: a
 // row swap with itself leaves the two partners' values in the two results.
 __device__ __forceinline__ float rows_max(float x) {
@@ -329,17 +337,35 @@ __global__ __launch_bounds__(kPfThreads, 2) void ragged_prefill_kernel(PrefillAr
     const uint16_t* cV = sVt + (kt & 1) * VBUF;
 
     // ---- Sᵀ = K·Qᵀ: 4 key tiles x 2 row tiles -------------------------------------------------
+    // Step st = (mt, ks) reads one K operand and feeds two MFMAs; operand reads run kPfLookahead
+    // steps ahead of their MFMAs so that LDS latency overlaps matrix work.
+    constexpr int NQK = 4 * KS;
+    auto kread = [&](int st) {
+      return __builtin_bit_cast(
+          V8, *reinterpret_cast<const u32x4*>(&cK[(16 * (st / KS) + lr) * KLD + 32 * (st % KS) + 8 * g]));
+    };
     f32x4 sacc[4][2];
+    {
+      V8 kop[kPfLookahead + 1];
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
+      for (int i = 0; i < kPfLookahead; ++i) kop[i] = kread(i);
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt) sacc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int st = 0; st < NQK; ++st) {
+        if (st + kPfLookahead < NQK) kop[(st + kPfLookahead) % (kPfLookahead + 1)] = kread(st + kPfLookahead);
+        const int mt = st / KS, ks = st % KS;
+        const V8 ka = kop[st % (kPfLookahead + 1)];
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const V8 ka = __builtin_bit_cast(V8, *reinterpret_cast<const u32x4*>(&cK[(16 * mt + lr) * KLD + 32 * ks + 8 * g]));
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt) sacc[mt][nt] = M::mma(ka, qb[nt][ks], sacc[mt][nt]);
+        for (int nt = 0; nt < 2; ++nt)
+          sacc[mt][nt] = M::mma(ka, qb[nt][ks], ks == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : sacc[mt][nt]);
       }
+#if PF_SCHED
+      __builtin_amdgcn_sched_group_barrier(0x100, kPfLookahead, 1);
+#pragma unroll
+      for (int st = 0; st < NQK; ++st) {
+        if (st + kPfLookahead < NQK) __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 1);
+      }
+#endif
     }
 
     // ---- causal mask and online softmax (per query row = per lane column) ----------------------
@@ -413,20 +439,37 @@ __global__ __launch_bounds__(kPfThreads, 2) void ragged_prefill_kernel(PrefillAr
     }
 
     // ---- Oᵀ += Vᵀ·Pᵀ with the same key order in both operands ---------------------------------
-#pragma unroll
-    for (int dt = 0; dt < DT16; ++dt) {
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const uint16_t* vrow = &cV[(16 * dt + lr) * VLD + 32 * j + 4 * g];
+    // Step st = (dt, j) reads one V operand and feeds four MFMAs; reads run ahead as above.
+    {
+      constexpr int NPV = DT16 * 2;
+      auto vread = [&](int st) {
+        const uint16_t* vrow = &cV[(16 * (st / 2) + lr) * VLD + 32 * (st % 2) + 4 * g];
         const u32x2 x0 = *reinterpret_cast<const u32x2*>(vrow);
         const u32x2 x1 = *reinterpret_cast<const u32x2*>(vrow + 16);
-        const V8 va = __builtin_bit_cast(V8, u32x4{x0[0], x0[1], x1[0], x1[1]});
+        return __builtin_bit_cast(V8, u32x4{x0[0], x0[1], x1[0], x1[1]});
+      };
+      V8 vop[kPfLookahead + 1];
+#pragma unroll
+      for (int i = 0; i < kPfLookahead; ++i) vop[i] = vread(i);
+#pragma unroll
+      for (int st = 0; st < NPV; ++st) {
+        if (st + kPfLookahead < NPV) vop[(st + kPfLookahead) % (kPfLookahead + 1)] = vread(st + kPfLookahead);
+        const int dt = st / 2, j = st % 2;
+        const V8 va = vop[st % (kPfLookahead + 1)];
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) {
           oacc[dt][nt] = M::mma(va, phi[nt][j], oacc[dt][nt]);
           oacc[dt][nt] = M::mma(va, plo[nt][j], oacc[dt][nt]);
         }
       }
+#if PF_SCHED
+      __builtin_amdgcn_sched_group_barrier(0x100, kPfLookahead, 2);
+#pragma unroll
+      for (int st = 0; st < NPV; ++st) {
+        if (st + kPfLookahead < NPV) __builtin_amdgcn_sched_group_barrier(0x100, 1, 2);
+        __builtin_amdgcn_sched_group_barrier(0x008, 4, 2);
+      }
+#endif
     }
     __syncthreads();  // buffer kt&1 is free for tile kt+2; buffer (kt+1)&1 is complete
   }
