@@ -55,7 +55,7 @@ def decode_algorithmic_bytes(ctx_lens, w, out_bytes_per_el):
 class DecodeLoop:
     """Steady-state decode steps over a resident workload (state advances every step)."""
 
-    def __init__(self, w, steps_total, device="cuda"):
+    def __init__(self, w, steps_total, device="cuda", work_list=True):
         import torch
         from paged_kv_cache_323_amd import native as pk
         from paged_kv_cache_323_amd import runner as R
@@ -69,10 +69,20 @@ class DecodeLoop:
         self.seqs = np.asarray(w.query_seqs, dtype=np.int64)
         self.max_ctx_final = max(w.context_lens) + steps_total
         self.max_blocks = -(-self.max_ctx_final // w.block_size)
-        # one pinned staging area per parity of the step: [slots S | ctx S | tables S*MB]
+        self.partition = pk.decode_partition_size(self.S, w.num_q_heads, self.max_ctx_final,
+                                                  pk.CacheDesc.make(w.num_blocks, w.block_size, w.num_kv_heads,
+                                                                    w.head_dim, w.dtype))
+        # The partition launch takes a work list of (sequence, partition) items built on the host
+        # from the lengths it uploads anyway (work_list=False: the dense grid sized for the
+        # longest context in every sequence).
+        self.work_list = work_list
+        self.max_items = self.S * -(-self.max_ctx_final // self.partition)
+        self.n_items = [0, 0]
+        # one pinned staging area per parity of the step: [slots S | ctx S | tables S*MB | items]
         # Two staging sets (host pinned + device) so that the upload of step k+1 runs on a copy
         # stream while step k's kernels still read their own device copy.
-        n = 2 * self.S + self.S * self.max_blocks
+        self.items_off = 2 * self.S + self.S * self.max_blocks
+        n = self.items_off + self.max_items
         self.host = [torch.empty(n, dtype=torch.int32).pin_memory() for _ in range(2)]
         self.host_np = [h.numpy() for h in self.host]
         self.dev = [torch.empty(n, dtype=torch.int32, device=device) for _ in range(2)]
@@ -90,7 +100,7 @@ class DecodeLoop:
         self.out = torch.empty_like(self.q)  # pool dtype output, as a serving engine consumes it
         nbytes = pk.decode_workspace_bytes(self.S, w.num_q_heads, self.max_ctx_final, self.st.desc)
         self.ws = torch.zeros(max(nbytes, 1), dtype=torch.uint8, device=device)
-        self.partition = pk.decode_partition_size(self.S, w.num_q_heads, self.max_ctx_final, self.st.desc)
+        assert self.partition == pk.decode_partition_size(self.S, w.num_q_heads, self.max_ctx_final, self.st.desc)
         self.step_idx = 0
         self.ctx_history = []
         self.pairs_total = 0
@@ -99,12 +109,26 @@ class DecodeLoop:
         d = self.dev[i]
         self.slots_d = d[: self.S]
         self.ctx_d = d[self.S: 2 * self.S]
-        self.tab_d = d[2 * self.S:].view(self.S, self.max_blocks)
+        self.tab_d = d[2 * self.S: self.items_off].view(self.S, self.max_blocks)
+        self.items_d = d[self.items_off: self.items_off + self.n_items[i]]
+
+    def attention(self):
+        """The step's two attention launches (partitions, then merge)."""
+        pk, w = self.pk, self.w
+        args = (self.out, self.q, self.st.k_cache, self.st.v_cache, self.tab_d, self.ctx_d, w.scale,
+                self.max_ctx_final, self.st.desc)
+        if self.work_list:
+            pk.paged_attention_decode_partitions_items(*args, self.partition, self.items_d, self.ws)
+        else:
+            pk.paged_attention_decode(*args, self.ws, self.partition, stage="partitions")
+        yield
+        pk.paged_attention_decode(*args, self.ws, self.partition, stage="merge")
+        yield
 
     def repeat_attention(self, n):
         for _ in range(n):
-            self.pk.paged_attention_decode(self.out, self.q, self.st.k_cache, self.st.v_cache, self.tab_d,
-                                           self.ctx_d, self.w.scale, self.max_ctx_final, self.st.desc, self.ws)
+            for _ in self.attention():
+                pass
 
     def step(self, ev=None):
         torch, pk, w = self.torch, self.pk, self.w
@@ -114,8 +138,11 @@ class DecodeLoop:
         hn = self.host_np[buf]
         slots, pairs = self.st.bm.append(self.seqs, np.ones(self.S, dtype=np.int32))
         hn[: self.S] = slots
-        tab = hn[2 * self.S:].reshape(self.S, self.max_blocks)
+        tab = hn[2 * self.S: self.items_off].reshape(self.S, self.max_blocks)
         self.st.bm.block_tables(self.seqs, self.max_blocks, out=tab, ctx_out=hn[self.S: 2 * self.S])
+        if self.work_list:
+            self.n_items[buf] = pk.decode_items_into(hn[self.S: 2 * self.S], self.partition,
+                                                     hn[self.items_off: self.items_off + self.max_items])
         main = torch.cuda.current_stream()
         with torch.cuda.stream(self.copy_stream):
             if self.consumed[buf] is not None:
@@ -131,14 +158,13 @@ class DecodeLoop:
             pk.copy_blocks(self.st.k_cache, self.st.v_cache,
                            torch.from_numpy(np.ascontiguousarray(pairs)).to("cuda", non_blocking=False), self.st.desc)
         pk.kv_cache_write(self.k_new, self.v_new, self.st.k_cache, self.st.v_cache, self.slots_d, self.st.desc)
-        args = (self.out, self.q, self.st.k_cache, self.st.v_cache, self.tab_d, self.ctx_d, w.scale,
-                self.max_ctx_final, self.st.desc, self.ws)
         if ev is not None:
             ev[0].record()
-        pk.paged_attention_decode(*args, stage="partitions")
+        launches = self.attention()
+        next(launches)                       # partition launch
         if ev is not None:
             ev[1].record()
-        pk.paged_attention_decode(*args, stage="merge")
+        next(launches, None)                 # merge launch
         if ev is not None:
             ev[2].record()
         done = torch.cuda.Event()
@@ -153,7 +179,7 @@ def run_headline(args):
     from workloads import make_workload
     w = make_workload("gqa", "full", block_size=args.block_size)
     ramp_repeats = 400
-    loop = DecodeLoop(w, args.warmup + args.steps)
+    loop = DecodeLoop(w, args.warmup + args.steps, work_list=not args.dense_grid)
     util = kv_utilisation(w, loop.st.bm, MAX_LEN["gqa"])
     for _ in range(args.warmup):
         loop.step()
@@ -610,6 +636,9 @@ def main():
     ap.add_argument("--block-size", type=int, default=16)
     ap.add_argument("--no-extra", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--dense-grid", action="store_true",
+                    help="time the dense partition grid (every sequence sized for the longest context) "
+                         "instead of the host-built work list")
     ap.add_argument("--profile-copy", action="store_true",
                     help="only run the copy kernel used to calibrate HBM byte counters")
     args = ap.parse_args()
@@ -647,7 +676,8 @@ def main():
                                f"shuffled pool",
                    "seqs": len(w.query_seqs), "block_size": w.block_size,
                    "sum_ctx_first_step": int(sum(w.context_lens)) + len(w.context_lens),
-                   "partition_tokens": h["partition"], "mean_ctx_timed": round(h["mean_ctx"], 1)},
+                   "partition_tokens": h["partition"], "mean_ctx_timed": round(h["mean_ctx"], 1),
+                   "partition_launch": "dense grid" if args.dense_grid else "host-built work list"},
         "seqs_per_s": round(h["seqs_per_s"], 1),
         "kv_memory_utilisation": h["util"],
         "pct_hbm_peak_step": round(100 * h["kv_gbs"] / HBM_PEAK_GBS, 2),

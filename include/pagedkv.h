@@ -210,6 +210,38 @@ int32_t pkv_paged_attention_decode_merge(void* out, int32_t out_dtype, const voi
                                          const pkv_cache_desc* cache, int32_t partition_size,
                                          void* workspace, size_t workspace_bytes, void* stream);
 
+/* Work-list form of pkv_paged_attention_decode_partitions, for callers that know the context
+ * lengths on the host (a serving loop's block manager does). items: device int32 [num_items],
+ * item = seq | (part << 16), part counted with the given partition_size (> 0, the size the
+ * launch uses; see pkv_decode_partition_size). The launch has exactly one workgroup per (kv
+ * head, item), so no workgroup is spent on partitions that do not exist, which the dense launch
+ * sizes for max_context_len in every sequence. Items are independent, so their order only
+ * steers scheduling: pkv_decode_items puts the last partitions first. An item whose partition
+ * does not exist for the device context length, or whose sequence index is >= num_seqs, does
+ * nothing. With every item of every sequence listed, the result equals
+ * pkv_paged_attention_decode_partitions, and pkv_paged_attention_decode_merge completes it.
+ * num_seqs <= 65536. Errors as pkv_paged_attention_decode_ex; PKV_EINVAL also for
+ * partition_size <= 0 or a null items with num_items > 0. */
+int32_t pkv_paged_attention_decode_partitions_items(void* out, int32_t out_dtype, const void* q,
+                                                    const void* k_cache, const void* v_cache,
+                                                    const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                                    const int32_t* context_lens, int32_t num_seqs,
+                                                    int32_t num_q_heads, float scale,
+                                                    int32_t max_context_len, const pkv_cache_desc* cache,
+                                                    int32_t partition_size, const int32_t* items,
+                                                    int32_t num_items, void* workspace,
+                                                    size_t workspace_bytes, void* stream);
+
+/* Host helper (no device work): the decode work list for host context lengths
+ * context_lens[0..num_seqs) and a partition size (a positive multiple of 64). Lists every
+ * (s, p) with p < ceil(context_lens[s] / partition_size) (p = 0 alone for a length of 0) as
+ * s | (p << 16), ordered by descending p, then ascending s. With items == NULL returns the item
+ * count; otherwise writes the items (capacity must hold them) and returns their count.
+ * PKV_EINVAL for bad arguments or too small a capacity, PKV_ESHAPE beyond 65536 sequences or
+ * partitions. */
+int32_t pkv_decode_items(const int32_t* context_lens, int32_t num_seqs, int32_t partition_size,
+                         int32_t* items, int32_t capacity);
+
 size_t pkv_decode_workspace_bytes_ex(int32_t num_seqs, int32_t num_q_heads,
                                      int32_t max_context_len, const pkv_cache_desc* cache,
                                      int32_t partition_size);

@@ -187,7 +187,8 @@ static int32_t decode_common_cu(void* out, int32_t out_dtype, const void* q, con
                                 const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads, float scale,
                                 int32_t max_context_len, const pkv_cache_desc* c, int32_t partition_size,
                                 void* workspace, size_t workspace_bytes, void* stream, const int32_t* cu,
-                                int stage = 0, int32_t num_rows = -1) {
+                                int stage = 0, int32_t num_rows = -1, const int32_t* items = nullptr,
+                                int32_t num_items = 0) {
   int32_t st = check_cache(c);
   if (st != PKV_OK) return st;
   if ((st = check_heads(num_q_heads, c)) != PKV_OK) return st;
@@ -231,6 +232,8 @@ static int32_t decode_common_cu(void* out, int32_t out_dtype, const void* q, con
   L.cu = cu;
   L.num_blocks = c->num_blocks;
   L.num_rows = num_rows >= 0 ? num_rows : num_seqs;
+  L.items = items;
+  L.num_items = num_items;
   return launched(pkv::launch_decode(L, (hipStream_t)stream));
 }
 
@@ -266,6 +269,54 @@ int32_t pkv_paged_attention_decode_partitions(void* out, int32_t out_dtype, cons
   return decode_common(out, out_dtype, q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens,
                        num_seqs, num_q_heads, scale, max_context_len, c, partition_size, workspace,
                        workspace_bytes, stream, 1);
+}
+
+int32_t pkv_paged_attention_decode_partitions_items(void* out, int32_t out_dtype, const void* q,
+                                                    const void* k_cache, const void* v_cache,
+                                                    const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                                    const int32_t* context_lens, int32_t num_seqs,
+                                                    int32_t num_q_heads, float scale, int32_t max_context_len,
+                                                    const pkv_cache_desc* c, int32_t partition_size,
+                                                    const int32_t* items, int32_t num_items, void* workspace,
+                                                    size_t workspace_bytes, void* stream) {
+  if (partition_size <= 0 || num_items < 0 || (num_items > 0 && !items)) return PKV_EINVAL;
+  if (c && (int64_t)num_items * (c->num_kv_heads > 0 ? c->num_kv_heads : 1) > 0x7fffffffLL) return PKV_ESHAPE;
+  if (num_seqs > 65536) return PKV_ESHAPE;  // items carry 16-bit sequence indices
+  if (num_items == 0 && num_seqs > 0) {
+    // Nothing to launch; still report argument errors like the other entry points.
+    return decode_common_cu(out, out_dtype, q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens,
+                            0, num_q_heads, scale, max_context_len, c, partition_size, workspace, workspace_bytes,
+                            stream, nullptr, 1);
+  }
+  return decode_common_cu(out, out_dtype, q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens,
+                          num_seqs, num_q_heads, scale, max_context_len, c, partition_size, workspace,
+                          workspace_bytes, stream, nullptr, 1, -1, items, num_items);
+}
+
+int32_t pkv_decode_items(const int32_t* context_lens, int32_t num_seqs, int32_t partition_size, int32_t* items,
+                         int32_t capacity) {
+  if (!context_lens || num_seqs < 0 || partition_size <= 0 || partition_size % 64 || capacity < 0) return PKV_EINVAL;
+  if (num_seqs > 65536) return PKV_ESHAPE;
+  int64_t total = 0;
+  int32_t max_parts = 0;
+  for (int32_t s = 0; s < num_seqs; ++s) {
+    const int32_t ctx = context_lens[s];
+    const int32_t n = ctx > 0 ? (int32_t)(((int64_t)ctx + partition_size - 1) / partition_size) : 1;
+    total += n;
+    if (n > max_parts) max_parts = n;
+  }
+  if (max_parts > 65536 || total > 0x7fffffff) return PKV_ESHAPE;
+  if (!items) return (int32_t)total;  // size query
+  if (total > capacity) return PKV_EINVAL;
+  int32_t k = 0;
+  for (int32_t p = max_parts - 1; p >= 0; --p) {  // last partitions first, as in the dense launch
+    for (int32_t s = 0; s < num_seqs; ++s) {
+      const int32_t ctx = context_lens[s];
+      const int32_t n = ctx > 0 ? (int32_t)(((int64_t)ctx + partition_size - 1) / partition_size) : 1;
+      if (p < n) items[k++] = (int32_t)((uint32_t)s | ((uint32_t)p << 16));
+    }
+  }
+  return k;
 }
 
 int32_t pkv_paged_attention_decode_merge(void* out, int32_t out_dtype, const void* q, const void* k_cache,

@@ -53,6 +53,8 @@ struct DecodeArgs {
   int max_parts;
   int num_blocks;  // pool blocks (debug builds check table entries)
   int num_rows;    // rows of q / out (debug builds check ragged row offsets)
+  const uint32_t* items;  // work list: item i = seq | part << 16 (null: dense grid)
+  int num_seqs;
 };
 
 // Raw words of one lane's slice of a V row (PV mapping): 8, 16 or 32 bytes.
@@ -120,11 +122,26 @@ __global__ __launch_bounds__(kDecThreads, PKV_DECODE_MIN_WG) void paged_decode_k
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int kvh = blockIdx.x;
-  const int s = blockIdx.y;
-  // Last partitions are dispatched first: they exist only for long contexts and are always
-  // full, while partition 0 of every sequence (often partial) fills the tail of the launch.
-  const int part = (int)gridDim.z - 1 - (int)blockIdx.z;
+  int kvh, s, part;
+  if (a.items) {
+    // Work list: workgroup x serves kv head x mod Hkv of item x / Hkv, so the kv heads of one
+    // item (which read neighbouring parts of the same blocks) are dispatched together.
+    const uint32_t item = blockIdx.x / (uint32_t)a.hkv;
+    kvh = (int)(blockIdx.x - item * (uint32_t)a.hkv);
+    const uint32_t it = a.items[item];
+    s = (int)(it & 0xffffu);
+    part = (int)(it >> 16);
+    if (s >= a.num_seqs) {  // an item naming no sequence: nothing to do
+      if (kDebugChecks && tid == 0) debug_flag(DBG_RAGGED);
+      return;  // uniform over the workgroup
+    }
+  } else {
+    kvh = blockIdx.x;
+    s = blockIdx.y;
+    // Last partitions are dispatched first: they exist only for long contexts and are always
+    // full, while partition 0 of every sequence (often partial) fills the tail of the launch.
+    part = (int)gridDim.z - 1 - (int)blockIdx.z;
+  }
 
   // In a ragged batch only single-row (decode) sequences are handled here.
   int row = s;
@@ -399,6 +416,8 @@ static DecodeArgs make_args(const DecodeLaunch& L) {
   a.max_parts = L.max_parts;
   a.num_blocks = L.num_blocks;
   a.num_rows = L.num_rows;
+  a.items = reinterpret_cast<const uint32_t*>(L.items);
+  a.num_seqs = L.num_seqs;
   return a;
 }
 
@@ -408,9 +427,12 @@ template <int DT, int D, int G>
 static hipError_t launch_decode_t(const DecodeLaunch& L, hipStream_t stream) {
   const DecodeArgs a = make_args(L);
   if (L.stage != 2) {
-    const hipError_t e = launch_kernel(paged_decode_kernel<DT, D, G, kPrefetch>,
-                                       dim3(L.num_kv_heads, L.num_seqs, L.max_parts), dim3(kDecThreads), stream, a);
-    if (e != hipSuccess) return e;
+    const dim3 grid = L.items ? dim3((unsigned)L.num_items * (unsigned)L.num_kv_heads)
+                              : dim3(L.num_kv_heads, L.num_seqs, L.max_parts);
+    if (!L.items || L.num_items > 0) {
+      const hipError_t e = launch_kernel(paged_decode_kernel<DT, D, G, kPrefetch>, grid, dim3(kDecThreads), stream, a);
+      if (e != hipSuccess) return e;
+    }
   }
   if (L.stage != 1 && L.max_parts > 1) {
     const int outs = L.num_q_heads * D;

@@ -79,6 +79,8 @@ struct DecodeLaunch {
   int stage;       // 0: partitions then merge; 1: partitions only; 2: merge only
   int num_blocks;  // pool blocks (debug builds check table entries against it)
   int num_rows;    // rows of q / out (debug builds check ragged row offsets against it)
+  const int32_t* items = nullptr;  // optional work list of (seq | part << 16) for the partition launch
+  int num_items = 0;
 };
 
 hipError_t launch_decode(const DecodeLaunch& a, hipStream_t stream);

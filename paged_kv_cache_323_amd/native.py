@@ -107,6 +107,10 @@ _SIGS = {
                                                      ctypes.c_float, _I32, _DESC, _I32, _P, _SZ, _P]),
     "pkv_paged_attention_decode_merge": (_I32, [_P, _I32, _P, _P, _P, _P, _I32, _P, _I32, _I32, ctypes.c_float,
                                                 _I32, _DESC, _I32, _P, _SZ, _P]),
+    "pkv_paged_attention_decode_partitions_items": (_I32, [_P, _I32, _P, _P, _P, _P, _I32, _P, _I32, _I32,
+                                                           ctypes.c_float, _I32, _DESC, _I32, _P, _I32, _P, _SZ,
+                                                           _P]),
+    "pkv_decode_items": (_I32, [_I32P, _I32, _I32, _I32P, _I32]),
     "pkv_ragged_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32, _I32, _DESC]),
     "pkv_paged_attention_ragged": (_I32, [_P, _I32, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32,
                                           ctypes.c_float, _I32, _I32, _DESC, _P, _SZ, _P]),
@@ -297,6 +301,50 @@ def paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_lens,
             _dev(context_lens, "context_lens", torch.int32), S, hq, float(scale), int(max_context_len),
             ctypes.byref(desc), int(partition_size), ws, wsb, _stream(stream))
     _check(st, f"paged_attention_decode[{stage}]")
+
+
+def decode_items(context_lens_host, partition_size: int) -> np.ndarray:
+    """Host work list for the items form of the partition launch (see include/pagedkv.h)."""
+    ctx = np.ascontiguousarray(context_lens_host, dtype=np.int32)
+    ptr = ctx.ctypes.data_as(_I32P)
+    n = int(_lib.pkv_decode_items(ptr, len(ctx), int(partition_size), None, 0))
+    _check(min(n, 0), "decode_items")
+    items = np.empty(max(n, 1), dtype=np.int32)
+    k = int(_lib.pkv_decode_items(ptr, len(ctx), int(partition_size), items.ctypes.data_as(_I32P), len(items)))
+    _check(min(k, 0), "decode_items")
+    return items[:k]
+
+
+def decode_items_into(context_lens_host: np.ndarray, partition_size: int, out: np.ndarray) -> int:
+    """decode_items writing into a caller's int32 array (e.g. a pinned staging buffer); returns the count."""
+    if context_lens_host.dtype != np.int32 or out.dtype != np.int32 or not out.flags.c_contiguous \
+            or not context_lens_host.flags.c_contiguous:
+        raise ValueError("int32 contiguous arrays expected")
+    k = int(_lib.pkv_decode_items(context_lens_host.ctypes.data_as(_I32P), len(context_lens_host),
+                                  int(partition_size), out.ctypes.data_as(_I32P), len(out)))
+    _check(min(k, 0), "decode_items")
+    return k
+
+
+def paged_attention_decode_partitions_items(out, q, k_cache, v_cache, block_tables, context_lens, scale: float,
+                                            max_context_len: int, desc: CacheDesc, partition_size: int, items,
+                                            workspace=None, stream=None) -> None:
+    """Partition launch over a work list ``items`` (device int32, from decode_items); complete it
+    with paged_attention_decode(..., stage="merge")."""
+    torch = _torch()
+    S, hq, d = q.shape
+    if out.shape != q.shape or block_tables.dim() != 2 or block_tables.shape[0] != S:
+        raise ValueError("shape mismatch")
+    ws = _dev(workspace, "workspace") if workspace is not None else None
+    wsb = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    n = int(items.shape[0])
+    st = _lib.pkv_paged_attention_decode_partitions_items(
+        _dev(out, "out"), _tdtype_code(out), _dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
+        _dev(block_tables, "block_tables", torch.int32), int(block_tables.shape[1]),
+        _dev(context_lens, "context_lens", torch.int32), S, hq, float(scale), int(max_context_len),
+        ctypes.byref(desc), int(partition_size), _dev(items, "items", torch.int32) if n else None, n, ws, wsb,
+        _stream(stream))
+    _check(st, "paged_attention_decode_partitions_items")
 
 
 def ragged_workspace_bytes(num_seqs: int, num_tokens: int, num_q_heads: int, max_q_len: int,

@@ -147,3 +147,39 @@ def test_debug_library_exports_every_symbol_and_reports_its_mode():
 
 def test_debug_flags_rejects_null():
     assert L.pkv_debug_flags(None, 0) == -1
+
+
+def _items_reference(ctx, P):
+    n = [max(1, -(-int(c) // P)) if c > 0 else 1 for c in ctx]
+    return [s | (p << 16) for p in range(max(n, default=0) - 1, -1, -1) for s in range(len(ctx)) if p < n[s]]
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_decode_items_matches_reference(seed):
+    import numpy as np
+    rng = np.random.default_rng(seed)
+    ctx = rng.integers(0, 5000, size=int(rng.integers(0, 300))).astype(np.int32)
+    ctx[rng.random(len(ctx)) < 0.1] = 0
+    for P in (64, 256, 1024):
+        got = pk.decode_items(ctx, P)
+        assert got.tolist() == _items_reference(ctx.tolist(), P)
+
+
+def test_decode_items_rejects_bad_arguments():
+    import numpy as np
+    ctx = np.array([100, 2000], dtype=np.int32)
+    p = ctx.ctypes.data_as(pk._I32P)
+    buf = np.zeros(1, dtype=np.int32)
+    assert L.pkv_decode_items(p, 2, 100, None, 0) == -1           # not a multiple of 64
+    assert L.pkv_decode_items(p, 2, 0, None, 0) == -1
+    assert L.pkv_decode_items(None, 2, 1024, None, 0) == -1
+    assert L.pkv_decode_items(p, 2, 1024, None, 0) == 3          # size query
+    assert L.pkv_decode_items(p, 2, 1024, buf.ctypes.data_as(pk._I32P), 1) == -1  # capacity too small
+
+
+def test_decode_items_launch_validation():
+    c = desc()
+    args = [ctypes.c_void_p(1), c.dtype, ctypes.c_void_p(1), ctypes.c_void_p(1), ctypes.c_void_p(1),
+            ctypes.c_void_p(1), 8, ctypes.c_void_p(1), 2, 4, 0.125, 100, ctypes.byref(c)]
+    assert L.pkv_paged_attention_decode_partitions_items(*args, 0, ctypes.c_void_p(1), 3, None, 0, None) == -1
+    assert L.pkv_paged_attention_decode_partitions_items(*args, 128, None, 3, None, 0, None) == -1

@@ -121,6 +121,38 @@ def test_physical_permutation_bit_identical():
     assert np.array_equal(outs[0], outs[1])
 
 
+@pytest.mark.parametrize("name,size,partition", [("gqa", "small", 128), ("gqa", "small", 1024),
+                                                 ("llama7b", "small", 256), ("tiny", "full", 64)])
+def test_work_list_launch_bit_identical(name, size, partition):
+    """The work-list partition launch (items from host copies of the lengths, in the helper's
+    order and shuffled) followed by the merge equals the dense launch bit for bit, and the
+    oracle within tolerance."""
+    import torch
+    from paged_kv_cache_323_amd import native as pk
+    w = make_workload(name, size)
+    _announce(f"decode work list {w.name} partition={partition}")
+    R = _runner()
+    _, ref = oracle.run_workload(w)
+    st = R.play_script(w)
+    dense, inp = R.attention(w, st, "f32", partition_size=partition)
+    bt, cl, q, ws = inp["block_tables"], inp["context_lens"], inp["q"], inp["workspace"]
+    mx = int(inp["lens_host"].max())
+    items_h = pk.decode_items(inp["lens_host"], partition)
+    nparts = np.maximum(1, -(-inp["lens_host"].astype(np.int64) // partition))
+    assert len(items_h) == int(nparts.sum())
+    for order in ("helper", "shuffled"):
+        ih = items_h if order == "helper" else np.random.default_rng(5).permutation(items_h)
+        items = torch.from_numpy(np.ascontiguousarray(ih)).cuda()
+        out = torch.full_like(dense, float("nan"))
+        pk.paged_attention_decode_partitions_items(out, q, st.k_cache, st.v_cache, bt, cl, w.scale, mx, st.desc,
+                                                   partition, items, ws)
+        pk.paged_attention_decode(out, q, st.k_cache, st.v_cache, bt, cl, w.scale, mx, st.desc, ws, partition,
+                                  stage="merge")
+        torch.cuda.synchronize()
+        assert torch.equal(out, dense), f"{order}: work-list output differs from the dense launch"
+    _check_attention(w, out, ref)
+
+
 CASES = []
 for dt in ("f32", "f16", "bf16"):
     for B in (8, 16, 32):
