@@ -644,7 +644,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the path has no "
-              f"multi-GPU sharding in this build)", file=sys.stderr)
+              f"multi-GPU sharding: one GPU runs one shard of the path)", file=sys.stderr)
         sys.exit(2)
     import torch
     if not torch.cuda.is_available():
