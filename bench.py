@@ -55,7 +55,7 @@ def decode_algorithmic_bytes(ctx_lens, w, out_bytes_per_el):
 class DecodeLoop:
     """Steady-state decode steps over a resident workload (state advances every step)."""
 
-    def __init__(self, w, steps_total, device="cuda", work_list=True):
+    def __init__(self, w, steps_total, device="cuda", work_list=True, partition=0):
         import torch
         from paged_kv_cache_323_amd import native as pk
         from paged_kv_cache_323_amd import runner as R
@@ -69,9 +69,9 @@ class DecodeLoop:
         self.seqs = np.asarray(w.query_seqs, dtype=np.int64)
         self.max_ctx_final = max(w.context_lens) + steps_total
         self.max_blocks = -(-self.max_ctx_final // w.block_size)
-        self.partition = pk.decode_partition_size(self.S, w.num_q_heads, self.max_ctx_final,
-                                                  pk.CacheDesc.make(w.num_blocks, w.block_size, w.num_kv_heads,
-                                                                    w.head_dim, w.dtype))
+        self.partition = partition or pk.decode_partition_size(
+            self.S, w.num_q_heads, self.max_ctx_final,
+            pk.CacheDesc.make(w.num_blocks, w.block_size, w.num_kv_heads, w.head_dim, w.dtype))
         # The partition launch takes a work list of (sequence, partition) items built on the host
         # from the lengths it uploads anyway (work_list=False: the dense grid sized for the
         # longest context in every sequence).
@@ -98,9 +98,8 @@ class DecodeLoop:
         self.k_new = R.to_device(kv[0], w.dtype, device)
         self.v_new = R.to_device(kv[1], w.dtype, device)
         self.out = torch.empty_like(self.q)  # pool dtype output, as a serving engine consumes it
-        nbytes = pk.decode_workspace_bytes(self.S, w.num_q_heads, self.max_ctx_final, self.st.desc)
+        nbytes = pk.decode_workspace_bytes(self.S, w.num_q_heads, self.max_ctx_final, self.st.desc, self.partition)
         self.ws = torch.zeros(max(nbytes, 1), dtype=torch.uint8, device=device)
-        assert self.partition == pk.decode_partition_size(self.S, w.num_q_heads, self.max_ctx_final, self.st.desc)
         self.step_idx = 0
         self.ctx_history = []
         self.pairs_total = 0
@@ -179,7 +178,7 @@ def run_headline(args):
     from workloads import make_workload
     w = make_workload("gqa", "full", block_size=args.block_size)
     ramp_repeats = 400
-    loop = DecodeLoop(w, args.warmup + 2 * args.steps, work_list=not args.dense_grid)
+    loop = DecodeLoop(w, args.warmup + 2 * args.steps, work_list=not args.dense_grid, partition=args.partition)
     util = kv_utilisation(w, loop.st.bm, MAX_LEN["gqa"])
     for _ in range(args.warmup):
         loop.step()
@@ -640,6 +639,8 @@ def main():
     ap.add_argument("--block-size", type=int, default=16)
     ap.add_argument("--no-extra", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--partition", type=int, default=0,
+                    help="decode partition size in tokens (default: the library's choice)")
     ap.add_argument("--dense-grid", action="store_true",
                     help="time the dense partition grid (every sequence sized for the longest context) "
                          "instead of the host-built work list")
