@@ -58,6 +58,9 @@ RAGGED_CASES = [
     ("bf16", 32, 64, 4, 2, [17, 1, 1, 300], [17, 64, 1025, 300]),                       # head_dim 64
     ("f16", 32, 64, 2, 2, [2, 0, 40], [2, 5, 100]),                                     # a sequence with no rows
     ("bf16", 16, 128, 16, 2, [1, 1, 1], [5, 1100, 2500]),                               # decode-only ragged
+    # a prefill chunk behind 19800 cached tokens at B=8: 2500 blocks, more than the prefill
+    # kernel's 1024-entry LDS table window, so the window moves during the key loop
+    ("bf16", 8, 64, 4, 2, [200, 1], [20000, 9000]),
 ]
 
 
