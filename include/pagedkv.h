@@ -17,8 +17,11 @@
  *   - Pointers documented as "device" are HIP device memory owned by the caller; the library
  *     never allocates, frees or retains device memory. "host" pointers are ordinary CPU memory.
  *   - Device work is enqueued asynchronously on `stream` (a hipStream_t; NULL = the default
- *     stream). The return value only reports host-side validation and the launch itself; on
- *     any error status nothing has been enqueued.
+ *     stream). The return value only reports host-side validation and the launches themselves.
+ *     After a validation error nothing has been enqueued. PKV_ELAUNCH means one launch failed;
+ *     in an entry point that issues several (decode partitions then merge, ragged decode rows
+ *     then prefill rows, copies in chunks of 65535 pairs) the launches before it stay enqueued
+ *     and their results are incomplete.
  *   - Device-resident indices (block ids, slots, lengths) are trusted: the caller guarantees
  *     they are in range. Host-visible scalars and shapes are validated.
  *   - Ordering between calls is the caller's job: on one stream, copy_blocks for an append's
@@ -220,8 +223,8 @@ int32_t pkv_paged_attention_decode_merge(void* out, int32_t out_dtype, const voi
  * does not exist for the device context length, or whose sequence index is >= num_seqs, does
  * nothing. With every item of every sequence listed, the result equals
  * pkv_paged_attention_decode_partitions, and pkv_paged_attention_decode_merge completes it.
- * num_seqs <= 65536. Errors as pkv_paged_attention_decode_ex; PKV_EINVAL also for
- * partition_size <= 0 or a null items with num_items > 0. */
+ * num_seqs <= 65535 (as for every decode launch). Errors as pkv_paged_attention_decode_ex;
+ * PKV_EINVAL also for partition_size <= 0 or a null items with num_items > 0. */
 int32_t pkv_paged_attention_decode_partitions_items(void* out, int32_t out_dtype, const void* q,
                                                     const void* k_cache, const void* v_cache,
                                                     const int32_t* block_tables, int32_t max_blocks_per_seq,
@@ -237,8 +240,8 @@ int32_t pkv_paged_attention_decode_partitions_items(void* out, int32_t out_dtype
  * (s, p) with p < ceil(context_lens[s] / partition_size) (p = 0 alone for a length of 0) as
  * s | (p << 16), ordered by descending p, then ascending s. With items == NULL returns the item
  * count; otherwise writes the items (capacity must hold them) and returns their count.
- * PKV_EINVAL for bad arguments or too small a capacity, PKV_ESHAPE beyond 65536 sequences or
- * partitions. */
+ * PKV_EINVAL for bad arguments or too small a capacity, PKV_ESHAPE beyond 65535 sequences or
+ * 65536 partitions of one sequence. */
 int32_t pkv_decode_items(const int32_t* context_lens, int32_t num_seqs, int32_t partition_size,
                          int32_t* items, int32_t capacity);
 

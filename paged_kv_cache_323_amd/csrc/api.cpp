@@ -281,7 +281,7 @@ int32_t pkv_paged_attention_decode_partitions_items(void* out, int32_t out_dtype
                                                     size_t workspace_bytes, void* stream) {
   if (partition_size <= 0 || num_items < 0 || (num_items > 0 && !items)) return PKV_EINVAL;
   if (c && (int64_t)num_items * (c->num_kv_heads > 0 ? c->num_kv_heads : 1) > 0x7fffffffLL) return PKV_ESHAPE;
-  if (num_seqs > 65536) return PKV_ESHAPE;  // items carry 16-bit sequence indices
+  if (num_seqs > 65535) return PKV_ESHAPE;  // items carry 16-bit sequence indices; merge grid limit
   if (num_items == 0 && num_seqs > 0) {
     // Nothing to launch; still report argument errors like the other entry points.
     return decode_common_cu(out, out_dtype, q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens,
@@ -296,7 +296,7 @@ int32_t pkv_paged_attention_decode_partitions_items(void* out, int32_t out_dtype
 int32_t pkv_decode_items(const int32_t* context_lens, int32_t num_seqs, int32_t partition_size, int32_t* items,
                          int32_t capacity) {
   if (!context_lens || num_seqs < 0 || partition_size <= 0 || partition_size % 64 || capacity < 0) return PKV_EINVAL;
-  if (num_seqs > 65536) return PKV_ESHAPE;
+  if (num_seqs > 65535) return PKV_ESHAPE;
   int64_t total = 0;
   int32_t max_parts = 0;
   for (int32_t s = 0; s < num_seqs; ++s) {
