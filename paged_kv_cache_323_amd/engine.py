@@ -103,6 +103,13 @@ class Engine:
         self._next_seq = 0
         self.ws = torch.zeros(1, dtype=torch.uint8, device=device)
         self.scale = float(np.float32(1.0 / np.sqrt(head_dim)))
+        # Per-step index data (slots, cu_seqlens, lengths, tables) goes up in one asynchronous copy
+        # from one of two pinned staging buffers, so the host prepares step k+1 while the GPU
+        # runs step k; a buffer is rewritten only after the copy that last read it has run.
+        self._stage_host = [None, None]
+        self._stage_done = [None, None]
+        self._stage_dev = None
+        self.max_len = 0                  # longest context any request can reach (sizes tables)
 
     # ---- requests -------------------------------------------------------------------------------
     def add_request(self, prompt_len: int, max_new_tokens: int) -> int:
@@ -110,6 +117,7 @@ class Engine:
         self._next_seq += 1
         self.requests[seq] = Request(seq, int(prompt_len), int(max_new_tokens))
         self.waiting.append(seq)
+        self.max_len = max(self.max_len, int(prompt_len) + int(max_new_tokens))
         return seq
 
     def has_work(self) -> bool:
@@ -251,6 +259,33 @@ class Engine:
         w.ops = list(self.ops[: rec.ops_end])
         return w
 
+    # ---- per-step uploads -----------------------------------------------------------------------
+    def _staging(self, n: int) -> np.ndarray:
+        """An int32 view of n elements of the pinned staging buffer for this step."""
+        i = self.step_idx & 1
+        if self._stage_done[i] is not None:
+            self._stage_done[i].synchronize()   # the upload that last read this buffer has run
+        buf = self._stage_host[i]
+        if buf is None or buf.numel() < n:
+            buf = torch.empty(max(n, 2 * (buf.numel() if buf is not None else 0), 1 << 16),
+                              dtype=torch.int32).pin_memory()
+            self._stage_host[i] = buf
+        return buf.numpy()[:n]
+
+    def _upload(self, host: np.ndarray) -> torch.Tensor:
+        """Copy this step's staging contents to the device (asynchronously, on the current stream)."""
+        i = self.step_idx & 1
+        n = len(host)
+        if self._stage_dev is None or self._stage_dev.numel() < n:
+            self._stage_dev = torch.empty(max(n, 1 << 16, 2 * (self._stage_dev.numel() if self._stage_dev is not None
+                                                                else 0)), dtype=torch.int32, device=self.device)
+        dev = self._stage_dev[:n]
+        dev.copy_(self._stage_host[i][:n], non_blocking=True)
+        ev = torch.cuda.Event()
+        ev.record()
+        self._stage_done[i] = ev
+        return dev
+
     # ---- one model step -------------------------------------------------------------------------
     def step(self) -> Optional[StepRecord]:
         from workloads import AppendOp, FreeOp
@@ -264,19 +299,28 @@ class Engine:
             pk.copy_blocks(self.k_cache, self.v_cache, torch.from_numpy(np.ascontiguousarray(pairs)).to(self.device),
                            self.desc)
         k, v = self._kv(seqs, ns, tag)
-        sd = torch.from_numpy(np.ascontiguousarray(slots)).to(self.device)
+        S, T = len(seqs), len(slots)
+        max_blocks = -(-self.max_len // self.B)
+        host = self._staging(T + 2 * S + 1 + S * max_blocks)
+        host[:T] = slots
+        cu = host[T: T + S + 1]
+        cu[0] = 0
+        np.cumsum(ns, out=cu[1:])
+        lens = host[T + S + 1: T + 2 * S + 1]
+        tables = host[T + 2 * S + 1: T + 2 * S + 1 + S * max_blocks].reshape(S, max_blocks)
+        self.bm.block_tables(seqs, max_blocks, out=tables, ctx_out=lens)
+        dev = self._upload(host)
+        sd, cu_d = dev[:T], dev[T: T + S + 1]
+        lens_d = dev[T + S + 1: T + 2 * S + 1]
+        tab_d = dev[T + 2 * S + 1: T + 2 * S + 1 + S * max_blocks].view(S, max_blocks)
         pk.kv_cache_write(k, v, self.k_cache, self.v_cache, sd, self.desc)
-        max_blocks = max(len(self.bm.block_table(s)) for s in seqs)
-        tables, lens = self.bm.block_tables(seqs, max_blocks)
-        cu = np.concatenate([[0], np.cumsum(ns)]).astype(np.int32)
         q = self._q(seqs, ns)
         out = torch.empty(q.shape, dtype=torch.float32 if self.keep_outputs else q.dtype, device=self.device)
         max_ctx, max_q = int(lens.max()), int(max(ns))
-        nbytes = pk.ragged_workspace_bytes(len(seqs), int(cu[-1]), self.hq, max_q, max_ctx, self.desc)
+        nbytes = pk.ragged_workspace_bytes(S, int(cu[-1]), self.hq, max_q, max_ctx, self.desc)
         if self.ws.numel() < nbytes:
             self.ws = torch.zeros(nbytes, dtype=torch.uint8, device=self.device)
-        pk.paged_attention_ragged(out, q, torch.from_numpy(cu).to(self.device), torch.from_numpy(lens).to(self.device),
-                                  self.k_cache, self.v_cache, torch.from_numpy(tables).to(self.device), self.scale,
+        pk.paged_attention_ragged(out, q, cu_d, lens_d, self.k_cache, self.v_cache, tab_d, self.scale,
                                   max_q, max_ctx, self.desc, self.ws)
         rec = StepRecord(self.step_idx, list(seqs), list(ns), [int(x) for x in lens], len(self.ops),
                          out if self.keep_outputs else None)
