@@ -25,6 +25,7 @@
 
 #include <deque>
 #include <new>
+#include <algorithm>
 #include <unordered_map>
 #include <vector>
 
@@ -36,6 +37,11 @@ struct Seq {
   std::vector<int32_t> table;  // GPU block ids, or host block ids while swapped out
   int32_t len = 0;
   bool on_host = false;
+  // Scratch of the batch simulation in preflight(), valid while sim_epoch equals the manager's
+  // current epoch (so no per-call maps are needed).
+  mutable uint64_t sim_epoch = 0;
+  mutable int32_t sim_len = 0;
+  mutable bool sim_private = false;
 };
 
 }  // namespace
@@ -49,6 +55,11 @@ struct pkv_bm {
   int32_t num_host_blocks = 0;
   std::deque<int32_t> host_free;
   std::vector<int32_t> host_rc;
+  // preflight() scratch: a batch number, and per block the batch that last changed its simulated
+  // reference count and that change.
+  mutable uint64_t epoch = 0;
+  mutable std::vector<uint64_t> rc_epoch;
+  mutable std::vector<int32_t> rc_delta;
 
   // Moves the blocks of a set of sequences to the other pool (see the file comment). On
   // success writes (src, dst) pairs in first-reference order.
@@ -114,9 +125,11 @@ struct pkv_bm {
   // New blocks an append would take, simulating the batch in order (a sequence may appear
   // more than once). cow_out counts copy-on-write pairs. Returns <0 on an unknown sequence.
   int64_t preflight(const int64_t* ids, const int32_t* n, int32_t count, int64_t* cow_out) const {
-    std::unordered_map<int64_t, int32_t> sim_len;     // length after earlier entries
-    std::unordered_map<int64_t, bool> sim_private;    // last block already private this batch
-    std::unordered_map<int32_t, int32_t> rc_delta;
+    const uint64_t ep = ++epoch;  // a sequence's or block's sim_* fields count only if stamped ep
+    if (rc_epoch.size() != rc.size()) {
+      rc_epoch.assign(rc.size(), 0);
+      rc_delta.assign(rc.size(), 0);
+    }
     int64_t need = 0, cow = 0;
     for (int32_t i = 0; i < count; ++i) {
       auto it = seqs.find(ids[i]);
@@ -125,16 +138,21 @@ struct pkv_bm {
       if (it->second.on_host) return PKV_ENOTRESIDENT;
       if (n[i] == 0) continue;
       const Seq& sq = it->second;
-      auto ls = sim_len.find(ids[i]);
-      const int64_t len = ls == sim_len.end() ? sq.len : ls->second;
-      bool priv = sim_private.count(ids[i]) ? sim_private[ids[i]] : false;
+      if (sq.sim_epoch != ep) {  // first entry of this sequence in the batch
+        sq.sim_epoch = ep;
+        sq.sim_len = sq.len;      // length after earlier entries
+        sq.sim_private = false;   // last block already private this batch
+      }
+      const int64_t len = sq.sim_len;
+      bool priv = sq.sim_private;
       if (len % B != 0 && !priv) {
         const int32_t b = sq.table[len / B];
-        const int32_t eff = rc[b] + rc_delta[b];
-        if (eff > 1) {
+        const int32_t delta = rc_epoch[b] == ep ? rc_delta[b] : 0;
+        if (rc[b] + delta > 1) {
           ++need;
           ++cow;
-          --rc_delta[b];
+          rc_epoch[b] = ep;
+          rc_delta[b] = delta - 1;
         }
         priv = true;  // from here on the last block is this sequence's own
       }
@@ -143,8 +161,8 @@ struct pkv_bm {
       if (after > before) priv = true;
       need += after - before;
       if (len + n[i] > INT32_MAX) return PKV_EINVAL;
-      sim_len[ids[i]] = (int32_t)(len + n[i]);
-      sim_private[ids[i]] = priv;
+      sq.sim_len = (int32_t)(len + n[i]);
+      sq.sim_private = priv;
     }
     if (cow_out) *cow_out = cow;
     return need;
@@ -266,7 +284,8 @@ int32_t pkv_bm_block_tables(const pkv_bm* bm, const int64_t* ids, int32_t count,
     const Seq& sq = bm->seqs.find(ids[i])->second;
     int32_t* row = tables_out + (int64_t)i * max_blocks;
     const int32_t nt = (int32_t)sq.table.size();
-    for (int32_t j = 0; j < max_blocks; ++j) row[j] = j < nt ? sq.table[j] : -1;
+    std::copy(sq.table.begin(), sq.table.end(), row);
+    std::fill(row + nt, row + max_blocks, -1);
     if (ctx_out) ctx_out[i] = sq.len;
   }
   return PKV_OK;

@@ -306,11 +306,11 @@ def paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_lens,
 def decode_items(context_lens_host, partition_size: int) -> np.ndarray:
     """Host work list for the items form of the partition launch (see include/pagedkv.h)."""
     ctx = np.ascontiguousarray(context_lens_host, dtype=np.int32)
-    ptr = ctx.ctypes.data_as(_I32P)
+    ptr = _i32p(ctx)
     n = int(_lib.pkv_decode_items(ptr, len(ctx), int(partition_size), None, 0))
     _check(min(n, 0), "decode_items")
     items = np.empty(max(n, 1), dtype=np.int32)
-    k = int(_lib.pkv_decode_items(ptr, len(ctx), int(partition_size), items.ctypes.data_as(_I32P), len(items)))
+    k = int(_lib.pkv_decode_items(ptr, len(ctx), int(partition_size), _i32p(items), len(items)))
     _check(min(k, 0), "decode_items")
     return items[:k]
 
@@ -320,8 +320,8 @@ def decode_items_into(context_lens_host: np.ndarray, partition_size: int, out: n
     if context_lens_host.dtype != np.int32 or out.dtype != np.int32 or not out.flags.c_contiguous \
             or not context_lens_host.flags.c_contiguous:
         raise ValueError("int32 contiguous arrays expected")
-    k = int(_lib.pkv_decode_items(context_lens_host.ctypes.data_as(_I32P), len(context_lens_host),
-                                  int(partition_size), out.ctypes.data_as(_I32P), len(out)))
+    k = int(_lib.pkv_decode_items(_i32p(context_lens_host), len(context_lens_host), int(partition_size),
+                                  _i32p(out), len(out)))
     _check(min(k, 0), "decode_items")
     return k
 
@@ -375,12 +375,18 @@ def paged_attention_ragged(out, q, cu_seqlens_q, context_lens, k_cache, v_cache,
 # ------------------------------------------------------------------------------------------------
 # Host block manager
 # ------------------------------------------------------------------------------------------------
+# ndarray.ctypes builds a helper object on every access (tens of microseconds); the data address
+# from the array interface is all a call needs.
+def _addr(a: np.ndarray) -> int:
+    return a.__array_interface__["data"][0]
+
+
 def _i32p(a: np.ndarray):
-    return a.ctypes.data_as(_I32P)
+    return ctypes.cast(_addr(a), _I32P)
 
 
 def _i64p(a: np.ndarray):
-    return a.ctypes.data_as(_I64P)
+    return ctypes.cast(_addr(a), _I64P)
 
 
 class BlockManager:
