@@ -631,6 +631,34 @@ def profile_copy(reps: int = 10):
                       "bytes_written_per_launch": 2 * 4096 * H * B * D * 2, "launches": reps}))
 
 
+def profile_prefill(reps: int = 20, warm: int = 50):
+    """Profiling target for the prefill kernel: the 8 prompt sequences of the 13B-shaped mixed
+    step (40 heads, head_dim 128, bf16, B=16, no cached prefix) attended alone: ``warm`` untimed
+    launches (clock ramp), then ``reps`` timed ones."""
+    import torch
+    from paged_kv_cache_323_amd import native as pk
+    from paged_kv_cache_323_amd import runner as R
+    from workloads import make_ragged_workload, make_workload
+    pre = [q for q in make_workload("mixed", "full").q_lens if q > 1]
+    w = make_ragged_workload(5, pre, pre, 40, 40, 128, "bf16", 16, name="prefill8")
+    st = R.play_script(w, threads=16)
+    q = R.to_device(w.queries(), w.dtype)
+    out = torch.empty_like(q)
+    tables, lens = st.bm.block_tables(w.query_seqs, w.max_blocks_per_seq())
+    bt, cl = torch.from_numpy(tables).cuda(), torch.from_numpy(lens).cuda()
+    cu = torch.from_numpy(w.cu_seqlens()).cuda()
+    mx = int(lens.max())
+    ws = torch.zeros(max(pk.ragged_workspace_bytes(len(lens), q.shape[0], w.num_q_heads, mx, mx, st.desc), 1),
+                     dtype=torch.uint8, device="cuda")
+    med, _ = _time_events(lambda: pk.paged_attention_ragged(out, q, cu, cl, st.k_cache, st.v_cache, bt, w.scale,
+                                                            mx, mx, st.desc, ws), reps=reps, warm=warm)
+    flops = prefill_flops(pre, pre, w.num_q_heads, w.head_dim)
+    print(json.dumps({"prefill_rows": int(sum(pre)), "sequences": len(pre), "launches": reps + warm,
+                      "gflop_per_launch": round(flops / 1e9, 2), "median_us": round(med, 1),
+                      "tflops": round(flops / med / 1e6, 1),
+                      "mfma_util": round(flops / med / 1e6 / MFMA_BF16_PEAK_TFLOPS, 4)}))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -644,6 +672,8 @@ def main():
     ap.add_argument("--dense-grid", action="store_true",
                     help="time the dense partition grid (every sequence sized for the longest context) "
                          "instead of the host-built work list")
+    ap.add_argument("--profile-prefill", action="store_true",
+                    help="only run the prefill kernel on the 13B-shaped step's prompts (profiling target)")
     ap.add_argument("--profile-copy", action="store_true",
                     help="only run the copy kernel used to calibrate HBM byte counters")
     args = ap.parse_args()
@@ -658,6 +688,9 @@ def main():
     torch.cuda.set_device(0)
     if args.profile_copy:
         profile_copy()
+        return
+    if args.profile_prefill:
+        profile_prefill()
         return
     h = run_headline(args)
     w = h["w"]
