@@ -659,6 +659,43 @@ def profile_prefill(reps: int = 20, warm: int = 50):
                       "mfma_util": round(flops / med / 1e6 / MFMA_BF16_PEAK_TFLOPS, 4)}))
 
 
+HOST_LINK_GBS = 64.0  # PCIe 5.0 x16 per direction, the swap path's link
+
+
+def row_rooflines(result, extra, read_peak, copy_peak):
+    """Each hot-path row beside the ceiling that bounds it: achieved, ceiling, fraction. HBM rows
+    are set against the 8 TB/s specification and the measured read (decode) or copy (write and
+    copy kernels, read + write) ceiling; prefill against the bf16 MFMA peak; swap against the
+    host link."""
+    def hbm(achieved, measured):
+        return {"achieved_gbs": round(achieved, 1), "frac_of_spec": round(achieved / HBM_PEAK_GBS, 4),
+                "measured_ceiling_gbs": round(measured, 1), "frac_of_measured": round(achieved / measured, 4)}
+    rows = {"a5_a6_decode_gqa": dict(hbm(result["roofline"]["achieved"], read_peak),
+                                     kernel_us=result["roofline"]["kernel_avg_us"])}
+    for key in ("llama7b", "gqa_B32", "gqa_B8"):
+        e = extra.get(key, {})
+        if "kv_gbs_partition_launch" in e:
+            rows[f"a5_decode_{key}"] = hbm(e["kv_gbs_partition_launch"], read_peak)
+    m = extra.get("mixed", {})
+    if "kv_cache_write_gbs" in m:
+        rows["a4_kv_cache_write"] = dict(hbm(m["kv_cache_write_gbs"], copy_peak), us=m["kv_cache_write_us"])
+    if "prefill_tflops" in m:
+        rows["a7_prefill"] = {"achieved_tflops": m["prefill_tflops"], "peak_tflops": MFMA_BF16_PEAK_TFLOPS,
+                              "frac": m["prefill_mfma_util"], "us": m["prefill_only_us"]}
+    if "attention_us" in m:
+        rows["a7_mixed_step"] = {"step_us": m["step_us"], "seqs_per_s": m["seqs_per_s"]}
+    sp = extra.get("shared_prefix", {})
+    if "copy_4096_pairs_gbs" in sp:
+        rows["a3_copy_blocks_4096_pairs"] = hbm(sp["copy_4096_pairs_gbs"], copy_peak)
+        rows["a3_copy_blocks_48_pairs"] = {"us": sp["copy_us"], "bound": "launch latency (24 MiB)"}
+    sw = extra.get("swap", {})
+    if "swap_out_gbs" in sw:
+        rows["swap"] = {"out_gbs": sw["swap_out_gbs"], "in_gbs": sw["swap_in_gbs"], "link_gbs": HOST_LINK_GBS,
+                        "frac_out": round(sw["swap_out_gbs"] / HOST_LINK_GBS, 4),
+                        "frac_in": round(sw["swap_in_gbs"] / HOST_LINK_GBS, 4)}
+    return rows
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -749,6 +786,7 @@ def main():
             except Exception as e:  # keep the headline line even if a side measurement fails
                 extra[key] = {"error": repr(e)}
         result["extra"] = extra
+        result["rows"] = row_rooflines(result, extra, read_peak, copy_peak)
     if not args.no_cpu:
         log("timing the oracle on the host CPU")
         result["cpu_baseline"] = cpu_baseline(w)
