@@ -127,16 +127,37 @@ __device__ __forceinline__ float sum8(float x) {
   return x;
 }
 
+// Over lanes l, l^16, l^32, l^48 (the wave's four 16-lane rows), in VALU: a row swap of a value
+// with itself leaves the two partners' values in the two results (gfx950 permlane swaps).
+__device__ __forceinline__ float max_rows4(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  const auto t = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(t[0]), __uint_as_float(t[1]));
+}
+__device__ __forceinline__ float sum_rows4(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  const auto t = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(t[0]) + __uint_as_float(t[1]);
+}
+
+// Whole-wave max / sum, every lane gets the result: DPP within each 16-lane row (pairs, quads,
+// half-row mirror, row mirror), then the row swaps above. No LDS traffic.
 __device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, kWave));
-  return x;
+  x = fmaxf(x, dpp<kDppQuadXor1>(x));
+  x = fmaxf(x, dpp<kDppQuadXor2>(x));
+  x = fmaxf(x, dpp<kDppRowHalfMirror>(x));
+  x = fmaxf(x, dpp<kDppRowMirror>(x));
+  return max_rows4(x);
 }
 
 __device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, kWave);
-  return x;
+  x += dpp<kDppQuadXor1>(x);
+  x += dpp<kDppQuadXor2>(x);
+  x += dpp<kDppRowHalfMirror>(x);
+  x += dpp<kDppRowMirror>(x);
+  return sum_rows4(x);
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }

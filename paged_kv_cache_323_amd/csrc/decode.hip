@@ -311,10 +311,7 @@ __global__ __launch_bounds__(kDecThreads, PKV_DECODE_MIN_WG) void paged_decode_k
   for (int g = 0; g < G; ++g)
 #pragma unroll
     for (int e = 0; e < EPL; ++e) {
-      float x = acc[g][e];
-      x += __shfl_xor(x, 16, kWave);
-      x += __shfl_xor(x, 32, kWave);
-      acc[g][e] = x;
+      acc[g][e] = sum_rows4(acc[g][e]);
     }
   if (rv == 0) {
 #pragma unroll

@@ -96,20 +96,6 @@ constexpr int kPfTab = 1024;  // block-table entries cached in LDS at a time
 #endif
 constexpr int kPfLookahead = PF_LOOKAHEAD;  // MFMA operand reads issued this many steps ahead
 
-// Max / sum over the four 16-lane rows of a wave (lanes l, l^16, l^32, l^48), all in VALU: a
-// row swap with itself leaves the two partners' values in the two results.
-__device__ __forceinline__ float rows_max(float x) {
-  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  x = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-  const auto t = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(t[0]), __uint_as_float(t[1]));
-}
-__device__ __forceinline__ float rows_sum(float x) {
-  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
-  const auto t = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(t[0]) + __uint_as_float(t[1]);
-}
 
 template <int DT, int D>
 // Two workgroups per CU: the register budget is capped at 256 per lane so that one wave's MFMA
@@ -386,7 +372,7 @@ __global__ __launch_bounds__(kPfThreads, 2) void ragged_prefill_kernel(PrefillAr
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
         mx = fmaxf(fmaxf(mx, fmaxf(sacc[mt][nt][0], sacc[mt][nt][1])), fmaxf(sacc[mt][nt][2], sacc[mt][nt][3]));
-      mx = rows_max(mx);
+      mx = max_rows4(mx);
       // Lazy rescaling: the reference max m_run only moves when some row's tile max exceeds it by
       // more than 2^8 in probability terms; until then probabilities may reach 2^8, which fp32
       // sums and the 16-bit split represent as well as values below 1. A row with no visible key
@@ -477,7 +463,7 @@ __global__ __launch_bounds__(kPfThreads, 2) void ragged_prefill_kernel(PrefillAr
   // ---- normalise and store: lane writes dims 16*dt + 4*g .. +3 of its row ----------------------
 #pragma unroll
   for (int nt = 0; nt < 2; ++nt) {
-    const float l = rows_sum(l_part[nt]);
+    const float l = sum_rows4(l_part[nt]);
     if (!qvalid[nt]) continue;
     const float inv = l > 0.f ? 1.f / l : 0.f;
     const size_t orow = ((size_t)(q0 + wave * 32 + nt * 16 + lr + row0) * a.hq + h) * D;
