@@ -219,7 +219,7 @@ int32_t pkv_paged_attention_decode_merge(void* out, int32_t out_dtype, const voi
  * launch uses; see pkv_decode_partition_size). The launch has exactly one workgroup per (kv
  * head, item), so no workgroup is spent on partitions that do not exist, which the dense launch
  * sizes for max_context_len in every sequence. Items are independent, so their order only
- * steers scheduling: pkv_decode_items puts the last partitions first. An item whose partition
+ * steers scheduling: pkv_decode_items puts the longest items first. An item whose partition
  * does not exist for the device context length, or whose sequence index is >= num_seqs, does
  * nothing. With every item of every sequence listed, the result equals
  * pkv_paged_attention_decode_partitions, and pkv_paged_attention_decode_merge completes it.
@@ -238,8 +238,12 @@ int32_t pkv_paged_attention_decode_partitions_items(void* out, int32_t out_dtype
 /* Host helper (no device work): the decode work list for host context lengths
  * context_lens[0..num_seqs) and a partition size (a positive multiple of 64). Lists every
  * (s, p) with p < ceil(context_lens[s] / partition_size) (p = 0 alone for a length of 0) as
- * s | (p << 16), ordered by descending p, then ascending s. With items == NULL returns the item
- * count; otherwise writes the items (capacity must hold them) and returns their count.
+ * s | (p << 16). Longest items first: an item's length is the token count of its partition
+ * (a context of n partitions is split into equal parts of ceil(ctx / n) rounded up to a multiple
+ * of 64, at most partition_size, the last part taking the rest); ties in descending p, then
+ * ascending s. Dispatching the longest partitions first leaves the shortest for the launch's
+ * tail. With items == NULL returns the item count; otherwise writes the items (capacity must
+ * hold them) and returns their count.
  * PKV_EINVAL for bad arguments or too small a capacity, PKV_ESHAPE beyond 65535 sequences or
  * 65536 partitions of one sequence. */
 int32_t pkv_decode_items(const int32_t* context_lens, int32_t num_seqs, int32_t partition_size,

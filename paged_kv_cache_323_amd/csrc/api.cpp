@@ -3,6 +3,8 @@
 // block_manager.cpp.
 #include <hip/hip_runtime.h>
 #include <math.h>
+
+#include <algorithm>
 #include <stdint.h>
 
 #include "../../include/pagedkv.h"
@@ -309,13 +311,24 @@ int32_t pkv_decode_items(const int32_t* context_lens, int32_t num_seqs, int32_t 
   if (!items) return (int32_t)total;  // size query
   if (total > capacity) return PKV_EINVAL;
   int32_t k = 0;
-  for (int32_t p = max_parts - 1; p >= 0; --p) {  // last partitions first, as in the dense launch
+  for (int32_t p = max_parts - 1; p >= 0; --p) {  // last partitions first, then sequence order
     for (int32_t s = 0; s < num_seqs; ++s) {
       const int32_t ctx = context_lens[s];
       const int32_t n = ctx > 0 ? (int32_t)(((int64_t)ctx + partition_size - 1) / partition_size) : 1;
       if (p < n) items[k++] = (int32_t)((uint32_t)s | ((uint32_t)p << 16));
     }
   }
+  // Longest items first (ties keep the order above), so that the launch's tail holds the shortest
+  // ones; an item's length is the token count of its partition as the kernel splits the context.
+  auto tokens = [&](int32_t it) {
+    const int32_t s = it & 0xffff, p = (int32_t)((uint32_t)it >> 16);
+    const int32_t ctx = context_lens[s];
+    if (ctx <= 0) return 0;
+    const int32_t n = (int32_t)(((int64_t)ctx + partition_size - 1) / partition_size);
+    const int32_t psz = std::min(partition_size, (((ctx + n - 1) / n) + 63) & ~63);
+    return std::max(0, std::min(psz, ctx - p * psz));
+  };
+  std::stable_sort(items, items + k, [&](int32_t x, int32_t y) { return tokens(x) > tokens(y); });
   return k;
 }
 

@@ -151,7 +151,16 @@ def test_debug_flags_rejects_null():
 
 def _items_reference(ctx, P):
     n = [max(1, -(-int(c) // P)) if c > 0 else 1 for c in ctx]
-    return [s | (p << 16) for p in range(max(n, default=0) - 1, -1, -1) for s in range(len(ctx)) if p < n[s]]
+    items = [s | (p << 16) for p in range(max(n, default=0) - 1, -1, -1) for s in range(len(ctx)) if p < n[s]]
+
+    def tokens(it):  # the partition's token count as the decode kernel splits the context
+        s, p = it & 0xFFFF, it >> 16
+        c = int(ctx[s])
+        if c <= 0:
+            return 0
+        psz = min(P, (-(-c // n[s]) + 63) // 64 * 64)
+        return max(0, min(psz, c - p * psz))
+    return sorted(items, key=lambda it: -tokens(it))  # stable: ties keep (p desc, s asc)
 
 
 @pytest.mark.parametrize("seed", range(4))
