@@ -314,12 +314,12 @@ def kv_utilisation(w, bm, max_len, stored_tokens=None):
             "max_len": max_len, "blocks_in_use": int(used)}
 
 
-def run_decode_config(name, block_size=None, steps=30, warmup=5):
+def run_decode_config(name, block_size=None, steps=30, warmup=5, partition=0):
     """Decode-step loop for another configuration; returns partition-launch and step figures."""
     import torch
     from workloads import make_workload
     w = make_workload(name, "full", block_size=block_size)
-    loop = DecodeLoop(w, warmup + steps + 2)
+    loop = DecodeLoop(w, warmup + steps + 2, partition=partition)
     util = kv_utilisation(w, loop.st.bm, MAX_LEN[name])
     for _ in range(warmup):
         loop.step()
@@ -334,7 +334,7 @@ def run_decode_config(name, block_size=None, steps=30, warmup=5):
     kern = float(np.mean([a.elapsed_time(b) for a, b, _ in evs])) * 1e-3
     merge = float(np.mean([b.elapsed_time(c) for _, b, c in evs])) * 1e-3
     kv = float(np.mean([decode_algorithmic_bytes(c, w, 2)[0] for c in loop.ctx_history]))
-    res = {"workload": w.name, "seqs": len(w.query_seqs), "step_us": round(el * 1e6, 1),
+    res = {"workload": w.name, "seqs": len(w.query_seqs), "partition": loop.partition, "step_us": round(el * 1e6, 1),
            "seqs_per_s": round(len(w.query_seqs) / el, 1), "kv_gbs_step": round(kv / el / 1e9, 1),
            "partition_launch_us": round(kern * 1e6, 1), "merge_launch_us": round(merge * 1e6, 1),
            "kv_gbs_partition_launch": round(kv / kern / 1e9, 1),

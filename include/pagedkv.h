@@ -140,15 +140,27 @@ int32_t pkv_copy_blocks(void* k_cache, void* v_cache, const int32_t* block_pairs
 /*
  * Workspace of the decode attention: per-partition partial results (running max, sum and
  * unnormalised output, fp32) of sequences whose context spans more than one partition.
- *   Returns the bytes needed for these arguments; 0 means no workspace is needed (every context
- *   fits one partition) or the arguments are invalid. The contents need no initialisation and
- *   are scratch between calls; calls that share a workspace must not run concurrently.
+ *   Returns bytes enough for a call at the automatic partition size with these arguments and
+ *   for every such call with fewer sequences or a smaller max_context_len (same heads and pool),
+ *   so one workspace sized for the largest batch serves every step; at most about 1024 (sequence,
+ *   kv head, partition) partials beyond what the largest call itself needs. 0 means no such call
+ *   needs a workspace (no context longer than 256 tokens, or num_seqs == 0) or the arguments
+ *   are invalid. The contents need no initialisation and are scratch between calls; calls that
+ *   share a workspace must not run concurrently.
  */
 size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t max_context_len,
                                   const pkv_cache_desc* cache);
 
 /* Tokens per context partition the decode kernel uses for these arguments
- * (partition_size argument 0 of the _ex entry point). */
+ * (partition_size argument 0 of the _ex entry point). It starts from max_context_len rounded up
+ * to a multiple of 64 when that fits the largest partition for the head grouping, else that
+ * largest partition; while num_seqs x num_kv_heads x ceil(max_context_len / partition) is below
+ * 512 workgroups (two per CU), it is halved (rounded up to a multiple of 64), down to 256, so a
+ * small batch of long contexts still fills the GPU. The largest partition is
+ * 8192 / (num_q_heads / num_kv_heads) tokens: 8192, 4096, 2048 and 1024 for 1, 2, 4 and 8 query
+ * heads per kv head (one workgroup keeps a score per token and query head in 32 KiB of LDS).
+ * The workspace and the launch must see the same arguments, since the size depends on all of
+ * them. Returns PKV_EINVAL for an invalid cache, head count or negative length or count. */
 int32_t pkv_decode_partition_size(int32_t num_seqs, int32_t num_q_heads, int32_t max_context_len,
                                   const pkv_cache_desc* cache);
 
@@ -181,7 +193,8 @@ int32_t pkv_paged_attention_decode(void* out, int32_t out_dtype, const void* q,
                                    size_t workspace_bytes, void* stream);
 
 /* As pkv_paged_attention_decode with an explicit partition size in tokens (0 = automatic;
- * otherwise a multiple of 64 and of the block size, at most 1024). The workspace must then be
+ * otherwise a multiple of 64 and of the block size, at most the largest partition for the head
+ * grouping given under pkv_decode_partition_size). The workspace must then be
  * sized with pkv_decode_workspace_bytes_ex. */
 int32_t pkv_paged_attention_decode_ex(void* out, int32_t out_dtype, const void* q,
                                       const void* k_cache, const void* v_cache,
@@ -249,6 +262,10 @@ int32_t pkv_paged_attention_decode_partitions_items(void* out, int32_t out_dtype
 int32_t pkv_decode_items(const int32_t* context_lens, int32_t num_seqs, int32_t partition_size,
                          int32_t* items, int32_t capacity);
 
+/* Workspace bytes for an explicit partition size: exactly what a call with these arguments
+ * needs (which covers any call with fewer sequences or a smaller max_context_len at that
+ * partition size); 0 when every context fits one partition or the arguments are invalid.
+ * partition_size 0 gives pkv_decode_workspace_bytes. */
 size_t pkv_decode_workspace_bytes_ex(int32_t num_seqs, int32_t num_q_heads,
                                      int32_t max_context_len, const pkv_cache_desc* cache,
                                      int32_t partition_size);

@@ -40,35 +40,67 @@ int32_t check_out_dtype(int32_t out_dt, const pkv_cache_desc* c) {
   return (out_dt == PKV_F32 || out_dt == c->dtype) ? PKV_OK : PKV_EDTYPE;
 }
 
-#ifndef PKV_AUTO_PARTITION
-#define PKV_AUTO_PARTITION 1024
-#endif
+// Automatic partition size. Contexts that fit the largest partition the LDS score buffer allows
+// for this head grouping take one partition (rounded up to 64 tokens), longer ones partitions of
+// that size. While the launch would then have fewer than kMinWorkgroups workgroups (sequences x
+// kv heads x partitions of the longest context), the partition is halved, down to
+// kMinAutoPartition tokens, so that a small batch of long contexts still spreads over the CUs.
+constexpr int64_t kMinWorkgroups = 512;  // two per CU
+constexpr int kMinAutoPartition = 256;
 
-// Contexts up to the automatic partition size take one partition (rounded up to 64 tokens);
-// longer ones are split into partitions of that size.
-int auto_partition(int32_t max_ctx) {
-  constexpr int kAuto = PKV_AUTO_PARTITION <= pkv::kMaxPartition ? PKV_AUTO_PARTITION : pkv::kMaxPartition;
-  if (max_ctx <= kAuto) return ((max_ctx > 0 ? max_ctx : 1) + 63) / 64 * 64;
-  return kAuto;
+int auto_partition(int32_t num_seqs, int32_t hkv, int g, int32_t max_ctx) {
+  const int cap = pkv::max_partition(g);
+  const int64_t ctx = max_ctx > 0 ? max_ctx : 1;
+  int p = ctx <= cap ? (int)((ctx + 63) / 64 * 64) : cap;
+  auto workgroups = [&](int part) { return (int64_t)num_seqs * hkv * ((ctx + part - 1) / part); };
+  while (p > kMinAutoPartition && workgroups(p) < kMinWorkgroups)
+    p = std::max(kMinAutoPartition, (p / 2 + 63) / 64 * 64);
+  return p;
 }
 
-bool valid_partition(int p, int bs) {
-  return p >= 64 && p <= pkv::kMaxPartition && p % 64 == 0 && p % bs == 0;
+bool valid_partition(int p, int bs, int g) {
+  return p >= 64 && p <= pkv::max_partition(g) && p % 64 == 0 && p % bs == 0;
 }
 
 struct DecodeWs {
   size_t acc, ml, total;
 };
 
-DecodeWs decode_ws_layout(int32_t S, int32_t hq, int32_t hkv, int32_t head_dim, int max_parts) {
+// Partial results of `items` (sequence, kv head, partition) triples, g query heads each.
+DecodeWs decode_ws_items(size_t items, int g, int32_t head_dim) {
   DecodeWs w{0, 0, 0};
-  if (max_parts <= 1) return w;
-  const size_t items = (size_t)S * hkv * max_parts;
-  const int g = hq / hkv;
+  if (items == 0) return w;
   w.acc = 0;
   w.ml = align_up(items * g * head_dim * sizeof(float));
   w.total = w.ml + align_up(items * g * 2 * sizeof(float));
   return w;
+}
+
+// Layout a launch indexes: dense over (sequence, kv head, partition < max_parts); none when every
+// context fits one partition.
+DecodeWs decode_ws_layout(int32_t S, int32_t hq, int32_t hkv, int32_t head_dim, int max_parts) {
+  if (max_parts <= 1) return DecodeWs{0, 0, 0};
+  return decode_ws_items((size_t)S * hkv * max_parts, hq / hkv, head_dim);
+}
+
+// Workspace bytes that cover every call at the automatic partition size with at most S sequences
+// and a max_context_len of at most max_ctx (same heads and pool). A call whose partition was not
+// halved has max(1, ceil(ctx / largest partition)) partitions, which grows with both arguments. A
+// call whose partition was halved has fewer than 2 * kMinWorkgroups (sequence, kv head, partition)
+// triples, since one halving at most doubles a count that was below kMinWorkgroups, and its
+// partitions are at least kMinAutoPartition tokens long.
+size_t decode_ws_auto_bound(int32_t S, int32_t hq, int32_t hkv, int32_t head_dim, int32_t max_ctx) {
+  const int g = hq / hkv;
+  const int cap = pkv::max_partition(g);
+  const int64_t ctx = max_ctx;
+  size_t whole = 0;
+  if (ctx > cap) whole = decode_ws_layout(S, hq, hkv, head_dim, (int)((ctx + cap - 1) / cap)).total;
+  size_t halved = 0;
+  if (ctx > kMinAutoPartition) {
+    const int64_t most = (int64_t)S * hkv * ((ctx + kMinAutoPartition - 1) / kMinAutoPartition);
+    halved = decode_ws_items((size_t)std::min<int64_t>(2 * kMinWorkgroups - 1, most), g, head_dim).total;
+  }
+  return std::max(whole, halved);
 }
 
 // HIP status of the most recent kernel launch made by an entry point on this thread.
@@ -163,20 +195,18 @@ int32_t pkv_swap_blocks(void* dst_k, void* dst_v, const void* src_k, const void*
 
 int32_t pkv_decode_partition_size(int32_t num_seqs, int32_t num_q_heads, int32_t max_ctx,
                                   const pkv_cache_desc* c) {
-  (void)num_seqs;
-  (void)num_q_heads;
-  if (check_cache(c) != PKV_OK || max_ctx < 0) return PKV_EINVAL;
-  int p = auto_partition(max_ctx);
-  while (p % c->block_size) p += 64;
-  return p;
+  if (check_cache(c) != PKV_OK || check_heads(num_q_heads, c) != PKV_OK || max_ctx < 0 || num_seqs < 0)
+    return PKV_EINVAL;
+  // a multiple of 64, hence of every block size
+  return auto_partition(num_seqs, c->num_kv_heads, num_q_heads / c->num_kv_heads, max_ctx);
 }
 
 size_t pkv_decode_workspace_bytes_ex(int32_t S, int32_t hq, int32_t max_ctx, const pkv_cache_desc* c,
                                      int32_t partition) {
   if (check_cache(c) != PKV_OK || check_heads(hq, c) != PKV_OK || S < 0 || max_ctx < 0) return 0;
-  const int p = partition > 0 ? partition : pkv_decode_partition_size(S, hq, max_ctx, c);
-  if (!valid_partition(p, c->block_size)) return 0;
-  const int max_parts = max_ctx > 0 ? (max_ctx + p - 1) / p : 1;
+  if (partition <= 0) return S > 0 ? decode_ws_auto_bound(S, hq, c->num_kv_heads, c->head_dim, max_ctx) : 0;
+  if (!valid_partition(partition, c->block_size, hq / c->num_kv_heads)) return 0;
+  const int max_parts = max_ctx > 0 ? (max_ctx + partition - 1) / partition : 1;
   return decode_ws_layout(S, hq, c->num_kv_heads, c->head_dim, max_parts).total;
 }
 
@@ -203,7 +233,7 @@ static int32_t decode_common_cu(void* out, int32_t out_dtype, const void* q, con
   if (!(scale > 0.f) || !(scale < INFINITY)) return PKV_EINVAL;  // a positive, finite multiplier
   const int p = partition_size > 0 ? partition_size
                                    : pkv_decode_partition_size(num_seqs, num_q_heads, max_context_len, c);
-  if (!valid_partition(p, c->block_size)) return PKV_EINVAL;
+  if (!valid_partition(p, c->block_size, num_q_heads / c->num_kv_heads)) return PKV_EINVAL;
   const int max_parts = max_context_len > 0 ? (max_context_len + p - 1) / p : 1;
   if (max_parts > 65535) return PKV_ESHAPE;
   const DecodeWs ws = decode_ws_layout(num_seqs, num_q_heads, c->num_kv_heads, c->head_dim, max_parts);

@@ -112,10 +112,15 @@ __global__ __launch_bounds__(kDecThreads, PKV_DECODE_MIN_WG) void paged_decode_k
   constexpr int NWORDS = EPL * ES / 4;
   static_assert(NCH >= 1 && EPL * ES % 8 == 0, "unsupported head dim");
 
-  __shared__ int32_t s_tab[kMaxPartition / 8];
-  __shared__ float s_p[kMaxPartition * G + kWave];  // [token][head]: scaled scores, then probabilities;
-                                                    // the tail absorbs discarded writes
-  __shared__ float s_red[kDecWaves * G * D];
+  constexpr int kPart = max_partition(G);
+  constexpr int kScores = kPart * G + kWave;  // the tail absorbs discarded writes
+  constexpr int kRed = kDecWaves * G * D;
+  __shared__ int32_t s_tab[kPart / 8];
+  // [token][head]: scaled scores, then probabilities; after the last probability is read, the
+  // same words hold the per-wave partial outputs, so LDS stays within four workgroups per CU.
+  __shared__ float s_buf[kScores > kRed ? kScores : kRed];
+  float* const s_p = s_buf;
+  float* const s_red = s_buf;
   __shared__ float s_m[G];
   __shared__ float s_l[G];
 
@@ -243,7 +248,7 @@ __global__ __launch_bounds__(kDecThreads, PKV_DECODE_MIN_WG) void paged_decode_k
 #pragma unroll
         for (int g = 1; g < G; ++g) mine = (c == g) ? sc[g] : mine;
         // Branch-free store: lanes with nothing to keep write into the discard tail.
-        const int dst = (c < G && i < nw) ? tl * G + c : kMaxPartition * G + lane;
+        const int dst = (c < G && i < nw) ? tl * G + c : kPart * G + lane;
         s_p[dst] = tl < n ? mine * a.scale_log2 : -INFINITY;
       }
     }
@@ -313,6 +318,7 @@ __global__ __launch_bounds__(kDecThreads, PKV_DECODE_MIN_WG) void paged_decode_k
     for (int e = 0; e < EPL; ++e) {
       acc[g][e] = sum_rows4(acc[g][e]);
     }
+  __syncthreads();  // every wave is done reading probabilities before s_red overwrites them
   if (rv == 0) {
 #pragma unroll
     for (int g = 0; g < G; ++g)
@@ -457,7 +463,8 @@ static hipError_t launch_decode_dt(const DecodeLaunch& L, hipStream_t stream) {
 }
 
 hipError_t launch_decode(const DecodeLaunch& L, hipStream_t stream) {
-  if (L.partition > kMaxPartition || L.partition % 64 != 0) return hipErrorInvalidConfiguration;
+  const int g = L.num_kv_heads > 0 ? L.num_q_heads / L.num_kv_heads : 0;
+  if (g < 1 || L.partition > max_partition(g) || L.partition % 64 != 0) return hipErrorInvalidConfiguration;
   switch (L.dt) {
     case DT_F32: return launch_decode_dt<DT_F32>(L, stream);
     case DT_F16: return launch_decode_dt<DT_F16>(L, stream);

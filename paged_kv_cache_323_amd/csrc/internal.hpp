@@ -4,8 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#ifndef PKV_MAX_PARTITION
-#define PKV_MAX_PARTITION 1024
+#ifndef PKV_SCORE_FLOATS
+#define PKV_SCORE_FLOATS 8192
 #endif
 #ifndef PKV_DECODE_PREFETCH
 #define PKV_DECODE_PREFETCH 3
@@ -13,8 +13,11 @@
 
 namespace pkv {
 
-// Largest decode partition in tokens (sizes the kernel's LDS score buffer).
-constexpr int kMaxPartition = PKV_MAX_PARTITION;
+// Scores a decode workgroup holds in LDS: partition tokens x query heads per kv head (32 KiB, which
+// keeps four 256-thread workgroups per CU for every head grouping).
+constexpr int kScoreFloats = PKV_SCORE_FLOATS;
+// Largest decode partition in tokens for g query heads per kv head.
+constexpr int max_partition(int g) { return kScoreFloats / g; }
 
 inline int ilog2(int x) {
   int r = 0;

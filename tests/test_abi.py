@@ -8,6 +8,7 @@ import subprocess
 import sys
 
 import pytest
+from hypothesis import given, settings, strategies as st
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "pagedkv.h")
@@ -73,22 +74,61 @@ def test_decode_rejects_bad_heads_and_dtypes():
 
 
 def test_decode_workspace_validation():
-    c = desc()
-    need = L.pkv_decode_workspace_bytes(2, 4, 5000, ctypes.byref(c))
+    c = desc()  # 4 query heads over 4 kv heads: partitions of up to 8192 tokens
+    need = L.pkv_decode_workspace_bytes(2, 4, 10000, ctypes.byref(c))
     assert need > 0
-    assert decode(c, max_ctx=5000, mb=400) == -4
-    assert decode(c, max_ctx=5000, mb=400, ws=ctypes.c_void_p(1), wsb=need - 1) == -4
-    assert L.pkv_decode_workspace_bytes(2, 4, 1000, ctypes.byref(c)) == 0  # one partition: none
+    assert decode(c, max_ctx=10000, mb=700) == -4
+    assert decode(c, max_ctx=10000, mb=700, ws=ctypes.c_void_p(1), wsb=need - 1) == -4
+    assert L.pkv_decode_workspace_bytes(512, 4, 256, ctypes.byref(c)) == 0  # never more than one partition
+    assert L.pkv_decode_workspace_bytes(0, 4, 8000, ctypes.byref(c)) == 0
+    assert L.pkv_decode_workspace_bytes_ex(512, 4, 8000, ctypes.byref(c), 8192) == 0  # one partition: none
+    assert L.pkv_decode_workspace_bytes_ex(512, 16, 8000, ctypes.byref(c), 2048) > 0
     assert decode(c, part=100) == -1      # not a multiple of 64
-    assert decode(c, part=2048) == -1     # too large
+    assert decode(c, part=8192 + 64) == -1            # too large for 1 query head per kv head
+    assert decode(c, hq=8, part=4096 + 64) == -1      # 2 per kv head
+    assert decode(c, hq=16, part=2048 + 64) == -1     # 4 per kv head
+    assert decode(c, hq=32, part=1024 + 64) == -1     # 8 per kv head
+    assert L.pkv_decode_workspace_bytes_ex(2, 32, 5000, ctypes.byref(c), 2048) == 0  # invalid: 0
 
 
 def test_partition_size_rule():
-    c = desc()
-    assert L.pkv_decode_partition_size(1, 4, 100, ctypes.byref(c)) == 128
-    assert L.pkv_decode_partition_size(1, 4, 5000, ctypes.byref(c)) == 1024
-    assert L.pkv_decode_partition_size(1, 4, 1000, ctypes.byref(c)) == 1024
-    assert L.pkv_decode_partition_size(1, 4, 0, ctypes.byref(c)) == 64
+    c = desc()  # 4 kv heads
+    size = lambda S, hq, ctx: L.pkv_decode_partition_size(S, hq, ctx, ctypes.byref(c))
+    # enough sequences to fill the GPU: the largest partition for the head grouping
+    assert size(512, 4, 100) == 128
+    assert size(512, 4, 0) == 64
+    assert size(512, 4, 5000) == 5056     # fits one partition of up to 8192
+    assert size(512, 4, 10000) == 8192
+    assert size(512, 8, 5000) == 4096
+    assert size(512, 16, 1000) == 1024
+    assert size(512, 16, 5000) == 2048
+    assert size(512, 32, 5000) == 1024
+    # fewer than 512 workgroups: halved, not below 256
+    assert size(8, 16, 32768) == 2048     # 8 x 4 x 16 = 512
+    assert size(4, 16, 32768) == 1024     # 4 x 4 x 32 = 512
+    assert size(1, 16, 32768) == 256      # 1 x 4 x 128 = 512
+    assert size(1, 16, 3000) == 256       # floor: 1 x 4 x 12 = 48
+    assert size(32, 4, 3000) == 768       # 3008 -> 1536 -> 768: 32 x 4 x 4 = 512
+    assert size(6, 6, 5000) == -1         # 6 query heads over 4 kv heads
+    assert size(-1, 4, 5000) == -1
+
+
+@settings(max_examples=300, derandomize=True, deadline=None, database=None)
+@given(st.sampled_from([1, 2, 4, 8]), st.sampled_from([1, 2, 8, 40]), st.integers(1, 600),
+       st.integers(0, 200_000), st.floats(0, 1), st.floats(0, 1))
+def test_auto_workspace_covers_smaller_calls(g, hkv, S, ctx, fs, fc):
+    """The automatic-size workspace for (S, ctx) is at least what the launch of any call with
+    S' <= S sequences and max_context_len ctx' <= ctx needs (exact bytes at that call's own
+    automatic partition), so one workspace sized for the largest batch serves every step."""
+    c = desc(num_kv_heads=hkv, head_dim=128)
+    hq = g * hkv
+    S2, ctx2 = max(1, int(S * fs)), int(ctx * fc)
+    bound = L.pkv_decode_workspace_bytes(S, hq, ctx, ctypes.byref(c))
+    for s_, c_ in ((S, ctx), (S2, ctx), (S, ctx2), (S2, ctx2)):
+        p = L.pkv_decode_partition_size(s_, hq, c_, ctypes.byref(c))
+        assert p >= 64 and p % 64 == 0 and p <= 8192 // g
+        need = L.pkv_decode_workspace_bytes_ex(s_, hq, c_, ctypes.byref(c), p)
+        assert need <= bound, (s_, c_, p, need, bound)
 
 
 def test_write_and_copy_validation():

@@ -105,6 +105,24 @@ def test_split_context_equals_oracle(partition):
     _check_attention(w, out, ref)
 
 
+@pytest.mark.parametrize("g,dt", [(1, "f16"), (2, "bf16"), (4, "bf16"), (8, "f32")])
+def test_largest_partition_per_head_grouping(g, dt):
+    """The largest partition for g query heads per kv head (8192 / g tokens, the LDS score buffer
+    full) on contexts that fill one, span two with a ragged tail, fall just short of one, and hold
+    a single token; then the automatic size, which for four sequences is the smallest (too few
+    workgroups otherwise)."""
+    cap = 8192 // g
+    ctx = [cap, 2 * cap + 37, cap - 5, 1]
+    w = make_decode_workload(70 + g, ctx, 2 * g, 2, 128, dt, 16, name=f"largest-partition-g{g}")
+    _announce(f"decode largest partition g={g} {dt} ctx={ctx}")
+    R = _runner()
+    _, ref = oracle.run_workload(w)
+    st = R.play_script(w)
+    for part in (cap, 0):
+        out, _ = R.attention(w, st, "f32", partition_size=part)
+        _check_attention(w, out, ref)
+
+
 def test_physical_permutation_bit_identical():
     """Two different physical placements of the same logical caches give bit-identical
     outputs: the kernel's reduction order depends on logical positions only."""
