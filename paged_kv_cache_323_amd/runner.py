@@ -132,7 +132,8 @@ def attention(w, st: DeviceState, out_dtype: Optional[str] = "f32", device="cuda
     if q is None:
         q = to_device(w.queries(), w.dtype, device)
     odt = TORCH_DTYPE[out_dtype or w.dtype]
-    out = torch.empty(q.shape, dtype=odt, device=device)
+    # NaN-filled, so a row the kernels leave unwritten fails the callers' finiteness checks
+    out = torch.full(q.shape, float("nan"), dtype=odt, device=device)
     max_ctx = int(lens.max()) if len(lens) else 0
     if w.is_decode:
         nbytes = pk.decode_workspace_bytes(len(lens), w.num_q_heads, max_ctx, st.desc, partition_size)
