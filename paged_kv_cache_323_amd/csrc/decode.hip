@@ -344,49 +344,58 @@ __global__ __launch_bounds__(kDecThreads, PKV_DECODE_MIN_WG) void paged_decode_k
   }
 }
 
-// Log-sum-exp merge of the partitions of every multi-partition sequence: one thread per output
-// element; single-partition sequences were finished by the partition kernel.
+// Log-sum-exp merge of the partitions' partial results. A workgroup covers 256 / NG outputs of
+// one sequence with NG threads each: thread group k merges partitions k, k + NG, ... with a
+// running maximum, and the NG (max, sum, value) triples of an output are then combined through
+// LDS. NG grows with the partition count (up to 8), so that up to 64 partitions take one round
+// of loads per thread: a long context's merge is not a chain of dependent loads.
+template <int NG>
 __global__ __launch_bounds__(256) void paged_decode_merge_kernel(DecodeArgs a, int head_dim, int group) {
+  constexpr int kOuts = 256 / NG;
+  __shared__ float s_ml[NG > 1 ? 3 * NG * kOuts : 1];
   const int s = blockIdx.y;
-  const int o = blockIdx.x * 256 + threadIdx.x;
-  if (o >= a.hq * head_dim) return;
+  const int oi = threadIdx.x % kOuts;
+  const int grp = threadIdx.x / kOuts;
+  const int o = blockIdx.x * kOuts + oi;
+  const bool active = o < a.hq * head_dim;
   int row = s;
   if (a.cu) {
     row = a.cu[s];
-    if (a.cu[s + 1] - row != 1) return;
+    if (a.cu[s + 1] - row != 1) return;                              // uniform over the workgroup
     if (kDebugChecks && (row < 0 || row >= a.num_rows)) return;  // flagged by the partition kernel
   }
   const int ctx = min(a.ctx_lens[s], min(a.max_blocks * a.bs, a.max_parts * a.partition));
   const int nparts = ctx > 0 ? (ctx + a.partition - 1) / a.partition : 1;
-  if (nparts <= 1) return;
-  const int h = o / head_dim;
+  if (nparts <= 1) return;  // uniform
+  const int h = active ? o / head_dim : 0;
   const int kvh = h / group;
   const int g = h - kvh * group;
-  const int d = o - h * head_dim;
+  const int d = active ? o - h * head_dim : 0;
   const size_t item = ((size_t)s * a.hkv + kvh) * a.max_parts;
-  // Partials are read in chunks of 8 whose loads are all issued before any is used, and merged
-  // with a running log-sum-exp.
+  // This thread's partitions grp, grp + NG, ... are read in chunks of 8 whose loads are all issued
+  // before any is used, and merged with a running log-sum-exp.
   constexpr int kChunk = 8;
+  const int mine = nparts > grp ? (nparts - grp + NG - 1) / NG : 0;
   float mx = -INFINITY, l = 0.f, v = 0.f;
-  for (int p0 = 0; p0 < nparts; p0 += kChunk) {
+  for (int j0 = 0; active && j0 < mine; j0 += kChunk) {
     float2 ml[kChunk];
     float av[kChunk];
 #pragma unroll
     for (int j = 0; j < kChunk; ++j) {
-      const int p = min(p0 + j, nparts - 1);  // padding lanes re-read the last partial; dropped below
+      const int p = grp + NG * min(j0 + j, mine - 1);  // padding re-reads the last one; dropped below
       ml[j] = a.ws_ml[(item + p) * group + g];
       av[j] = a.ws_acc[((item + p) * group + g) * head_dim + d];
     }
     float cm = mx;
 #pragma unroll
     for (int j = 0; j < kChunk; ++j)
-      if (p0 + j < nparts) cm = fmaxf(cm, ml[j].x);
+      if (j0 + j < mine) cm = fmaxf(cm, ml[j].x);
     const float r = fast_exp2(mx - cm);  // rescale what was merged so far (0 on the first chunk)
     l *= r;
     v *= r;
 #pragma unroll
     for (int j = 0; j < kChunk; ++j) {
-      if (p0 + j < nparts) {
+      if (j0 + j < mine) {
         const float w = fast_exp2(ml[j].x - cm);
         l = __builtin_fmaf(w, ml[j].y, l);
         v = __builtin_fmaf(w, av[j], v);
@@ -394,7 +403,29 @@ __global__ __launch_bounds__(256) void paged_decode_merge_kernel(DecodeArgs a, i
     }
     mx = cm;
   }
-  store_out(a.out, (size_t)row * a.hq * head_dim + o, l > 0.f ? v / l : 0.f, a.out_dt);
+  if constexpr (NG > 1) {
+    float* s_m = s_ml;
+    float* s_l = s_ml + NG * kOuts;
+    float* s_v = s_ml + 2 * NG * kOuts;
+    s_m[grp * kOuts + oi] = mx;
+    s_l[grp * kOuts + oi] = l;
+    s_v[grp * kOuts + oi] = v;
+    __syncthreads();
+    if (grp != 0) return;
+    float m_all = mx;
+#pragma unroll
+    for (int k = 1; k < NG; ++k) m_all = fmaxf(m_all, s_m[k * kOuts + oi]);
+    l = 0.f;
+    v = 0.f;
+#pragma unroll
+    for (int k = 0; k < NG; ++k) {
+      const float mk = s_m[k * kOuts + oi];
+      const float w = mk == -INFINITY ? 0.f : fast_exp2(mk - m_all);  // a group with no partition
+      l = __builtin_fmaf(w, s_l[k * kOuts + oi], l);
+      v = __builtin_fmaf(w, s_v[k * kOuts + oi], v);
+    }
+  }
+  if (active) store_out(a.out, (size_t)row * a.hq * head_dim + o, l > 0.f ? v / l : 0.f, a.out_dt);
 }
 
 static DecodeArgs make_args(const DecodeLaunch& L) {
@@ -439,7 +470,15 @@ static hipError_t launch_decode_t(const DecodeLaunch& L, hipStream_t stream) {
   }
   if (L.stage != 1 && L.max_parts > 1) {
     const int outs = L.num_q_heads * D;
-    return launch_kernel(paged_decode_merge_kernel, dim3((outs + 255) / 256, L.num_seqs), dim3(256), stream, a, D, G);
+    // threads per output: enough that each merges at most one chunk of 8 partitions
+    const int ng = L.max_parts <= 8 ? 1 : L.max_parts <= 16 ? 2 : L.max_parts <= 32 ? 4 : 8;
+    const dim3 grid((unsigned)((outs * ng + 255) / 256), (unsigned)L.num_seqs);
+    switch (ng) {
+      case 1: return launch_kernel(paged_decode_merge_kernel<1>, grid, dim3(256), stream, a, D, G);
+      case 2: return launch_kernel(paged_decode_merge_kernel<2>, grid, dim3(256), stream, a, D, G);
+      case 4: return launch_kernel(paged_decode_merge_kernel<4>, grid, dim3(256), stream, a, D, G);
+      default: return launch_kernel(paged_decode_merge_kernel<8>, grid, dim3(256), stream, a, D, G);
+    }
   }
   return hipSuccess;
 }
