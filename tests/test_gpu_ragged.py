@@ -114,3 +114,26 @@ def test_mixed_full_sampled():
     rows = [r for i in seqs for r in range(cu[i], cu[i + 1])]
     err = _check(w, out, ref, rows=rows)
     print(f"  checked {len(rows)} rows, max abs err {err:.3g}")
+
+
+def test_ragged_on_caller_stream():
+    """The ragged step on a non-default stream: a copy enqueued on that stream right after the
+    call sees every row, prefill and decode (outputs start as NaN), for two calls on two streams."""
+    import torch
+    from paged_kv_cache_323_amd import runner as R
+    cases = [make_ragged_workload(31, [300, 1, 1, 257], [300, 900, 40, 400], 8, 4, 128, "bf16", 16, name="join-a"),
+             make_ragged_workload(32, [1, 129, 1], [2000, 129, 3], 4, 4, 64, "f16", 16, name="join-b")]
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    copies = []
+    for w, s in zip(cases, streams):
+        _announce(f"ragged on a side stream {w.name}")
+        st = R.play_script(w, threads=16)
+        torch.cuda.synchronize()
+        with torch.cuda.stream(s):
+            out, _ = R.attention(w, st, "f32")
+            copies.append(out.clone())  # same stream: ordered after both launches
+    for s in streams:
+        s.synchronize()
+    for w, got in zip(cases, copies):
+        _, ref = oracle.run_workload(w)
+        _check(w, got, ref)
