@@ -285,6 +285,47 @@ def measured_read_peak():
     return best  # GB/s
 
 
+def measured_gather_peak(loop):
+    """Tile-gather probe (libpkv_probe.so) over the headline's own pools: every (block, kv head)
+    tile of the current step's contexts, listed per (sequence, kv head) in table order, read from
+    the K pool and then the V pool, with no arithmetic; the best of 16, 32, 64 and 128 tiles per
+    workgroup, median of 20 each. The attainable rate of the decode kernel's access pattern (None
+    for tiles smaller than 4 KiB)."""
+    import ctypes
+    import torch
+    w = loop.w
+    tile_bytes = w.block_size * w.head_dim * {"f32": 4, "f16": 2, "bf16": 2}[w.dtype]
+    if tile_bytes % 4096:
+        return None
+    lib = ctypes.CDLL(os.path.join(ROOT, "paged_kv_cache_323_amd", "libpkv_probe.so"))
+    lib.pkvprobe_gather_read.restype = ctypes.c_int32
+    lib.pkvprobe_gather_read.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
+                                         ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
+    tables, lens = loop.st.bm.block_tables(loop.seqs, loop.max_blocks)
+    H = w.num_kv_heads
+    parts = []
+    for s in range(len(lens)):
+        blocks = tables[s, : -(-int(lens[s]) // w.block_size)].astype(np.int64)
+        parts.append((blocks[None, :] * H + np.arange(H)[:, None]).ravel())
+    tiles_h = np.concatenate(parts)
+    assert tiles_h.min() >= 0 and tiles_h.max() < w.num_blocks * H  # every tile inside both pools
+    tiles = torch.from_numpy(tiles_h.astype(np.int32)).cuda()
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    best = 0.0
+    for per_wg in (16, 32, 64, 128):
+        def call(p=per_wg):
+            st = lib.pkvprobe_gather_read(ctypes.c_void_p(loop.st.k_cache.data_ptr()),
+                                          ctypes.c_void_p(loop.st.v_cache.data_ptr()),
+                                          ctypes.c_void_p(tiles.data_ptr()), len(tiles_h), tile_bytes, p,
+                                          ctypes.c_void_p(sink.data_ptr()), stream)
+            if st != 0:
+                raise RuntimeError(f"gather probe failed: {st}")
+        med, _ = _time_events(call, reps=20, warm=3)
+        best = max(best, 2 * len(tiles_h) * tile_bytes / med / 1e3)
+    return best  # GB/s
+
+
 def measured_copy_peak():
     """Streaming-copy probe: torch copy of 1 GiB into another 1 GiB buffer (read + write), median
     of 20; the achievable counterpart of the 8 TB/s specification."""
@@ -672,6 +713,9 @@ def row_rooflines(result, extra, read_peak, copy_peak):
                 "measured_ceiling_gbs": round(measured, 1), "frac_of_measured": round(achieved / measured, 4)}
     rows = {"a5_a6_decode_gqa": dict(hbm(result["roofline"]["achieved"], read_peak),
                                      kernel_us=result["roofline"]["kernel_avg_us"])}
+    if "measured_gather_peak" in result["roofline"]:  # the same tiles read with no arithmetic
+        rows["a5_a6_decode_gqa"]["gather_ceiling_gbs"] = result["roofline"]["measured_gather_peak"]
+        rows["a5_a6_decode_gqa"]["frac_of_gather"] = result["roofline"]["frac_of_measured_gather_peak"]
     for key in ("llama7b", "gqa_B32", "gqa_B8"):
         e = extra.get(key, {})
         if "kv_gbs_partition_launch" in e:
@@ -771,6 +815,12 @@ def main():
     result["roofline"]["measured_read_peak"] = round(read_peak, 1)
     result["roofline"]["frac_of_measured_read_peak"] = round(h["achieved"] / read_peak, 4)
     result["roofline"]["measured_copy_peak"] = round(copy_peak, 1)
+    # The decode kernel's own access pattern (whole K then V tiles gathered through the tables)
+    # without its arithmetic: the attainable rate for this layout and block size.
+    gather_peak = measured_gather_peak(h["loop"])
+    if gather_peak:
+        result["roofline"]["measured_gather_peak"] = round(gather_peak, 1)
+        result["roofline"]["frac_of_measured_gather_peak"] = round(h["achieved"] / gather_peak, 4)
     if not args.no_extra:
         extra = {}
         for key, fn in (("gqa_B32", lambda: run_decode_config("gqa", 32)),

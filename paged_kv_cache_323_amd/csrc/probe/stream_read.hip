@@ -36,3 +36,60 @@ extern "C" int32_t pkvprobe_stream_read(const void* buf, size_t bytes, uint32_t*
   return (int32_t)hipLaunchKernel(reinterpret_cast<const void*>(&stream_read_kernel), dim3(grid), dim3(256), args,
                                   0, (hipStream_t)stream);
 }
+
+// Tile-gather probe: the read pattern of the decode kernel without its arithmetic. Workgroup w
+// takes list entries [w * per_wg, (w + 1) * per_wg) and reads each entry's whole tile from the K
+// pool, then the same tiles from the V pool (as one decode workgroup reads a partition's K tiles,
+// then its V tiles), 16 bytes per thread per 4 KiB with 8 loads in flight, folding every word
+// into a checksum stored only if it equals a value that pools of one repeated byte cannot give.
+//
+//   int32_t pkvprobe_gather_read(const void* pool_k, const void* pool_v, const uint32_t* tiles,
+//                                int32_t num_tiles, int32_t tile_bytes, int32_t per_wg,
+//                                uint32_t* sink, void* stream)
+// pool_k, pool_v: device memory, 16-byte aligned; tiles: device list of tile indices (tile i is
+// bytes [i * tile_bytes, (i + 1) * tile_bytes) of each pool; the caller keeps every index inside
+// both pools); tile_bytes: a positive multiple of 4096; per_wg: list entries per workgroup.
+// Returns 0, -1 on bad arguments, or the hipError_t of the launch.
+__global__ __launch_bounds__(256) void gather_read_kernel(const u32x4* __restrict__ pk, const u32x4* __restrict__ pv,
+                                                          const uint32_t* __restrict__ tiles, int32_t n,
+                                                          int32_t per_wg, int32_t chunks, uint32_t* __restrict__ sink) {
+  constexpr int U = 8;
+  const long long i0 = (long long)blockIdx.x * per_wg * chunks;
+  const long long i1 = min((long long)n, (long long)(blockIdx.x + 1) * per_wg) * chunks;
+  uint32_t acc = 0;
+  for (int pass = 0; pass < 2; ++pass) {
+    const u32x4* pool = pass ? pv : pk;
+    auto addr = [&](long long i) {  // chunk c of list entry t: 256 threads x 16 bytes
+      const long long t = i / chunks, c = i - t * chunks;
+      return pool + ((size_t)tiles[t] * chunks + c) * 256 + threadIdx.x;
+    };
+    long long i = i0;
+    for (; i + U <= i1; i += U) {
+      u32x4 v[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) v[u] = __builtin_nontemporal_load(addr(i + u));
+#pragma unroll
+      for (int u = 0; u < U; ++u) acc ^= v[u][0] ^ v[u][1] ^ v[u][2] ^ v[u][3];
+    }
+    for (; i < i1; ++i) {
+      const u32x4 v = __builtin_nontemporal_load(addr(i));
+      acc ^= v[0] ^ v[1] ^ v[2] ^ v[3];
+    }
+  }
+  if (acc == 0x12345679u) sink[0] = acc;
+}
+
+extern "C" int32_t pkvprobe_gather_read(const void* pool_k, const void* pool_v, const uint32_t* tiles,
+                                        int32_t num_tiles, int32_t tile_bytes, int32_t per_wg, uint32_t* sink,
+                                        void* stream) {
+  if (!pool_k || !pool_v || !tiles || !sink || (uintptr_t)pool_k % 16 || (uintptr_t)pool_v % 16) return -1;
+  if (num_tiles < 1 || tile_bytes < 4096 || tile_bytes % 4096 || per_wg < 1) return -1;
+  const long long grid = ((long long)num_tiles + per_wg - 1) / per_wg;
+  if (grid > 0x7fffffff) return -1;
+  const u32x4* pk = static_cast<const u32x4*>(pool_k);
+  const u32x4* pv = static_cast<const u32x4*>(pool_v);
+  int32_t n = num_tiles, chunks = tile_bytes / 4096;
+  void* args[] = {&pk, &pv, &tiles, &n, &per_wg, &chunks, &sink};
+  return (int32_t)hipLaunchKernel(reinterpret_cast<const void*>(&gather_read_kernel), dim3((unsigned)grid), dim3(256),
+                                  args, 0, (hipStream_t)stream);
+}
