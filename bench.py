@@ -672,16 +672,16 @@ def profile_copy(reps: int = 10):
                       "bytes_written_per_launch": 2 * 4096 * H * B * D * 2, "launches": reps}))
 
 
-def profile_prefill(reps: int = 20, warm: int = 50):
-    """Profiling target for the prefill kernel: the 8 prompt sequences of the 13B-shaped mixed
-    step (40 heads, head_dim 128, bf16, B=16, no cached prefix) attended alone: ``warm`` untimed
-    launches (clock ramp), then ``reps`` timed ones."""
+def prefill_only(dtype: str = "bf16", reps: int = 20, warm: int = 50):
+    """The prefill kernel alone on the 8 prompt sequences of the 13B-shaped mixed step (40 heads,
+    head_dim 128, B=16, no cached prefix) in the given pool dtype: ``warm`` untimed launches
+    (clock ramp), then ``reps`` timed ones; median duration and MFMA utilisation."""
     import torch
     from paged_kv_cache_323_amd import native as pk
     from paged_kv_cache_323_amd import runner as R
     from workloads import make_ragged_workload, make_workload
     pre = [q for q in make_workload("mixed", "full").q_lens if q > 1]
-    w = make_ragged_workload(5, pre, pre, 40, 40, 128, "bf16", 16, name="prefill8")
+    w = make_ragged_workload(5, pre, pre, 40, 40, 128, dtype, 16, name=f"prefill8-{dtype}")
     st = R.play_script(w, threads=16)
     q = R.to_device(w.queries(), w.dtype)
     out = torch.empty_like(q)
@@ -694,10 +694,17 @@ def profile_prefill(reps: int = 20, warm: int = 50):
     med, _ = _time_events(lambda: pk.paged_attention_ragged(out, q, cu, cl, st.k_cache, st.v_cache, bt, w.scale,
                                                             mx, mx, st.desc, ws), reps=reps, warm=warm)
     flops = prefill_flops(pre, pre, w.num_q_heads, w.head_dim)
-    print(json.dumps({"prefill_rows": int(sum(pre)), "sequences": len(pre), "launches": reps + warm,
-                      "gflop_per_launch": round(flops / 1e9, 2), "median_us": round(med, 1),
-                      "tflops": round(flops / med / 1e6, 1),
-                      "mfma_util": round(flops / med / 1e6 / MFMA_BF16_PEAK_TFLOPS, 4)}))
+    res = {"dtype": dtype, "prefill_rows": int(sum(pre)), "sequences": len(pre), "launches": reps + warm,
+           "gflop_per_launch": round(flops / 1e9, 2), "median_us": round(med, 1),
+           "tflops": round(flops / med / 1e6, 1), "mfma_util": round(flops / med / 1e6 / MFMA_BF16_PEAK_TFLOPS, 4)}
+    del st
+    torch.cuda.empty_cache()
+    return res
+
+
+def profile_prefill(dtype: str = "bf16"):
+    """Profiling target for the prefill kernel (see prefill_only); prints one JSON line."""
+    print(json.dumps(prefill_only(dtype)))
 
 
 HOST_LINK_GBS = 64.0  # PCIe 5.0 x16 per direction, the swap path's link
@@ -728,6 +735,10 @@ def row_rooflines(result, extra, read_peak, copy_peak):
                               "frac": m["prefill_mfma_util"], "us": m["prefill_only_us"]}
     if "attention_us" in m:
         rows["a7_mixed_step"] = {"step_us": m["step_us"], "seqs_per_s": m["seqs_per_s"]}
+    pf = extra.get("prefill_f16", {})
+    if "tflops" in pf:  # the same prompts from an f16 pool: one f16 P operand, no split
+        rows["a7_prefill_f16"] = {"achieved_tflops": pf["tflops"], "peak_tflops": MFMA_BF16_PEAK_TFLOPS,
+                                  "frac": pf["mfma_util"], "us": pf["median_us"]}
     sp = extra.get("shared_prefix", {})
     if "copy_4096_pairs_gbs" in sp:
         rows["a3_copy_blocks_4096_pairs"] = hbm(sp["copy_4096_pairs_gbs"], copy_peak)
@@ -755,6 +766,8 @@ def main():
                          "instead of the host-built work list")
     ap.add_argument("--profile-prefill", action="store_true",
                     help="only run the prefill kernel on the 13B-shaped step's prompts (profiling target)")
+    ap.add_argument("--prefill-dtype", default="bf16", choices=("bf16", "f16"),
+                    help="pool dtype of --profile-prefill")
     ap.add_argument("--profile-copy", action="store_true",
                     help="only run the copy kernel used to calibrate HBM byte counters")
     args = ap.parse_args()
@@ -771,7 +784,7 @@ def main():
         profile_copy()
         return
     if args.profile_prefill:
-        profile_prefill()
+        profile_prefill(args.prefill_dtype)
         return
     h = run_headline(args)
     w = h["w"]
@@ -829,7 +842,8 @@ def main():
                         ("shared_prefix", run_shared_prefix),
                         ("swap", run_swap),
                         ("engine", run_engine),
-                        ("mixed", run_mixed)):
+                        ("mixed", run_mixed),
+                        ("prefill_f16", lambda: prefill_only("f16"))):
             log(f"extra: {key}")
             try:
                 extra[key] = fn()

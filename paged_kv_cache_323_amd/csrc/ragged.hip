@@ -12,9 +12,11 @@
 //   online softmax        (row max across the 4 lane groups; fp32; exp2 on log2-scaled scores)
 //   Oᵀ += Vᵀ·Pᵀ          (M = head_dim, N = 32 rows, K = 64 keys)    -> lane holds 4 dims x 1 row
 // The P operand comes straight from the Sᵀ accumulators: MFMA sums over k, so any fixed order of
-// the 32 keys of a k-step works as long as the Vᵀ operand uses the same order. P is split into
-// a 16-bit high part and a 16-bit remainder, each multiplied by V, so the products keep about
-// 16 significant bits (a single 16-bit P would cost up to ~1e-2 relative on short rows).
+// the 32 keys of a k-step works as long as the Vᵀ operand uses the same order. For bf16 pools P
+// is split into a bf16 high part and a bf16 remainder, each multiplied by V, so the products
+// keep about 16 significant bits (one bf16 P, 8 bits, would cost up to ~1e-2 relative on short
+// rows). For f16 pools one f16 P rounded to nearest (11 bits, at most 2^-12 relative) is enough,
+// and Oᵀ takes one MFMA per step instead of two.
 // A query row at position p sees keys 0..p (the block-wise equation's ⌈i/B⌉ limit,
 // 「PagedAttention原理」 §实现一个虚拟内存).
 #include "common.hpp"
@@ -50,20 +52,19 @@ template <> struct Mfma<DT_F16> {
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 
-// Split two probabilities x = hi + lo into 16-bit high parts and 16-bit remainders, each pair
-// packed into one 32-bit operand word (element 0 in the low half). hi is truncated, the
-// remainder carries the rest, so hi + lo keeps about 16 significant bits.
-template <int DT> __device__ __forceinline__ void split_pair(float x0, float x1, uint32_t& hi, uint32_t& lo);
-template <> __device__ __forceinline__ void split_pair<DT_BF16>(float x0, float x1, uint32_t& hi, uint32_t& lo) {
+// Split two probabilities x = hi + lo into bf16 high parts and bf16 remainders, each pair packed
+// into one 32-bit operand word (element 0 in the low half). hi is truncated, the remainder
+// carries the rest, so hi + lo keeps about 16 significant bits.
+__device__ __forceinline__ void split_pair_bf16(float x0, float x1, uint32_t& hi, uint32_t& lo) {
   const uint32_t u0 = __float_as_uint(x0), u1 = __float_as_uint(x1);
   hi = __builtin_amdgcn_perm(u1, u0, 0x07060302u);  // upper halves: bf16 truncation of both
   const f32x2 r = {x0 - __uint_as_float(u0 & 0xffff0000u), x1 - __uint_as_float(u1 & 0xffff0000u)};
   lo = __builtin_bit_cast(uint32_t, __builtin_convertvector(r, bf16x2));
 }
-template <> __device__ __forceinline__ void split_pair<DT_F16>(float x0, float x1, uint32_t& hi, uint32_t& lo) {
-  const auto h = __builtin_amdgcn_cvt_pkrtz(x0, x1);  // round toward zero; the remainder is exact
-  hi = __builtin_bit_cast(uint32_t, h);
-  lo = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(x0 - (float)h[0], x1 - (float)h[1]));
+// Two probabilities as f16 rounded to nearest, packed into one 32-bit operand word.
+__device__ __forceinline__ uint32_t pack_f16(float x0, float x1) {
+  const f32x2 x = {x0, x1};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(x, f16x2));
 }
 
 struct PrefillArgs {
@@ -358,7 +359,10 @@ __global__ __launch_bounds__(kPfThreads, 2) void ragged_prefill_kernel(PrefillAr
     // Scores stay unscaled here; exp2((s - m)·scale·log2 e) is one FMA per score. Only tiles that
     // reach past a wave's first row need the causal mask (a wave-uniform test).
     const bool need_mask = k0 + kPfKeys - 1 > pos0 + wave * 32;
-    V8 phi[2][2], plo[2][2];  // [row tile][k-step of 32 keys]
+    // P operands [row tile][k-step of 32 keys]: the only part (f16) or the high part and the
+    // remainder (bf16)
+    constexpr bool kSplitP = DT == DT_BF16;
+    V8 phi[2][2], plo[2][2];
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
       if (need_mask) {
@@ -405,13 +409,18 @@ __global__ __launch_bounds__(kPfThreads, 2) void ragged_prefill_kernel(PrefillAr
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
           const int e = 2 * w;
-          uint32_t h, l;
-          split_pair<DT>(p[2 * j + (e >> 2)][e & 3], p[2 * j + (e >> 2)][(e & 3) + 1], h, l);
-          hw[w] = h;
-          lw[w] = l;
+          const float x0 = p[2 * j + (e >> 2)][e & 3], x1 = p[2 * j + (e >> 2)][(e & 3) + 1];
+          if constexpr (kSplitP) {
+            uint32_t h, l;
+            split_pair_bf16(x0, x1, h, l);
+            hw[w] = h;
+            lw[w] = l;
+          } else {
+            hw[w] = pack_f16(x0, x1);
+          }
         }
         phi[nt][j] = __builtin_bit_cast(V8, hw);
-        plo[nt][j] = __builtin_bit_cast(V8, lw);
+        if constexpr (kSplitP) plo[nt][j] = __builtin_bit_cast(V8, lw);
       }
     }
 
@@ -425,7 +434,8 @@ __global__ __launch_bounds__(kPfThreads, 2) void ragged_prefill_kernel(PrefillAr
     }
 
     // ---- Oᵀ += Vᵀ·Pᵀ with the same key order in both operands ---------------------------------
-    // Step st = (dt, j) reads one V operand and feeds four MFMAs; reads run ahead as above.
+    // Step st = (dt, j) reads one V operand and feeds two MFMAs per row tile with a split P (one
+    // otherwise); reads run ahead as above.
     {
       constexpr int NPV = DT16 * 2;
       auto vread = [&](int st) {
@@ -445,7 +455,7 @@ __global__ __launch_bounds__(kPfThreads, 2) void ragged_prefill_kernel(PrefillAr
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) {
           oacc[dt][nt] = M::mma(va, phi[nt][j], oacc[dt][nt]);
-          oacc[dt][nt] = M::mma(va, plo[nt][j], oacc[dt][nt]);
+          if constexpr (kSplitP) oacc[dt][nt] = M::mma(va, plo[nt][j], oacc[dt][nt]);
         }
       }
 #if PF_SCHED
@@ -453,7 +463,7 @@ __global__ __launch_bounds__(kPfThreads, 2) void ragged_prefill_kernel(PrefillAr
 #pragma unroll
       for (int st = 0; st < NPV; ++st) {
         if (st + kPfLookahead < NPV) __builtin_amdgcn_sched_group_barrier(0x100, 1, 2);
-        __builtin_amdgcn_sched_group_barrier(0x008, 4, 2);
+        __builtin_amdgcn_sched_group_barrier(0x008, kSplitP ? 4 : 2, 2);
       }
 #endif
     }
