@@ -12,13 +12,15 @@
 //   online softmax        (row max across the 4 lane groups; fp32; exp2 on log2-scaled scores)
 //   Oᵀ += Vᵀ·Pᵀ          (M = head_dim, N = 32 rows, K = 64 keys)    -> lane holds 4 dims x 1 row
 // The P operand comes straight from the Sᵀ accumulators: MFMA sums over k, so any fixed order of
-// the 32 keys of a k-step works as long as the Vᵀ operand uses the same order. For bf16 pools P
-// is split into a bf16 high part and a bf16 remainder, each multiplied by V, so the products
-// keep about 16 significant bits (one bf16 P, 8 bits, would cost up to ~1e-2 relative on short
-// rows). For f16 pools one f16 P rounded to nearest (11 bits, at most 2^-12 relative) is enough,
-// and Oᵀ takes one MFMA per step instead of two.
+// the 32 keys of a k-step works as long as the Vᵀ operand uses the same order. P goes to MFMA as
+// f16 rounded to nearest (11 bits, at most 2^-12 relative; one bf16 P, 8 bits, would cost up to
+// ~1e-2 relative on short rows), so Vᵀ is staged as f16 too: a bf16 pool's values are converted,
+// which is exact inside the f16 range. A tile whose V leaves that range is recomputed with bf16
+// Vᵀ and P split into a bf16 high part and remainder (two MFMAs per step, about 16 bits).
 // A query row at position p sees keys 0..p (the block-wise equation's ⌈i/B⌉ limit,
 // 「PagedAttention原理」 §实现一个虚拟内存).
+#include <type_traits>
+
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -218,256 +220,294 @@ __global__ __launch_bounds__(kPfThreads, 2) void ragged_prefill_kernel(PrefillAr
   }
 
   f32x4 oacc[DT16][2];
-#pragma unroll
-  for (int dt = 0; dt < DT16; ++dt)
-#pragma unroll
-    for (int nt = 0; nt < 2; ++nt) oacc[dt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run[2] = {-INFINITY, -INFINITY};    // reference max of each row (raw score units)
+  float m_run[2];                              // reference max of each row (raw score units)
   const float lazy_thr = 8.f / a.scale_log2;  // 2^8 in probability terms, in raw score units
-  float l_part[2] = {0.f, 0.f};  // this lane's share of the row sum (its 4-key slices)
+  float l_part[2];                             // this lane's share of the row sum (its 4-key slices)
 
   const int32_t* trow = a.tables + (size_t)s * a.max_blocks;
   const uint32_t blk_elems = (uint32_t)(a.hkv * a.bs * D);  // elements of one pool block
   const uint32_t head_off = (uint32_t)(kvh * a.bs * D);      // this kv head's rows in a block
   const int nblk = (kend + a.bs - 1) >> a.log2_bs;
-  int tab_base = -kPfTab;  // first table entry held in s_tab
 
-  // Global -> register staging of one key tile. Keys past kend are clamped to key kend-1 (a
-  // written row, so finite): such keys are masked for every row that is stored, and their V
-  // rows meet a zero probability. All loads are unconditional, so their table lookups and
-  // addresses are computed together and the loads issue back to back.
-  u32x4 kreg[KIT];
-  u32x4 vreg[VIT][2];
-  auto fetch = [&](int kt) {
-    const int k0 = kt * kPfKeys;
-    uint32_t inner[KIT], phys[KIT];
+  // The key loop, in one of two modes for Oᵀ = Vᵀ·Pᵀ:
+  //   kSplitP == false: Vᵀ as f16 in LDS (an f16 pool's values, or a bf16 pool's converted: exact
+  //     for |v| in [2^-14, 65504], within 2^-25 below) and one f16 P rounded to nearest: one MFMA
+  //     per step.
+  //   kSplitP == true (bf16 pools only): Vᵀ as bf16 and P as a bf16 high part plus remainder: two
+  //     MFMAs per step, exact for every bf16 value.
+  // A bf16 pool runs the first mode; a value beyond the f16 range becomes infinite there and
+  // reaches every output row of the tile as inf or NaN, and then the workgroup runs the key
+  // loop again in the second mode.
+  auto run_keys = [&](auto split_mode) {
+    constexpr bool kSplitP = decltype(split_mode)::value;
+    using PV = Mfma<kSplitP ? DT_BF16 : DT_F16>;
+    using PV8 = typename PV::V8;
 #pragma unroll
-    for (int it = 0; it < KIT; ++it) {
-      const int kk = min(k0 + (it * kPfThreads + tid) / CPR, kend - 1);
-      phys[it] = (uint32_t)s_tab[(kk >> a.log2_bs) - tab_base];
-      inner[it] = head_off + (uint32_t)(kk & (a.bs - 1)) * D + ((it * kPfThreads + tid) % CPR) * 8;
-    }
-    // Every V chunk of this thread covers the same key pair (kp = tid mod 32); the pair shares
-    // a block because B is even.
-    const int kv0 = min(k0 + 2 * (tid & (kPfKeys / 2 - 1)), kend - 1);
-    const int kv1 = min(k0 + 2 * (tid & (kPfKeys / 2 - 1)) + 1, kend - 1);
-    const uint32_t vphys = (uint32_t)s_tab[(kv0 >> a.log2_bs) - tab_base];
-    const uint64_t vbase = (uint64_t)vphys * blk_elems + head_off;
-    const uint32_t v0 = (uint32_t)(kv0 & (a.bs - 1)) * D, v1 = (uint32_t)(kv1 & (a.bs - 1)) * D;
+    for (int dt = 0; dt < DT16; ++dt)
 #pragma unroll
-    for (int it = 0; it < KIT; ++it)
-      kreg[it] = *reinterpret_cast<const u32x4*>(a.kc + ((uint64_t)phys[it] * blk_elems + inner[it]));
+      for (int nt = 0; nt < 2; ++nt) oacc[dt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    m_run[0] = m_run[1] = -INFINITY;
+    l_part[0] = l_part[1] = 0.f;
+    int tab_base = -kPfTab;  // first table entry held in s_tab
+
+    // Global -> register staging of one key tile. Keys past kend are clamped to key kend-1 (a
+    // written row, so finite): such keys are masked for every row that is stored, and their V
+    // rows meet a zero probability. All loads are unconditional, so their table lookups and
+    // addresses are computed together and the loads issue back to back.
+    u32x4 kreg[KIT];
+    u32x4 vreg[VIT][2];
+    auto fetch = [&](int kt) {
+      const int k0 = kt * kPfKeys;
+      uint32_t inner[KIT], phys[KIT];
 #pragma unroll
-    for (int it = 0; it < VIT; ++it) {
-      const uint32_t ch8 = ((it * kPfThreads + tid) / (kPfKeys / 2)) * 8;
-      vreg[it][0] = *reinterpret_cast<const u32x4*>(a.vc + (vbase + v0 + ch8));
-      vreg[it][1] = *reinterpret_cast<const u32x4*>(a.vc + (vbase + v1 + ch8));
-    }
-  };
-  // Registers -> LDS buffer b: K row-major, V transposed (word = two adjacent keys).
-  auto stage = [&](int b) {
-    uint16_t* k_dst = sK + b * KBUF;
-    uint16_t* v_dst = sVt + b * VBUF;
-#pragma unroll
-    for (int it = 0; it < KIT; ++it) {
-      const int idx = it * kPfThreads + tid;
-      const int key = idx / CPR;
-      const int ch = idx - key * CPR;
-      *reinterpret_cast<u32x4*>(&k_dst[key * KLD + ch * 8]) = kreg[it];
-    }
-#pragma unroll
-    for (int it = 0; it < VIT; ++it) {
-      const int idx = it * kPfThreads + tid;
-      const int kp = idx & (kPfKeys / 2 - 1);
-      const int ch = idx / (kPfKeys / 2);
-      const u32x4 w0 = vreg[it][0], w1 = vreg[it][1];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint32_t lo = __builtin_amdgcn_perm(w1[e], w0[e], 0x05040100u);  // low halves
-        const uint32_t hi = __builtin_amdgcn_perm(w1[e], w0[e], 0x07060302u);  // high halves
-        *reinterpret_cast<uint32_t*>(&v_dst[(ch * 8 + 2 * e) * VLD + 2 * kp]) = lo;
-        *reinterpret_cast<uint32_t*>(&v_dst[(ch * 8 + 2 * e + 1) * VLD + 2 * kp]) = hi;
+      for (int it = 0; it < KIT; ++it) {
+        const int kk = min(k0 + (it * kPfThreads + tid) / CPR, kend - 1);
+        phys[it] = (uint32_t)s_tab[(kk >> a.log2_bs) - tab_base];
+        inner[it] = head_off + (uint32_t)(kk & (a.bs - 1)) * D + ((it * kPfThreads + tid) % CPR) * 8;
       }
-    }
-  };
-  // Makes s_tab hold the entries of key tiles kt (and kt+1 when it is in range). Uniform.
-  auto ensure_table = [&](int kt) {
-    const int jlo = (kt * kPfKeys) >> a.log2_bs;
-    const int jhi = min(nblk, (min(kt + 2, nkt) * kPfKeys + a.bs - 1) >> a.log2_bs);
-    if (jlo >= tab_base && jhi <= tab_base + kPfTab) return;
-    __syncthreads();  // nobody still reads the old entries
-    tab_base = jlo;
-    for (int i = tid; i < kPfTab && jlo + i < nblk; i += kPfThreads) {
-      int b = trow[jlo + i];
-      if (kDebugChecks && (b < 0 || b >= a.num_blocks)) {
-        debug_flag(DBG_BLOCK);
-        b = 0;
+      // Every V chunk of this thread covers the same key pair (kp = tid mod 32); the pair shares
+      // a block because B is even.
+      const int kv0 = min(k0 + 2 * (tid & (kPfKeys / 2 - 1)), kend - 1);
+      const int kv1 = min(k0 + 2 * (tid & (kPfKeys / 2 - 1)) + 1, kend - 1);
+      const uint32_t vphys = (uint32_t)s_tab[(kv0 >> a.log2_bs) - tab_base];
+      const uint64_t vbase = (uint64_t)vphys * blk_elems + head_off;
+      const uint32_t v0 = (uint32_t)(kv0 & (a.bs - 1)) * D, v1 = (uint32_t)(kv1 & (a.bs - 1)) * D;
+#pragma unroll
+      for (int it = 0; it < KIT; ++it)
+        kreg[it] = *reinterpret_cast<const u32x4*>(a.kc + ((uint64_t)phys[it] * blk_elems + inner[it]));
+#pragma unroll
+      for (int it = 0; it < VIT; ++it) {
+        const uint32_t ch8 = ((it * kPfThreads + tid) / (kPfKeys / 2)) * 8;
+        vreg[it][0] = *reinterpret_cast<const u32x4*>(a.vc + (vbase + v0 + ch8));
+        vreg[it][1] = *reinterpret_cast<const u32x4*>(a.vc + (vbase + v1 + ch8));
       }
-      s_tab[i] = b;
+    };
+    // Registers -> LDS buffer b: K row-major, V transposed (word = two adjacent keys).
+    auto stage = [&](int b) {
+      uint16_t* k_dst = sK + b * KBUF;
+      uint16_t* v_dst = sVt + b * VBUF;
+#pragma unroll
+      for (int it = 0; it < KIT; ++it) {
+        const int idx = it * kPfThreads + tid;
+        const int key = idx / CPR;
+        const int ch = idx - key * CPR;
+        *reinterpret_cast<u32x4*>(&k_dst[key * KLD + ch * 8]) = kreg[it];
+      }
+#pragma unroll
+      for (int it = 0; it < VIT; ++it) {
+        const int idx = it * kPfThreads + tid;
+        const int kp = idx & (kPfKeys / 2 - 1);
+        const int ch = idx / (kPfKeys / 2);
+        const u32x4 w0 = vreg[it][0], w1 = vreg[it][1];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          uint32_t lo, hi;  // dims ch*8 + 2e and ch*8 + 2e + 1 of keys kv0 (low half), kv1
+          if constexpr (DT == DT_BF16 && !kSplitP) {
+            // bf16 -> f32 is a shift into the upper half; f32 -> f16 rounds to nearest
+            lo = pack_f16(__uint_as_float(w0[e] << 16), __uint_as_float(w1[e] << 16));
+            hi = pack_f16(__uint_as_float(w0[e] & 0xffff0000u), __uint_as_float(w1[e] & 0xffff0000u));
+          } else {
+            lo = __builtin_amdgcn_perm(w1[e], w0[e], 0x05040100u);  // low halves
+            hi = __builtin_amdgcn_perm(w1[e], w0[e], 0x07060302u);  // high halves
+          }
+          *reinterpret_cast<uint32_t*>(&v_dst[(ch * 8 + 2 * e) * VLD + 2 * kp]) = lo;
+          *reinterpret_cast<uint32_t*>(&v_dst[(ch * 8 + 2 * e + 1) * VLD + 2 * kp]) = hi;
+        }
+      }
+    };
+    // Makes s_tab hold the entries of key tiles kt (and kt+1 when it is in range). Uniform.
+    auto ensure_table = [&](int kt) {
+      const int jlo = (kt * kPfKeys) >> a.log2_bs;
+      const int jhi = min(nblk, (min(kt + 2, nkt) * kPfKeys + a.bs - 1) >> a.log2_bs);
+      if (jlo >= tab_base && jhi <= tab_base + kPfTab) return;
+      __syncthreads();  // nobody still reads the old entries
+      tab_base = jlo;
+      for (int i = tid; i < kPfTab && jlo + i < nblk; i += kPfThreads) {
+        int b = trow[jlo + i];
+        if (kDebugChecks && (b < 0 || b >= a.num_blocks)) {
+          debug_flag(DBG_BLOCK);
+          b = 0;
+        }
+        s_tab[i] = b;
+      }
+      __syncthreads();
+    };
+
+    // Two LDS buffers: tile kt is computed from buffer kt&1 while tile kt+1 (loaded into registers
+    // during the previous tile) is staged into the other one and tile kt+2's loads go out. One
+    // barrier per tile separates a buffer's last reads from its next writes.
+    if (nkt > 0) {  // nkt <= 0 only when a context is shorter than its query rows: nothing to read
+      ensure_table(0);
+      fetch(0);
+      stage(0);
     }
     __syncthreads();
-  };
+    if (nkt > 1) fetch(1);
+    for (int kt = 0; kt < nkt; ++kt) {
+      const int k0 = kt * kPfKeys;
+      const uint16_t* cK = sK + (kt & 1) * KBUF;
+      const uint16_t* cV = sVt + (kt & 1) * VBUF;
 
-  // Two LDS buffers: tile kt is computed from buffer kt&1 while tile kt+1 (loaded into registers
-  // during the previous tile) is staged into the other one and tile kt+2's loads go out. One
-  // barrier per tile separates a buffer's last reads from its next writes.
-  if (nkt > 0) {  // nkt <= 0 only when a context is shorter than its query rows: nothing to read
-    ensure_table(0);
-    fetch(0);
-    stage(0);
-  }
-  __syncthreads();
-  if (nkt > 1) fetch(1);
-  for (int kt = 0; kt < nkt; ++kt) {
-    const int k0 = kt * kPfKeys;
-    const uint16_t* cK = sK + (kt & 1) * KBUF;
-    const uint16_t* cV = sVt + (kt & 1) * VBUF;
-
-    // ---- Sᵀ = K·Qᵀ: 4 key tiles x 2 row tiles -------------------------------------------------
-    // Step st = (mt, ks) reads one K operand and feeds two MFMAs; operand reads run kPfLookahead
-    // steps ahead of their MFMAs so that LDS latency overlaps matrix work.
-    constexpr int NQK = 4 * KS;
-    auto kread = [&](int st) {
-      return __builtin_bit_cast(
-          V8, *reinterpret_cast<const u32x4*>(&cK[(16 * (st / KS) + lr) * KLD + 32 * (st % KS) + 8 * g]));
-    };
-    f32x4 sacc[4][2];
-    {
-      V8 kop[kPfLookahead + 1];
+      // ---- Sᵀ = K·Qᵀ: 4 key tiles x 2 row tiles -------------------------------------------------
+      // Step st = (mt, ks) reads one K operand and feeds two MFMAs; operand reads run kPfLookahead
+      // steps ahead of their MFMAs so that LDS latency overlaps matrix work.
+      constexpr int NQK = 4 * KS;
+      auto kread = [&](int st) {
+        return __builtin_bit_cast(
+            V8, *reinterpret_cast<const u32x4*>(&cK[(16 * (st / KS) + lr) * KLD + 32 * (st % KS) + 8 * g]));
+      };
+      f32x4 sacc[4][2];
+      {
+        V8 kop[kPfLookahead + 1];
 #pragma unroll
-      for (int i = 0; i < kPfLookahead; ++i) kop[i] = kread(i);
+        for (int i = 0; i < kPfLookahead; ++i) kop[i] = kread(i);
 #pragma unroll
-      for (int st = 0; st < NQK; ++st) {
-        if (st + kPfLookahead < NQK) kop[(st + kPfLookahead) % (kPfLookahead + 1)] = kread(st + kPfLookahead);
-        const int mt = st / KS, ks = st % KS;
-        const V8 ka = kop[st % (kPfLookahead + 1)];
+        for (int st = 0; st < NQK; ++st) {
+          if (st + kPfLookahead < NQK) kop[(st + kPfLookahead) % (kPfLookahead + 1)] = kread(st + kPfLookahead);
+          const int mt = st / KS, ks = st % KS;
+          const V8 ka = kop[st % (kPfLookahead + 1)];
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt)
-          sacc[mt][nt] = M::mma(ka, qb[nt][ks], ks == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : sacc[mt][nt]);
-      }
+          for (int nt = 0; nt < 2; ++nt)
+            sacc[mt][nt] = M::mma(ka, qb[nt][ks], ks == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : sacc[mt][nt]);
+        }
 #if PF_SCHED
-      __builtin_amdgcn_sched_group_barrier(0x100, kPfLookahead, 1);
+        __builtin_amdgcn_sched_group_barrier(0x100, kPfLookahead, 1);
 #pragma unroll
-      for (int st = 0; st < NQK; ++st) {
-        if (st + kPfLookahead < NQK) __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
-        __builtin_amdgcn_sched_group_barrier(0x008, 2, 1);
-      }
+        for (int st = 0; st < NQK; ++st) {
+          if (st + kPfLookahead < NQK) __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
+          __builtin_amdgcn_sched_group_barrier(0x008, 2, 1);
+        }
 #endif
-    }
+      }
 
-    // ---- causal mask and online softmax (per query row = per lane column) ----------------------
-    // Scores stay unscaled here; exp2((s - m)·scale·log2 e) is one FMA per score. Only tiles that
-    // reach past a wave's first row need the causal mask (a wave-uniform test).
-    const bool need_mask = k0 + kPfKeys - 1 > pos0 + wave * 32;
-    // P operands [row tile][k-step of 32 keys]: the only part (f16) or the high part and the
-    // remainder (bf16)
-    constexpr bool kSplitP = DT == DT_BF16;
-    V8 phi[2][2], plo[2][2];
+      // ---- causal mask and online softmax (per query row = per lane column) ----------------------
+      // Scores stay unscaled here; exp2((s - m)·scale·log2 e) is one FMA per score. Only tiles that
+      // reach past a wave's first row need the causal mask (a wave-uniform test).
+      const bool need_mask = k0 + kPfKeys - 1 > pos0 + wave * 32;
+      // P operands [row tile][k-step of 32 keys]: the only part (f16) or the high part and the
+      // remainder (bf16)
+      PV8 phi[2][2], plo[2][2];
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-      if (need_mask) {
+      for (int nt = 0; nt < 2; ++nt) {
+        if (need_mask) {
+#pragma unroll
+          for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              if (k0 + 16 * mt + 4 * g + i > qpos[nt]) sacc[mt][nt][i] = -INFINITY;
+        }
+        float mx = -INFINITY;
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+          mx = fmaxf(fmaxf(mx, fmaxf(sacc[mt][nt][0], sacc[mt][nt][1])), fmaxf(sacc[mt][nt][2], sacc[mt][nt][3]));
+        mx = max_rows4(mx);
+        // Lazy rescaling: the reference max m_run only moves when some row's tile max exceeds it by
+        // more than 2^8 in probability terms; until then probabilities may reach 2^8, which fp32
+        // sums and the 16-bit split represent as well as values below 1. A row with no visible key
+        // yet keeps m_run = -inf (its probabilities are exactly 0).
+        const bool grow = mx > m_run[nt] + lazy_thr;
+        if (__builtin_amdgcn_read_exec() & __ballot(grow)) {  // wave-uniform
+          const float m_new = fmaxf(m_run[nt], mx);
+          const float alpha = m_run[nt] == -INFINITY ? 0.f : fast_exp2((m_run[nt] - m_new) * a.scale_log2);
+          m_run[nt] = m_new;
+          l_part[nt] *= alpha;
+#pragma unroll
+          for (int dt = 0; dt < DT16; ++dt) oacc[dt][nt] *= alpha;
+        }
+        const float off = -(m_run[nt] == -INFINITY ? 0.f : m_run[nt]) * a.scale_log2;
+        float lsum = 0.f;
+        float p[4][4];
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
-            if (k0 + 16 * mt + 4 * g + i > qpos[nt]) sacc[mt][nt][i] = -INFINITY;
-      }
-      float mx = -INFINITY;
+          for (int i = 0; i < 4; ++i) {
+            p[mt][i] = fast_exp2(__builtin_fmaf(sacc[mt][nt][i], a.scale_log2, off));
+            lsum += p[mt][i];
+          }
+        l_part[nt] += lsum;
+        // B operand of k-step j: keys 32j + 4g + (0..3) then 32j + 16 + 4g + (0..3); element e of
+        // the operand is the low (e even) or high half of word e/2.
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-        mx = fmaxf(fmaxf(mx, fmaxf(sacc[mt][nt][0], sacc[mt][nt][1])), fmaxf(sacc[mt][nt][2], sacc[mt][nt][3]));
-      mx = max_rows4(mx);
-      // Lazy rescaling: the reference max m_run only moves when some row's tile max exceeds it by
-      // more than 2^8 in probability terms; until then probabilities may reach 2^8, which fp32
-      // sums and the 16-bit split represent as well as values below 1. A row with no visible key
-      // yet keeps m_run = -inf (its probabilities are exactly 0).
-      const bool grow = mx > m_run[nt] + lazy_thr;
-      if (__builtin_amdgcn_read_exec() & __ballot(grow)) {  // wave-uniform
-        const float m_new = fmaxf(m_run[nt], mx);
-        const float alpha = m_run[nt] == -INFINITY ? 0.f : fast_exp2((m_run[nt] - m_new) * a.scale_log2);
-        m_run[nt] = m_new;
-        l_part[nt] *= alpha;
+        for (int j = 0; j < 2; ++j) {
+          u32x4 hw, lw;
 #pragma unroll
-        for (int dt = 0; dt < DT16; ++dt) oacc[dt][nt] *= alpha;
-      }
-      const float off = -(m_run[nt] == -INFINITY ? 0.f : m_run[nt]) * a.scale_log2;
-      float lsum = 0.f;
-      float p[4][4];
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          p[mt][i] = fast_exp2(__builtin_fmaf(sacc[mt][nt][i], a.scale_log2, off));
-          lsum += p[mt][i];
+          for (int w = 0; w < 4; ++w) {
+            const int e = 2 * w;
+            const float x0 = p[2 * j + (e >> 2)][e & 3], x1 = p[2 * j + (e >> 2)][(e & 3) + 1];
+            if constexpr (kSplitP) {
+              uint32_t h, l;
+              split_pair_bf16(x0, x1, h, l);
+              hw[w] = h;
+              lw[w] = l;
+            } else {
+              hw[w] = pack_f16(x0, x1);
+            }
+          }
+          phi[nt][j] = __builtin_bit_cast(PV8, hw);
+          if constexpr (kSplitP) plo[nt][j] = __builtin_bit_cast(PV8, lw);
         }
-      l_part[nt] += lsum;
-      // B operand of k-step j: keys 32j + 4g + (0..3) then 32j + 16 + 4g + (0..3); element e of
-      // the operand is the low (e even) or high half of word e/2.
+      }
+
+      // ---- the next tile goes to the other buffer; the one after it starts loading ---------------
+      if (kt + 1 < nkt) {
+        stage((kt + 1) & 1);
+        if (kt + 2 < nkt) {
+          ensure_table(kt + 2);
+          fetch(kt + 2);
+        }
+      }
+
+      // ---- Oᵀ += Vᵀ·Pᵀ with the same key order in both operands ---------------------------------
+      // Step st = (dt, j) reads one V operand and feeds two MFMAs per row tile with a split P (one
+      // otherwise); reads run ahead as above.
+      {
+        constexpr int NPV = DT16 * 2;
+        auto vread = [&](int st) {
+          const uint16_t* vrow = &cV[(16 * (st / 2) + lr) * VLD + 32 * (st % 2) + 4 * g];
+          const u32x2 x0 = *reinterpret_cast<const u32x2*>(vrow);
+          const u32x2 x1 = *reinterpret_cast<const u32x2*>(vrow + 16);
+          return __builtin_bit_cast(PV8, u32x4{x0[0], x0[1], x1[0], x1[1]});
+        };
+        PV8 vop[kPfLookahead + 1];
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        u32x4 hw, lw;
+        for (int i = 0; i < kPfLookahead; ++i) vop[i] = vread(i);
 #pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          const int e = 2 * w;
-          const float x0 = p[2 * j + (e >> 2)][e & 3], x1 = p[2 * j + (e >> 2)][(e & 3) + 1];
-          if constexpr (kSplitP) {
-            uint32_t h, l;
-            split_pair_bf16(x0, x1, h, l);
-            hw[w] = h;
-            lw[w] = l;
-          } else {
-            hw[w] = pack_f16(x0, x1);
+        for (int st = 0; st < NPV; ++st) {
+          if (st + kPfLookahead < NPV) vop[(st + kPfLookahead) % (kPfLookahead + 1)] = vread(st + kPfLookahead);
+          const int dt = st / 2, j = st % 2;
+          const PV8 va = vop[st % (kPfLookahead + 1)];
+#pragma unroll
+          for (int nt = 0; nt < 2; ++nt) {
+            oacc[dt][nt] = PV::mma(va, phi[nt][j], oacc[dt][nt]);
+            if constexpr (kSplitP) oacc[dt][nt] = PV::mma(va, plo[nt][j], oacc[dt][nt]);
           }
         }
-        phi[nt][j] = __builtin_bit_cast(V8, hw);
-        if constexpr (kSplitP) plo[nt][j] = __builtin_bit_cast(V8, lw);
-      }
-    }
-
-    // ---- the next tile goes to the other buffer; the one after it starts loading ---------------
-    if (kt + 1 < nkt) {
-      stage((kt + 1) & 1);
-      if (kt + 2 < nkt) {
-        ensure_table(kt + 2);
-        fetch(kt + 2);
-      }
-    }
-
-    // ---- Oᵀ += Vᵀ·Pᵀ with the same key order in both operands ---------------------------------
-    // Step st = (dt, j) reads one V operand and feeds two MFMAs per row tile with a split P (one
-    // otherwise); reads run ahead as above.
-    {
-      constexpr int NPV = DT16 * 2;
-      auto vread = [&](int st) {
-        const uint16_t* vrow = &cV[(16 * (st / 2) + lr) * VLD + 32 * (st % 2) + 4 * g];
-        const u32x2 x0 = *reinterpret_cast<const u32x2*>(vrow);
-        const u32x2 x1 = *reinterpret_cast<const u32x2*>(vrow + 16);
-        return __builtin_bit_cast(V8, u32x4{x0[0], x0[1], x1[0], x1[1]});
-      };
-      V8 vop[kPfLookahead + 1];
-#pragma unroll
-      for (int i = 0; i < kPfLookahead; ++i) vop[i] = vread(i);
-#pragma unroll
-      for (int st = 0; st < NPV; ++st) {
-        if (st + kPfLookahead < NPV) vop[(st + kPfLookahead) % (kPfLookahead + 1)] = vread(st + kPfLookahead);
-        const int dt = st / 2, j = st % 2;
-        const V8 va = vop[st % (kPfLookahead + 1)];
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt) {
-          oacc[dt][nt] = M::mma(va, phi[nt][j], oacc[dt][nt]);
-          if constexpr (kSplitP) oacc[dt][nt] = M::mma(va, plo[nt][j], oacc[dt][nt]);
-        }
-      }
 #if PF_SCHED
-      __builtin_amdgcn_sched_group_barrier(0x100, kPfLookahead, 2);
+        __builtin_amdgcn_sched_group_barrier(0x100, kPfLookahead, 2);
 #pragma unroll
-      for (int st = 0; st < NPV; ++st) {
-        if (st + kPfLookahead < NPV) __builtin_amdgcn_sched_group_barrier(0x100, 1, 2);
-        __builtin_amdgcn_sched_group_barrier(0x008, kSplitP ? 4 : 2, 2);
-      }
+        for (int st = 0; st < NPV; ++st) {
+          if (st + kPfLookahead < NPV) __builtin_amdgcn_sched_group_barrier(0x100, 1, 2);
+          __builtin_amdgcn_sched_group_barrier(0x008, kSplitP ? 4 : 2, 2);
+        }
 #endif
+      }
+      __syncthreads();  // buffer kt&1 is free for tile kt+2; buffer (kt+1)&1 is complete
     }
-    __syncthreads();  // buffer kt&1 is free for tile kt+2; buffer (kt+1)&1 is complete
+  };  // run_keys
+
+  run_keys(std::false_type{});
+  if constexpr (DT == DT_BF16) {
+    // A value of V beyond the f16 range left inf or NaN in every row's output of this tile. The
+    // test reads the exponent bits as an integer: this file is compiled assuming no NaN, so a
+    // floating-point NaN test could be folded away.
+    uint32_t bad = 0;
+#pragma unroll
+    for (int dt = 0; dt < DT16; ++dt)
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) bad |= (~__float_as_uint(oacc[dt][nt][i]) & 0x7f800000u) == 0u;
+    if (__syncthreads_or((int)bad)) run_keys(std::true_type{});  // uniform over the workgroup
   }
 
   // ---- normalise and store: lane writes dims 16*dt + 4*g .. +3 of its row ----------------------

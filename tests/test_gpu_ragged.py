@@ -137,3 +137,21 @@ def test_ragged_on_caller_stream():
     for w, got in zip(cases, copies):
         _, ref = oracle.run_workload(w)
         _check(w, got, ref)
+
+
+@pytest.mark.parametrize("shift", [10, 17])
+def test_ragged_bf16_values_beyond_f16(shift):
+    """A bf16 V pool scaled by 2^shift (exact). Prefill stages bf16 values as f16: at 2^10 every
+    value still fits; at 2^17 values pass 65504, so every prefill tile is recomputed with bf16 Vᵀ
+    and a split P. Attention is linear in V, so the oracle's output times 2^shift is the
+    reference, with the tolerance scaled alike."""
+    from paged_kv_cache_323_amd import runner as R
+    w = make_ragged_workload(41, [130, 1, 257, 1, 64], [130, 700, 300, 50, 1000], 8, 4, 128, "bf16", 16,
+                             name=f"bf16-v-x2^{shift}")
+    _announce(f"{w.name}")
+    _, ref = oracle.run_workload(w)
+    st = R.play_script(w, threads=16)
+    st.v_cache.mul_(2.0 ** shift)
+    out, _ = R.attention(w, st, "f32")
+    err = _check(w, out, ref * 2.0 ** shift, tol=TOL[w.dtype] * 2.0 ** shift)
+    print(f"  max abs err {err:.3g} (scale 2^{shift})")
