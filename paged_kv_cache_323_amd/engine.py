@@ -150,7 +150,7 @@ class Engine:
         self._ops_add(SwapOutOp([victim]))
         if len(pairs):
             pk.swap_blocks(self.host_k, self.host_v, self.k_cache, self.v_cache,
-                           torch.from_numpy(np.ascontiguousarray(pairs)).to(self.device), self.desc)
+                           self._pairs_to_device(pairs), self.desc)
         self.running.pop()
         self.requests[victim].state = SWAPPED
         self.swapped.appendleft(victim)
@@ -168,7 +168,7 @@ class Engine:
             self._ops_add(SwapInOp([seq]))
             if len(pairs):
                 pk.swap_blocks(self.k_cache, self.v_cache, self.host_k, self.host_v,
-                               torch.from_numpy(np.ascontiguousarray(pairs)).to(self.device), self.desc)
+                               self._pairs_to_device(pairs), self.desc)
             self.swapped.popleft()
             self.requests[seq].state = DECODING
             self.running.append(seq)
@@ -181,12 +181,18 @@ class Engine:
         for seq in [s for s in self.running if self.requests[s].state == FINISHED]:
             self.running.remove(seq)
         self._resume()
-        # admit first come first served (none while preempted requests wait)
-        budget = self.max_step_tokens - sum(1 for s in self.running if self.requests[s].state == DECODING)
+        # Admit first come first served (none while preempted requests wait), while the step's
+        # token budget and the pool both hold the next prompt beside the running decodes' growth:
+        # the longest prefix of the queue that fits.
+        dec = [s for s in self.running if self.requests[s].state == DECODING]
+        budget = self.max_step_tokens - len(dec)
+        free = self.bm.num_free() - (self.bm.blocks_needed(dec, [1] * len(dec)) if dec else 0)
         while (self.waiting and not self.swapped and len(self.running) < self.max_num_seqs):
             req = self.requests[self.waiting[0]]
-            if req.prompt_len > budget:
+            need = -(-req.prompt_len // self.B)
+            if req.prompt_len > budget or need > free:
                 break
+            free -= need
             self.waiting.popleft()
             self.bm.add_seq(req.seq)
             self._ops_add(AddOp(req.seq))
@@ -260,6 +266,13 @@ class Engine:
         return w
 
     # ---- per-step uploads -----------------------------------------------------------------------
+    def _pairs_to_device(self, pairs) -> torch.Tensor:
+        """A (src, dst) pair list on the device, copied asynchronously from pinned memory (torch's
+        pinned allocator keeps the host block until the copy has run), so the host does not wait
+        for the GPU here."""
+        host = torch.from_numpy(np.ascontiguousarray(pairs, dtype=np.int32)).pin_memory()
+        return host.to(self.device, non_blocking=True)
+
     def _staging(self, n: int) -> np.ndarray:
         """An int32 view of n elements of the pinned staging buffer for this step."""
         i = self.step_idx & 1
@@ -296,7 +309,7 @@ class Engine:
         slots, pairs = self.bm.append(seqs, ns)
         self._ops_add(AppendOp(list(seqs), list(ns), tag))
         if len(pairs):
-            pk.copy_blocks(self.k_cache, self.v_cache, torch.from_numpy(np.ascontiguousarray(pairs)).to(self.device),
+            pk.copy_blocks(self.k_cache, self.v_cache, self._pairs_to_device(pairs),
                            self.desc)
         k, v = self._kv(seqs, ns, tag)
         S, T = len(seqs), len(slots)
@@ -322,7 +335,7 @@ class Engine:
             self.ws = torch.zeros(nbytes, dtype=torch.uint8, device=self.device)
         pk.paged_attention_ragged(out, q, cu_d, lens_d, self.k_cache, self.v_cache, tab_d, self.scale,
                                   max_q, max_ctx, self.desc, self.ws)
-        rec = StepRecord(self.step_idx, list(seqs), list(ns), [int(x) for x in lens], len(self.ops),
+        rec = StepRecord(self.step_idx, list(seqs), list(ns), lens.tolist(), len(self.ops),
                          out if self.keep_outputs else None)
         self.records.append(rec)
         # every row group yields one generated token (the prompt's last row, or the decode row)
