@@ -53,6 +53,8 @@ def _run(cmd):
 
 def build(verbose: bool = False, jobs: int = 8, defines=(), out: str = LIB, build_dir: str = BUILD) -> str:
     """Compile and link; ``defines`` are extra -D macros (kernel tuning knobs)."""
+    if not out.endswith(".so"):
+        raise ValueError(f"output must be a .so path, got {out!r}")
     if not os.path.exists(HIPCC):
         raise RuntimeError(f"hipcc not found at {HIPCC}")
     os.makedirs(build_dir, exist_ok=True)
@@ -85,7 +87,8 @@ PROBE_LIB = os.path.join(PKG, "libpkv_probe.so")
 
 
 def build_probe() -> str:
-    """The benchmark's streaming-read probe (its own small library, outside libpagedkv)."""
+    """The benchmark's streaming-read and tile-gather probes (their own small library, outside
+    libpagedkv)."""
     tmp = PROBE_LIB + ".tmp"
     _run([HIPCC, *HIP_FLAGS, "-shared", PROBE_SRC, "-o", tmp])
     os.replace(tmp, PROBE_LIB)
