@@ -153,8 +153,8 @@ size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t
 
 /* Tokens per context partition the decode kernel uses for these arguments
  * (partition_size argument 0 of the _ex entry point). It starts from max_context_len rounded up
- * to a multiple of 64 when that fits the largest partition for the head grouping, else that
- * largest partition; while num_seqs x num_kv_heads x ceil(max_context_len / partition) is below
+ * to a multiple of 64 when that fits min(4096, the largest partition for the head grouping),
+ * else that size; while num_seqs x num_kv_heads x ceil(max_context_len / partition) is below
  * 512 workgroups (two per CU), it is halved (rounded up to a multiple of 64), down to 256, so a
  * small batch of long contexts still fills the GPU. The largest partition is
  * 8192 / (num_q_heads / num_kv_heads) tokens: 8192, 4096, 2048 and 1024 for 1, 2, 4 and 8 query

@@ -82,6 +82,7 @@ def test_decode_workspace_validation():
     assert L.pkv_decode_workspace_bytes(512, 4, 256, ctypes.byref(c)) == 0  # never more than one partition
     assert L.pkv_decode_workspace_bytes(0, 4, 8000, ctypes.byref(c)) == 0
     assert L.pkv_decode_workspace_bytes_ex(512, 4, 8000, ctypes.byref(c), 8192) == 0  # one partition: none
+    assert L.pkv_decode_workspace_bytes(512, 4, 8000, ctypes.byref(c)) > 0  # automatic: two of 4096
     assert L.pkv_decode_workspace_bytes_ex(512, 16, 8000, ctypes.byref(c), 2048) > 0
     assert decode(c, part=100) == -1      # not a multiple of 64
     assert decode(c, part=8192 + 64) == -1            # too large for 1 query head per kv head
@@ -94,11 +95,12 @@ def test_decode_workspace_validation():
 def test_partition_size_rule():
     c = desc()  # 4 kv heads
     size = lambda S, hq, ctx: L.pkv_decode_partition_size(S, hq, ctx, ctypes.byref(c))
-    # enough sequences to fill the GPU: the largest partition for the head grouping
+    # enough sequences to fill the GPU: the largest partition for the head grouping, at most 4096
     assert size(512, 4, 100) == 128
     assert size(512, 4, 0) == 64
-    assert size(512, 4, 5000) == 5056     # fits one partition of up to 8192
-    assert size(512, 4, 10000) == 8192
+    assert size(512, 4, 4000) == 4032     # fits one partition of up to 4096
+    assert size(512, 4, 5000) == 4096
+    assert size(512, 4, 10000) == 4096
     assert size(512, 8, 5000) == 4096
     assert size(512, 16, 1000) == 1024
     assert size(512, 16, 5000) == 2048
@@ -126,7 +128,7 @@ def test_auto_workspace_covers_smaller_calls(g, hkv, S, ctx, fs, fc):
     bound = L.pkv_decode_workspace_bytes(S, hq, ctx, ctypes.byref(c))
     for s_, c_ in ((S, ctx), (S2, ctx), (S, ctx2), (S2, ctx2)):
         p = L.pkv_decode_partition_size(s_, hq, c_, ctypes.byref(c))
-        assert p >= 64 and p % 64 == 0 and p <= 8192 // g
+        assert p >= 64 and p % 64 == 0 and p <= min(8192 // g, 4096)
         need = L.pkv_decode_workspace_bytes_ex(s_, hq, c_, ctypes.byref(c), p)
         assert need <= bound, (s_, c_, p, need, bound)
 
