@@ -30,9 +30,10 @@ HIP_FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-function", "-Wno-unused-variable",
 ]
-# Per-source extra flags. The prefill kernel never sees a NaN (its clamped keys are written rows
-# and masking selects by position), so it runs with IEEE mode off: fmax then needs no quieting
-# of its operands, which would otherwise cost one extra instruction per score.
+# Per-source extra flags. The prefill kernel's scores are never NaN (its clamped keys are written
+# rows and masking selects by position), so it runs with IEEE mode off: fmax then needs no
+# quieting of its operands, which would otherwise cost one extra instruction per score. Its one
+# inf/NaN test (a V value beyond the f16 range) reads exponent bits as integers.
 FILE_FLAGS = {"ragged.hip": ["-mno-amdgpu-ieee", "-fno-honor-nans"]}
 HOST_FLAGS = ["-O2", "-fPIC", "-std=c++17", "-Wall", "-I", INCLUDE]
 

@@ -143,10 +143,6 @@ class Workload:
     def is_decode(self) -> bool:
         return all(n == 1 for n in self.q_lens)
 
-    @property
-    def num_query_tokens(self) -> int:
-        return int(sum(self.q_lens))
-
     def cu_seqlens(self) -> np.ndarray:
         return np.concatenate([[0], np.cumsum(self.q_lens)]).astype(np.int32)
 
