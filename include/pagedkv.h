@@ -285,8 +285,9 @@ size_t pkv_decode_workspace_bytes_ex(int32_t num_seqs, int32_t num_q_heads,
  *   context_lens  device int32 [num_seqs], context_lens[s] >= q_len_s.
  *   max_q_len, max_context_len  host upper bounds (launch sizing only).
  *   scale         multiplier of q·k, positive and finite.
- *   Rows of prefill chunks (q_len > 1) need an f16 or bf16 pool (PKV_EDTYPE for f32); rows of
- *   decode sequences work for every dtype.
+ *   Every dtype serves every row. f16/bf16 prefill chunks (q_len > 1) run on MFMA; with an f32
+ *   pool and max_q_len > 1 every row runs through the decode kernels in fp32, one query row
+ *   per item (at most 65535 rows in one call, PKV_ESHAPE beyond).
  *   workspace     device, >= pkv_ragged_workspace_bytes(...) bytes (NULL when that is 0);
  *                 scratch between calls, as for decode.
  */

@@ -226,7 +226,7 @@ static int32_t decode_common_cu(void* out, int32_t out_dtype, const void* q, con
                                 int32_t max_context_len, const pkv_cache_desc* c, int32_t partition_size,
                                 void* workspace, size_t workspace_bytes, void* stream, const int32_t* cu,
                                 int stage = 0, int32_t num_rows = -1, const int32_t* items = nullptr,
-                                int32_t num_items = 0) {
+                                int32_t num_items = 0, bool causal_rows = false) {
   int32_t st = check_cache(c);
   if (st != PKV_OK) return st;
   if ((st = check_heads(num_q_heads, c)) != PKV_OK) return st;
@@ -237,12 +237,16 @@ static int32_t decode_common_cu(void* out, int32_t out_dtype, const void* q, con
   if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens) return PKV_EINVAL;
   if ((int64_t)max_blocks_per_seq * c->block_size < max_context_len) return PKV_EINVAL;
   if (!(scale > 0.f) || !(scale < INFINITY)) return PKV_EINVAL;  // a positive, finite multiplier
+  // Items of the launch: sequences, or in causal-rows mode the query rows of a ragged batch.
+  if (causal_rows && (!cu || num_rows < 1)) return PKV_EINVAL;
+  if (causal_rows && num_rows > 65535) return PKV_ESHAPE;
+  const int32_t n_items = causal_rows ? num_rows : num_seqs;
   const int p = partition_size > 0 ? partition_size
-                                   : pkv_decode_partition_size(num_seqs, num_q_heads, max_context_len, c);
+                                   : pkv_decode_partition_size(n_items, num_q_heads, max_context_len, c);
   if (!valid_partition(p, c->block_size, num_q_heads / c->num_kv_heads)) return PKV_EINVAL;
   const int max_parts = max_context_len > 0 ? (max_context_len + p - 1) / p : 1;
   if (max_parts > 65535) return PKV_ESHAPE;
-  const DecodeWs ws = decode_ws_layout(num_seqs, num_q_heads, c->num_kv_heads, c->head_dim, max_parts);
+  const DecodeWs ws = decode_ws_layout(n_items, num_q_heads, c->num_kv_heads, c->head_dim, max_parts);
   if (ws.total > 0 && (!workspace || workspace_bytes < ws.total)) return PKV_EWORKSPACE;
 
   pkv::DecodeLaunch L;
@@ -272,6 +276,7 @@ static int32_t decode_common_cu(void* out, int32_t out_dtype, const void* q, con
   L.num_rows = num_rows >= 0 ? num_rows : num_seqs;
   L.items = items;
   L.num_items = num_items;
+  L.causal_rows = causal_rows ? 1 : 0;
   return launched(pkv::launch_decode(L, (hipStream_t)stream));
 }
 
@@ -382,8 +387,9 @@ int32_t pkv_paged_attention_decode_merge(void* out, int32_t out_dtype, const voi
 
 size_t pkv_ragged_workspace_bytes(int32_t num_seqs, int32_t num_tokens, int32_t num_q_heads, int32_t max_q_len,
                                   int32_t max_context_len, const pkv_cache_desc* c) {
-  (void)num_tokens;
-  (void)max_q_len;
+  // An fp32 pool serves prefill rows through the decode kernels with one item per query row.
+  if (c && c->dtype == PKV_F32 && max_q_len > 1)
+    return pkv_decode_workspace_bytes_ex(num_tokens, num_q_heads, max_context_len, c, 0);
   return pkv_decode_workspace_bytes_ex(num_seqs, num_q_heads, max_context_len, c, 0);
 }
 
@@ -401,9 +407,13 @@ int32_t pkv_paged_attention_ragged(void* out, int32_t out_dtype, const void* q, 
     return PKV_EINVAL;
   if (num_seqs == 0 || num_tokens == 0) return PKV_OK;
   if (max_q_len > max_context_len || max_q_len > num_tokens) return PKV_EINVAL;
-  // Prefill rows run on 16-bit MFMA; fp32 pools are served only for decode-only batches.
-  if (max_q_len > 1 && c->dtype == PKV_F32) return PKV_EDTYPE;
   if (!out || !q || !cu_seqlens_q || !context_lens || !k_cache || !v_cache || !block_tables) return PKV_EINVAL;
+  // Prefill rows run on 16-bit MFMA. An fp32 pool serves them through the decode kernels instead,
+  // one item per query row attending keys up to its own position (fp32 throughout).
+  if (max_q_len > 1 && c->dtype == PKV_F32)
+    return decode_common_cu(out, out_dtype, q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens,
+                            num_seqs, num_q_heads, scale, max_context_len, c, 0, workspace, workspace_bytes, stream,
+                            cu_seqlens_q, 0, num_tokens, nullptr, 0, true);
   // decode rows (q_len == 1) through the decode kernels with row indirection
   st = decode_common_cu(out, out_dtype, q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens,
                         num_seqs, num_q_heads, scale, max_context_len, c, 0, workspace, workspace_bytes, stream,

@@ -55,7 +55,20 @@ struct DecodeArgs {
   int num_rows;    // rows of q / out (debug builds check ragged row offsets)
   const uint32_t* items;  // work list: item i = seq | part << 16 (null: dense grid)
   int num_seqs;
+  int causal_rows;  // 1: one item per query row of a ragged batch (every row, any q_len)
 };
+
+// Index of the sequence whose query rows cu[s]..cu[s+1]-1 hold `row` (cu non-decreasing, cu[0] =
+// 0): the number of s in 1..num_seqs with cu[s] <= row. Every thread of the 256-thread workgroup
+// calls it; it ends with a barrier. scratch: 4 ints of LDS.
+__device__ __forceinline__ int seq_of_row(const int32_t* cu, int num_seqs, int row, int* scratch) {
+  int c = 0;
+  for (int j = (int)threadIdx.x + 1; j <= num_seqs; j += 256) c += cu[j] <= row ? 1 : 0;
+  for (int off = 32; off > 0; off >>= 1) c += __shfl_xor(c, off);
+  if ((threadIdx.x & 63) == 0) scratch[threadIdx.x >> 6] = c;
+  __syncthreads();
+  return scratch[0] + scratch[1] + scratch[2] + scratch[3];
+}
 
 // Raw words of one lane's slice of a V row (PV mapping): 8, 16 or 32 bytes.
 template <int NWORDS> struct Words { uint32_t w[NWORDS]; };
@@ -123,12 +136,25 @@ __global__ __launch_bounds__(kDecThreads, PKV_DECODE_MIN_WG) void paged_decode_k
   float* const s_red = s_buf;
   __shared__ float s_m[G];
   __shared__ float s_l[G];
+  __shared__ int s_cnt[kDecWaves];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   int kvh, s, part;
-  if (a.items) {
+  int row = -1;  // query / output row; set here in causal-rows mode
+  if (a.causal_rows) {
+    // Causal rows: workgroup x serves kv head x mod Hkv of query row x / Hkv, which attends its
+    // sequence's keys up to and including its own position.
+    row = (int)(blockIdx.x / (uint32_t)a.hkv);
+    kvh = (int)(blockIdx.x - (uint32_t)row * (uint32_t)a.hkv);
+    part = (int)gridDim.z - 1 - (int)blockIdx.z;
+    s = seq_of_row(a.cu, a.num_seqs, row, s_cnt);
+    if (s >= a.num_seqs) {  // offsets that do not cover the row: nothing to do
+      if (kDebugChecks && tid == 0) debug_flag(DBG_RAGGED);
+      return;  // uniform over the workgroup
+    }
+  } else if (a.items) {
     // Work list: workgroup x serves kv head x mod Hkv of item x / Hkv, so the kv heads of one
     // item (which read neighbouring parts of the same blocks) are dispatched together.
     const uint32_t item = blockIdx.x / (uint32_t)a.hkv;
@@ -148,19 +174,24 @@ __global__ __launch_bounds__(kDecThreads, PKV_DECODE_MIN_WG) void paged_decode_k
     part = (int)gridDim.z - 1 - (int)blockIdx.z;
   }
 
-  // In a ragged batch only single-row (decode) sequences are handled here.
-  int row = s;
-  if (a.cu) {
+  int ctx_s = a.ctx_lens[s];
+  if (a.causal_rows) {
+    ctx_s -= a.cu[s + 1] - 1 - row;  // keys 0..this row's position
+  } else if (a.cu) {
+    // In a ragged batch only single-row (decode) sequences are handled here.
     row = a.cu[s];
     if (a.cu[s + 1] - row != 1) return;
     if (kDebugChecks && (row < 0 || row >= a.num_rows)) {
       if (tid == 0) debug_flag(DBG_RAGGED);
       return;  // uniform over the workgroup
     }
+  } else {
+    row = s;
   }
+  const int wi = a.causal_rows ? row : s;  // workspace index of this item's partials
   // A length beyond the table or the launch's partitions breaks the caller's contract; clamping
   // keeps every access inside the table and the workspace.
-  const int ctx = min(a.ctx_lens[s], min(a.max_blocks * a.bs, a.max_parts * a.partition));
+  const int ctx = max(0, min(ctx_s, min(a.max_blocks * a.bs, a.max_parts * a.partition)));
   const int nparts = ctx > 0 ? (ctx + a.partition - 1) / a.partition : 1;
   if (part >= nparts) return;  // uniform over the workgroup
   // Balanced split: the sequence's partitions get equal sizes (a multiple of 64 tokens, so each
@@ -328,7 +359,7 @@ __global__ __launch_bounds__(kDecThreads, PKV_DECODE_MIN_WG) void paged_decode_k
   __syncthreads();
 
   const size_t out_row = (size_t)row * a.hq + (size_t)kvh * G;  // first of the G query heads
-  const size_t item = ((size_t)s * a.hkv + kvh) * a.max_parts + part;
+  const size_t item = ((size_t)wi * a.hkv + kvh) * a.max_parts + part;
   for (int o = tid; o < G * D; o += kDecThreads) {
     float v = 0.f;
 #pragma unroll
@@ -353,25 +384,35 @@ template <int NG>
 __global__ __launch_bounds__(256) void paged_decode_merge_kernel(DecodeArgs a, int head_dim, int group) {
   constexpr int kOuts = 256 / NG;
   __shared__ float s_ml[NG > 1 ? 3 * NG * kOuts : 1];
-  const int s = blockIdx.y;
+  __shared__ int s_cnt[4];
   const int oi = threadIdx.x % kOuts;
   const int grp = threadIdx.x / kOuts;
   const int o = blockIdx.x * kOuts + oi;
   const bool active = o < a.hq * head_dim;
-  int row = s;
-  if (a.cu) {
-    row = a.cu[s];
-    if (a.cu[s + 1] - row != 1) return;                              // uniform over the workgroup
-    if (kDebugChecks && (row < 0 || row >= a.num_rows)) return;  // flagged by the partition kernel
+  int s, row, ctx_s;
+  if (a.causal_rows) {  // workgroup row y: one query row of a ragged batch
+    row = blockIdx.y;
+    s = seq_of_row(a.cu, a.num_seqs, row, s_cnt);
+    if (s >= a.num_seqs) return;  // uniform; flagged by the partition kernel
+    ctx_s = a.ctx_lens[s] - (a.cu[s + 1] - 1 - row);
+  } else {
+    s = blockIdx.y;
+    row = s;
+    if (a.cu) {
+      row = a.cu[s];
+      if (a.cu[s + 1] - row != 1) return;                              // uniform over the workgroup
+      if (kDebugChecks && (row < 0 || row >= a.num_rows)) return;  // flagged by the partition kernel
+    }
+    ctx_s = a.ctx_lens[s];
   }
-  const int ctx = min(a.ctx_lens[s], min(a.max_blocks * a.bs, a.max_parts * a.partition));
+  const int ctx = max(0, min(ctx_s, min(a.max_blocks * a.bs, a.max_parts * a.partition)));
   const int nparts = ctx > 0 ? (ctx + a.partition - 1) / a.partition : 1;
   if (nparts <= 1) return;  // uniform
   const int h = active ? o / head_dim : 0;
   const int kvh = h / group;
   const int g = h - kvh * group;
   const int d = active ? o - h * head_dim : 0;
-  const size_t item = ((size_t)s * a.hkv + kvh) * a.max_parts;
+  const size_t item = ((size_t)(a.causal_rows ? row : s) * a.hkv + kvh) * a.max_parts;
   // This thread's partitions grp, grp + NG, ... are read in chunks of 8 whose loads are all issued
   // before any is used, and merged with a running log-sum-exp.
   constexpr int kChunk = 8;
@@ -452,6 +493,7 @@ static DecodeArgs make_args(const DecodeLaunch& L) {
   a.num_rows = L.num_rows;
   a.items = reinterpret_cast<const uint32_t*>(L.items);
   a.num_seqs = L.num_seqs;
+  a.causal_rows = L.causal_rows;
   return a;
 }
 
@@ -461,8 +503,9 @@ template <int DT, int D, int G>
 static hipError_t launch_decode_t(const DecodeLaunch& L, hipStream_t stream) {
   const DecodeArgs a = make_args(L);
   if (L.stage != 2) {
-    const dim3 grid = L.items ? dim3((unsigned)L.num_items * (unsigned)L.num_kv_heads)
-                              : dim3(L.num_kv_heads, L.num_seqs, L.max_parts);
+    const dim3 grid = L.causal_rows ? dim3((unsigned)L.num_rows * (unsigned)L.num_kv_heads, 1, L.max_parts)
+                      : L.items     ? dim3((unsigned)L.num_items * (unsigned)L.num_kv_heads)
+                                    : dim3(L.num_kv_heads, L.num_seqs, L.max_parts);
     if (!L.items || L.num_items > 0) {
       const hipError_t e = launch_kernel(paged_decode_kernel<DT, D, G, kPrefetch>, grid, dim3(kDecThreads), stream, a);
       if (e != hipSuccess) return e;
@@ -472,7 +515,7 @@ static hipError_t launch_decode_t(const DecodeLaunch& L, hipStream_t stream) {
     const int outs = L.num_q_heads * D;
     // threads per output: enough that each merges at most one chunk of 8 partitions
     const int ng = L.max_parts <= 8 ? 1 : L.max_parts <= 16 ? 2 : L.max_parts <= 32 ? 4 : 8;
-    const dim3 grid((unsigned)((outs * ng + 255) / 256), (unsigned)L.num_seqs);
+    const dim3 grid((unsigned)((outs * ng + 255) / 256), (unsigned)(L.causal_rows ? L.num_rows : L.num_seqs));
     switch (ng) {
       case 1: return launch_kernel(paged_decode_merge_kernel<1>, grid, dim3(256), stream, a, D, G);
       case 2: return launch_kernel(paged_decode_merge_kernel<2>, grid, dim3(256), stream, a, D, G);

@@ -84,6 +84,9 @@ struct DecodeLaunch {
   int num_rows;    // rows of q / out (debug builds check ragged row offsets against it)
   const int32_t* items = nullptr;  // optional work list of (seq | part << 16) for the partition launch
   int num_items = 0;
+  // 1: every query row of a ragged batch (cu set) is its own item and attends keys up to its own
+  // position; partials are indexed by row (num_rows of them)
+  int causal_rows = 0;
 };
 
 hipError_t launch_decode(const DecodeLaunch& a, hipStream_t stream);

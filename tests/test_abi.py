@@ -158,7 +158,14 @@ def ragged(c, hq=4, out_dt=None, S=2, T=5, max_q=3, max_ctx=100, mb=8):
 
 
 def test_ragged_validation():
-    assert ragged(desc(dtype=pk.F32), max_q=3) == -2     # prefill rows need a 16-bit pool
+    # an f32 pool serves prefill rows through the decode kernels, one item per query row
+    assert ragged(desc(dtype=pk.F32), max_q=3, max_ctx=5000, mb=400) == -4  # partials need a workspace
+    assert ragged(desc(dtype=pk.F32), max_q=3, T=70000) == -3               # at most 65535 rows
+    c32 = desc(dtype=pk.F32)
+    rows_ws = L.pkv_ragged_workspace_bytes(2, 5, 4, 3, 5000, ctypes.byref(c32))
+    assert rows_ws == L.pkv_decode_workspace_bytes(5, 4, 5000, ctypes.byref(c32)) > 0  # sized by rows
+    assert L.pkv_ragged_workspace_bytes(2, 5, 4, 1, 5000, ctypes.byref(c32)) == \
+        L.pkv_decode_workspace_bytes(2, 4, 5000, ctypes.byref(c32))                    # decode rows only
     assert ragged(desc(), max_q=200, max_ctx=100) == -1  # q_len cannot exceed the context
     assert ragged(desc(), max_q=6, T=5) == -1            # nor the token count
     assert ragged(desc(), hq=6) == -3

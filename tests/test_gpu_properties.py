@@ -59,7 +59,7 @@ def test_decode_random_shapes(case):
 
 @st.composite
 def ragged_cases(draw):
-    dt = draw(st.sampled_from(["f16", "bf16"]))
+    dt = draw(st.sampled_from(["f16", "bf16", "f32"]))
     B = draw(st.sampled_from([8, 16, 32]))
     d = draw(st.sampled_from([64, 128]))
     hkv = draw(st.sampled_from([1, 2]))

@@ -58,6 +58,10 @@ RAGGED_CASES = [
     ("bf16", 32, 64, 4, 2, [17, 1, 1, 300], [17, 64, 1025, 300]),                       # head_dim 64
     ("f16", 32, 64, 2, 2, [2, 0, 40], [2, 5, 100]),                                     # a sequence with no rows
     ("bf16", 16, 128, 16, 2, [1, 1, 1], [5, 1100, 2500]),                               # decode-only ragged
+    # f32 pools: every row through the decode kernels, one item per query row
+    ("f32", 16, 128, 4, 4, [1, 130, 1, 2, 257, 1], [90, 130, 1, 40, 300, 700]),
+    ("f32", 8, 64, 8, 2, [65, 1, 200, 0], [65, 33, 450, 5]),                            # GQA, empty sequence
+    ("f32", 16, 128, 4, 2, [300, 1], [5000, 3000]),                                     # split partitions
     # a prefill chunk behind 19800 cached tokens at B=8: 2500 blocks, more than the prefill
     # kernel's 1024-entry LDS table window, so the window moves during the key loop
     ("bf16", 8, 64, 4, 2, [200, 1], [20000, 9000]),
