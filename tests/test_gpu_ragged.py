@@ -62,6 +62,7 @@ RAGGED_CASES = [
     ("f32", 16, 128, 4, 4, [1, 130, 1, 2, 257, 1], [90, 130, 1, 40, 300, 700]),
     ("f32", 8, 64, 8, 2, [65, 1, 200, 0], [65, 33, 450, 5]),                            # GQA, empty sequence
     ("f32", 16, 128, 4, 2, [300, 1], [5000, 3000]),                                     # split partitions
+    ("f32", 16, 64, 4, 2, [3, 1], [20000, 500]),      # few rows, many partitions each: 8-thread merge
     # a prefill chunk behind 19800 cached tokens at B=8: 2500 blocks, more than the prefill
     # kernel's 1024-entry LDS table window, so the window moves during the key loop
     ("bf16", 8, 64, 4, 2, [200, 1], [20000, 9000]),
@@ -159,3 +160,17 @@ def test_ragged_bf16_values_beyond_f16(shift):
     out, _ = R.attention(w, st, "f32")
     err = _check(w, out, ref * 2.0 ** shift, tol=TOL[w.dtype] * 2.0 ** shift)
     print(f"  max abs err {err:.3g} (scale 2^{shift})")
+
+
+def test_ragged_f32_many_sequences():
+    """An f32 pool's ragged step over 300 sequences (290 decode rows, 10 prefill chunks): each
+    query row finds its sequence by counting row offsets, which takes two passes over 256 threads."""
+    rng = np.random.default_rng(17)
+    q_lens = [1] * 290 + [5] * 10
+    rng.shuffle(q_lens)
+    ctx = [int(q) + int(rng.integers(0, 300)) for q in q_lens]
+    w = make_ragged_workload(17, q_lens, ctx, 4, 2, 64, "f32", 16, name="ragged-f32-300seqs")
+    _announce(f"{w.name}")
+    _, ref = oracle.run_workload(w)
+    _, out = _run(w)
+    _check(w, out, ref)
