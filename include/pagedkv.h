@@ -285,9 +285,10 @@ size_t pkv_decode_workspace_bytes_ex(int32_t num_seqs, int32_t num_q_heads,
  *   context_lens  device int32 [num_seqs], context_lens[s] >= q_len_s.
  *   max_q_len, max_context_len  host upper bounds (launch sizing only).
  *   scale         multiplier of q·k, positive and finite.
- *   Every dtype serves every row. f16/bf16 prefill chunks (q_len > 1) run on MFMA; with an f32
- *   pool and max_q_len > 1 every row runs through the decode kernels in fp32, one query row
- *   per item (at most 65535 rows in one call, PKV_ESHAPE beyond).
+ *   Every dtype serves every row. f16/bf16 prefill chunks (q_len > 1) run on MFMA, except when
+ *   max_q_len <= num_q_heads / num_kv_heads (and num_tokens <= 65535): then, as always for an
+ *   f32 pool with max_q_len > 1, every row runs through the decode kernels in fp32, one query
+ *   row per item (an f32 pool's call takes at most 65535 rows, PKV_ESHAPE beyond).
  *   workspace     device, >= pkv_ragged_workspace_bytes(...) bytes (NULL when that is 0);
  *                 scratch between calls, as for decode.
  */

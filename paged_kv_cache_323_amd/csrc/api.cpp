@@ -385,12 +385,24 @@ int32_t pkv_paged_attention_decode_merge(void* out, int32_t out_dtype, const voi
                        workspace_bytes, stream, 2);
 }
 
+// Whether a ragged call runs every query row through the decode kernels (causal-rows mode): an
+// fp32 pool with prefill rows (the prefill kernel is 16-bit MFMA), or short chunks only. The
+// prefill kernel works per query head and so reads each kv head's keys and values g times; the
+// decode kernels read them once per query row, so with max_q_len <= g they read no more (measured
+// at g = 4: 188 against 424 us for 2-row chunks, 315 against 432 us for 4, 523 against 433 us for
+// 8). Requires a valid cache and head count.
+static bool ragged_rows_mode(int32_t num_tokens, int32_t num_q_heads, int32_t max_q_len, const pkv_cache_desc* c) {
+  if (max_q_len <= 1) return false;
+  if (c->dtype == PKV_F32) return true;
+  return max_q_len <= num_q_heads / c->num_kv_heads && num_tokens <= 65535;
+}
+
 size_t pkv_ragged_workspace_bytes(int32_t num_seqs, int32_t num_tokens, int32_t num_q_heads, int32_t max_q_len,
                                   int32_t max_context_len, const pkv_cache_desc* c) {
-  // An fp32 pool serves prefill rows through the decode kernels with one item per query row.
-  if (c && c->dtype == PKV_F32 && max_q_len > 1)
-    return pkv_decode_workspace_bytes_ex(num_tokens, num_q_heads, max_context_len, c, 0);
-  return pkv_decode_workspace_bytes_ex(num_seqs, num_q_heads, max_context_len, c, 0);
+  if (check_cache(c) != PKV_OK || check_heads(num_q_heads, c) != PKV_OK) return 0;
+  // one item per query row in causal-rows mode, else per sequence
+  const int32_t items = ragged_rows_mode(num_tokens, num_q_heads, max_q_len, c) ? num_tokens : num_seqs;
+  return pkv_decode_workspace_bytes_ex(items, num_q_heads, max_context_len, c, 0);
 }
 
 int32_t pkv_paged_attention_ragged(void* out, int32_t out_dtype, const void* q, const int32_t* cu_seqlens_q,
@@ -408,9 +420,10 @@ int32_t pkv_paged_attention_ragged(void* out, int32_t out_dtype, const void* q, 
   if (num_seqs == 0 || num_tokens == 0) return PKV_OK;
   if (max_q_len > max_context_len || max_q_len > num_tokens) return PKV_EINVAL;
   if (!out || !q || !cu_seqlens_q || !context_lens || !k_cache || !v_cache || !block_tables) return PKV_EINVAL;
-  // Prefill rows run on 16-bit MFMA. An fp32 pool serves them through the decode kernels instead,
-  // one item per query row attending keys up to its own position (fp32 throughout).
-  if (max_q_len > 1 && c->dtype == PKV_F32)
+  // Every row through the decode kernels, one item per query row attending keys up to its own
+  // position (fp32 throughout), when ragged_rows_mode says so; else decode rows there and
+  // prefill chunks on the MFMA kernel.
+  if (ragged_rows_mode(num_tokens, num_q_heads, max_q_len, c))
     return decode_common_cu(out, out_dtype, q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens,
                             num_seqs, num_q_heads, scale, max_context_len, c, 0, workspace, workspace_bytes, stream,
                             cu_seqlens_q, 0, num_tokens, nullptr, 0, true);

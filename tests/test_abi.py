@@ -166,6 +166,12 @@ def test_ragged_validation():
     assert rows_ws == L.pkv_decode_workspace_bytes(5, 4, 5000, ctypes.byref(c32)) > 0  # sized by rows
     assert L.pkv_ragged_workspace_bytes(2, 5, 4, 1, 5000, ctypes.byref(c32)) == \
         L.pkv_decode_workspace_bytes(2, 4, 5000, ctypes.byref(c32))                    # decode rows only
+    # 16-bit pools: chunks of at most g rows also go through the decode kernels, one item per row
+    c16 = desc()  # 4 kv heads; 16 query heads: g = 4
+    assert L.pkv_ragged_workspace_bytes(2, 8, 16, 4, 5000, ctypes.byref(c16)) == \
+        L.pkv_decode_workspace_bytes(8, 16, 5000, ctypes.byref(c16))
+    assert L.pkv_ragged_workspace_bytes(2, 10, 16, 5, 5000, ctypes.byref(c16)) == \
+        L.pkv_decode_workspace_bytes(2, 16, 5000, ctypes.byref(c16))
     assert ragged(desc(), max_q=200, max_ctx=100) == -1  # q_len cannot exceed the context
     assert ragged(desc(), max_q=6, T=5) == -1            # nor the token count
     assert ragged(desc(), hq=6) == -3

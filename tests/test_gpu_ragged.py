@@ -63,6 +63,9 @@ RAGGED_CASES = [
     ("f32", 8, 64, 8, 2, [65, 1, 200, 0], [65, 33, 450, 5]),                            # GQA, empty sequence
     ("f32", 16, 128, 4, 2, [300, 1], [5000, 3000]),                                     # split partitions
     ("f32", 16, 64, 4, 2, [3, 1], [20000, 500]),      # few rows, many partitions each: 8-thread merge
+    # 16-bit chunks of at most g rows: every row through the decode kernels as well
+    ("bf16", 16, 128, 32, 8, [2, 4, 1, 3], [1500, 40, 700, 3]),
+    ("f16", 16, 64, 8, 1, [8, 1, 5], [100, 2000, 8]),
     # a prefill chunk behind 19800 cached tokens at B=8: 2500 blocks, more than the prefill
     # kernel's 1024-entry LDS table window, so the window moves during the key loop
     ("bf16", 8, 64, 4, 2, [200, 1], [20000, 9000]),
