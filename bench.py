@@ -672,16 +672,17 @@ def profile_copy(reps: int = 10):
                       "bytes_written_per_launch": 2 * 4096 * H * B * D * 2, "launches": reps}))
 
 
-def prefill_only(dtype: str = "bf16", reps: int = 20, warm: int = 50):
-    """The prefill kernel alone on the 8 prompt sequences of the 13B-shaped mixed step (40 heads,
-    head_dim 128, B=16, no cached prefix) in the given pool dtype: ``warm`` untimed launches
-    (clock ramp), then ``reps`` timed ones; median duration and MFMA utilisation."""
+def prefill_only(dtype: str = "bf16", reps: int = 20, warm: int = 50, prompts=None):
+    """The prefill kernel alone on the 8 prompt sequences of the 13B-shaped mixed step (or the
+    given prompt lengths; 40 heads, head_dim 128, B=16, no cached prefix) in the given pool dtype:
+    ``warm`` untimed launches (clock ramp), then ``reps`` timed ones; median duration and MFMA
+    utilisation."""
     import torch
     from paged_kv_cache_323_amd import native as pk
     from paged_kv_cache_323_amd import runner as R
     from workloads import make_ragged_workload, make_workload
-    pre = [q for q in make_workload("mixed", "full").q_lens if q > 1]
-    w = make_ragged_workload(5, pre, pre, 40, 40, 128, dtype, 16, name=f"prefill8-{dtype}")
+    pre = list(prompts) if prompts else [q for q in make_workload("mixed", "full").q_lens if q > 1]
+    w = make_ragged_workload(5, pre, pre, 40, 40, 128, dtype, 16, name=f"prefill{len(pre)}-{dtype}")
     st = R.play_script(w, threads=16)
     q = R.to_device(w.queries(), w.dtype)
     out = torch.empty_like(q)
@@ -735,10 +736,12 @@ def row_rooflines(result, extra, read_peak, copy_peak):
                               "frac": m["prefill_mfma_util"], "us": m["prefill_only_us"]}
     if "attention_us" in m:
         rows["a7_mixed_step"] = {"step_us": m["step_us"], "seqs_per_s": m["seqs_per_s"]}
-    pf = extra.get("prefill_f16", {})
-    if "tflops" in pf:  # the same prompts from an f16 pool: one f16 P operand, no split
-        rows["a7_prefill_f16"] = {"achieved_tflops": pf["tflops"], "peak_tflops": MFMA_BF16_PEAK_TFLOPS,
-                                  "frac": pf["mfma_util"], "us": pf["median_us"]}
+    for key, row in (("prefill_f16", "a7_prefill_f16"), ("prefill_long", "a7_prefill_long_prompts")):
+        # the 13B prompts from an f16 pool (one f16 P operand), and 4 prompts of 8192 tokens (bf16)
+        pf = extra.get(key, {})
+        if "tflops" in pf:
+            rows[row] = {"achieved_tflops": pf["tflops"], "peak_tflops": MFMA_BF16_PEAK_TFLOPS,
+                         "frac": pf["mfma_util"], "us": pf["median_us"]}
     sp = extra.get("shared_prefix", {})
     if "copy_4096_pairs_gbs" in sp:
         rows["a3_copy_blocks_4096_pairs"] = hbm(sp["copy_4096_pairs_gbs"], copy_peak)
@@ -843,7 +846,8 @@ def main():
                         ("swap", run_swap),
                         ("engine", run_engine),
                         ("mixed", run_mixed),
-                        ("prefill_f16", lambda: prefill_only("f16"))):
+                        ("prefill_f16", lambda: prefill_only("f16")),
+                        ("prefill_long", lambda: prefill_only("bf16", reps=10, warm=10, prompts=[8192] * 4))):
             log(f"extra: {key}")
             try:
                 extra[key] = fn()
