@@ -229,6 +229,9 @@ __global__ __launch_bounds__(kPfThreads, 2) void ragged_prefill_kernel(PrefillAr
   const uint32_t head_off = (uint32_t)(kvh * a.bs * D);      // this kv head's rows in a block
   const int nblk = (kend + a.bs - 1) >> a.log2_bs;
 
+  // Position of this wave's last valid row; -1 (before every key) when the wave has none.
+  const int wave_last_pos = wave * 32 < nrows ? pos0 + min(wave * 32 + 31, nrows - 1) : -1;
+
   // The key loop, in one of two modes for Oᵀ = Vᵀ·Pᵀ:
   //   kSplitP == false: Vᵀ as f16 in LDS (an f16 pool's values, or a bf16 pool's converted: exact
   //     for |v| in [2^-14, 65504], within 2^-25 below) and one f16 P rounded to nearest: one MFMA
@@ -343,7 +346,10 @@ __global__ __launch_bounds__(kPfThreads, 2) void ragged_prefill_kernel(PrefillAr
     }
     __syncthreads();
     if (nkt > 1) fetch(1);
-    for (int kt = 0; kt < nkt; ++kt) {
+    // Key tiles this wave computes: the rest (at most the last two of a causal row tile, or all
+    // of them for a wave without valid rows) have every key masked for its rows.
+    const int nkt_w = wave_last_pos < 0 ? 0 : min(nkt, wave_last_pos / kPfKeys + 1);
+    for (int kt = 0; kt < nkt_w; ++kt) {
       const int k0 = kt * kPfKeys;
       const uint16_t* cK = sK + (kt & 1) * KBUF;
       const uint16_t* cV = sVt + (kt & 1) * VBUF;
@@ -492,6 +498,18 @@ __global__ __launch_bounds__(kPfThreads, 2) void ragged_prefill_kernel(PrefillAr
 #endif
       }
       __syncthreads();  // buffer kt&1 is free for tile kt+2; buffer (kt+1)&1 is complete
+    }
+    // The masked tiles: no products or softmax, only this wave's share of the staging and the
+    // same barriers as the other waves.
+    for (int kt = nkt_w; kt < nkt; ++kt) {
+      if (kt + 1 < nkt) {
+        stage((kt + 1) & 1);
+        if (kt + 2 < nkt) {
+          ensure_table(kt + 2);
+          fetch(kt + 2);
+        }
+      }
+      __syncthreads();
     }
   };  // run_keys
 
