@@ -627,11 +627,17 @@ def cpu_baseline(w, budget_s=12.0):
 
 
 def source_digest() -> str:
-    """Digest of the decode kernel source: counter-derived figures are only valid for it."""
+    """Digest of the decode kernel's code: counter-derived figures are only valid for it. Comments
+    and whitespace are left out, so editing a comment does not invalidate the counters."""
     import hashlib
+    import re
     src = os.path.join(ROOT, "paged_kv_cache_323_amd", "csrc", "decode.hip")
-    with open(src, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    with open(src, encoding="utf-8") as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)  # block comments
+    text = re.sub(r"//[^\n]*", " ", text)                 # line comments
+    code = "".join(text.split())
+    return hashlib.sha256(code.encode()).hexdigest()[:16]
 
 
 def load_traffic(block_size: int):

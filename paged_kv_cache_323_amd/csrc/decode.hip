@@ -1,8 +1,9 @@
 // Paged decode attention for gfx950.
 //
-// One workgroup (4 waves) per (kv head, sequence, context partition). The g = Hq/Hkv query
-// heads that share a kv head are served by the same workgroup, so every K/V tile is read from
-// HBM once per step. The partition's tokens are walked through the block table in units of 8
+// One workgroup (4 waves) per (kv head, sequence, context partition), or in causal-rows mode per
+// (kv head, query row of a ragged batch, partition), the row attending its sequence's keys up to
+// its own position. The g = Hq/Hkv query heads that share a kv head are served by the same
+// workgroup, so every K/V tile is read from HBM once per item. The partition's tokens are walked through the block table in units of 8
 // tokens (units never straddle a block, since B is a multiple of 8); unit u belongs to wave
 // u mod 4, and each wave keeps PF units of loads in flight:
 //
@@ -12,7 +13,8 @@
 //   softmax  per head over the partition: max, exp2, sum (one wave per head).
 //   phase 2  values: 16 lanes per token, each lane owns D/16 contiguous elements of the row;
 //            fp32 accumulators for all g heads; probabilities read from LDS.
-//   merge    lane groups and waves are summed through LDS.
+//   merge    the four token rows of a wave are summed across lanes (permlane swaps), then the
+//            waves through LDS (the score buffer's words, reused after a barrier).
 //
 // A sequence whose context fits one partition writes its normalised output directly. Longer
 // contexts write (max, sum, unnormalised output) per partition to the workspace, and a second
