@@ -177,3 +177,41 @@ def test_ragged_f32_many_sequences():
     _, ref = oracle.run_workload(w)
     _, out = _run(w)
     _check(w, out, ref)
+
+
+def test_ragged_step_graph_replay_matches_eager():
+    """The ragged mixed step (decode rows, then MFMA prefill rows) captured in a HIP graph: every
+    replay, with eager GPU work between replays, gives the eager output bit for bit."""
+    import torch
+    from paged_kv_cache_323_amd import native as pk
+    from paged_kv_cache_323_amd import runner as R
+    w = make_workload("mixed", "small")
+    _announce(f"ragged step in a HIP graph {w.name}")
+    st = R.play_script(w, threads=16)
+    eager, inp = R.attention(w, st, "f32")
+    cu = torch.from_numpy(w.cu_seqlens()).cuda()
+    mx, mq = int(inp["lens_host"].max()), int(max(w.q_lens))
+    out = torch.full_like(eager, float("nan"))
+
+    def step():
+        pk.paged_attention_ragged(out, inp["q"], cu, inp["context_lens"], st.k_cache, st.v_cache,
+                                  inp["block_tables"], w.scale, mq, mx, st.desc, inp["workspace"])
+
+    step()
+    torch.cuda.synchronize()
+    assert torch.equal(out, eager)
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g):
+            step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    scratch = torch.randn(512, 512, device="cuda")
+    for rep in range(3):
+        out.fill_(float("nan"))
+        scratch = scratch @ scratch.T / 512.0
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), f"replay {rep} differs from the eager step"
