@@ -14,10 +14,16 @@ at 8192, physical blocks in a seeded random order):
 
 Inputs are resident in HBM before timing starts. The JSON line reports whole-step throughput
 (KV bytes read by attention per second, and sequences per second), the decode kernel against
-the HBM roofline (timed with HIP events on the launch stream), the oracle timed on this host's
-CPU on a bounded sample, and secondary measurements of the other workloads.
+the HBM roofline (timed with HIP events on the launch stream) and against measured read, gather
+and copy ceilings, the oracle timed on this host's CPU on a bounded sample, and secondary
+measurements of the other workloads (block sizes 8/32, Llama-7B-shaped decode, shared prefix,
+swap, the continuous-batching engine, the 13B-shaped mixed step, prefill from an f16 pool and on
+long prompts), each row beside the ceiling that bounds it.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--block-size 16] [--no-extra]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--block-size 16] [--no-extra] [--no-cpu]
+                    [--partition P] [--dense-grid]
+    python bench.py --profile-prefill [--prefill-dtype bf16|f16]   # profiling targets
+    python bench.py --profile-copy
 """
 from __future__ import annotations
 
