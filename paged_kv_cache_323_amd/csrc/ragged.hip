@@ -121,77 +121,77 @@ __global__ __launch_bounds__(kPfThreads, 2) void ragged_prefill_kernel(PrefillAr
   __shared__ __attribute__((aligned(16))) uint16_t sK[2 * KBUF];
   __shared__ __attribute__((aligned(16))) uint16_t sVt[2 * VBUF];
   __shared__ int s_tab[kPfTab];
-  __shared__ int s_scan[kPfThreads];
-  __shared__ int s_seq, s_tile;
+  __shared__ int s_wtot[kPfThreads / kWave];
+  __shared__ int s_seq, s_tile, s_q0, s_ql, s_ctx;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int h = blockIdx.x;
   const int kvh = h / (a.hq / a.hkv);
-  // Row tiles of sequence sq (0 for decode rows). Debug builds reject row offsets that are
-  // negative, decreasing or past the batch, and treat such a sequence as empty.
-  auto tiles_of = [&](int sq) {
-    const int c0 = a.cu[sq], c1 = a.cu[sq + 1];
-    if (kDebugChecks && (c0 < 0 || c1 < c0 || c1 > a.num_tokens)) {
-      debug_flag(DBG_RAGGED);
-      return 0;
-    }
-    const int ql = c1 - c0;
-    return ql > 1 ? (ql + kPfRows - 1) / kPfRows : 0;
-  };
-
   // ---- which (sequence, row tile) this workgroup owns ----------------------------------------
-  // Slots are numbered from the end: the last row tiles of the last sequences (the longest
-  // causal rows, hence the most key tiles) are dispatched first, short ones fill the tail.
+  // Slot y is the y-th row tile counted back from the last tile of the last sequence: the last
+  // row tiles of the last sequences (the longest causal rows, hence the most key tiles) are
+  // dispatched first and short ones fill the tail. One pass over the sequences, last first, one
+  // sequence per thread: a wave prefix sum of the row-tile counts and the four wave totals give
+  // each sequence's running count, and the thread whose sequence holds the slot publishes it with
+  // its row offset, row count and context length (read in the same pass). Decode rows (one query
+  // row) have no row tiles. Debug builds reject row offsets that are negative, decreasing or past
+  // the batch, and treat such a sequence as empty.
   if (tid == 0) s_seq = -1;
   {
-    int total_all = 0;  // total tiles, needed to reverse the slot order
+    const int slot = (int)blockIdx.y;
+    int base = 0;  // row tiles of the sequences after this chunk
     for (int c0 = 0; c0 < a.num_seqs; c0 += kPfThreads) {
-      const int sq = c0 + tid;
-      const int nt = sq < a.num_seqs ? tiles_of(sq) : 0;
-      s_scan[tid] = nt;
-      __syncthreads();
-      for (int off = kPfThreads / 2; off > 0; off >>= 1) {
-        if (tid < off) s_scan[tid] += s_scan[tid + off];
-        __syncthreads();
-      }
-      total_all += s_scan[0];
-      __syncthreads();
-    }
-    const int slot = total_all - 1 - (int)blockIdx.y;
-    int base = 0;
-    for (int c0 = 0; slot >= 0 && c0 < a.num_seqs; c0 += kPfThreads) {
-      const int sq = c0 + tid;
-      const int nt = sq < a.num_seqs ? tiles_of(sq) : 0;
-      s_scan[tid] = nt;
-      __syncthreads();
-      for (int off = 1; off < kPfThreads; off <<= 1) {
-        const int v = tid >= off ? s_scan[tid - off] : 0;
-        __syncthreads();
-        s_scan[tid] += v;
-        __syncthreads();
-      }
-      const int total = s_scan[kPfThreads - 1];
-      const int target = slot - base;
-      if (target < total) {
-        if (nt > 0 && s_scan[tid] > target && s_scan[tid] - nt <= target) {
-          s_seq = sq;
-          s_tile = target - (s_scan[tid] - nt);
+      const int sq = a.num_seqs - 1 - (c0 + tid);
+      int nt = 0, cq0 = 0, cql = 0, cctx = 0;
+      if (sq >= 0) {
+        cq0 = a.cu[sq];
+        const int c1 = a.cu[sq + 1];
+        cctx = a.ctx_lens[sq];
+        if (kDebugChecks && (cq0 < 0 || c1 < cq0 || c1 > a.num_tokens)) {
+          debug_flag(DBG_RAGGED);
+        } else {
+          cql = c1 - cq0;
+          nt = cql > 1 ? (cql + kPfRows - 1) / kPfRows : 0;
         }
-        __syncthreads();
+      }
+      int incl = nt;
+#pragma unroll
+      for (int d = 1; d < kWave; d <<= 1) {
+        const int v = __shfl_up(incl, d);
+        if (lane >= d) incl += v;
+      }
+      if (lane == kWave - 1) s_wtot[wave] = incl;
+      __syncthreads();
+      int total = 0;
+#pragma unroll
+      for (int w = 0; w < kPfThreads / kWave; ++w) {
+        const int t = s_wtot[w];
+        if (w < wave) incl += t;
+        total += t;
+      }
+      const int target = slot - base;
+      if (target < total) {  // uniform
+        if (nt > 0 && incl > target && incl - nt <= target) {
+          s_seq = sq;
+          s_tile = nt - 1 - (target - (incl - nt));
+          s_q0 = cq0;
+          s_ql = cql;
+          s_ctx = cctx;
+        }
         break;
       }
       base += total;
-      __syncthreads();
+      __syncthreads();  // s_wtot is rewritten by the next chunk
     }
   }
   __syncthreads();
   const int s = s_seq;
   if (s < 0) return;  // uniform: this slot of the launch has no tile
-  const int q0 = a.cu[s];
-  const int ql = a.cu[s + 1] - q0;
-  const int ctx = min(a.ctx_lens[s], a.max_blocks * a.bs);  // contract: ctx fits the table
+  const int q0 = s_q0;
+  const int ql = s_ql;
+  const int ctx = min(s_ctx, a.max_blocks * a.bs);  // contract: ctx fits the table
   const int row0 = s_tile * kPfRows;
   const int nrows = min(kPfRows, ql - row0);
   const int pos0 = ctx - ql + row0;      // position of the tile's first query row

@@ -179,6 +179,22 @@ def test_ragged_f32_many_sequences():
     _check(w, out, ref)
 
 
+def test_ragged_bf16_many_sequences():
+    """A bf16 ragged step over 600 sequences, mostly decode rows, with MFMA prefill chunks in the
+    first, middle and last of the prefill kernel's 256-sequence passes over the row offsets (each
+    workgroup finds its row tile by counting tiles back from the last sequence)."""
+    rng = np.random.default_rng(23)
+    q_lens = [1] * 600
+    for i, q in ((0, 130), (1, 2), (255, 70), (256, 129), (300, 257), (511, 9), (599, 65)):
+        q_lens[i] = q
+    ctx = [int(q) + int(rng.integers(0, 200)) for q in q_lens]
+    w = make_ragged_workload(23, q_lens, ctx, 4, 2, 64, "bf16", 16, name="ragged-bf16-600seqs")
+    _announce(f"{w.name}")
+    _, ref = oracle.run_workload(w)
+    _, out = _run(w)
+    _check(w, out, ref)
+
+
 def test_ragged_step_graph_replay_matches_eager():
     """The ragged mixed step (decode rows, then MFMA prefill rows) captured in a HIP graph: every
     replay, with eager GPU work between replays, gives the eager output bit for bit."""
