@@ -126,7 +126,7 @@ __global__ __launch_bounds__(kPfThreads, 2) void ragged_prefill_kernel(PrefillAr
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar branches on it
   const int h = blockIdx.x;
   const int kvh = h / (a.hq / a.hkv);
   // ---- which (sequence, row tile) this workgroup owns ----------------------------------------
@@ -396,11 +396,13 @@ __global__ __launch_bounds__(kPfThreads, 2) void ragged_prefill_kernel(PrefillAr
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt) {
         if (need_mask) {
+          // key k0 + 16·mt + 4g + i is masked when 16·mt + i exceeds the row's threshold
+          const int thr = qpos[nt] - k0 - 4 * g;
 #pragma unroll
           for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-              if (k0 + 16 * mt + 4 * g + i > qpos[nt]) sacc[mt][nt][i] = -INFINITY;
+              if (16 * mt + i > thr) sacc[mt][nt][i] = -INFINITY;
         }
         float mx = -INFINITY;
 #pragma unroll
