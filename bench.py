@@ -179,55 +179,84 @@ class DecodeLoop:
         self.step_idx += 1
 
 
+def _timed_windows(loop, K, min_total_s, min_windows, max_windows, ev=False):
+    """Repeated K-step windows, each from the same saved block-manager state, so every window
+    times the same K steps (same contexts, same slots, same values written). Each window is
+    bracketed by device synchronisations on both sides. Returns per-window seconds and, with
+    ``ev``, per-launch event times (partition launch, merge launch) in ms."""
+    import torch
+    snap = loop.snapshot
+    times, kern_ms, merge_ms = [], [], []
+    while (len(times) < min_windows or sum(times) < min_total_s) and len(times) < max_windows:
+        loop.st.bm = snap.clone()
+        loop.ctx_history.clear()
+        evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(K)] if ev else None
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(K):
+            loop.step(evs[i] if ev else None)
+        torch.cuda.synchronize()
+        times.append(time.perf_counter() - t0)
+        if ev:
+            kern_ms += [a.elapsed_time(b) for a, b, _ in evs]
+            merge_ms += [b.elapsed_time(c) for _, b, c in evs]
+    return times, kern_ms, merge_ms
+
+
 def run_headline(args):
+    import gc
     import torch
     from workloads import make_workload
     w = make_workload("gqa", "full", block_size=args.block_size)
     ramp_repeats = 400
-    loop = DecodeLoop(w, args.warmup + 2 * args.steps, work_list=not args.dense_grid, partition=args.partition)
+    loop = DecodeLoop(w, args.warmup + args.steps + 1, work_list=not args.dense_grid, partition=args.partition)
     util = kv_utilisation(w, loop.st.bm, MAX_LEN["gqa"])
     for _ in range(args.warmup):
         loop.step()
     torch.cuda.synchronize()
+    # Every timed window restarts from this state: its K steps append to the same contexts.
+    loop.snapshot = loop.st.bm.clone()
     # Keep the GPU busy for a moment so clocks have ramped before the timed steps: repeat the
     # last step's attention without advancing the state (a fixed count, so every run of this
     # command times the same launches).
     loop.repeat_attention(ramp_repeats)
     torch.cuda.synchronize()
     K = args.steps
-    # Timed region 1: K steps with no instrumentation -> throughput (value, ms_per_step).
-    loop.ctx_history.clear()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(K):
-        loop.step()
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    kv_total = sum(decode_algorithmic_bytes(ctx, w, 2)[0] for ctx in loop.ctx_history)
-    # Timed region 2: the next K steps with HIP events around the partition and merge launches
-    # (on the stream they run on) -> per-launch durations for the roofline. Event records cost
-    # about 8 us per step, which is why they stay out of region 1.
-    loop.ctx_history.clear()
-    evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(K)]
-    torch.cuda.synchronize()
-    for i in range(K):
-        loop.step(evs[i])
-    torch.cuda.synchronize()
-    kern_ms = [a.elapsed_time(b) for a, b, _ in evs]
-    merge_ms = [b.elapsed_time(c) for _, b, c in evs]
-    alg_total = sum(decode_algorithmic_bytes(ctx, w, 2)[1] for ctx in loop.ctx_history)
-    ms_per_step = elapsed / K * 1e3
-    kv_per_step = kv_total / K
-    alg_per_launch = alg_total / K
+    # The interpreter's cyclic garbage collector can stop the host for milliseconds at a point
+    # of its choosing; a serving loop keeps it out of its steps, and so does this one.
+    gc.collect()
+    gc.freeze()
+    gc.disable()
+    try:
+        # Throughput: K-step windows with no instrumentation, repeated until they cover at least
+        # 0.25 s (and at least 10 windows) -> value and ms_per_step from the median window.
+        win_s, _, _ = _timed_windows(loop, K, 0.25, 10, 1000)
+        ctx_hist = list(loop.ctx_history)
+        # Roofline: more windows of the same K steps with HIP events around the partition and merge
+        # launches (on the stream they run on). Event records cost about 8 us per step, which is why
+        # they stay out of the throughput windows.
+        _, kern_ms, merge_ms = _timed_windows(loop, K, 0.05, 5, 1000, ev=True)
+    finally:
+        gc.enable()
+        gc.unfreeze()
+    kv_per_step = sum(decode_algorithmic_bytes(ctx, w, 2)[0] for ctx in ctx_hist) / K
+    alg_per_launch = sum(decode_algorithmic_bytes(ctx, w, 2)[1] for ctx in ctx_hist) / K
+    med_s = float(np.median(win_s))
+    step_s = med_s / K
     kern_avg_s = float(np.mean(kern_ms)) * 1e-3
     achieved = alg_per_launch / kern_avg_s / 1e9
     return dict(
-        w=w, loop=loop, ms_per_step=ms_per_step, seqs_per_s=len(w.query_seqs) / (elapsed / K),
-        kv_gbs=kv_per_step / (elapsed / K) / 1e9, kern_avg_us=kern_avg_s * 1e6, kern_med_us=float(np.median(kern_ms)) * 1e3,
+        w=w, loop=loop, ms_per_step=step_s * 1e3, seqs_per_s=len(w.query_seqs) / step_s,
+        kv_gbs=kv_per_step / step_s / 1e9, kern_avg_us=kern_avg_s * 1e6, kern_med_us=float(np.median(kern_ms)) * 1e3,
         achieved=achieved, alg_per_launch=alg_per_launch, kv_per_step=kv_per_step,
         kern_kv_gbs=kv_per_step / kern_avg_s / 1e9, partition=loop.partition,
-        mean_ctx=float(np.mean([c.mean() for c in loop.ctx_history])), util=util,
-        merge_avg_us=float(np.mean(merge_ms)) * 1e3)
+        mean_ctx=float(np.mean([c.mean() for c in ctx_hist])), util=util,
+        merge_avg_us=float(np.mean(merge_ms)) * 1e3, kern_launches=len(kern_ms),
+        windows={"count": len(win_s), "steps_each": K, "total_s": round(sum(win_s), 4),
+                 "step_us_median": round(step_s * 1e6, 2),
+                 "step_us_min": round(min(win_s) / K * 1e6, 2), "step_us_max": round(max(win_s) / K * 1e6, 2),
+                 "step_us_p10": round(float(np.percentile(win_s, 10)) / K * 1e6, 2),
+                 "step_us_p90": round(float(np.percentile(win_s, 90)) / K * 1e6, 2)})
 
 
 _EVICT = None
@@ -482,7 +511,7 @@ def run_engine(n_requests=512, max_steps=400):
     from paged_kv_cache_323_amd.engine import Engine
     rng = np.random.default_rng(21)
     eng = Engine(num_blocks=9000, block_size=16, num_q_heads=40, num_kv_heads=40, head_dim=128, dtype="bf16",
-                 max_num_seqs=256, max_step_tokens=8192, num_host_blocks=6000, seed=21, values="device")
+                 max_num_seqs=256, max_step_tokens=8192, num_host_blocks=6000, seed=21)
     for _ in range(n_requests):
         eng.add_request(int(rng.integers(128, 1025)), int(rng.integers(32, 257)))
     for _ in range(10):  # warm-up steps (first admissions)
@@ -647,8 +676,9 @@ def source_digest() -> str:
 
 
 def load_traffic(block_size: int):
-    """HBM bytes per decode partition launch from the committed counter summary, or None when
-    that summary was taken on a different kernel source or workload."""
+    """The decode partition launch's HBM traffic over its algorithmic bytes, from the committed
+    counter summary (FETCH_SIZE + WRITE_SIZE, calibrated on a copy of known size), or None when
+    that summary was taken on a different kernel source."""
     path = os.path.join(ROOT, "profiles", f"decode_gqa_B{block_size}_traffic.txt")
     if not os.path.exists(path):
         return None
@@ -661,8 +691,10 @@ def load_traffic(block_size: int):
     if kv.get("source_digest") != source_digest():
         return None
     try:
-        return float(kv["traffic_bytes_per_launch"])
-    except (KeyError, ValueError):
+        return {"ratio": float(kv["traffic_bytes_per_launch"]) / float(kv["algorithmic_bytes_per_launch"]),
+                "profile_traffic_bytes": float(kv["traffic_bytes_per_launch"]),
+                "profile_algorithmic_bytes": float(kv["algorithmic_bytes_per_launch"])}
+    except (KeyError, ValueError, ZeroDivisionError):
         return None
 
 
@@ -769,8 +801,8 @@ def row_rooflines(result, extra, read_peak, copy_peak):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--block-size", type=int, default=16)
     ap.add_argument("--no-extra", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
@@ -829,12 +861,21 @@ def main():
         "kv_memory_utilisation": h["util"],
         "pct_hbm_peak_step": round(100 * h["kv_gbs"] / HBM_PEAK_GBS, 2),
         "roofline": {"bound": "hbm", "achieved": round(h["achieved"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(h["achieved"] / HBM_PEAK_GBS, 4), "traffic": load_traffic(w.block_size),
+                     "frac": round(h["achieved"] / HBM_PEAK_GBS, 4), "traffic": None,
                      "kernel": "paged_decode_kernel<bf16,128,4> (partition launch)",
                      "kernel_avg_us": round(h["kern_avg_us"], 2),
                      "merge_launch_avg_us": round(h["merge_avg_us"], 2),
                      "algorithmic_bytes_per_launch": int(h["alg_per_launch"])},
     }
+    tr = load_traffic(w.block_size)
+    if tr is not None:
+        # The counters' bytes over the algorithmic bytes of the profiled run (the same command's
+        # launches), applied to this run's algorithmic bytes per launch.
+        result["roofline"]["traffic"] = int(round(tr["ratio"] * h["alg_per_launch"]))
+        result["roofline"]["traffic_over_algorithmic"] = round(tr["ratio"], 4)
+        result["roofline"]["traffic_profile_algorithmic_bytes"] = int(tr["profile_algorithmic_bytes"])
+    result["windows"] = h["windows"]
+    result["roofline"]["event_timed_launches"] = h["kern_launches"]
     log("streaming read and copy probes")
     read_peak = measured_read_peak()
     copy_peak = measured_copy_peak()

@@ -352,6 +352,13 @@ typedef struct pkv_bm pkv_bm;
 pkv_bm* pkv_bm_create(int32_t num_blocks, int32_t block_size, const int32_t* free_order);
 void pkv_bm_destroy(pkv_bm* bm);
 
+/* An independent copy of a block manager's whole state (tables, lengths, reference counts, free
+ * lists in order, host pool): later operations on either one leave the other unchanged. The
+ * caller destroys it with pkv_bm_destroy. Returns NULL for a NULL argument or when memory runs
+ * out. For callers that need to restart from a saved allocation state, e.g. repeated timing of
+ * the same steps. */
+pkv_bm* pkv_bm_clone(const pkv_bm* bm);
+
 int32_t pkv_bm_add_seq(pkv_bm* bm, int64_t seq_id);
 int32_t pkv_bm_fork(pkv_bm* bm, int64_t parent_id, int64_t child_id);
 int32_t pkv_bm_free_seq(pkv_bm* bm, int64_t seq_id);

@@ -23,7 +23,11 @@ Sources (titles of the pages this follows):
 Parity status: every function here is pinned by ``tests/test_oracle_*.py``
 (closed forms, a library routine, the page's block-wise equation, physical
 permutation invariance, hand-traced copy-on-write fixtures and the
-fragmentation expectation). No function is "parity unpinned".
+fragmentation expectation). ``paged_decode`` in particular is pinned with one,
+two, four and eight query heads per KV head against torch's grouped-query
+scaled_dot_product_attention over the contiguous histories, and against
+``paged_ragged``; planted mistakes in its head mapping, query row and context
+length trip those pins. No function is "parity unpinned".
 """
 from .attention import (  # noqa: F401
     upcast,

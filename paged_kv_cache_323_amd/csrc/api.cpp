@@ -5,6 +5,7 @@
 #include <math.h>
 
 #include <algorithm>
+#include <vector>
 #include <stdint.h>
 
 #include "../../include/pagedkv.h"
@@ -361,6 +362,8 @@ int32_t pkv_decode_items(const int32_t* context_lens, int32_t num_seqs, int32_t 
   }
   // Longest items first (ties keep the order above), so that the launch's tail holds the shortest
   // ones; an item's length is the token count of its partition as the kernel splits the context.
+  // A counting sort on that length, stable by construction (a comparison sort when lengths
+  // exceed 65536 tokens, to bound the buckets).
   auto tokens = [&](int32_t it) {
     const int32_t s = it & 0xffff, p = (int32_t)((uint32_t)it >> 16);
     const int32_t ctx = context_lens[s];
@@ -369,7 +372,25 @@ int32_t pkv_decode_items(const int32_t* context_lens, int32_t num_seqs, int32_t 
     const int32_t psz = std::min(partition_size, (((ctx + n - 1) / n) + 63) & ~63);
     return std::max(0, std::min(psz, ctx - p * psz));
   };
-  std::stable_sort(items, items + k, [&](int32_t x, int32_t y) { return tokens(x) > tokens(y); });
+  thread_local std::vector<int32_t> keys, order, start;
+  keys.resize(k);
+  order.resize(k);
+  int32_t longest = 0;
+  for (int32_t i = 0; i < k; ++i) {
+    keys[i] = tokens(items[i]);
+    longest = std::max(longest, keys[i]);
+  }
+  if (longest > 65536) {
+    for (int32_t i = 0; i < k; ++i) order[i] = i;
+    std::stable_sort(order.begin(), order.end(), [&](int32_t x, int32_t y) { return keys[x] > keys[y]; });
+    for (int32_t i = 0; i < k; ++i) order[i] = items[order[i]];
+  } else {
+    start.assign(longest + 2, 0);
+    for (int32_t i = 0; i < k; ++i) ++start[longest - keys[i] + 1];  // ascending key = descending length
+    for (int32_t v = 0; v <= longest; ++v) start[v + 1] += start[v];
+    for (int32_t i = 0; i < k; ++i) order[start[longest - keys[i]]++] = items[i];
+  }
+  std::copy(order.begin(), order.end(), items);
   return k;
 }
 

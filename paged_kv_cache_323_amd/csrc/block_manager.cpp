@@ -194,6 +194,15 @@ pkv_bm* pkv_bm_create(int32_t num_blocks, int32_t block_size, const int32_t* fre
 
 void pkv_bm_destroy(pkv_bm* bm) { delete bm; }
 
+pkv_bm* pkv_bm_clone(const pkv_bm* bm) {
+  if (!bm) return nullptr;
+  try {
+    return new pkv_bm(*bm);  // every member is a value: the copy shares nothing with the original
+  } catch (const std::bad_alloc&) {
+    return nullptr;
+  }
+}
+
 int32_t pkv_bm_add_seq(pkv_bm* bm, int64_t id) {
   if (!bm) return PKV_EINVAL;
   if (bm->seqs.count(id)) return PKV_EEXIST;

@@ -140,7 +140,7 @@ __global__ __launch_bounds__(kPfThreads, 2) void ragged_prefill_kernel(PrefillAr
   // the batch, and treat such a sequence as empty.
   if (tid == 0) s_seq = -1;
   {
-    const int slot = (int)blockIdx.y;
+    const int slot = (int)(blockIdx.y + blockIdx.z * gridDim.y);
     int base = 0;  // row tiles of the sequences after this chunk
     for (int c0 = 0; c0 < a.num_seqs; c0 += kPfThreads) {
       const int sq = a.num_seqs - 1 - (c0 + tid);
@@ -566,9 +566,12 @@ static hipError_t launch_prefill_dt(const PrefillLaunch& L, hipStream_t stream) 
   // sequences); slots past the real count exit at once.
   const long long slots = (L.num_tokens + kPfRows - 1) / kPfRows + (L.num_seqs < L.num_tokens / 2 ? L.num_seqs : L.num_tokens / 2);
   if (slots <= 0) return hipSuccess;
-  if (slots > 65535 || L.num_q_heads > 0x7fffffff) return hipErrorInvalidConfiguration;
-  // Heads are the fast grid dimension so the heaviest row tiles of every head go out first.
-  const dim3 grid(L.num_q_heads, (unsigned)slots);
+  // Heads are the fast grid dimension so the heaviest row tiles of every head go out first. Slots
+  // run over y, then z (slot = y + z * gridDim.y keeps the dispatch order), so there is no limit
+  // below the 2^31 row offsets: slots < T/128 + T/2 + 1 < 65535^2.
+  const unsigned gy = slots > 65535 ? 65535u : (unsigned)slots;
+  const unsigned gz = (unsigned)((slots + gy - 1) / gy);
+  const dim3 grid(L.num_q_heads, gy, gz);
   if (L.head_dim == 128) return launch_kernel(ragged_prefill_kernel<DT, 128>, grid, dim3(kPfThreads), stream, a);
   return launch_kernel(ragged_prefill_kernel<DT, 64>, grid, dim3(kPfThreads), stream, a);
 }

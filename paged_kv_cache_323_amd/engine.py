@@ -19,8 +19,12 @@ hot path as an engine drives it, step after step with changing tables:
     「Paged Attention&Orca Paper笔记与解读」 §PagedAttention的方法: no new admissions while
     preempted requests wait).
 
-Every block-manager operation is recorded as a script op (the same ops the synthetic workloads
-use), so any step can be replayed elsewhere.
+Every block-manager operation is recorded in an operation log (:mod:`.oplog`), so any step can
+be replayed elsewhere. The new tokens' values come from a provider object: the default fills
+them from a fixed random device buffer (throughput runs); a caller may pass its own provider
+with ``kv(seqs, n_tokens, tag) -> (k, v)`` and ``q(seqs, n_tokens) -> q`` returning host arrays
+of storage values ``[T, heads, head_dim]`` (bf16 as uint16 bits), e.g. to replay steps against
+a reference.
 """
 from __future__ import annotations
 
@@ -32,6 +36,7 @@ import numpy as np
 import torch
 
 from . import native as pk
+from .oplog import AddOp, AppendOp, FreeOp, SwapInOp, SwapOutOp
 from .runner import TORCH_DTYPE, to_device
 
 WAITING, PREFILL, DECODING, SWAPPED, FINISHED = "waiting", "prefill", "decoding", "swapped", "finished"
@@ -70,7 +75,7 @@ class EngineStats:
 class Engine:
     def __init__(self, num_blocks: int, block_size: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
                  dtype: str, max_num_seqs: int = 64, max_step_tokens: int = 8192, num_host_blocks: int = 0,
-                 seed: int = 0, values: str = "generator", keep_outputs: bool = False, device: str = "cuda"):
+                 seed: int = 0, values=None, keep_outputs: bool = False, device: str = "cuda"):
         self.B, self.hq, self.hkv, self.d, self.dtype = block_size, num_q_heads, num_kv_heads, head_dim, dtype
         self.max_num_seqs, self.max_step_tokens = max_num_seqs, max_step_tokens
         self.seed, self.values, self.keep_outputs, self.device = seed, values, keep_outputs, device
@@ -133,7 +138,6 @@ class Engine:
         if not self.running:
             return False
         victim = self.running[-1]
-        from workloads import FreeOp, SwapOutOp
         if self.requests[victim].state == PREFILL:
             self.bm.free_seq(victim)
             self._ops_add(FreeOp(victim))
@@ -158,7 +162,6 @@ class Engine:
         return True
 
     def _resume(self) -> None:
-        from workloads import SwapInOp
         while self.swapped and len(self.running) < self.max_num_seqs:
             seq = self.swapped[0]
             try:
@@ -176,7 +179,6 @@ class Engine:
 
     def _schedule(self):
         """Returns (seqs, n_tokens) of this step's batch (prompts first, then decodes)."""
-        from workloads import AddOp
         # retire
         for seq in [s for s in self.running if self.requests[s].state == FINISHED]:
             self.running.remove(seq)
@@ -219,21 +221,16 @@ class Engine:
 
     # ---- values ---------------------------------------------------------------------------------
     def _kv(self, seqs, ns, tag):
-        if self.values == "generator":
-            from workloads import AppendOp
-            from workloads.synth import Workload
-            w = self._workload_stub()
-            k, v = w.append_values(AppendOp(list(seqs), list(ns), tag), threads=8)
+        if self.values is not None:
+            k, v = self.values.kv(list(seqs), list(ns), tag)
             return to_device(k, self.dtype, self.device), to_device(v, self.dtype, self.device)
         T = int(sum(ns))
         k, v, _ = self._device_values(T)
         return k, v
 
     def _q(self, seqs, ns):
-        if self.values == "generator":
-            from workloads import gen_q
-            parts = [gen_q(self.seed, s, n, self.hq, self.d, self.dtype) for s, n in zip(seqs, ns)]
-            return to_device(np.concatenate(parts), self.dtype, self.device)
+        if self.values is not None:
+            return to_device(self.values.q(list(seqs), list(ns)), self.dtype, self.device)
         T = int(sum(ns))
         return self._device_values(T)[2]
 
@@ -250,20 +247,6 @@ class Engine:
                                for h in (self.hkv, self.hkv, self.hq))
             self._vals_cap = cap
         return tuple(x[:T] for x in self._vals)
-
-    def _workload_stub(self, query=None):
-        from workloads.synth import Workload
-        seqs, ql, ctx = query if query is not None else ([], [], [])
-        return Workload("engine", self.seed, self.dtype, self.B, self.hq, self.hkv, self.d, self.num_blocks,
-                        self.free_order, list(self.ops), list(seqs), list(ql), list(ctx),
-                        num_host_blocks=self.num_host_blocks, host_free_order=self.host_free_order)
-
-    def replay_workload(self, rec: StepRecord):
-        """The script of steps up to ``rec`` with ``rec``'s rows as the query (for the oracle)."""
-        from workloads.synth import Workload
-        w = self._workload_stub((rec.seqs, rec.q_lens, rec.context_lens))
-        w.ops = list(self.ops[: rec.ops_end])
-        return w
 
     # ---- per-step uploads -----------------------------------------------------------------------
     def _pairs_to_device(self, pairs) -> torch.Tensor:
@@ -301,7 +284,6 @@ class Engine:
 
     # ---- one model step -------------------------------------------------------------------------
     def step(self) -> Optional[StepRecord]:
-        from workloads import AppendOp, FreeOp
         seqs, ns = self._schedule()
         if not seqs:
             return None

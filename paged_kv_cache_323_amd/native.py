@@ -116,6 +116,7 @@ _SIGS = {
                                           ctypes.c_float, _I32, _I32, _DESC, _P, _SZ, _P]),
     "pkv_bm_create": (_P, [_I32, _I32, _I32P]),
     "pkv_bm_destroy": (None, [_P]),
+    "pkv_bm_clone": (_P, [_P]),
     "pkv_bm_add_seq": (_I32, [_P, _I64]),
     "pkv_bm_fork": (_I32, [_P, _I64, _I64]),
     "pkv_bm_free_seq": (_I32, [_P, _I64]),
@@ -405,6 +406,16 @@ class BlockManager:
         if h and _lib is not None:  # at interpreter shutdown the module may already be torn down
             _lib.pkv_bm_destroy(h)
             self._h = None
+
+    def clone(self) -> "BlockManager":
+        """An independent copy of the whole state (pkv_bm_clone)."""
+        h = _lib.pkv_bm_clone(self._h)
+        if not h:
+            raise MemoryError("pkv_bm_clone failed")
+        other = BlockManager.__new__(BlockManager)
+        other.__dict__.update({k: v for k, v in self.__dict__.items() if k != "_h"})
+        other._h = ctypes.c_void_p(h)
+        return other
 
     def add_seq(self, seq: int) -> None:
         _check(_lib.pkv_bm_add_seq(self._h, int(seq)), "bm_add_seq")

@@ -216,6 +216,42 @@ def pin_closed_forms():
     assert np.array_equal(out[3], np.zeros((H, d)))
 
 
+def pin_paged_decode_gqa(groups=(1, 2, 4, 8), tol=1e-12):
+    """The oracle's single-query entry point (``paged_decode``) with g = Hq / Hkv query heads per
+    kv head, against torch's scaled_dot_product_attention with ``enable_gqa`` (its own
+    contiguous-group mapping: query head h reads kv head ⌊h/g⌋) over each sequence's contiguous
+    history from the script (no pool, no block table), and against the oracle's ragged entry
+    point with one query row per sequence. Eight query heads over 8, 4, 2 and 1 kv heads, so that
+    h mod Hkv and ⌊h/g⌋ differ for g = 2 and 4; contexts cover an empty one, one token, a full
+    block, a ragged tail and several blocks."""
+    from workloads import make_decode_workload
+    worst = 0.0
+    for g in groups:
+        for dtype, B in (("f32", 8), ("bf16", 16)):
+            hq = 8
+            w = make_decode_workload(900 + g, [0, 1, B, 3 * B + 5, 2 * B - 1, 70], hq, hq // g, 16, dtype, B,
+                                     name=f"pin-decode-g{g}-{dtype}")
+            st, _ = oracle.run_workload(w, attend=False)
+            tables, lens = st.bm.padded_tables(w.query_seqs, w.max_blocks_per_seq())
+            q = w.queries()
+            got = oracle.paged_decode(q, st.pool_k, st.pool_v, tables, lens, w.scale, B, dtype)
+            rag = oracle.paged_ragged(q, w.cu_seqlens(), lens, tables, st.pool_k, st.pool_v, w.scale, B, dtype)
+            assert np.array_equal(got, rag), f"g={g} {dtype}: decode and ragged entry points differ"
+            hist = contiguous_history(w)
+            for i, s in enumerate(w.query_seqs):
+                K, V = hist[s]
+                if K.shape[0] == 0:
+                    assert np.array_equal(got[i], np.zeros_like(got[i])), "empty context must give zeros"
+                    continue
+                qs = _to_f64_torch(q[i], dtype)[:, None, :]                       # [Hq, 1, d]
+                Kt = _to_f64_torch(K, dtype).permute(1, 0, 2)                      # [Hkv, ctx, d]
+                Vt = _to_f64_torch(V, dtype).permute(1, 0, 2)
+                ref = F.scaled_dot_product_attention(qs, Kt, Vt, scale=w.scale, enable_gqa=True)[:, 0].numpy()
+                worst = max(worst, float(np.max(np.abs(got[i] - ref))))
+    assert worst <= tol, f"paged_decode vs SDPA (GQA) max abs err {worst:g}"
+    return worst
+
+
 # ---------------------------------------------------------------------------------------------
 # Block-manager pins
 # ---------------------------------------------------------------------------------------------

@@ -227,6 +227,10 @@ def test_decode_items_matches_reference(seed):
     for P in (64, 256, 1024):
         got = pk.decode_items(ctx, P)
         assert got.tolist() == _items_reference(ctx.tolist(), P)
+    # partitions longer than 65536 tokens take the comparison sort instead of the counting sort
+    big = (ctx.astype(np.int64) * 97).astype(np.int32)
+    for P in (1024, 131072):
+        assert pk.decode_items(big, P).tolist() == _items_reference(big.tolist(), P)
 
 
 def test_decode_items_rejects_bad_arguments():

@@ -242,3 +242,36 @@ def test_native_errors():
     assert bm.num_free() == 4 and bm.context_len(1) == 0
     with pytest.raises(ValueError):
         pk.BlockManager(4, 4, [0, 1, 1, 2])
+
+
+def test_native_clone_is_independent():
+    """pkv_bm_clone copies the whole state: the clone answers every query like the original, and
+    later operations on either one (appends with copy-on-write, frees, swaps) leave the other as
+    it was, so replaying the same operations on both gives the same slots and pairs."""
+    bm = pk.BlockManager(40, 4, np.random.default_rng(3).permutation(40).astype(np.int32))
+    bm.attach_host_pool(16, np.arange(16, dtype=np.int32))
+    for s in range(3):
+        bm.add_seq(s)
+    bm.append([0, 1, 2], [5, 9, 2])
+    bm.fork(0, 3)
+    bm.swap_out([2])
+
+    def snapshot(m):
+        return ({s: m.block_table(s) for s in (0, 1, 3)}, {s: m.context_len(s) for s in (0, 1, 3)},
+                m.free_list(), [m.refcount(b) for b in range(40)], m.host_free_list())
+
+    c = bm.clone()
+    before = snapshot(bm)
+    assert snapshot(c) == before
+    r1 = bm.append([0, 3, 1], [1, 1, 6])                  # seq 3 shares seq 0's partial block: COW
+    assert snapshot(c) == before                          # the clone did not move
+    r2 = c.append([0, 3, 1], [1, 1, 6])
+    assert [x.tolist() for x in r1] == [x.tolist() for x in r2]
+    assert snapshot(c) == snapshot(bm)
+    bm.free_seq(1)
+    assert c.context_len(1) == 15 and bm.num_free() != c.num_free()
+    c.swap_in([2])
+    assert not bm.is_resident(2) and c.is_resident(2)
+    del bm                                                # destroying one leaves the other usable
+    c.append([0], [1])
+    assert c.context_len(0) == 7

@@ -28,6 +28,17 @@ from workloads import make_workload, make_ragged_workload
 def say(msg):
     print("[case] " + msg, file=sys.stderr, flush=True)
 
+# Guard: the bad indices below are safe only in the bounds-checked build. Refuse to launch
+# anything unless the mapped library is the debug one and it reports its checks compiled in.
+import os
+if os.path.basename(os.path.realpath(pk.LIB_PATH)) != "libpagedkv_debug.so" or not pk.debug_checks_enabled():
+    print("[guard] not the bounds-checked library: " + pk.LIB_PATH, file=sys.stderr, flush=True)
+    sys.exit(3)
+with open("/proc/self/maps") as f:
+    mapped = {ln.split()[-1] for ln in f if "libpagedkv" in ln}
+if {os.path.basename(m) for m in mapped} != {"libpagedkv_debug.so"}:
+    print("[guard] unexpected libraries mapped: " + repr(sorted(mapped)), file=sys.stderr, flush=True)
+    sys.exit(3)
 res = {"enabled": pk.debug_checks_enabled()}
 pk.debug_flags(clear=True)
 
@@ -96,6 +107,7 @@ def test_debug_build_checks_device_indices():
     print("[case] debug build, child process", flush=True)
     # the child's progress lines go straight to this process's stderr
     p = subprocess.run([sys.executable, "-c", code], env=env, stdout=subprocess.PIPE, text=True, timeout=240)
+    assert p.returncode != 3, "the child did not load the bounds-checked library and launched nothing"
     assert p.returncode == 0, p.stdout[-2000:]
     res = json.loads([ln for ln in p.stdout.splitlines() if ln.startswith("{")][-1])
     assert res["enabled"] is True

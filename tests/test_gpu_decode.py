@@ -208,22 +208,30 @@ def st_v_row(R, st, w, seq):
 
 
 @pytest.mark.parametrize("name,B", [("gqa", 16), ("gqa", 32), ("llama7b", 16), ("shared_prefix", 16)])
-def test_decode_full_size_sampled(name, B):
-    """Full-size configuration in the launch configuration the benchmark uses; the oracle
-    checks a sample of sequences (including the longest and shortest) one by one."""
+def test_decode_full_size_every_row(name, B):
+    """Full-size configuration in the launch configuration the benchmark uses (automatic partition
+    size, pool-dtype inputs, fp32 outputs): every sequence's output against the oracle, the slots
+    and copy-on-write pairs of every append, and both full pools bit for bit after the setup
+    writes (and, for the shared prefix, the copy-on-write copies)."""
+    from support import compare_pool_bits, oracle_attention_threaded
     w = make_workload(name, "full", block_size=B)
-    _announce(f"decode full {w.name}")
+    _announce(f"decode full {w.name}: {len(w.query_seqs)} seqs, sum ctx {sum(w.context_lens)}")
     R = _runner()
     st = R.play_script(w, threads=16)
     out, _ = R.attention(w, st, "f32")
-    ctx = np.array(w.context_lens)
-    rng = np.random.default_rng(0)
-    pick = sorted(set([int(ctx.argmax()), int(ctx.argmin())] + rng.choice(len(ctx), 10, replace=False).tolist()))
-    seqs = [w.query_seqs[i] for i in pick]
-    st_or, ref = oracle.run_workload(w, only_seqs=seqs)
+    got = out.cpu().numpy()
+    st_or, _ = oracle.run_workload(w, attend=False, threads=16)
     _compare_bookkeeping(st, st_or)
-    err = _check_attention(w, out, ref, rows=pick)
-    print(f"  sampled {len(pick)} seqs, max abs err {err:.3g}")
+    n_k = compare_pool_bits(R.to_host_storage(st.k_cache, w.dtype), st_or.pool_k, w)
+    n_v = compare_pool_bits(R.to_host_storage(st.v_cache, w.dtype), st_or.pool_v, w)
+    del st
+    ref = oracle_attention_threaded(w, st_or)
+    err = float(np.max(np.abs(got.astype(np.float64) - ref)))
+    assert np.isfinite(got).all(), "non-finite output"
+    assert err <= TOL[w.dtype], f"{w.name}: max abs err {err:.3g} > {TOL[w.dtype]}"
+    pairs = sum(len(p) for p in st_or.pairs_per_append)
+    print(f"  {w.name}: all {len(w.query_seqs)} seqs, max abs err {err:.3g}; pools bit-exact "
+          f"({n_k + n_v} written elements); {pairs} copy-on-write pairs", flush=True)
 
 
 def test_decode_very_long_context_many_partitions():

@@ -7,8 +7,32 @@ import numpy as np
 import pytest
 
 import oracle
+from workloads import gen_kv, gen_q
+from workloads.synth import Workload
 
 pytestmark = pytest.mark.gpu
+
+
+class SeededValues:
+    """The engine's value provider for parity runs: the shared seeded generator, keyed by the
+    append's tag and each sequence id, so a replayed script regenerates the same values."""
+
+    def __init__(self, seed, hq, hkv, d, dtype):
+        self.seed, self.hq, self.hkv, self.d, self.dtype = seed, hq, hkv, d, dtype
+
+    def kv(self, seqs, ns, tag):
+        parts = [gen_kv(self.seed, tag, s, n, self.hkv, self.d, self.dtype) for s, n in zip(seqs, ns)]
+        return np.concatenate([p[0] for p in parts]), np.concatenate([p[1] for p in parts])
+
+    def q(self, seqs, ns):
+        return np.concatenate([gen_q(self.seed, s, n, self.hq, self.d, self.dtype) for s, n in zip(seqs, ns)])
+
+
+def replay_workload(eng, rec):
+    """The engine's op log up to ``rec`` as a script, with ``rec``'s rows as the query."""
+    return Workload("engine", eng.seed, eng.dtype, eng.B, eng.hq, eng.hkv, eng.d, eng.num_blocks, eng.free_order,
+                    list(eng.ops[: rec.ops_end]), list(rec.seqs), list(rec.q_lens), list(rec.context_lens),
+                    num_host_blocks=eng.num_host_blocks, host_free_order=eng.host_free_order)
 
 
 @pytest.mark.parametrize("dt,B,host", [("bf16", 16, 64), ("f16", 8, 0)])
@@ -17,7 +41,8 @@ def test_engine_steps_match_oracle(dt, B, host):
     rng = np.random.default_rng(7)
     # a pool too small for all requests at once, so admission waits and (with a host pool) swaps
     eng = Engine(num_blocks=28 if host else 200, block_size=B, num_q_heads=4, num_kv_heads=2, head_dim=128,
-                 dtype=dt, max_num_seqs=6, max_step_tokens=400, num_host_blocks=host, seed=11, keep_outputs=True)
+                 dtype=dt, max_num_seqs=6, max_step_tokens=400, num_host_blocks=host, seed=11, keep_outputs=True,
+                 values=SeededValues(11, 4, 2, 128, dt))
     for _ in range(14):
         eng.add_request(int(rng.integers(20, 150)), int(rng.integers(3, 25)))
     print(f"[case] engine {dt} B={B} host={host}", flush=True)
@@ -36,7 +61,7 @@ def test_engine_steps_match_oracle(dt, B, host):
                        [i for i, r in enumerate(eng.records) if any(q > 1 for q in r.q_lens)][:4]))
     for i in picks:
         rec = eng.records[i]
-        w = eng.replay_workload(rec)
+        w = replay_workload(eng, rec)
         _, ref = oracle.run_workload(w)
         got = rec.out.cpu().numpy().astype(np.float64)
         err = float(np.max(np.abs(got - ref)))

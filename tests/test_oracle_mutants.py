@@ -47,6 +47,7 @@ def _install(monkeypatch, module, mutant):
 
 def _attention_pins():
     P.pin_closed_forms()
+    P.pin_paged_decode_gqa()
     for name in ("tiny", "gqa", "mixed", "shared_prefix"):
         P.pin_sdpa(make_workload(name, "small"))
 
@@ -74,6 +75,14 @@ MUTANTS = [
     # attention
     ("attention", "kh = h // g", "kh = h % hkv", _attention_pins),
     ("attention", "logits = scale * (q @ k.T)", "logits = (q @ k.T)", _attention_pins),
+    # the single-query entry point alone (the anchors exist only in paged_decode)
+    ("attention", "            kh = h // g\n            out[s, h] = softmax_attention(qs[h:h + 1]",
+     "            kh = h % hkv\n            out[s, h] = softmax_attention(qs[h:h + 1]", _attention_pins),
+    ("attention", "softmax_attention(qs[h:h + 1], K[:, kh], V[:, kh], scale)",
+     "softmax_attention(qs[kh:kh + 1], K[:, kh], V[:, kh], scale)", _attention_pins),
+    ("attention", "        if ctx == 0:\n            continue\n        K = upcast(gather_kv(pool_k, block_tables[s], ctx, block_size), dtype)\n        V = upcast(gather_kv(pool_v, block_tables[s], ctx, block_size), dtype)\n        qs = upcast(q[s], dtype)",
+     "        if ctx == 0:\n            continue\n        K = upcast(gather_kv(pool_k, block_tables[s], ctx - 1, block_size), dtype)\n        V = upcast(gather_kv(pool_v, block_tables[s], ctx - 1, block_size), dtype)\n        qs = upcast(q[s], dtype)",
+     _attention_pins),
     ("attention", "phys = int(table[p // block_size])", "phys = int(table[p % block_size])", _attention_pins),
     ("attention", "rows.append(pool[phys, p % block_size])",
      "rows.append(pool[phys, (p + 1) % block_size])", _attention_pins),

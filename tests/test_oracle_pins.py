@@ -37,6 +37,10 @@ def test_oracle_brute_force_mixed_rows():
     P.pin_brute_force(make_workload("mixed", "small"), max_rows=40)
 
 
+def test_oracle_paged_decode_gqa():
+    P.pin_paged_decode_gqa()
+
+
 def test_oracle_closed_forms():
     P.pin_closed_forms()
 
