@@ -271,6 +271,32 @@ size_t pkv_decode_workspace_bytes_ex(int32_t num_seqs, int32_t num_q_heads,
                                      int32_t partition_size);
 
 /*
+ * paged_attention_decode_noalloc — pkv_paged_attention_decode without a caller workspace, for
+ *   callers that cannot allocate device memory: code under HIP graph capture, tight serving
+ *   loops, harnesses that forbid hipMalloc. Same arguments, layouts and results as
+ *   pkv_paged_attention_decode (the same kernels at the same automatic partition size, so the
+ *   outputs are bit-identical), minus workspace and workspace_bytes.
+ *   The split-context partials go to a file-scope device array of PKV_NOALLOC_SCRATCH_BYTES
+ *   bytes inside the library (64 MiB; each GPU the library runs on holds its own copy until the
+ *   process ends). Nothing is allocated or freed, on the device or the host.
+ *   A call whose partials would need more (pkv_decode_workspace_bytes_ex at the automatic
+ *   partition size) returns PKV_EWORKSPACE before any device call; the other validation errors
+ *   are those of pkv_paged_attention_decode. The first call on a device looks up that device's
+ *   address of the array (PKV_ELAUNCH, with pkv_last_launch_error naming the cause, if the
+ *   lookup fails).
+ *   Every call on one GPU shares that GPU's array and leaves its partials there: calls that
+ *   overlap on one GPU (several streams, or several host threads) race and must be ordered by
+ *   the caller. The partials need no initial value, so no clearing is done between calls.
+ */
+#define PKV_NOALLOC_SCRATCH_BYTES (64u << 20)
+int32_t pkv_paged_attention_decode_noalloc(void* out, int32_t out_dtype, const void* q,
+                                           const void* k_cache, const void* v_cache,
+                                           const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                           const int32_t* context_lens, int32_t num_seqs,
+                                           int32_t num_q_heads, float scale, int32_t max_context_len,
+                                           const pkv_cache_desc* cache, void* stream);
+
+/*
  * paged_attention_ragged — one selective-batching step: a flattened batch of query rows
  * from several sequences, some prefill chunks and some single decode rows
  * (「Paged Attention&Orca Paper笔记与解读」 §Orca的Solution).

@@ -120,6 +120,10 @@ int32_t launched(hipError_t e) {
 
 }  // namespace
 
+namespace pkv {
+void set_last_launch_error(hipError_t e) { g_last_launch = e; }
+}  // namespace pkv
+
 extern "C" {
 
 const char* pkv_last_launch_error(void) { return hipGetErrorName(g_last_launch); }

@@ -25,6 +25,9 @@ inline int ilog2(int x) {
   return r;
 }
 
+// Records the HIP status that pkv_last_launch_error() reports (api.cpp).
+void set_last_launch_error(hipError_t e);
+
 template <class T> struct NonDeduced { using type = T; };
 
 // Enqueue kernel<<<grid, block, 0, stream>>>(args...) and return the status of this launch

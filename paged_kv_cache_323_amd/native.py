@@ -101,6 +101,8 @@ _SIGS = {
     "pkv_decode_partition_size": (_I32, [_I32, _I32, _I32, _DESC]),
     "pkv_paged_attention_decode": (_I32, [_P, _I32, _P, _P, _P, _P, _I32, _P, _I32, _I32, ctypes.c_float,
                                           _I32, _DESC, _P, _SZ, _P]),
+    "pkv_paged_attention_decode_noalloc": (_I32, [_P, _I32, _P, _P, _P, _P, _I32, _P, _I32, _I32, ctypes.c_float,
+                                                  _I32, _DESC, _P]),
     "pkv_paged_attention_decode_ex": (_I32, [_P, _I32, _P, _P, _P, _P, _I32, _P, _I32, _I32, ctypes.c_float,
                                              _I32, _DESC, _I32, _P, _SZ, _P]),
     "pkv_paged_attention_decode_partitions": (_I32, [_P, _I32, _P, _P, _P, _P, _I32, _P, _I32, _I32,
@@ -302,6 +304,25 @@ def paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_lens,
             _dev(context_lens, "context_lens", torch.int32), S, hq, float(scale), int(max_context_len),
             ctypes.byref(desc), int(partition_size), ws, wsb, _stream(stream))
     _check(st, f"paged_attention_decode[{stage}]")
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20  # PKV_NOALLOC_SCRATCH_BYTES
+
+
+def paged_attention_decode_noalloc(out, q, k_cache, v_cache, block_tables, context_lens, scale: float,
+                                   max_context_len: int, desc: CacheDesc, stream=None) -> None:
+    """paged_attention_decode with the library's own fixed scratch array instead of a workspace
+    (see include/pagedkv.h); raises PagedKVError(PKV_EWORKSPACE) when the call needs more."""
+    torch = _torch()
+    S, hq, d = q.shape
+    if out.shape != q.shape or block_tables.dim() != 2 or block_tables.shape[0] != S:
+        raise ValueError("shape mismatch")
+    st = _lib.pkv_paged_attention_decode_noalloc(
+        _dev(out, "out"), _tdtype_code(out), _dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
+        _dev(block_tables, "block_tables", torch.int32), int(block_tables.shape[1]),
+        _dev(context_lens, "context_lens", torch.int32), S, hq, float(scale), int(max_context_len),
+        ctypes.byref(desc), _stream(stream))
+    _check(st, "paged_attention_decode_noalloc")
 
 
 def decode_items(context_lens_host, partition_size: int) -> np.ndarray:

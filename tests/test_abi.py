@@ -251,3 +251,18 @@ def test_decode_items_launch_validation():
             ctypes.c_void_p(1), 8, ctypes.c_void_p(1), 2, 4, 0.125, 100, ctypes.byref(c)]
     assert L.pkv_paged_attention_decode_partitions_items(*args, 0, ctypes.c_void_p(1), 3, None, 0, None) == -1
     assert L.pkv_paged_attention_decode_partitions_items(*args, 128, None, 3, None, 0, None) == -1
+
+
+def test_noalloc_decode_host_validation():
+    """The no-alloc decode entry point sizes its partials on the host before any device call:
+    too large for the library's scratch array gives PKV_EWORKSPACE, a bad cache or head count
+    the usual codes, and an empty batch succeeds without touching a device."""
+    def call(c, S, hq, max_ctx, mb=8):
+        return L.pkv_paged_attention_decode_noalloc(ctypes.c_void_p(1), c.dtype, ctypes.c_void_p(1),
+                                                    ctypes.c_void_p(1), ctypes.c_void_p(1), ctypes.c_void_p(1), mb,
+                                                    ctypes.c_void_p(1), S, hq, 0.125, max_ctx, ctypes.byref(c), NULL)
+    big = desc(num_blocks=1 << 16, num_kv_heads=8, head_dim=128, dtype=pk.BF16)
+    assert call(big, 4096, 32, 131072, mb=8192) == -4        # 4.3 GB of partials > 64 MiB
+    assert call(desc(block_size=12), 2, 4, 100) == -3
+    assert call(desc(), 2, 6, 100) == -3                       # 6 query heads over 4 kv heads
+    assert call(desc(), 0, 4, 0) == 0                          # nothing to do, nothing touched
