@@ -362,17 +362,36 @@ def measured_gather_peak(loop):
 
 
 def measured_copy_peak():
-    """Streaming-copy probe: torch copy of 1 GiB into another 1 GiB buffer (read + write), median
-    of 20; the achievable counterpart of the 8 TB/s specification."""
+    """Streaming-copy probe (libpkv_probe.so): 1 GiB copied into another 1 GiB buffer with
+    16-byte non-temporal loads and stores, 4 in flight per thread, best grid of 8192/16384/32768
+    workgroups, median of 20 each; counted as read + write bytes. The attainable rate of a
+    contiguous copy, which copy_blocks, the cache write and swap are set against."""
+    import ctypes
     import torch
+    lib = ctypes.CDLL(os.path.join(ROOT, "paged_kv_cache_323_amd", "libpkv_probe.so"))
+    lib.pkvprobe_stream_copy.restype = ctypes.c_int32
+    lib.pkvprobe_stream_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32,
+                                         ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p]
     n = 1 << 30
     src = torch.empty(n, dtype=torch.uint8, device="cuda")
     src.fill_(3)
     dst = torch.empty_like(src)
-    med, _ = _time_events(lambda: dst.copy_(src), reps=20, warm=3)
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    best = 0.0
+    for grid in (8192, 16384, 32768):
+        def call(g=grid):
+            st = lib.pkvprobe_stream_copy(ctypes.c_void_p(dst.data_ptr()), ctypes.c_void_p(src.data_ptr()), n, g, 4,
+                                          3, stream)
+            if st != 0:
+                raise RuntimeError(f"stream-copy probe failed: {st}")
+        med, _ = _time_events(call, reps=20, warm=3)
+        best = max(best, 2 * n / med / 1e3)
+    ok = bool(torch.equal(dst[:: 1 << 20], src[:: 1 << 20]))
     del src, dst
     torch.cuda.empty_cache()
-    return 2 * n / med / 1e3  # GB/s
+    if not ok:
+        raise RuntimeError("stream-copy probe did not copy")
+    return best  # GB/s
 
 
 # Longest length a request of each workload may reach: what max-length preallocation reserves.
@@ -470,6 +489,12 @@ def run_shared_prefix():
     med, _ = _time_events(lambda: pk.copy_blocks(kc, vc, big, desc), reps=20)
     res["copy_4096_pairs_us"] = round(med, 1)
     res["copy_4096_pairs_gbs"] = round(2 * 2 * 4096 * blk_bytes / med / 1e3, 1)
+    # the same copy between two runs of consecutive blocks: what the kernel moves when the pool's
+    # placement is not scattered (the gap to the random pairs is the cost of placement)
+    seq = torch.from_numpy(np.ascontiguousarray(np.stack([np.arange(4096), np.arange(4096, 8192)], 1)
+                                                .astype(np.int32))).cuda()
+    med, _ = _time_events(lambda: pk.copy_blocks(kc, vc, seq, desc), reps=20)
+    res["copy_4096_sequential_pairs_gbs"] = round(2 * 2 * 4096 * blk_bytes / med / 1e3, 1)
     del kc, vc
     torch.cuda.empty_cache()
     return res
@@ -608,6 +633,12 @@ def run_mixed():
     w_us, _ = _time_events(lambda: pk.kv_cache_write(kd, vd, st.k_cache, st.v_cache, slots, st.desc), reps=20)
     res["kv_cache_write_us"] = round(w_us, 1)
     res["kv_cache_write_gbs"] = round(write_bytes / w_us / 1e3, 1)
+    # from cold caches (a 512 MiB write before each call), as when the step's K/V rows come from
+    # elsewhere: 186 MB moved, so part of it would otherwise stay in the 256 MB MALL
+    w_us, _ = _time_events(lambda: pk.kv_cache_write(kd, vd, st.k_cache, st.v_cache, slots, st.desc), reps=20,
+                           evict=True)
+    res["kv_cache_write_cold_us"] = round(w_us, 1)
+    res["kv_cache_write_cold_gbs"] = round(write_bytes / w_us / 1e3, 1)
     del st
     torch.cuda.empty_cache()
     return res
@@ -661,18 +692,42 @@ def cpu_baseline(w, budget_s=12.0):
                       f"({n1} runs with 1 thread)"}
 
 
-def source_digest() -> str:
-    """Digest of the decode kernel's code: counter-derived figures are only valid for it. Comments
+def source_digest(name: str = "decode.hip") -> str:
+    """Digest of a kernel source's code: counter-derived figures are only valid for it. Comments
     and whitespace are left out, so editing a comment does not invalidate the counters."""
     import hashlib
     import re
-    src = os.path.join(ROOT, "paged_kv_cache_323_amd", "csrc", "decode.hip")
+    src = os.path.join(ROOT, "paged_kv_cache_323_amd", "csrc", name)
     with open(src, encoding="utf-8") as f:
         text = f.read()
     text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)  # block comments
     text = re.sub(r"//[^\n]*", " ", text)                 # line comments
     code = "".join(text.split())
     return hashlib.sha256(code.encode()).hexdigest()[:16]
+
+
+def _read_summary(path):
+    kv = {}
+    with open(path) as f:
+        for line in f:
+            if "=" in line and not line.startswith("#"):
+                k, v = line.strip().split("=", 1)
+                kv[k.strip()] = v.strip()
+    return kv
+
+
+def load_copy_traffic():
+    """HBM traffic over algorithmic bytes of the copy kernels (copy_blocks, the cache write, swap)
+    from the committed counter summary, keyed by workload, or {} when it was taken on a different
+    cache_ops.hip."""
+    path = os.path.join(ROOT, "profiles", "copy_kernels_traffic.txt")
+    if not os.path.exists(path):
+        return {}
+    kv = _read_summary(path)
+    if kv.get("source_digest") != source_digest("cache_ops.hip"):
+        return {}
+    return {k[: -len("_traffic_over_algorithmic")]: float(v) for k, v in kv.items()
+            if k.endswith("_traffic_over_algorithmic")}
 
 
 def load_traffic(block_size: int):
@@ -682,12 +737,7 @@ def load_traffic(block_size: int):
     path = os.path.join(ROOT, "profiles", f"decode_gqa_B{block_size}_traffic.txt")
     if not os.path.exists(path):
         return None
-    kv = {}
-    with open(path) as f:
-        for line in f:
-            if "=" in line and not line.startswith("#"):
-                k, v = line.strip().split("=", 1)
-                kv[k.strip()] = v.strip()
+    kv = _read_summary(path)
     if kv.get("source_digest") != source_digest():
         return None
     try:
@@ -699,8 +749,8 @@ def load_traffic(block_size: int):
 
 
 def profile_copy(reps: int = 10):
-    """Calibration for HBM counters: copy_blocks of 4096 whole blocks (f16, 32 heads x 16 slots
-    x 128 dims), 1 GiB read and 1 GiB written per launch."""
+    """Counter target and calibration for HBM counters: copy_blocks of 4096 whole blocks (f16, 32
+    heads x 16 slots x 128 dims, random pairs), 1 GiB read and 1 GiB written per launch."""
     import torch
     from paged_kv_cache_323_amd import native as pk
     nb, H, B, D = 8192, 32, 16, 128
@@ -714,6 +764,55 @@ def profile_copy(reps: int = 10):
     torch.cuda.synchronize()
     print(json.dumps({"copy_blocks_pairs": 4096, "bytes_read_per_launch": 2 * 4096 * H * B * D * 2,
                       "bytes_written_per_launch": 2 * 4096 * H * B * D * 2, "launches": reps}))
+
+
+def profile_write(reps: int = 10):
+    """Counter target: kv_cache_write of the 13B-shaped mixed step's new tokens (9421 tokens x 40
+    kv heads x 128 dims, bf16, B=16) into the slots the block manager gives them."""
+    import torch
+    from paged_kv_cache_323_amd import native as pk
+    from paged_kv_cache_323_amd import runner as R
+    from workloads import make_workload
+    w = make_workload("mixed", "full")
+    st = R.play_script(w, threads=16)
+    step_op = w.ops[-1]
+    k, v = w.append_values(step_op, threads=16)
+    kd, vd = R.to_device(k, w.dtype), R.to_device(v, w.dtype)
+    slots = torch.from_numpy(np.ascontiguousarray(st.slots_per_append[-1])).cuda()
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        pk.kv_cache_write(kd, vd, st.k_cache, st.v_cache, slots, st.desc)
+    torch.cuda.synchronize()
+    T = int(kd.shape[0])
+    row = w.num_kv_heads * w.head_dim * 2
+    print(json.dumps({"kv_cache_write_tokens": T, "bytes_read_per_launch": 2 * T * row,
+                      "bytes_written_per_launch": 2 * T * row, "launches": reps,
+                      "setup_launches_before": "the script's own cache writes (one per append)"}))
+
+
+def profile_swap(reps: int = 5):
+    """Counter target: pkv_swap_blocks of 4096 GQA-shaped blocks (8 kv heads x 16 slots x 128 dims,
+    bf16) out to a pinned host pool, then back in; 256 MiB each way per launch."""
+    import torch
+    from paged_kv_cache_323_amd import native as pk
+    nb, H, B, D = 8192, 8, 16, 128
+    dk = torch.empty((nb, H, B, D), dtype=torch.bfloat16, device="cuda").normal_()
+    dv = torch.empty_like(dk).normal_()
+    hk = torch.empty((nb, H, B, D), dtype=torch.bfloat16, pin_memory=True)
+    hv = torch.empty_like(hk, pin_memory=True)
+    desc = pk.CacheDesc.make(nb, B, H, D, "bf16")
+    n = 4096
+    perm = np.random.default_rng(9).permutation(nb).astype(np.int32)
+    out_pairs = torch.from_numpy(np.ascontiguousarray(np.stack([perm[:n], perm[n:2 * n]], 1))).cuda()
+    in_pairs = torch.from_numpy(np.ascontiguousarray(np.stack([perm[n:2 * n], perm[:n]], 1))).cuda()
+    for _ in range(reps):
+        pk.swap_blocks(hk, hv, dk, dv, out_pairs, desc)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        pk.swap_blocks(dk, dv, hk, hv, in_pairs, desc)
+    torch.cuda.synchronize()
+    print(json.dumps({"swap_blocks": n, "bytes_per_direction_per_launch": 2 * n * H * B * D * 2,
+                      "launches_out_then_in": reps}))
 
 
 def prefill_only(dtype: str = "bf16", reps: int = 20, warm: int = 50, prompts=None):
@@ -755,7 +854,7 @@ def profile_prefill(dtype: str = "bf16"):
 HOST_LINK_GBS = 64.0  # PCIe 5.0 x16 per direction, the swap path's link
 
 
-def row_rooflines(result, extra, read_peak, copy_peak):
+def row_rooflines(result, extra, read_peak, copy_peak, copy_traffic=None):
     """Each hot-path row beside the ceiling that bounds it: achieved, ceiling, fraction. HBM rows
     are set against the 8 TB/s specification and the measured read (decode) or copy (write and
     copy kernels, read + write) ceiling; prefill against the bf16 MFMA peak; swap against the
@@ -763,6 +862,7 @@ def row_rooflines(result, extra, read_peak, copy_peak):
     def hbm(achieved, measured):
         return {"achieved_gbs": round(achieved, 1), "frac_of_spec": round(achieved / HBM_PEAK_GBS, 4),
                 "measured_ceiling_gbs": round(measured, 1), "frac_of_measured": round(achieved / measured, 4)}
+    copy_traffic = copy_traffic or {}
     rows = {"a5_a6_decode_gqa": dict(hbm(result["roofline"]["achieved"], read_peak),
                                      kernel_us=result["roofline"]["kernel_avg_us"])}
     if "measured_gather_peak" in result["roofline"]:  # the same tiles read with no arithmetic
@@ -775,6 +875,11 @@ def row_rooflines(result, extra, read_peak, copy_peak):
     m = extra.get("mixed", {})
     if "kv_cache_write_gbs" in m:
         rows["a4_kv_cache_write"] = dict(hbm(m["kv_cache_write_gbs"], copy_peak), us=m["kv_cache_write_us"])
+        if "kv_cache_write_cold_gbs" in m:
+            rows["a4_kv_cache_write"]["cold_caches_gbs"] = m["kv_cache_write_cold_gbs"]
+            rows["a4_kv_cache_write"]["cold_frac_of_measured"] = round(m["kv_cache_write_cold_gbs"] / copy_peak, 4)
+        if "kv_cache_write" in copy_traffic:
+            rows["a4_kv_cache_write"]["traffic_over_algorithmic"] = copy_traffic["kv_cache_write"]
     if "prefill_tflops" in m:
         rows["a7_prefill"] = {"achieved_tflops": m["prefill_tflops"], "peak_tflops": MFMA_BF16_PEAK_TFLOPS,
                               "frac": m["prefill_mfma_util"], "us": m["prefill_only_us"]}
@@ -789,12 +894,22 @@ def row_rooflines(result, extra, read_peak, copy_peak):
     sp = extra.get("shared_prefix", {})
     if "copy_4096_pairs_gbs" in sp:
         rows["a3_copy_blocks_4096_pairs"] = hbm(sp["copy_4096_pairs_gbs"], copy_peak)
+        if "copy_4096_sequential_pairs_gbs" in sp:
+            # the same copy between consecutive blocks: the kernel without the pool's scatter
+            rows["a3_copy_blocks_4096_pairs"]["sequential_pairs_gbs"] = sp["copy_4096_sequential_pairs_gbs"]
+            rows["a3_copy_blocks_4096_pairs"]["sequential_frac_of_measured"] = round(
+                sp["copy_4096_sequential_pairs_gbs"] / copy_peak, 4)
+        if "copy_blocks" in copy_traffic:
+            rows["a3_copy_blocks_4096_pairs"]["traffic_over_algorithmic"] = copy_traffic["copy_blocks"]
         rows["a3_copy_blocks_48_pairs"] = {"us": sp["copy_us"], "bound": "launch latency (24 MiB)"}
     sw = extra.get("swap", {})
     if "swap_out_gbs" in sw:
         rows["swap"] = {"out_gbs": sw["swap_out_gbs"], "in_gbs": sw["swap_in_gbs"], "link_gbs": HOST_LINK_GBS,
                         "frac_out": round(sw["swap_out_gbs"] / HOST_LINK_GBS, 4),
                         "frac_in": round(sw["swap_in_gbs"] / HOST_LINK_GBS, 4)}
+        for key in ("swap_out", "swap_in"):
+            if key in copy_traffic:
+                rows["swap"][f"{key}_traffic_over_algorithmic"] = copy_traffic[key]
     return rows
 
 
@@ -817,6 +932,10 @@ def main():
                     help="pool dtype of --profile-prefill")
     ap.add_argument("--profile-copy", action="store_true",
                     help="only run the copy kernel used to calibrate HBM byte counters")
+    ap.add_argument("--profile-write", action="store_true",
+                    help="only run the cache write of the 13B-shaped mixed step (counter target)")
+    ap.add_argument("--profile-swap", action="store_true",
+                    help="only run swap-out then swap-in of 4096 blocks (counter target)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the path has no "
@@ -829,6 +948,12 @@ def main():
     torch.cuda.set_device(0)
     if args.profile_copy:
         profile_copy()
+        return
+    if args.profile_write:
+        profile_write()
+        return
+    if args.profile_swap:
+        profile_swap()
         return
     if args.profile_prefill:
         profile_prefill(args.prefill_dtype)
@@ -907,7 +1032,7 @@ def main():
             except Exception as e:  # keep the headline line even if a side measurement fails
                 extra[key] = {"error": repr(e)}
         result["extra"] = extra
-        result["rows"] = row_rooflines(result, extra, read_peak, copy_peak)
+        result["rows"] = row_rooflines(result, extra, read_peak, copy_peak, load_copy_traffic())
     if not args.no_cpu:
         log("timing the oracle on the host CPU")
         result["cpu_baseline"] = cpu_baseline(w)

@@ -20,8 +20,7 @@
  *     stream). The return value only reports host-side validation and the launches themselves.
  *     After a validation error nothing has been enqueued. PKV_ELAUNCH means one launch failed;
  *     in an entry point that issues several (decode partitions then merge, ragged decode rows
- *     then prefill rows, copies in chunks of 65535 pairs) the launches before it stay enqueued
- *     and their results are incomplete.
+ *     then prefill rows) the launches before it stay enqueued and their results are incomplete.
  *   - Device-resident indices (block ids, slots, lengths) are trusted: the caller guarantees
  *     they are in range. Host-visible scalars and shapes are validated.
  *   - Ordering between calls is the caller's job: on one stream, copy_blocks for an append's

@@ -174,7 +174,8 @@ int32_t pkv_kv_cache_write(const void* k, const void* v, void* k_cache, void* v_
   if (k_token_stride < row || v_token_stride < row || k_token_stride % 8 || v_token_stride % 8)
     return PKV_EINVAL;
   const int es = elem_bytes(c->dtype);
-  if ((uint64_t)num_tokens * c->num_kv_heads * (c->head_dim * es / 16) > 0xffffffffull) return PKV_ESHAPE;
+  // 16-byte chunks are counted in 32 bits, with room for the launch's last group of 256 x 8
+  if ((uint64_t)num_tokens * c->num_kv_heads * (c->head_dim * es / 16) > 0xffffffffull - 2048) return PKV_ESHAPE;
   return launched(pkv::launch_kv_cache_write(k, v, k_cache, v_cache, slot_mapping, num_tokens,
                                              k_token_stride * es, v_token_stride * es, c->num_kv_heads,
                                              c->block_size, c->head_dim, es, c->num_blocks, (hipStream_t)stream));

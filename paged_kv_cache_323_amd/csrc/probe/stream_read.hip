@@ -93,3 +93,60 @@ extern "C" int32_t pkvprobe_gather_read(const void* pool_k, const void* pool_v, 
   return (int32_t)hipLaunchKernel(reinterpret_cast<const void*>(&gather_read_kernel), dim3((unsigned)grid), dim3(256),
                                   args, 0, (hipStream_t)stream);
 }
+
+// Streaming-copy probe: dst <- src over `bytes`, 16 bytes per thread access, U accesses in
+// flight per thread (all loads of a group issued before its stores), grid-stride over groups of
+// U x 256 chunks per workgroup. `nt` selects non-temporal loads (bit 0) and stores (bit 1). The
+// benchmark takes the best rate over a few grids and variants as the attainable copy bandwidth
+// (bytes read + bytes written per second) that copy_blocks, the cache write and swap face.
+//
+//   int32_t pkvprobe_stream_copy(void* dst, const void* src, size_t bytes, int32_t grid,
+//                                int32_t unroll, int32_t nt, void* stream)
+// dst, src: device memory, 16-byte aligned, not overlapping; bytes: a multiple of 16 * 256 *
+// unroll; unroll: 1, 2, 4 or 8; grid: workgroups of 256 threads (1..65535). Returns 0, -1 on bad
+// arguments, or the hipError_t of the launch.
+template <int U, int NT>
+__global__ __launch_bounds__(256) void stream_copy_kernel(u32x4* __restrict__ d, const u32x4* __restrict__ s,
+                                                          size_t groups) {
+  for (size_t g = blockIdx.x; g < groups; g += gridDim.x) {
+    const size_t base = g * (256 * U) + threadIdx.x;
+    u32x4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = (NT & 1) ? __builtin_nontemporal_load(s + base + 256 * u) : s[base + 256 * u];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (NT & 2)
+        __builtin_nontemporal_store(v[u], d + base + 256 * u);
+      else
+        d[base + 256 * u] = v[u];
+    }
+  }
+}
+
+template <int U>
+static const void* copy_kernel_for(int nt) {
+  switch (nt) {
+    case 0: return reinterpret_cast<const void*>(&stream_copy_kernel<U, 0>);
+    case 1: return reinterpret_cast<const void*>(&stream_copy_kernel<U, 1>);
+    case 2: return reinterpret_cast<const void*>(&stream_copy_kernel<U, 2>);
+    default: return reinterpret_cast<const void*>(&stream_copy_kernel<U, 3>);
+  }
+}
+
+extern "C" int32_t pkvprobe_stream_copy(void* dst, const void* src, size_t bytes, int32_t grid, int32_t unroll,
+                                        int32_t nt, void* stream) {
+  if (!dst || !src || (uintptr_t)dst % 16 || (uintptr_t)src % 16 || grid < 1 || grid > 65535) return -1;
+  if ((unroll != 1 && unroll != 2 && unroll != 4 && unroll != 8) || nt < 0 || nt > 3) return -1;
+  const size_t group_bytes = (size_t)16 * 256 * unroll;
+  if (bytes == 0 || bytes % group_bytes) return -1;
+  const char* s8 = static_cast<const char*>(src);
+  const char* d8 = static_cast<const char*>(dst);
+  if (!(d8 + bytes <= s8 || s8 + bytes <= d8)) return -1;  // overlapping ranges
+  u32x4* d = static_cast<u32x4*>(dst);
+  const u32x4* s = static_cast<const u32x4*>(src);
+  size_t groups = bytes / group_bytes;
+  void* args[] = {&d, &s, &groups};
+  const void* k = unroll == 1 ? copy_kernel_for<1>(nt) : unroll == 2 ? copy_kernel_for<2>(nt)
+                : unroll == 4 ? copy_kernel_for<4>(nt) : copy_kernel_for<8>(nt);
+  return (int32_t)hipLaunchKernel(k, dim3(grid), dim3(256), args, 0, (hipStream_t)stream);
+}
