@@ -314,6 +314,8 @@ int32_t pkv_paged_attention_decode_noalloc(void* out, int32_t out_dtype, const v
  *   max_q_len <= num_q_heads / num_kv_heads (and num_tokens <= 65535): then, as always for an
  *   f32 pool with max_q_len > 1, every row runs through the decode kernels in fp32, one query
  *   row per item (an f32 pool's call takes at most 65535 rows, PKV_ESHAPE beyond).
+ *   num_seqs is at most 65535 (PKV_ESHAPE beyond); the MFMA prefill launch itself has no row
+ *   limit. Every validation error is returned before anything is enqueued.
  *   workspace     device, >= pkv_ragged_workspace_bytes(...) bytes (NULL when that is 0);
  *                 scratch between calls, as for decode.
  */
