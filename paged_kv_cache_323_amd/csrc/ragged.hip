@@ -128,7 +128,8 @@ __global__ __launch_bounds__(kPfThreads, 2) void ragged_prefill_kernel(PrefillAr
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar branches on it
   const int h = blockIdx.x;
-  const int kvh = h / (a.hq / a.hkv);
+  // uniform (the integer division would otherwise leave it, and what depends on it, in VGPRs)
+  const int kvh = __builtin_amdgcn_readfirstlane(h / (a.hq / a.hkv));
   // ---- which (sequence, row tile) this workgroup owns ----------------------------------------
   // Slot y is the y-th row tile counted back from the last tile of the last sequence: the last
   // row tiles of the last sequences (the longest causal rows, hence the most key tiles) are
@@ -209,7 +210,10 @@ __global__ __launch_bounds__(kPfThreads, 2) void ragged_prefill_kernel(PrefillAr
   for (int nt = 0; nt < 2; ++nt) {
     const int r = wave * 32 + nt * 16 + lr;  // row within the tile
     qvalid[nt] = r < nrows;
-    qpos[nt] = pos0 + r;
+    // A padding row (past the tile's last row) is masked like the last row, so it never sees a key
+    // past the context: those keys' slots may hold anything, and its output is not stored, but
+    // a non-finite value in it would still send the tile down the bf16 fallback path.
+    qpos[nt] = pos0 + min(r, nrows - 1);
     const uint16_t* qp = a.q + ((size_t)(q0 + row0 + (qvalid[nt] ? r : 0)) * a.hq + h) * D + 8 * g;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
@@ -222,7 +226,10 @@ __global__ __launch_bounds__(kPfThreads, 2) void ragged_prefill_kernel(PrefillAr
   f32x4 oacc[DT16][2];
   float m_run[2];                              // reference max of each row (raw score units)
   const float lazy_thr = 8.f / a.scale_log2;  // 2^8 in probability terms, in raw score units
-  float l_part[2];                             // this lane's share of the row sum (its 4-key slices)
+  // Row sums of the probabilities as MFMA'd (f16, or the bf16 parts): ones·Pᵀ accumulated beside
+  // Oᵀ, so every element of a lane's accumulator holds its row's sum and the normaliser is taken
+  // from the same rounded probabilities as the products.
+  f32x4 lacc[2];
 
   const int32_t* trow = a.tables + (size_t)s * a.max_blocks;
   const uint32_t blk_elems = (uint32_t)(a.hkv * a.bs * D);  // elements of one pool block
@@ -250,7 +257,7 @@ __global__ __launch_bounds__(kPfThreads, 2) void ragged_prefill_kernel(PrefillAr
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt) oacc[dt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
     m_run[0] = m_run[1] = -INFINITY;
-    l_part[0] = l_part[1] = 0.f;
+    lacc[0] = lacc[1] = f32x4{0.f, 0.f, 0.f, 0.f};
     int tab_base = -kPfTab;  // first table entry held in s_tab
 
     // Global -> register staging of one key tile. Keys past kend are clamped to key kend-1 (a
@@ -261,12 +268,18 @@ __global__ __launch_bounds__(kPfThreads, 2) void ragged_prefill_kernel(PrefillAr
     u32x4 vreg[VIT][2];
     auto fetch = [&](int kt) {
       const int k0 = kt * kPfKeys;
-      uint32_t inner[KIT], phys[KIT];
+      // K: in iteration it, wave w reads the 64 chunks it..., i.e. keys key0 .. key0 + 64/CPR - 1 of
+      // the tile: 1 KiB that lies in one block (key0 is a multiple of 4 or 8, B of 8). Its base is
+      // wave-uniform (table entry read at a uniform LDS address, scalar arithmetic); each lane adds
+      // its own 16 bytes. A group past the context reads the last block's rows: those keys are
+      // masked for every row of the tile (their scores may be NaN; masking selects).
+      uint64_t kbase[KIT];
 #pragma unroll
       for (int it = 0; it < KIT; ++it) {
-        const int kk = min(k0 + (it * kPfThreads + tid) / CPR, kend - 1);
-        phys[it] = (uint32_t)s_tab[(kk >> a.log2_bs) - tab_base];
-        inner[it] = head_off + (uint32_t)(kk & (a.bs - 1)) * D + ((it * kPfThreads + tid) % CPR) * 8;
+        const int kk0 = k0 + (it * kPfThreads + kWave * wave) / CPR;  // uniform
+        const int j = min(kk0 >> a.log2_bs, nblk - 1);
+        const uint32_t phys = (uint32_t)__builtin_amdgcn_readfirstlane(s_tab[j - tab_base]);
+        kbase[it] = (uint64_t)phys * blk_elems + head_off + (uint32_t)(kk0 & (a.bs - 1)) * D;
       }
       // Every V chunk of this thread covers the same key pair (kp = tid mod 32); the pair shares
       // a block because B is even.
@@ -276,8 +289,7 @@ __global__ __launch_bounds__(kPfThreads, 2) void ragged_prefill_kernel(PrefillAr
       const uint64_t vbase = (uint64_t)vphys * blk_elems + head_off;
       const uint32_t v0 = (uint32_t)(kv0 & (a.bs - 1)) * D, v1 = (uint32_t)(kv1 & (a.bs - 1)) * D;
 #pragma unroll
-      for (int it = 0; it < KIT; ++it)
-        kreg[it] = *reinterpret_cast<const u32x4*>(a.kc + ((uint64_t)phys[it] * blk_elems + inner[it]));
+      for (int it = 0; it < KIT; ++it) kreg[it] = *reinterpret_cast<const u32x4*>(a.kc + kbase[it] + 8 * lane);
 #pragma unroll
       for (int it = 0; it < VIT; ++it) {
         const uint32_t ch8 = ((it * kPfThreads + tid) / (kPfKeys / 2)) * 8;
@@ -413,26 +425,25 @@ __global__ __launch_bounds__(kPfThreads, 2) void ragged_prefill_kernel(PrefillAr
         // more than 2^8 in probability terms; until then probabilities may reach 2^8, which fp32
         // sums and the 16-bit split represent as well as values below 1. A row with no visible key
         // yet keeps m_run = -inf (its probabilities are exactly 0).
+        // The wave's first tile sets the reference max directly (the accumulators are still zero;
+        // every row sees key 0, so the max is finite).
         const bool grow = mx > m_run[nt] + lazy_thr;
-        if (__builtin_amdgcn_read_exec() & __ballot(grow)) {  // wave-uniform
+        if (kt == 0) {
+          m_run[nt] = mx;
+        } else if (__builtin_amdgcn_read_exec() & __ballot(grow)) {  // wave-uniform
           const float m_new = fmaxf(m_run[nt], mx);
           const float alpha = m_run[nt] == -INFINITY ? 0.f : fast_exp2((m_run[nt] - m_new) * a.scale_log2);
           m_run[nt] = m_new;
-          l_part[nt] *= alpha;
+          lacc[nt] *= alpha;
 #pragma unroll
           for (int dt = 0; dt < DT16; ++dt) oacc[dt][nt] *= alpha;
         }
         const float off = -(m_run[nt] == -INFINITY ? 0.f : m_run[nt]) * a.scale_log2;
-        float lsum = 0.f;
         float p[4][4];
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            p[mt][i] = fast_exp2(__builtin_fmaf(sacc[mt][nt][i], a.scale_log2, off));
-            lsum += p[mt][i];
-          }
-        l_part[nt] += lsum;
+          for (int i = 0; i < 4; ++i) p[mt][i] = fast_exp2(__builtin_fmaf(sacc[mt][nt][i], a.scale_log2, off));
         // B operand of k-step j: keys 32j + 4g + (0..3) then 32j + 16 + 4g + (0..3); element e of
         // the operand is the low (e even) or high half of word e/2.
 #pragma unroll
@@ -490,6 +501,16 @@ __global__ __launch_bounds__(kPfThreads, 2) void ragged_prefill_kernel(PrefillAr
             if constexpr (kSplitP) oacc[dt][nt] = PV::mma(va, plo[nt][j], oacc[dt][nt]);
           }
         }
+        // row sums: a ones operand against the same P operands (1.0 is 0x3c00 in f16, 0x3f80 in bf16)
+        const uint32_t one2 = kSplitP ? 0x3f803f80u : 0x3c003c00u;
+        const PV8 ones = __builtin_bit_cast(PV8, u32x4{one2, one2, one2, one2});
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int nt = 0; nt < 2; ++nt) {
+            lacc[nt] = PV::mma(ones, phi[nt][j], lacc[nt]);
+            if constexpr (kSplitP) lacc[nt] = PV::mma(ones, plo[nt][j], lacc[nt]);
+          }
 #if PF_SCHED
         __builtin_amdgcn_sched_group_barrier(0x100, kPfLookahead, 2);
 #pragma unroll
@@ -533,7 +554,7 @@ __global__ __launch_bounds__(kPfThreads, 2) void ragged_prefill_kernel(PrefillAr
   // ---- normalise and store: lane writes dims 16*dt + 4*g .. +3 of its row ----------------------
 #pragma unroll
   for (int nt = 0; nt < 2; ++nt) {
-    const float l = sum_rows4(l_part[nt]);
+    const float l = lacc[nt][0];
     if (!qvalid[nt]) continue;
     const float inv = l > 0.f ? 1.f / l : 0.f;
     const size_t orow = ((size_t)(q0 + wave * 32 + nt * 16 + lr + row0) * a.hq + h) * D;
