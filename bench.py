@@ -748,6 +748,77 @@ def load_traffic(block_size: int):
         return None
 
 
+def layout_study(layout: str):
+    """The GQA decode step (B = 16) with the library PAGEDKV_LIB points to, whose pools are stored
+    head-major (the product) or token-major (the tuning build of build.py --token-major): the
+    partition launch's event time over 20-step windows, a row-gather probe reading exactly the
+    (block, kv head) tiles of the step in that layout's pattern, and the cache write. Prints one
+    JSON line; a rocprofv3 counter target as well."""
+    import ctypes
+    import torch
+    from paged_kv_cache_323_amd import native as pk
+    from workloads import make_workload
+    token_major = layout == "token"
+    w = make_workload("gqa", "full", block_size=16)
+    loop = DecodeLoop(w, 5 + 10 * 20 + 5)
+    for _ in range(5):
+        loop.step()
+    torch.cuda.synchronize()
+    loop.snapshot = loop.st.bm.clone()
+    loop.repeat_attention(200)
+    torch.cuda.synchronize()
+    _, kern_ms, merge_ms = _timed_windows(loop, 20, 0.05, 5, 50, ev=True)
+    alg = sum(decode_algorithmic_bytes(c, w, 2)[1] for c in loop.ctx_history) / 20
+    k_us = float(np.mean(kern_ms)) * 1e3
+    out = loop.out.float().cpu().numpy()
+    res = {"layout": "token-major" if token_major else "head-major", "library": os.path.basename(pk.LIB_PATH),
+           "partition_us": round(k_us, 1), "partition_gbs": round(alg / k_us / 1e3, 1),
+           "merge_us": round(float(np.mean(merge_ms)) * 1e3, 2), "algorithmic_bytes": int(alg),
+           "output_checksum": int(np.frombuffer(out.tobytes(), dtype=np.uint32).astype(np.uint64).sum() % (1 << 61))}
+    lib = ctypes.CDLL(os.path.join(ROOT, "paged_kv_cache_323_amd", "libpkv_probe.so"))
+    lib.pkvprobe_gather_rows.restype = ctypes.c_int32
+    lib.pkvprobe_gather_rows.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
+                                         ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int64, ctypes.c_int32,
+                                         ctypes.c_void_p, ctypes.c_void_p]
+    tables, lens = loop.st.bm.block_tables(loop.seqs, loop.max_blocks)
+    H, B, D = w.num_kv_heads, w.block_size, w.head_dim
+    row_bytes = D * 2
+    parts = []
+    for s in range(len(lens)):
+        blocks = tables[s, : -(-int(lens[s]) // B)].astype(np.int64)
+        if token_major:  # tile (b, h) starts at row b*B*H + h (rows of D elements); rows H*D apart
+            parts.append((blocks[None, :] * B * H + np.arange(H)[:, None]).ravel())
+        else:            # tile (b, h) starts at row (b*H + h)*B; rows contiguous
+            parts.append(((blocks[None, :] * H + np.arange(H)[:, None]) * B).ravel())
+    t = np.concatenate(parts)
+    stride = H * row_bytes if token_major else row_bytes
+    assert t.min() >= 0 and t.max() * row_bytes + (B - 1) * stride + row_bytes <= w.num_blocks * H * B * row_bytes
+    tiles = torch.from_numpy(t.astype(np.int32)).cuda()
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    best = 0.0
+    for per_wg in (16, 32, 64):
+        def call(p=per_wg):
+            st = lib.pkvprobe_gather_rows(ctypes.c_void_p(loop.st.k_cache.data_ptr()),
+                                          ctypes.c_void_p(loop.st.v_cache.data_ptr()), ctypes.c_void_p(tiles.data_ptr()),
+                                          len(t), row_bytes, B, row_bytes, stride, p, ctypes.c_void_p(sink.data_ptr()),
+                                          stream)
+            if st != 0:
+                raise RuntimeError(f"row-gather probe failed: {st}")
+        med, _ = _time_events(call, reps=20, warm=3)
+        best = max(best, 2 * len(t) * B * row_bytes / med / 1e3)
+    res["row_gather_probe_gbs"] = round(best, 1)
+    res["partition_frac_of_probe"] = round(alg / k_us / 1e3 / best, 4)
+    T = 65536
+    slots = torch.from_numpy(np.random.default_rng(1).permutation(w.num_blocks * B)[:T].astype(np.int32)).cuda()
+    k = torch.randn((T, H, D), device="cuda").to(torch.bfloat16)
+    v = torch.randn_like(k)
+    wus, _ = _time_events(lambda: pk.kv_cache_write(k, v, loop.st.k_cache, loop.st.v_cache, slots, loop.st.desc),
+                          reps=20, warm=3)
+    res["write_65536_tokens_gbs"] = round(2 * 2 * T * H * D * 2 / wus / 1e3, 1)
+    print(json.dumps(res), flush=True)
+
+
 def profile_copy(reps: int = 10):
     """Counter target and calibration for HBM counters: copy_blocks of 4096 whole blocks (f16, 32
     heads x 16 slots x 128 dims, random pairs), 1 GiB read and 1 GiB written per launch."""
@@ -934,6 +1005,8 @@ def main():
                     help="only run the copy kernel used to calibrate HBM byte counters")
     ap.add_argument("--profile-write", action="store_true",
                     help="only run the cache write of the 13B-shaped mixed step (counter target)")
+    ap.add_argument("--layout-study", choices=("head", "token"), default=None,
+                    help="GQA decode and cache write with the library PAGEDKV_LIB names, pools in this layout")
     ap.add_argument("--profile-swap", action="store_true",
                     help="only run swap-out then swap-in of 4096 blocks (counter target)")
     args = ap.parse_args()
@@ -948,6 +1021,9 @@ def main():
     torch.cuda.set_device(0)
     if args.profile_copy:
         profile_copy()
+        return
+    if args.layout_study:
+        layout_study(args.layout_study)
         return
     if args.profile_write:
         profile_write()

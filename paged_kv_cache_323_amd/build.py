@@ -96,6 +96,17 @@ def build_probe() -> str:
     return PROBE_LIB
 
 
+TOKEN_MAJOR_LIB = os.path.join(PKG, "tuning", "libpagedkv_token_major.so")
+
+
+def build_token_major() -> str:
+    """A tuning build that stores the pools token-major ([N][B][H][D]) in the cache write and reads
+    them so in decode, used only to measure the layout choice (bench.py --layout-study token). Its
+    prefill kernel and pool-layout contract are the head-major ones: not a product library."""
+    os.makedirs(os.path.dirname(TOKEN_MAJOR_LIB), exist_ok=True)
+    return build(defines=("PKV_TOKEN_MAJOR",), out=TOKEN_MAJOR_LIB, build_dir=os.path.join(BUILD, "token_major"))
+
+
 def build_all(verbose: bool = False):
     """The release library, the debug (bounds-checked) library and the benchmark's probe."""
     return [build(verbose=verbose),
@@ -105,4 +116,7 @@ def build_all(verbose: bool = False):
 
 
 if __name__ == "__main__":
-    print("\n".join(build_all(verbose="-v" in sys.argv)))
+    if "--token-major" in sys.argv:
+        print(build_token_major())
+    else:
+        print("\n".join(build_all(verbose="-v" in sys.argv)))

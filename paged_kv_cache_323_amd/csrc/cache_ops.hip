@@ -73,7 +73,11 @@ __global__ __launch_bounds__(256) void kv_cache_write_kernel(
         if (slot >= 0 && (!kDebugChecks || slot < num_slots)) {
           const int64_t blk = slot >> log2_block;
           const int64_t off = slot & (block_size - 1);
+#ifdef PKV_TOKEN_MAJOR  // tuning variant: token-major pool [N][B][H][D]
+          dst[u] = ((blk * block_size + off) * num_kv_heads + h) * row_bytes + ch * 16;
+#else
           dst[u] = ((blk * num_kv_heads + h) * block_size + off) * row_bytes + ch * 16;
+#endif
           const int64_t src_in_row = (int64_t)h * row_bytes + ch * 16;
           kk[u] = load16(k + t * k_stride_b + src_in_row);
           vv[u] = load16(v + t * v_stride_b + src_in_row);

@@ -227,9 +227,18 @@ __global__ __launch_bounds__(kDecThreads, PKV_DECODE_MIN_WG) void paged_decode_k
     for (int ch = 0; ch < NCH; ++ch) qr[g][ch] = *reinterpret_cast<const u32x4*>(qb + g * D + ch * 8 * VEC);
   __syncthreads();
 
-  // Base of the (physical block, kv head) tile holding unit u; units never straddle blocks.
+  // Base of the (physical block, kv head) tile holding unit u; units never straddle blocks. Rows of
+  // a tile are D elements apart (head-major pool). PKV_TOKEN_MAJOR builds a tuning variant for the
+  // token-major layout [N][B][H][D] (rows H·D apart), used only to measure the layout choice.
+#ifdef PKV_TOKEN_MAJOR
+  const size_t tile_rows = (size_t)a.bs * a.hkv;
+  const size_t head_rows = (size_t)kvh;
+  const size_t row_stride = (size_t)a.hkv * D;
+#else
   const size_t tile_rows = (size_t)a.hkv * a.bs;
   const size_t head_rows = (size_t)kvh * a.bs;
+  const size_t row_stride = D;
+#endif
   auto tile = [&](const T* base, int u) -> const T* {
     const int phys = s_tab[(u * 8) >> a.log2_bs];
     return base + ((size_t)phys * tile_rows + head_rows) * D;
@@ -241,14 +250,15 @@ __global__ __launch_bounds__(kDecThreads, PKV_DECODE_MIN_WG) void paged_decode_k
   const int rv = lane >> 4;                // value mapping: token row within a pass of 4
 
   auto load_k = [&](int u, u32x4 (&dst)[NCH]) {
-    const T* p = tile(kbase, u) + (size_t)((u * 8 + krow) & (a.bs - 1)) * D + c * VEC;
+    const T* p = tile(kbase, u) + (size_t)((u * 8 + krow) & (a.bs - 1)) * row_stride + c * VEC;
 #pragma unroll
     for (int ch = 0; ch < NCH; ++ch) dst[ch] = load_tile(reinterpret_cast<const u32x4*>(p + ch * 8 * VEC));
   };
   auto load_v = [&](int u, Words<NWORDS> (&dst)[2]) {
     const T* p = tile(vbase, u) + cv * EPL;
 #pragma unroll
-    for (int ps = 0; ps < 2; ++ps) dst[ps] = load_words<NWORDS>(p + (size_t)((u * 8 + ps * 4 + rv) & (a.bs - 1)) * D);
+    for (int ps = 0; ps < 2; ++ps)
+      dst[ps] = load_words<NWORDS>(p + (size_t)((u * 8 + ps * 4 + rv) & (a.bs - 1)) * row_stride);
   };
 
   // ---- phase 1: scores, PF units in flight per wave ---------------------------------------------

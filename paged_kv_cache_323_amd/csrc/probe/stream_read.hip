@@ -150,3 +150,64 @@ extern "C" int32_t pkvprobe_stream_copy(void* dst, const void* src, size_t bytes
                 : unroll == 4 ? copy_kernel_for<4>(nt) : copy_kernel_for<8>(nt);
   return (int32_t)hipLaunchKernel(k, dim3(grid), dim3(256), args, 0, (hipStream_t)stream);
 }
+
+// Row-gather probe: like the tile-gather probe, but a tile is `rows` rows of `row_bytes` bytes,
+// `row_stride` bytes apart, starting at tiles[t] * unit_bytes: the (block, kv head) tile of a
+// head-major pool (rows D·e apart, contiguous) or of a token-major pool (rows H·D·e apart). One
+// 16-byte load per thread per chunk, 8 in flight, K pool then V pool, checksum as above.
+//
+//   int32_t pkvprobe_gather_rows(const void* pool_k, const void* pool_v, const uint32_t* tiles,
+//                                int32_t num_tiles, int64_t unit_bytes, int32_t rows,
+//                                int32_t row_bytes, int64_t row_stride, int32_t per_wg,
+//                                uint32_t* sink, void* stream)
+// row_bytes: a multiple of 16, with rows * row_bytes a multiple of 4096;
+// the caller keeps every row inside both pools. Returns 0, -1 on bad arguments, or the
+// hipError_t of the launch.
+__global__ __launch_bounds__(256) void gather_rows_kernel(const char* __restrict__ pk, const char* __restrict__ pv,
+                                                          const uint32_t* __restrict__ tiles, int32_t n, int64_t unit,
+                                                          int32_t cpr, int32_t chunks, int64_t stride,
+                                                          int32_t per_wg, uint32_t* __restrict__ sink) {
+  constexpr int U = 8;
+  const long long i0 = (long long)blockIdx.x * per_wg * chunks;
+  const long long i1 = min((long long)n, (long long)(blockIdx.x + 1) * per_wg) * chunks;
+  uint32_t acc = 0;
+  for (int pass = 0; pass < 2; ++pass) {
+    const char* pool = pass ? pv : pk;
+    auto addr = [&](long long i) {  // 4 KiB chunk c of entry t: 256 threads x 16 bytes
+      const long long t = i / chunks, c = i - t * chunks;
+      const long long e = c * 256 + threadIdx.x;  // 16-byte piece within the tile
+      const long long row = e / cpr, col = e - row * cpr;
+      return reinterpret_cast<const u32x4*>(pool + (long long)tiles[t] * unit + row * stride + col * 16);
+    };
+    long long i = i0;
+    for (; i + U <= i1; i += U) {
+      u32x4 v[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) v[u] = __builtin_nontemporal_load(addr(i + u));
+#pragma unroll
+      for (int u = 0; u < U; ++u) acc ^= v[u][0] ^ v[u][1] ^ v[u][2] ^ v[u][3];
+    }
+    for (; i < i1; ++i) {
+      const u32x4 v = __builtin_nontemporal_load(addr(i));
+      acc ^= v[0] ^ v[1] ^ v[2] ^ v[3];
+    }
+  }
+  if (acc == 0x12345679u) sink[0] = acc;
+}
+
+extern "C" int32_t pkvprobe_gather_rows(const void* pool_k, const void* pool_v, const uint32_t* tiles,
+                                        int32_t num_tiles, int64_t unit_bytes, int32_t rows, int32_t row_bytes,
+                                        int64_t row_stride, int32_t per_wg, uint32_t* sink, void* stream) {
+  if (!pool_k || !pool_v || !tiles || !sink || (uintptr_t)pool_k % 16 || (uintptr_t)pool_v % 16) return -1;
+  if (num_tiles < 1 || rows < 1 || row_bytes < 16 || row_bytes % 16 || unit_bytes % 16 || row_stride % 16) return -1;
+  if (((long long)rows * row_bytes) % 4096 || per_wg < 1) return -1;
+  const long long grid = ((long long)num_tiles + per_wg - 1) / per_wg;
+  if (grid > 0x7fffffff) return -1;
+  const char* pk = static_cast<const char*>(pool_k);
+  const char* pv = static_cast<const char*>(pool_v);
+  int32_t n = num_tiles, cpr = row_bytes / 16, chunks = (int32_t)((long long)rows * row_bytes / 4096);
+  int64_t unit = unit_bytes, stride = row_stride;
+  void* args[] = {&pk, &pv, &tiles, &n, &unit, &cpr, &chunks, &stride, &per_wg, &sink};
+  return (int32_t)hipLaunchKernel(reinterpret_cast<const void*>(&gather_rows_kernel), dim3((unsigned)grid), dim3(256),
+                                  args, 0, (hipStream_t)stream);
+}
