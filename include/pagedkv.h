@@ -56,7 +56,7 @@ typedef enum {
   PKV_EINVAL = -1,      /* null pointer or out-of-range scalar argument */
   PKV_EDTYPE = -2,      /* unsupported element type (or out dtype)       */
   PKV_ESHAPE = -3,      /* unsupported block size, head dim or head ratio */
-  PKV_EWORKSPACE = -4,  /* workspace missing or smaller than required     */
+  PKV_EWORKSPACE = -4,  /* workspace missing, smaller than required or not 16-byte aligned */
   PKV_ELAUNCH = -5,     /* the HIP launch itself failed                   */
   PKV_ENOBLOCKS = -6,   /* block manager: pool exhausted (nothing changed) */
   PKV_ENOSEQ = -7,      /* block manager: unknown sequence id             */
@@ -179,7 +179,8 @@ int32_t pkv_decode_partition_size(int32_t num_seqs, int32_t num_q_heads, int32_t
  *                 so the row is then computed over the clamped context.
  *   max_context_len  host upper bound of context_lens (sizes the split; not a limit check).
  *   scale         multiplier of q·k, positive and finite (1/sqrt(D) for standard attention).
- *   workspace     device, >= pkv_decode_workspace_bytes(...) bytes (may be NULL when that is 0).
+ *   workspace     device, >= pkv_decode_workspace_bytes(...) bytes, 16-byte aligned (may be NULL
+ *                 when that is 0).
  *   Long contexts are cut into partitions that are processed independently and merged with
  *   log-sum-exp weights; the result does not depend on which physical blocks hold the data.
  */
@@ -316,7 +317,8 @@ int32_t pkv_paged_attention_decode_noalloc(void* out, int32_t out_dtype, const v
  *   row per item (an f32 pool's call takes at most 65535 rows, PKV_ESHAPE beyond).
  *   num_seqs is at most 65535 (PKV_ESHAPE beyond); the MFMA prefill launch itself has no row
  *   limit. Every validation error is returned before anything is enqueued.
- *   workspace     device, >= pkv_ragged_workspace_bytes(...) bytes (NULL when that is 0);
+ *   workspace     device, >= pkv_ragged_workspace_bytes(...) bytes, 16-byte aligned (NULL when
+ *                 that is 0);
  *                 scratch between calls, as for decode.
  */
 size_t pkv_ragged_workspace_bytes(int32_t num_seqs, int32_t num_tokens, int32_t num_q_heads,

@@ -253,7 +253,7 @@ static int32_t decode_common_cu(void* out, int32_t out_dtype, const void* q, con
   const int max_parts = max_context_len > 0 ? (max_context_len + p - 1) / p : 1;
   if (max_parts > 65535) return PKV_ESHAPE;
   const DecodeWs ws = decode_ws_layout(n_items, num_q_heads, c->num_kv_heads, c->head_dim, max_parts);
-  if (ws.total > 0 && (!workspace || workspace_bytes < ws.total)) return PKV_EWORKSPACE;
+  if (ws.total > 0 && (!workspace || workspace_bytes < ws.total || (uintptr_t)workspace % 16)) return PKV_EWORKSPACE;
 
   pkv::DecodeLaunch L;
   L.out = out;

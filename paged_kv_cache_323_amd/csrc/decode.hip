@@ -387,19 +387,22 @@ __global__ __launch_bounds__(kDecThreads, PKV_DECODE_MIN_WG) void paged_decode_k
   }
 }
 
-// Log-sum-exp merge of the partitions' partial results. A workgroup covers 256 / NG outputs of
-// one sequence with NG threads each: thread group k merges partitions k, k + NG, ... with a
-// running maximum, and the NG (max, sum, value) triples of an output are then combined through
-// LDS. NG grows with the partition count (up to 8), so that up to 64 partitions take one round
-// of loads per thread: a long context's merge is not a chain of dependent loads.
+// Log-sum-exp merge of the partitions' partial results. A thread merges four consecutive output
+// elements of one head (16-byte partial loads and output stores), and a workgroup covers
+// 4 * 256 / NG elements of one sequence with NG threads each: thread group k merges partitions
+// k, k + NG, ... with a running maximum, and the NG (max, sum, values) results of an element are
+// then combined through LDS. NG grows with the partition count (up to 8), so that up to 64
+// partitions take one round of loads per thread: a long context's merge is not a chain of
+// dependent loads.
 template <int NG>
 __global__ __launch_bounds__(256) void paged_decode_merge_kernel(DecodeArgs a, int head_dim, int group) {
-  constexpr int kOuts = 256 / NG;
-  __shared__ float s_ml[NG > 1 ? 3 * NG * kOuts : 1];
+  constexpr int kOuts = 256 / NG;  // threads per thread group; each merges 4 elements
+  typedef float f4 __attribute__((ext_vector_type(4)));
+  __shared__ float s_ml[NG > 1 ? 6 * NG * kOuts : 1];
   __shared__ int s_cnt[4];
   const int oi = threadIdx.x % kOuts;
   const int grp = threadIdx.x / kOuts;
-  const int o = blockIdx.x * kOuts + oi;
+  const int o = 4 * (blockIdx.x * kOuts + oi);  // first of this thread's 4 elements (one head)
   const bool active = o < a.hq * head_dim;
   int s, row, ctx_s;
   if (a.causal_rows) {  // workgroup row y: one query row of a ragged batch
@@ -429,15 +432,16 @@ __global__ __launch_bounds__(256) void paged_decode_merge_kernel(DecodeArgs a, i
   // before any is used, and merged with a running log-sum-exp.
   constexpr int kChunk = 8;
   const int mine = nparts > grp ? (nparts - grp + NG - 1) / NG : 0;
-  float mx = -INFINITY, l = 0.f, v = 0.f;
+  float mx = -INFINITY, l = 0.f;
+  f4 v = f4{0.f, 0.f, 0.f, 0.f};
   for (int j0 = 0; active && j0 < mine; j0 += kChunk) {
     float2 ml[kChunk];
-    float av[kChunk];
+    f4 av[kChunk];
 #pragma unroll
     for (int j = 0; j < kChunk; ++j) {
       const int p = grp + NG * min(j0 + j, mine - 1);  // padding re-reads the last one; dropped below
       ml[j] = a.ws_ml[(item + p) * group + g];
-      av[j] = a.ws_acc[((item + p) * group + g) * head_dim + d];
+      av[j] = *reinterpret_cast<const f4*>(&a.ws_acc[((item + p) * group + g) * head_dim + d]);
     }
     float cm = mx;
 #pragma unroll
@@ -451,7 +455,8 @@ __global__ __launch_bounds__(256) void paged_decode_merge_kernel(DecodeArgs a, i
       if (j0 + j < mine) {
         const float w = fast_exp2(ml[j].x - cm);
         l = __builtin_fmaf(w, ml[j].y, l);
-        v = __builtin_fmaf(w, av[j], v);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = __builtin_fmaf(w, av[j][e], v[e]);
       }
     }
     mx = cm;
@@ -459,7 +464,7 @@ __global__ __launch_bounds__(256) void paged_decode_merge_kernel(DecodeArgs a, i
   if constexpr (NG > 1) {
     float* s_m = s_ml;
     float* s_l = s_ml + NG * kOuts;
-    float* s_v = s_ml + 2 * NG * kOuts;
+    f4* s_v = reinterpret_cast<f4*>(s_ml + 2 * NG * kOuts);
     s_m[grp * kOuts + oi] = mx;
     s_l[grp * kOuts + oi] = l;
     s_v[grp * kOuts + oi] = v;
@@ -469,16 +474,19 @@ __global__ __launch_bounds__(256) void paged_decode_merge_kernel(DecodeArgs a, i
 #pragma unroll
     for (int k = 1; k < NG; ++k) m_all = fmaxf(m_all, s_m[k * kOuts + oi]);
     l = 0.f;
-    v = 0.f;
+    v = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int k = 0; k < NG; ++k) {
       const float mk = s_m[k * kOuts + oi];
       const float w = mk == -INFINITY ? 0.f : fast_exp2(mk - m_all);  // a group with no partition
       l = __builtin_fmaf(w, s_l[k * kOuts + oi], l);
-      v = __builtin_fmaf(w, s_v[k * kOuts + oi], v);
+      const f4 vk = s_v[k * kOuts + oi];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = __builtin_fmaf(w, vk[e], v[e]);
     }
   }
-  if (active) store_out(a.out, (size_t)row * a.hq * head_dim + o, l > 0.f ? v / l : 0.f, a.out_dt);
+  const f4 res = l > 0.f ? f4{v[0] / l, v[1] / l, v[2] / l, v[3] / l} : f4{0.f, 0.f, 0.f, 0.f};
+  if (active) store_out4(a.out, (size_t)row * a.hq * head_dim + o, res, a.out_dt);
 }
 
 static DecodeArgs make_args(const DecodeLaunch& L) {
@@ -527,7 +535,7 @@ static hipError_t launch_decode_t(const DecodeLaunch& L, hipStream_t stream) {
     const int outs = L.num_q_heads * D;
     // threads per output: enough that each merges at most one chunk of 8 partitions
     const int ng = L.max_parts <= 8 ? 1 : L.max_parts <= 16 ? 2 : L.max_parts <= 32 ? 4 : 8;
-    const dim3 grid((unsigned)((outs * ng + 255) / 256), (unsigned)(L.causal_rows ? L.num_rows : L.num_seqs));
+    const dim3 grid((unsigned)((outs / 4 * ng + 255) / 256), (unsigned)(L.causal_rows ? L.num_rows : L.num_seqs));
     switch (ng) {
       case 1: return launch_kernel(paged_decode_merge_kernel<1>, grid, dim3(256), stream, a, D, G);
       case 2: return launch_kernel(paged_decode_merge_kernel<2>, grid, dim3(256), stream, a, D, G);

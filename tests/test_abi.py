@@ -79,6 +79,7 @@ def test_decode_workspace_validation():
     assert need > 0
     assert decode(c, max_ctx=10000, mb=700) == -4
     assert decode(c, max_ctx=10000, mb=700, ws=ctypes.c_void_p(1), wsb=need - 1) == -4
+    assert decode(c, max_ctx=10000, mb=700, ws=ctypes.c_void_p(0x10008), wsb=need) == -4  # not 16-byte aligned
     assert L.pkv_decode_workspace_bytes(512, 4, 256, ctypes.byref(c)) == 0  # never more than one partition
     assert L.pkv_decode_workspace_bytes(0, 4, 8000, ctypes.byref(c)) == 0
     assert L.pkv_decode_workspace_bytes_ex(512, 4, 8000, ctypes.byref(c), 8192) == 0  # one partition: none
