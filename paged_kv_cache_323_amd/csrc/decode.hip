@@ -117,6 +117,29 @@ template <int DT, int NWORDS, int EPL> __device__ __forceinline__ void words_to_
 #define PKV_DECODE_MIN_WG 1
 #endif
 
+// Scores on MFMA for 16-bit pools with eight query heads per kv head: S = K·Qᵀ for 16 tokens at
+// a time (v_mfma_f32_16x16x32, tokens as M, the heads as N with the unused columns zero,
+// head_dim as K). The per-token dot products and 8-lane reductions this replaces are most of the
+// score phase's VALU work at eight heads, and the query operand takes D/32 registers instead of
+// G·D/64. Measured against the VALU score phase (GQA lengths, bf16, B 16): 64/8 heads +8 % at
+// d 64 (105 -> 88 VGPRs), equal at d 128; at four heads per kv head it was slower (-6 % at
+// d 128, -3 % at d 64), so there the VALU path stays.
+#ifndef PKV_DECODE_MFMA_SCORES
+#define PKV_DECODE_MFMA_SCORES 1
+#endif
+typedef __bf16 dec_bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 dec_f16x8 __attribute__((ext_vector_type(8)));
+typedef float dec_f32x4 __attribute__((ext_vector_type(4)));
+
+template <int DT> __device__ __forceinline__ dec_f32x4 score_mfma(const u32x4& k, const u32x4& q, const dec_f32x4& c) {
+  if constexpr (DT == DT_BF16)
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(dec_bf16x8, k), __builtin_bit_cast(dec_bf16x8, q),
+                                                   c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(dec_f16x8, k), __builtin_bit_cast(dec_f16x8, q), c,
+                                                  0, 0, 0);
+}
+
 template <int DT, int D, int G, int PF>
 __global__ __launch_bounds__(kDecThreads, PKV_DECODE_MIN_WG) void paged_decode_kernel(DecodeArgs a) {
   using T = typename Elem<DT>::T;
@@ -216,15 +239,31 @@ __global__ __launch_bounds__(kDecThreads, PKV_DECODE_MIN_WG) void paged_decode_k
     s_tab[i] = b;
   }
 
-  // Query slices of the G heads in the score mapping.
+  // Query slices of the G heads in the score mapping (VALU path), or the query as the MFMA B
+  // operand: lane (head column hc, group gg) holds dims 32·ks + 8·gg .. +7 of head hc for k-step
+  // ks, zero for the columns past G.
+  constexpr bool kMfma = PKV_DECODE_MFMA_SCORES && DT != DT_F32 && G == 8;
+  constexpr int KS = D / 32;
   const int c = lane & 7;   // 16-byte chunk column
   const int r = lane >> 3;  // token row within a unit
-  const T* qb = static_cast<const T*>(a.q) + ((size_t)row * a.hq + (size_t)kvh * G) * D + c * VEC;
-  u32x4 qr[G][NCH];
+  const int hc = lane & 15;  // MFMA mapping: token row (K operand) / head column (Q operand)
+  const int gg = lane >> 4;  // MFMA mapping: 8-dim group of a k-step
+  u32x4 qr[kMfma ? 1 : G][kMfma ? 1 : NCH];
+  u32x4 qm[kMfma ? KS : 1];
+  if constexpr (kMfma) {
+    const T* qp = static_cast<const T*>(a.q) + ((size_t)row * a.hq + (size_t)kvh * G + min(hc, G - 1)) * D + 8 * gg;
 #pragma unroll
-  for (int g = 0; g < G; ++g)
+    for (int ks = 0; ks < KS; ++ks) {
+      const u32x4 w = *reinterpret_cast<const u32x4*>(qp + 32 * ks);
+      qm[ks] = hc < G ? w : u32x4{0, 0, 0, 0};
+    }
+  } else {
+    const T* qb = static_cast<const T*>(a.q) + ((size_t)row * a.hq + (size_t)kvh * G) * D + c * VEC;
 #pragma unroll
-    for (int ch = 0; ch < NCH; ++ch) qr[g][ch] = *reinterpret_cast<const u32x4*>(qb + g * D + ch * 8 * VEC);
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+      for (int ch = 0; ch < NCH; ++ch) qr[g][ch] = *reinterpret_cast<const u32x4*>(qb + g * D + ch * 8 * VEC);
+  }
   __syncthreads();
 
   // Base of the (physical block, kv head) tile holding unit u; units never straddle blocks. Rows of
@@ -268,7 +307,52 @@ __global__ __launch_bounds__(kDecThreads, PKV_DECODE_MIN_WG) void paged_decode_k
   auto unit_of = [&](int i) { return min(wave + kDecWaves * i, last); };
   const int nw_pad = (nw + PF - 1) / PF * PF;
   Words<NWORDS> vb[PF][2];
-  if (nw > 0) {
+  if constexpr (kMfma) {
+    // Units of 16 tokens, unit v to wave v mod 4, two units of loads in flight. Lane (token hc,
+    // group gg) loads dims 32·ks + 8·gg .. +7 of its token's K row (the A operand of k-step ks);
+    // a token past the partition reads the last one (a written row) and its score is dropped.
+    // Scores go to LDS only for real heads and tokens; softmax reads no other entries.
+    constexpr int PF2 = 2;
+    const int nu16 = (n + 15) >> 4;
+    const int nw16 = nu16 > wave ? (nu16 - wave + kDecWaves - 1) / kDecWaves : 0;
+    const int last16 = wave + kDecWaves * (nw16 > 0 ? nw16 - 1 : 0);
+    auto unit16 = [&](int i) { return min(wave + kDecWaves * i, last16); };
+    auto load_k16 = [&](int v, u32x4 (&dst)[KS]) {
+      const int tk = min(16 * v + hc, n - 1);
+      const int phys = s_tab[tk >> a.log2_bs];
+      const T* p = kbase + ((size_t)phys * tile_rows + head_rows) * D + (size_t)(tk & (a.bs - 1)) * row_stride + 8 * gg;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) dst[ks] = load_tile(reinterpret_cast<const u32x4*>(p + 32 * ks));
+    };
+    if (nw16 > 0) {
+      u32x4 kb16[PF2][KS];
+#pragma unroll
+      for (int j = 0; j < PF2; ++j) load_k16(unit16(j), kb16[j]);
+      const int nw16_pad = (nw16 + PF2 - 1) / PF2 * PF2;
+      for (int i0 = 0; i0 < nw16_pad; i0 += PF2) {
+#pragma unroll
+        for (int j = 0; j < PF2; ++j) {
+          const int i = i0 + j;
+          const int v = unit16(i);
+          dec_f32x4 sacc = dec_f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks) sacc = score_mfma<DT>(kb16[j][ks], qm[ks], sacc);
+          load_k16(unit16(i + PF2), kb16[j]);
+          // lane holds tokens 16v + 4gg .. +3 of head column hc
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int tok = 16 * v + 4 * gg + e;
+            const int dst = (hc < G && i < nw16 && tok < n) ? tok * G + hc : kPart * G + lane;
+            s_p[dst] = sacc[e] * a.scale_log2;
+          }
+        }
+      }
+    }
+    if (nw > 0) {
+#pragma unroll
+      for (int j = 0; j < PF; ++j) load_v(unit_of(j), vb[j]);
+    }
+  } else if (nw > 0) {
     u32x4 kb[PF][NCH];
 #pragma unroll
     for (int j = 0; j < PF; ++j) load_k(unit_of(j), kb[j]);
