@@ -9,8 +9,9 @@ at 8192, physical blocks in a seeded random order):
   2. one pinned-memory upload of slots, context lengths and block tables (on a copy stream, so
      it overlaps the previous step's kernels);
   3. copy_blocks for any copy-on-write pairs (none in this workload);
-  4. kv_cache_write of the 256 new tokens;
-  5. paged decode attention of the 256 query rows over their whole contexts.
+  4. kv_cache_write of the 256 new tokens and 5. paged decode attention of the 256 query rows over
+     their whole contexts, in one pass: the partition launch of pkv_paged_attention_decode_append
+     stores each sequence's new token before attending it, then the merge launch.
 
 Inputs are resident in HBM before timing starts. The JSON line reports whole-step throughput
 (KV bytes read by attention per second, and sequences per second), the decode kernel against
@@ -109,6 +110,9 @@ class DecodeLoop:
         self.step_idx = 0
         self.ctx_history = []
         self.pairs_total = 0
+        # the throughput steps use the fused cache write + decode; the event-timed steps issue the
+        # cache write, the partition launch and the merge separately, to time the partition launch
+        self.fused = True
 
     def _views(self, i):
         d = self.dev[i]
@@ -162,6 +166,14 @@ class DecodeLoop:
             self.pairs_total += len(pairs)
             pk.copy_blocks(self.st.k_cache, self.st.v_cache,
                            torch.from_numpy(np.ascontiguousarray(pairs)).to("cuda", non_blocking=False), self.st.desc)
+        if self.fused and ev is None and self.work_list:
+            # the cache write and the partition launch in one pass (pkv_paged_attention_decode_append),
+            # then the merge
+            pk.paged_attention_decode_append(self.out, self.q, self.k_new, self.v_new, self.slots_d, self.st.k_cache,
+                                             self.st.v_cache, self.tab_d, self.ctx_d, w.scale, self.max_ctx_final,
+                                             self.st.desc, self.ws, self.partition, self.items_d)
+            self._finish_step(buf, hn, main)
+            return
         pk.kv_cache_write(self.k_new, self.v_new, self.st.k_cache, self.st.v_cache, self.slots_d, self.st.desc)
         if ev is not None:
             ev[0].record()
@@ -172,7 +184,10 @@ class DecodeLoop:
         next(launches, None)                 # merge launch
         if ev is not None:
             ev[2].record()
-        done = torch.cuda.Event()
+        self._finish_step(buf, hn, main)
+
+    def _finish_step(self, buf, hn, main):
+        done = self.torch.cuda.Event()
         done.record(main)
         self.consumed[buf] = done
         self.ctx_history.append(hn[self.S: 2 * self.S].copy())
@@ -187,6 +202,7 @@ def _timed_windows(loop, K, min_total_s, min_windows, max_windows, ev=False):
     import torch
     snap = loop.snapshot
     times, kern_ms, merge_ms = [], [], []
+    loop.host_s = []  # per window: host time to enqueue its K steps (before the closing synchronisation)
     while (len(times) < min_windows or sum(times) < min_total_s) and len(times) < max_windows:
         loop.st.bm = snap.clone()
         loop.ctx_history.clear()
@@ -195,6 +211,7 @@ def _timed_windows(loop, K, min_total_s, min_windows, max_windows, ev=False):
         t0 = time.perf_counter()
         for i in range(K):
             loop.step(evs[i] if ev else None)
+        loop.host_s.append(time.perf_counter() - t0)
         torch.cuda.synchronize()
         times.append(time.perf_counter() - t0)
         if ev:
@@ -231,7 +248,12 @@ def run_headline(args):
         # Throughput: K-step windows with no instrumentation, repeated until they cover at least
         # 0.25 s (and at least 10 windows) -> value and ms_per_step from the median window.
         win_s, _, _ = _timed_windows(loop, K, 0.25, 10, 1000)
+        host_s = list(loop.host_s)
         ctx_hist = list(loop.ctx_history)
+        # the same windows with the cache write as its own launch, for reference
+        loop.fused = False
+        unf_s, _, _ = _timed_windows(loop, K, 0.1, 5, 1000)
+        loop.fused = True
         # Roofline: more windows of the same K steps with HIP events around the partition and merge
         # launches (on the stream they run on). Event records cost about 8 us per step, which is why
         # they stay out of the throughput windows.
@@ -256,7 +278,12 @@ def run_headline(args):
                  "step_us_median": round(step_s * 1e6, 2),
                  "step_us_min": round(min(win_s) / K * 1e6, 2), "step_us_max": round(max(win_s) / K * 1e6, 2),
                  "step_us_p10": round(float(np.percentile(win_s, 10)) / K * 1e6, 2),
-                 "step_us_p90": round(float(np.percentile(win_s, 90)) / K * 1e6, 2)})
+                 "step_us_p90": round(float(np.percentile(win_s, 90)) / K * 1e6, 2),
+                 "step_us_median_separate_cache_write": round(float(np.median(unf_s)) / K * 1e6, 2),
+                 # host time to enqueue a window's steps: near the window's own time means the
+                 # host, not the GPU, paced it
+                 "host_enqueue_us_per_step_median": round(float(np.median(host_s)) / K * 1e6, 2),
+                 "host_enqueue_us_per_step_max": round(max(host_s) / K * 1e6, 2)})
 
 
 _EVICT = None

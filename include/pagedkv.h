@@ -271,6 +271,36 @@ size_t pkv_decode_workspace_bytes_ex(int32_t num_seqs, int32_t num_q_heads,
                                      int32_t partition_size);
 
 /*
+ * paged_attention_decode_append — one decode step's cache write and attention in one pass: each
+ *   sequence's new token is stored into its slot and then attended with the rest of its context
+ *   (a decode step stores its token's K/V and attends over the cache: 「vllm」 §2.2 Decode;
+ *   「PagedAttention原理」 §实现一个虚拟内存). Equal, bit for bit in outputs and pools, to
+ *   pkv_kv_cache_write(k_new, v_new, ..., slot_mapping, num_seqs, ...) followed by
+ *   pkv_paged_attention_decode_ex (items == NULL) or by the work-list partition launch and
+ *   pkv_paged_attention_decode_merge (items != NULL), with the same arguments; one launch fewer.
+ *   k_new, v_new  device [num_seqs][num_kv_heads][D] in the pool dtype (token stride Hkv·D).
+ *   slot_mapping  device int32 [num_seqs]: the slot of position context_lens[s] - 1 of sequence s
+ *                 (its newest token); < 0 stores nothing for that sequence. A slot elsewhere
+ *                 breaks the contract (the token may be read before it is stored).
+ *   k_cache, v_cache  device pools, written (the new rows) and read.
+ *   partition_size 0: automatic (items == NULL only); items / num_items: as for
+ *                 pkv_paged_attention_decode_partitions_items (every item of every sequence,
+ *                 num_items >= 1 when num_seqs > 0), with partition_size > 0.
+ *   The other arguments, the workspace and the errors are those of pkv_paged_attention_decode_ex;
+ *   PKV_EINVAL also for a null k_new, v_new or slot_mapping with num_seqs > 0. Debug builds skip
+ *   and flag a slot past the pool (PKV_DBG_SLOT).
+ */
+int32_t pkv_paged_attention_decode_append(void* out, int32_t out_dtype, const void* q,
+                                          const void* k_new, const void* v_new,
+                                          const int32_t* slot_mapping, void* k_cache, void* v_cache,
+                                          const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                          const int32_t* context_lens, int32_t num_seqs,
+                                          int32_t num_q_heads, float scale, int32_t max_context_len,
+                                          const pkv_cache_desc* cache, int32_t partition_size,
+                                          const int32_t* items, int32_t num_items, void* workspace,
+                                          size_t workspace_bytes, void* stream);
+
+/*
  * paged_attention_decode_noalloc — pkv_paged_attention_decode without a caller workspace, for
  *   callers that cannot allocate device memory: code under HIP graph capture, tight serving
  *   loops, harnesses that forbid hipMalloc. Same arguments, layouts and results as

@@ -232,7 +232,8 @@ static int32_t decode_common_cu(void* out, int32_t out_dtype, const void* q, con
                                 int32_t max_context_len, const pkv_cache_desc* c, int32_t partition_size,
                                 void* workspace, size_t workspace_bytes, void* stream, const int32_t* cu,
                                 int stage = 0, int32_t num_rows = -1, const int32_t* items = nullptr,
-                                int32_t num_items = 0, bool causal_rows = false) {
+                                int32_t num_items = 0, bool causal_rows = false, const void* k_new = nullptr,
+                                const void* v_new = nullptr, const int32_t* new_slots = nullptr) {
   int32_t st = check_cache(c);
   if (st != PKV_OK) return st;
   if ((st = check_heads(num_q_heads, c)) != PKV_OK) return st;
@@ -283,6 +284,9 @@ static int32_t decode_common_cu(void* out, int32_t out_dtype, const void* q, con
   L.items = items;
   L.num_items = num_items;
   L.causal_rows = causal_rows ? 1 : 0;
+  L.k_new = k_new;
+  L.v_new = v_new;
+  L.new_slots = new_slots;
   return launched(pkv::launch_decode(L, (hipStream_t)stream));
 }
 
@@ -340,6 +344,34 @@ int32_t pkv_paged_attention_decode_partitions_items(void* out, int32_t out_dtype
   return decode_common_cu(out, out_dtype, q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens,
                           num_seqs, num_q_heads, scale, max_context_len, c, partition_size, workspace,
                           workspace_bytes, stream, nullptr, 1, -1, items, num_items);
+}
+
+int32_t pkv_paged_attention_decode_append(void* out, int32_t out_dtype, const void* q, const void* k_new,
+                                          const void* v_new, const int32_t* slot_mapping, void* k_cache,
+                                          void* v_cache, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                          const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
+                                          float scale, int32_t max_context_len, const pkv_cache_desc* c,
+                                          int32_t partition_size, const int32_t* items, int32_t num_items,
+                                          void* workspace, size_t workspace_bytes, void* stream) {
+  if (num_seqs > 0 && (!k_new || !v_new || !slot_mapping)) return PKV_EINVAL;
+  if (items) {
+    // work list: partitions of the listed items (with the stores), then the merge
+    if (partition_size <= 0 || num_items < 0 || (num_seqs > 0 && num_items == 0)) return PKV_EINVAL;
+    if (c && (int64_t)num_items * (c->num_kv_heads > 0 ? c->num_kv_heads : 1) > 0x7fffffffLL) return PKV_ESHAPE;
+    if (num_seqs > 65535) return PKV_ESHAPE;
+    int32_t st = decode_common_cu(out, out_dtype, q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens,
+                                  num_items > 0 ? num_seqs : 0, num_q_heads, scale, max_context_len, c,
+                                  partition_size, workspace, workspace_bytes, stream, nullptr, 1, -1, items,
+                                  num_items, false, k_new, v_new, slot_mapping);
+    if (st != PKV_OK) return st;
+    return decode_common(out, out_dtype, q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens,
+                         num_seqs, num_q_heads, scale, max_context_len, c, partition_size, workspace,
+                         workspace_bytes, stream, 2);
+  }
+  if (num_items != 0) return PKV_EINVAL;
+  return decode_common_cu(out, out_dtype, q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens,
+                          num_seqs, num_q_heads, scale, max_context_len, c, partition_size, workspace,
+                          workspace_bytes, stream, nullptr, 0, -1, nullptr, 0, false, k_new, v_new, slot_mapping);
 }
 
 int32_t pkv_decode_items(const int32_t* context_lens, int32_t num_seqs, int32_t partition_size, int32_t* items,

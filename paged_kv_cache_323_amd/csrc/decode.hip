@@ -58,6 +58,9 @@ struct DecodeArgs {
   const uint32_t* items;  // work list: item i = seq | part << 16 (null: dense grid)
   int num_seqs;
   int causal_rows;  // 1: one item per query row of a ragged batch (every row, any q_len)
+  const void* k_new;          // optional new token per sequence, stored before it is attended
+  const void* v_new;
+  const int32_t* new_slots;   // null: nothing to store
 };
 
 // Index of the sequence whose query rows cu[s]..cu[s+1]-1 hold `row` (cu non-decreasing, cu[0] =
@@ -227,6 +230,22 @@ __global__ __launch_bounds__(kDecThreads, PKV_DECODE_MIN_WG) void paged_decode_k
   const int nunits = (n + 7) >> 3;
   const int nw = nunits > wave ? (nunits - wave + kDecWaves - 1) / kDecWaves : 0;  // this wave's units
 
+  // The sequence's new token (fused cache write). The workgroup of its last partition, which alone
+  // reads the token's position, takes that row's K and V from k_new / v_new instead of the pool
+  // (in the one unit holding it) and stores them into the pool at the end, so nothing waits for the
+  // stores. tn: the token's index in this partition, -1 when nothing is stored here.
+  int32_t new_slot = -1;
+  if (a.new_slots && part == nparts - 1) {
+    new_slot = a.new_slots[s];
+    if (kDebugChecks && new_slot >= (int64_t)a.num_blocks * a.bs) {
+      if (tid == 0) debug_flag(DBG_SLOT);
+      new_slot = -1;
+    }
+  }
+  const int tn = new_slot >= 0 && n > 0 ? n - 1 : -1;  // the newest token closes the last partition
+  const T* const knew = a.new_slots ? static_cast<const T*>(a.k_new) + ((size_t)s * a.hkv + kvh) * D : nullptr;
+  const T* const vnew = a.new_slots ? static_cast<const T*>(a.v_new) + ((size_t)s * a.hkv + kvh) * D : nullptr;
+
   // Block-table entries of this partition.
   const int nblk = (n + a.bs - 1) >> a.log2_bs;
   const int32_t* trow = a.tables + (size_t)s * a.max_blocks + (t0 >> a.log2_bs);
@@ -290,14 +309,22 @@ __global__ __launch_bounds__(kDecThreads, PKV_DECODE_MIN_WG) void paged_decode_k
 
   auto load_k = [&](int u, u32x4 (&dst)[NCH]) {
     const T* p = tile(kbase, u) + (size_t)((u * 8 + krow) & (a.bs - 1)) * row_stride + c * VEC;
+    if (u == (tn >> 3) && tn >= 0) {  // uniform: the unit holding the new token
+      if (u * 8 + krow == tn) p = knew + c * VEC;
+    }
 #pragma unroll
     for (int ch = 0; ch < NCH; ++ch) dst[ch] = load_tile(reinterpret_cast<const u32x4*>(p + ch * 8 * VEC));
   };
   auto load_v = [&](int u, Words<NWORDS> (&dst)[2]) {
     const T* p = tile(vbase, u) + cv * EPL;
 #pragma unroll
-    for (int ps = 0; ps < 2; ++ps)
-      dst[ps] = load_words<NWORDS>(p + (size_t)((u * 8 + ps * 4 + rv) & (a.bs - 1)) * row_stride);
+    for (int ps = 0; ps < 2; ++ps) {
+      const T* q = p + (size_t)((u * 8 + ps * 4 + rv) & (a.bs - 1)) * row_stride;
+      if (u == (tn >> 3) && tn >= 0) {  // uniform: the unit holding the new token
+        if (u * 8 + ps * 4 + rv == tn) q = vnew + cv * EPL;
+      }
+      dst[ps] = load_words<NWORDS>(q);
+    }
   };
 
   // ---- phase 1: scores, PF units in flight per wave ---------------------------------------------
@@ -321,6 +348,9 @@ __global__ __launch_bounds__(kDecThreads, PKV_DECODE_MIN_WG) void paged_decode_k
       const int tk = min(16 * v + hc, n - 1);
       const int phys = s_tab[tk >> a.log2_bs];
       const T* p = kbase + ((size_t)phys * tile_rows + head_rows) * D + (size_t)(tk & (a.bs - 1)) * row_stride + 8 * gg;
+      if (v == (tn >> 4) && tn >= 0) {  // uniform: the unit holding the new token
+        if (tk == tn) p = knew + 8 * gg;
+      }
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) dst[ks] = load_tile(reinterpret_cast<const u32x4*>(p + 32 * ks));
     };
@@ -453,6 +483,24 @@ __global__ __launch_bounds__(kDecThreads, PKV_DECODE_MIN_WG) void paged_decode_k
       for (int e = 0; e < EPL; ++e) s_red[(wave * G + g) * D + cv * EPL + e] = acc[g][e];
   }
   __syncthreads();
+
+  // The new token's rows into the pool (the fused cache write): nothing in this launch reads them.
+  if (new_slot >= 0) {
+    constexpr int kRowChunks = D * ES / 16;  // 16-byte chunks of one row
+    if (tid < 2 * kRowChunks) {
+      const bool is_v = tid >= kRowChunks;
+      const int ch = is_v ? tid - kRowChunks : tid;
+      const int64_t blk = new_slot >> a.log2_bs, off = new_slot & (a.bs - 1);
+#ifdef PKV_TOKEN_MAJOR
+      const int64_t dst_row = (blk * a.bs + off) * a.hkv + kvh;
+#else
+      const int64_t dst_row = (blk * a.hkv + kvh) * a.bs + off;
+#endif
+      const u32x4 x = *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(is_v ? vnew : knew) + ch * 16);
+      *reinterpret_cast<u32x4*>(static_cast<char*>(const_cast<void*>(is_v ? a.vc : a.kc)) + dst_row * D * ES +
+                                ch * 16) = x;
+    }
+  }
 
   const size_t out_row = (size_t)row * a.hq + (size_t)kvh * G;  // first of the G query heads
   const size_t item = ((size_t)wi * a.hkv + kvh) * a.max_parts + part;
@@ -598,6 +646,9 @@ static DecodeArgs make_args(const DecodeLaunch& L) {
   a.items = reinterpret_cast<const uint32_t*>(L.items);
   a.num_seqs = L.num_seqs;
   a.causal_rows = L.causal_rows;
+  a.k_new = L.k_new;
+  a.v_new = L.v_new;
+  a.new_slots = L.new_slots;
   return a;
 }
 

@@ -90,6 +90,11 @@ struct DecodeLaunch {
   // 1: every query row of a ragged batch (cu set) is its own item and attends keys up to its own
   // position; partials are indexed by row (num_rows of them)
   int causal_rows = 0;
+  // Optional: each sequence's new token, stored by the partition launch before it is attended
+  // (k_new / v_new [num_seqs][Hkv][D], slot per sequence, < 0: none).
+  const void* k_new = nullptr;
+  const void* v_new = nullptr;
+  const int32_t* new_slots = nullptr;
 };
 
 hipError_t launch_decode(const DecodeLaunch& a, hipStream_t stream);

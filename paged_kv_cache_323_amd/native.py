@@ -101,6 +101,8 @@ _SIGS = {
     "pkv_decode_partition_size": (_I32, [_I32, _I32, _I32, _DESC]),
     "pkv_paged_attention_decode": (_I32, [_P, _I32, _P, _P, _P, _P, _I32, _P, _I32, _I32, ctypes.c_float,
                                           _I32, _DESC, _P, _SZ, _P]),
+    "pkv_paged_attention_decode_append": (_I32, [_P, _I32, _P, _P, _P, _P, _P, _P, _P, _I32, _P, _I32, _I32,
+                                                 ctypes.c_float, _I32, _DESC, _I32, _P, _I32, _P, _SZ, _P]),
     "pkv_paged_attention_decode_noalloc": (_I32, [_P, _I32, _P, _P, _P, _P, _I32, _P, _I32, _I32, ctypes.c_float,
                                                   _I32, _DESC, _P]),
     "pkv_paged_attention_decode_ex": (_I32, [_P, _I32, _P, _P, _P, _P, _I32, _P, _I32, _I32, ctypes.c_float,
@@ -304,6 +306,29 @@ def paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_lens,
             _dev(context_lens, "context_lens", torch.int32), S, hq, float(scale), int(max_context_len),
             ctypes.byref(desc), int(partition_size), ws, wsb, _stream(stream))
     _check(st, f"paged_attention_decode[{stage}]")
+
+
+def paged_attention_decode_append(out, q, k_new, v_new, slot_mapping, k_cache, v_cache, block_tables, context_lens,
+                                  scale: float, max_context_len: int, desc: CacheDesc, workspace=None,
+                                  partition_size: int = 0, items=None, stream=None) -> None:
+    """The step's cache write and decode attention in one pass (see include/pagedkv.h)."""
+    torch = _torch()
+    S, hq, d = q.shape
+    if out.shape != q.shape or block_tables.dim() != 2 or block_tables.shape[0] != S:
+        raise ValueError("shape mismatch")
+    if k_new.shape != v_new.shape or k_new.shape[0] != S or not k_new.is_contiguous() or not v_new.is_contiguous():
+        raise ValueError("k_new / v_new must be contiguous [num_seqs, num_kv_heads, head_dim]")
+    ws = _dev(workspace, "workspace") if workspace is not None else None
+    wsb = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    it = _dev(items, "items", torch.int32) if items is not None else None
+    n_items = int(items.numel()) if items is not None else 0
+    st = _lib.pkv_paged_attention_decode_append(
+        _dev(out, "out"), _tdtype_code(out), _dev(q, "q"), _dev(k_new, "k_new"), _dev(v_new, "v_new"),
+        _dev(slot_mapping, "slot_mapping", torch.int32), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
+        _dev(block_tables, "block_tables", torch.int32), int(block_tables.shape[1]),
+        _dev(context_lens, "context_lens", torch.int32), S, hq, float(scale), int(max_context_len),
+        ctypes.byref(desc), int(partition_size), it, n_items, ws, wsb, _stream(stream))
+    _check(st, "paged_attention_decode_append")
 
 
 NOALLOC_SCRATCH_BYTES = 64 << 20  # PKV_NOALLOC_SCRATCH_BYTES

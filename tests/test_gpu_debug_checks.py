@@ -62,6 +62,19 @@ res["slot_flags"] = pk.debug_flags()
 res["slot_pool_unchanged"] = bool(torch.equal(kc.view(torch.int32), k0.view(torch.int32))
                                   and torch.equal(vc.view(torch.int32), v0.view(torch.int32)))
 
+say("fused cache write with a slot past the pool")
+k0, v0 = kc.clone(), vc.clone()
+S = inp["q"].shape[0]
+knew = torch.zeros((S, w.num_kv_heads, w.head_dim), dtype=kc.dtype, device="cuda")
+bad = torch.full((S,), -1, dtype=torch.int32, device="cuda")
+bad[0] = N * B + 3
+outa = torch.empty_like(out)
+pk.paged_attention_decode_append(outa, inp["q"], knew, knew.clone(), bad, kc, vc, inp["block_tables"],
+                                 inp["context_lens"], w.scale, int(inp["lens_host"].max()), desc, inp["workspace"])
+res["append_flags"] = pk.debug_flags()
+res["append_pool_unchanged"] = bool(torch.equal(kc.view(torch.int32), k0.view(torch.int32))
+                                    and torch.equal(vc.view(torch.int32), v0.view(torch.int32)))
+
 say("copy pairs past the pool")
 pairs = torch.tensor([[0, N], [N + 3, 1], [-1, 2]], dtype=torch.int32, device="cuda")
 pk.copy_blocks(kc, vc, pairs, desc)
@@ -114,5 +127,6 @@ def test_debug_build_checks_device_indices():
     assert res["parity_err"] <= 1e-5 and res["flags_clean"] == 0
     assert res["slot_flags"] == 1 and res["slot_pool_unchanged"]
     assert res["pair_flags"] == 8 and res["pair_pool_unchanged"]
+    assert res["append_flags"] == 1 and res["append_pool_unchanged"]
     assert res["block_flags"] == 2 and res["block_intact_err"] <= 1e-5
     assert res["ragged_flags"] == 4
