@@ -467,6 +467,40 @@ def run_decode_config(name, block_size=None, steps=30, warmup=5, partition=0):
     return res
 
 
+HEAD_SHAPES = ((64, 8, 128), (64, 8, 64), (32, 8, 64), (16, 8, 128), (32, 32, 128))
+
+
+def run_head_shapes(shapes=HEAD_SHAPES, K=20):
+    """Decode across head shapes at the GQA configuration's 256 lognormal lengths (bf16, block size
+    16, automatic partition): partition launch and merge, event-timed over K-step windows restarted
+    from one saved allocation state; KV bytes over the two launches' time. The headline shape
+    (32 query heads over 8 kv heads, head_dim 128) is the headline row."""
+    import torch
+    from workloads import make_decode_workload, make_workload
+    ctx = list(make_workload("gqa", "full").context_lens)
+    res = {}
+    for hq, hkv, d in shapes:
+        w = make_decode_workload(3, ctx, hq, hkv, d, "bf16", 16, name=f"heads-{hq}-{hkv}-d{d}")
+        loop = DecodeLoop(w, 5 + K + 5)
+        for _ in range(5):
+            loop.step()
+        torch.cuda.synchronize()
+        loop.snapshot = loop.st.bm.clone()
+        loop.repeat_attention(100)  # clocks up
+        torch.cuda.synchronize()
+        _, kern_ms, merge_ms = _timed_windows(loop, K, 0.05, 3, 20, ev=True)
+        kv = sum(decode_algorithmic_bytes(c, w, 2)[0] for c in loop.ctx_history) / len(loop.ctx_history)
+        k_us, m_us = float(np.mean(kern_ms)) * 1e3, float(np.mean(merge_ms)) * 1e3
+        res[f"{hq}/{hkv}/d{d}"] = {"partition": loop.partition, "partition_launch_us": round(k_us, 1),
+                                   "merge_launch_us": round(m_us, 1),
+                                   "kv_gbs": round(kv / (k_us + m_us) / 1e3, 1),
+                                   "pct_hbm": round(100 * kv / (k_us + m_us) / 1e3 / HBM_PEAK_GBS, 1),
+                                   "kv_gbs_partition_launch": round(kv / k_us / 1e3, 1)}
+        del loop
+        torch.cuda.empty_cache()
+    return res
+
+
 def run_shared_prefix():
     """Copy-on-write copies at the first generated token and decode over shared blocks."""
     import torch
@@ -970,6 +1004,10 @@ def row_rooflines(result, extra, read_peak, copy_peak, copy_traffic=None):
         e = extra.get(key, {})
         if "kv_gbs_partition_launch" in e:
             rows[f"a5_decode_{key}"] = hbm(e["kv_gbs_partition_launch"], read_peak)
+    for shape, e in extra.get("head_shapes", {}).items():
+        if isinstance(e, dict) and "kv_gbs" in e:  # partition launch + merge
+            rows[f"a5_a6_decode_heads_{shape.replace('/', '_')}"] = dict(hbm(e["kv_gbs"], read_peak),
+                                                                         partition=e["partition"])
     m = extra.get("mixed", {})
     if "kv_cache_write_gbs" in m:
         rows["a4_kv_cache_write"] = dict(hbm(m["kv_cache_write_gbs"], copy_peak), us=m["kv_cache_write_us"])
@@ -1120,7 +1158,8 @@ def main():
         result["roofline"]["frac_of_measured_gather_peak"] = round(h["achieved"] / gather_peak, 4)
     if not args.no_extra:
         extra = {}
-        for key, fn in (("gqa_B32", lambda: run_decode_config("gqa", 32)),
+        for key, fn in (("head_shapes", run_head_shapes),
+                        ("gqa_B32", lambda: run_decode_config("gqa", 32)),
                         ("gqa_B8", lambda: run_decode_config("gqa", 8)),
                         ("llama7b", lambda: run_decode_config("llama7b")),
                         ("shared_prefix", run_shared_prefix),

@@ -150,16 +150,22 @@ int32_t pkv_copy_blocks(void* k_cache, void* v_cache, const int32_t* block_pairs
 size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t max_context_len,
                                   const pkv_cache_desc* cache);
 
+/* Largest context partition, in tokens, the decode entry points accept for num_q_heads query
+ * heads over this cache (g = num_q_heads / num_kv_heads query heads per kv head). Two kernels
+ * serve decode. The one-pass kernel (16-bit pools with g = 8, and with g = 4 at head_dim 64)
+ * keeps a running softmax per wave and no scores: 4096 tokens. The three-phase kernel (every other
+ * case) keeps a score per token and query head in 32 KiB of LDS: 8192 / g tokens (8192, 4096,
+ * 2048, 1024 for g = 1, 2, 4, 8). Returns PKV_EINVAL for an invalid cache or head count. */
+int32_t pkv_decode_max_partition(int32_t num_q_heads, const pkv_cache_desc* cache);
+
 /* Tokens per context partition the decode kernel uses for these arguments
  * (partition_size argument 0 of the _ex entry point). It starts from max_context_len rounded up
- * to a multiple of 64 when that fits min(4096, the largest partition for the head grouping),
- * else that size; while num_seqs x num_kv_heads x ceil(max_context_len / partition) is below
- * 512 workgroups (two per CU), it is halved (rounded up to a multiple of 64), down to 256, so a
- * small batch of long contexts still fills the GPU. The largest partition is
- * 8192 / (num_q_heads / num_kv_heads) tokens: 8192, 4096, 2048 and 1024 for 1, 2, 4 and 8 query
- * heads per kv head (one workgroup keeps a score per token and query head in 32 KiB of LDS).
- * The workspace and the launch must see the same arguments, since the size depends on all of
- * them. Returns PKV_EINVAL for an invalid cache, head count or negative length or count. */
+ * to a multiple of 64 when that fits min(4096, pkv_decode_max_partition), else that size; while
+ * num_seqs x num_kv_heads x ceil(max_context_len / partition) is below 512 workgroups (two per
+ * CU), it is halved (rounded up to a multiple of 64), down to 256, so a small batch of long
+ * contexts still fills the GPU. The workspace and the launch must see the same arguments, since
+ * the size depends on all of them. Returns PKV_EINVAL for an invalid cache, head count or
+ * negative length or count. */
 int32_t pkv_decode_partition_size(int32_t num_seqs, int32_t num_q_heads, int32_t max_context_len,
                                   const pkv_cache_desc* cache);
 
@@ -193,8 +199,8 @@ int32_t pkv_paged_attention_decode(void* out, int32_t out_dtype, const void* q,
                                    size_t workspace_bytes, void* stream);
 
 /* As pkv_paged_attention_decode with an explicit partition size in tokens (0 = automatic;
- * otherwise a multiple of 64 and of the block size, at most the largest partition for the head
- * grouping given under pkv_decode_partition_size). The workspace must then be
+ * otherwise a multiple of 64 and of the block size, at most pkv_decode_max_partition). The
+ * workspace must then be
  * sized with pkv_decode_workspace_bytes_ex. */
 int32_t pkv_paged_attention_decode_ex(void* out, int32_t out_dtype, const void* q,
                                       const void* k_cache, const void* v_cache,

@@ -41,8 +41,8 @@ int32_t check_out_dtype(int32_t out_dt, const pkv_cache_desc* c) {
   return (out_dt == PKV_F32 || out_dt == c->dtype) ? PKV_OK : PKV_EDTYPE;
 }
 
-// Automatic partition size. Contexts that fit the largest partition the LDS score buffer allows
-// for this head grouping (at most kMaxAutoPartition) take one partition (rounded up to 64
+// Automatic partition size. Contexts that fit the largest partition of the kernel that serves this
+// head grouping, element type and head size (at most kMaxAutoPartition) take one partition (rounded up to 64
 // tokens), longer ones partitions of that size. While the launch would then have fewer than kMinWorkgroups workgroups (sequences x
 // kv heads x partitions of the longest context), the partition is halved, down to
 // kMinAutoPartition tokens, so that a small batch of long contexts still spreads over the CUs.
@@ -53,10 +53,10 @@ constexpr int kMinAutoPartition = 256;
 constexpr int kMaxAutoPartition = 4096;
 
 // Largest partition the automatic size starts from for g query heads per kv head.
-int auto_cap(int g) { return std::min(pkv::max_partition(g), kMaxAutoPartition); }
+int auto_cap(int g, int dt, int d) { return std::min(pkv::max_partition(g, dt, d), kMaxAutoPartition); }
 
-int auto_partition(int32_t num_seqs, int32_t hkv, int g, int32_t max_ctx) {
-  const int cap = auto_cap(g);
+int auto_partition(int32_t num_seqs, int32_t hkv, int g, int dt, int d, int32_t max_ctx) {
+  const int cap = auto_cap(g, dt, d);
   const int64_t ctx = max_ctx > 0 ? max_ctx : 1;
   int p = ctx <= cap ? (int)((ctx + 63) / 64 * 64) : cap;
   auto workgroups = [&](int part) { return (int64_t)num_seqs * hkv * ((ctx + part - 1) / part); };
@@ -65,8 +65,8 @@ int auto_partition(int32_t num_seqs, int32_t hkv, int g, int32_t max_ctx) {
   return p;
 }
 
-bool valid_partition(int p, int bs, int g) {
-  return p >= 64 && p <= pkv::max_partition(g) && p % 64 == 0 && p % bs == 0;
+bool valid_partition(int p, int bs, int g, int dt, int d) {
+  return p >= 64 && p <= pkv::max_partition(g, dt, d) && p % 64 == 0 && p % bs == 0;
 }
 
 struct DecodeWs {
@@ -96,9 +96,9 @@ DecodeWs decode_ws_layout(int32_t S, int32_t hq, int32_t hkv, int32_t head_dim, 
 // call whose partition was halved has fewer than 2 * kMinWorkgroups (sequence, kv head, partition)
 // triples, since one halving at most doubles a count that was below kMinWorkgroups, and its
 // partitions are at least kMinAutoPartition tokens long.
-size_t decode_ws_auto_bound(int32_t S, int32_t hq, int32_t hkv, int32_t head_dim, int32_t max_ctx) {
+size_t decode_ws_auto_bound(int32_t S, int32_t hq, int32_t hkv, int32_t head_dim, int dt, int32_t max_ctx) {
   const int g = hq / hkv;
-  const int cap = auto_cap(g);
+  const int cap = auto_cap(g, dt, head_dim);
   const int64_t ctx = max_ctx;
   size_t whole = 0;
   if (ctx > cap) whole = decode_ws_layout(S, hq, hkv, head_dim, (int)((ctx + cap - 1) / cap)).total;
@@ -205,19 +205,24 @@ int32_t pkv_swap_blocks(void* dst_k, void* dst_v, const void* src_k, const void*
       pkv::launch_copy_between(dst_k, dst_v, src_k, src_v, pairs, num_pairs, block_bytes, 0, 0, (hipStream_t)stream));
 }
 
+int32_t pkv_decode_max_partition(int32_t num_q_heads, const pkv_cache_desc* c) {
+  if (check_cache(c) != PKV_OK || check_heads(num_q_heads, c) != PKV_OK) return PKV_EINVAL;
+  return pkv::max_partition(num_q_heads / c->num_kv_heads, c->dtype, c->head_dim);
+}
+
 int32_t pkv_decode_partition_size(int32_t num_seqs, int32_t num_q_heads, int32_t max_ctx,
                                   const pkv_cache_desc* c) {
   if (check_cache(c) != PKV_OK || check_heads(num_q_heads, c) != PKV_OK || max_ctx < 0 || num_seqs < 0)
     return PKV_EINVAL;
   // a multiple of 64, hence of every block size
-  return auto_partition(num_seqs, c->num_kv_heads, num_q_heads / c->num_kv_heads, max_ctx);
+  return auto_partition(num_seqs, c->num_kv_heads, num_q_heads / c->num_kv_heads, c->dtype, c->head_dim, max_ctx);
 }
 
 size_t pkv_decode_workspace_bytes_ex(int32_t S, int32_t hq, int32_t max_ctx, const pkv_cache_desc* c,
                                      int32_t partition) {
   if (check_cache(c) != PKV_OK || check_heads(hq, c) != PKV_OK || S < 0 || max_ctx < 0) return 0;
-  if (partition <= 0) return S > 0 ? decode_ws_auto_bound(S, hq, c->num_kv_heads, c->head_dim, max_ctx) : 0;
-  if (!valid_partition(partition, c->block_size, hq / c->num_kv_heads)) return 0;
+  if (partition <= 0) return S > 0 ? decode_ws_auto_bound(S, hq, c->num_kv_heads, c->head_dim, c->dtype, max_ctx) : 0;
+  if (!valid_partition(partition, c->block_size, hq / c->num_kv_heads, c->dtype, c->head_dim)) return 0;
   const int max_parts = max_ctx > 0 ? (max_ctx + partition - 1) / partition : 1;
   return decode_ws_layout(S, hq, c->num_kv_heads, c->head_dim, max_parts).total;
 }
@@ -250,7 +255,7 @@ static int32_t decode_common_cu(void* out, int32_t out_dtype, const void* q, con
   const int32_t n_items = causal_rows ? num_rows : num_seqs;
   const int p = partition_size > 0 ? partition_size
                                    : pkv_decode_partition_size(n_items, num_q_heads, max_context_len, c);
-  if (!valid_partition(p, c->block_size, num_q_heads / c->num_kv_heads)) return PKV_EINVAL;
+  if (!valid_partition(p, c->block_size, num_q_heads / c->num_kv_heads, c->dtype, c->head_dim)) return PKV_EINVAL;
   const int max_parts = max_context_len > 0 ? (max_context_len + p - 1) / p : 1;
   if (max_parts > 65535) return PKV_ESHAPE;
   const DecodeWs ws = decode_ws_layout(n_items, num_q_heads, c->num_kv_heads, c->head_dim, max_parts);

@@ -3,18 +3,29 @@
 // One workgroup (4 waves) per (kv head, sequence, context partition), or in causal-rows mode per
 // (kv head, query row of a ragged batch, partition), the row attending its sequence's keys up to
 // its own position. The g = Hq/Hkv query heads that share a kv head are served by the same
-// workgroup, so every K/V tile is read from HBM once per item. The partition's tokens are walked through the block table in units of 8
+// workgroup, so every K/V tile is read from HBM once per item. Two kernels share this frame and
+// its epilogue; which one serves a (g, element type, head_dim) is fixed at compile time.
+//
+// Three-phase kernel (f32 pools, and 16-bit pools with one or two query heads per kv head, or four
+// at head_dim 128). The partition's tokens are walked through the block table in units of 8
 // tokens (units never straddle a block, since B is a multiple of 8); unit u belongs to wave
 // u mod 4, and each wave keeps PF units of loads in flight:
-//
 //   phase 1  scores: 8 lanes per token, each lane owns interleaved 16-byte chunks of the row;
 //            packed dot2 (bf16/f16) or fma (f32) against the query slices held in registers;
-//            an 8-lane DPP reduction; scores (pre-multiplied by scale·log2 e) go to LDS.
+//            an 8-lane DPP reduction (on MFMA instead at eight query heads per kv head); scores
+//            (pre-multiplied by scale·log2 e) go to LDS.
 //   softmax  per head over the partition: max, exp2, sum (one wave per head).
 //   phase 2  values: 16 lanes per token, each lane owns D/16 contiguous elements of the row;
 //            fp32 accumulators for all g heads; probabilities read from LDS.
 //   merge    the four token rows of a wave are summed across lanes (permlane swaps), then the
 //            waves through LDS (the score buffer's words, reused after a barrier).
+// LDS holds a score per token and head, which bounds the partition at 8192 / g tokens.
+//
+// One-pass kernel (16-bit pools with eight query heads per kv head, or four at head_dim 64): each
+// wave walks its 16-token units loading K and V together; S = K·Qᵀ and Oᵀ = Vᵀ·Pᵀ on MFMA with a
+// running (online) softmax per wave, V staged through LDS for the transposing read; the four
+// waves are combined with log-sum-exp weights. No scores are kept, so partitions of up to 4096
+// tokens fit, and no barrier separates a K stream from a V stream.
 //
 // A sequence whose context fits one partition writes its normalised output directly. Longer
 // contexts write (max, sum, unnormalised output) per partition to the workspace, and a second
@@ -24,6 +35,8 @@
 // denominator. The merge runs as its own launch so that no workgroup has to publish data to
 // another one inside a kernel (a device-scope fence per workgroup costs a full L2 write-back
 // and invalidate on this chip).
+#include <type_traits>
+
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -120,31 +133,62 @@ template <int DT, int NWORDS, int EPL> __device__ __forceinline__ void words_to_
 #define PKV_DECODE_MIN_WG 1
 #endif
 
-// Scores on MFMA for 16-bit pools with eight query heads per kv head: S = K·Qᵀ for 16 tokens at
-// a time (v_mfma_f32_16x16x32, tokens as M, the heads as N with the unused columns zero,
-// head_dim as K). The per-token dot products and 8-lane reductions this replaces are most of the
-// score phase's VALU work at eight heads, and the query operand takes D/32 registers instead of
-// G·D/64. Measured against the VALU score phase (GQA lengths, bf16, B 16): 64/8 heads +8 % at
-// d 64 (105 -> 88 VGPRs), equal at d 128; at four heads per kv head it was slower (-6 % at
-// d 128, -3 % at d 64), so there the VALU path stays.
-#ifndef PKV_DECODE_MFMA_SCORES
-#define PKV_DECODE_MFMA_SCORES 1
-#endif
+// S = K·Qᵀ and Oᵀ = Vᵀ·Pᵀ steps of the one-pass kernel: v_mfma_f32_16x16x32 on the pool's 16-bit
+// type (16 rows of A by 16 columns of B, 32 deep).
 typedef __bf16 dec_bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 dec_f16x8 __attribute__((ext_vector_type(8)));
 typedef float dec_f32x4 __attribute__((ext_vector_type(4)));
 
-template <int DT> __device__ __forceinline__ dec_f32x4 score_mfma(const u32x4& k, const u32x4& q, const dec_f32x4& c) {
+template <int DT> __device__ __forceinline__ dec_f32x4 mfma16x32(const u32x4& a, const u32x4& b, const dec_f32x4& c) {
   if constexpr (DT == DT_BF16)
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(dec_bf16x8, k), __builtin_bit_cast(dec_bf16x8, q),
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(dec_bf16x8, a), __builtin_bit_cast(dec_bf16x8, b),
                                                    c, 0, 0, 0);
   else
-    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(dec_f16x8, k), __builtin_bit_cast(dec_f16x8, q), c,
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(dec_f16x8, a), __builtin_bit_cast(dec_f16x8, b), c,
                                                   0, 0, 0);
 }
 
+// Units of loads in flight per wave in the one-pass kernel (two measured 6-10 % slower: the
+// second unit's registers cost a wave per SIMD at head_dim 128).
+#ifndef PKV_DECODE_FLASH_PF
+#define PKV_DECODE_FLASH_PF 1
+#endif
+
+// V reaches the A operand of Oᵀ = Vᵀ·Pᵀ through the wave's LDS staging tile and the transposing
+// LDS read of gfx950 (ds_read_b64_tr_b16): within each group of 16 lanes, lane i receives element
+// i % 4 of the 8-byte rows given by lanes 4j + i / 4, j = 0..3, which turns four staged token rows
+// into four tokens of one head_dim column per lane.
+
+template <int DT> __device__ __forceinline__ u32x2 lds_read_tr16(const unsigned char* p) {
+  typedef __bf16 bf16x4 __attribute__((__vector_size__(4 * sizeof(__bf16))));
+  typedef __fp16 f16x4 __attribute__((__vector_size__(4 * sizeof(__fp16))));
+  if constexpr (DT == DT_BF16)
+    return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                                         (__attribute__((address_space(3))) bf16x4*)(const_cast<unsigned char*>(p))));
+  else
+    return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4f16(
+                                         (__attribute__((address_space(3))) f16x4*)(const_cast<unsigned char*>(p))));
+}
+
+// Four probabilities as the B operand of a 32-deep MFMA: each rounded to the pool's 16-bit type,
+// then the four rounded remainders x - round(x), round to nearest even both times. P thus enters
+// with about 16 significant bits; one bf16 P alone (8 bits) can miss a 2e-3 error bound when a few
+// tokens carry most of the weight.
+template <int DT> __device__ __forceinline__ u32x4 p_operand(const dec_f32x4& p) {
+  using H = typename std::conditional<DT == DT_BF16, __bf16, _Float16>::type;
+  typedef H h8 __attribute__((ext_vector_type(8)));
+  h8 r;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const H hi = (H)p[e];
+    r[e] = hi;
+    r[e + 4] = (H)(p[e] - (float)hi);
+  }
+  return __builtin_bit_cast(u32x4, r);
+}
+
 template <int DT, int D, int G, int PF>
-__global__ __launch_bounds__(kDecThreads, PKV_DECODE_MIN_WG) void paged_decode_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(kDecThreads, one_pass(G, DT, D) ? 3 : PKV_DECODE_MIN_WG) void paged_decode_kernel(DecodeArgs a) {
   using T = typename Elem<DT>::T;
   constexpr int ES = sizeof(T);
   constexpr int VEC = 16 / ES;        // elements per 16-byte chunk
@@ -153,13 +197,21 @@ __global__ __launch_bounds__(kDecThreads, PKV_DECODE_MIN_WG) void paged_decode_k
   constexpr int NWORDS = EPL * ES / 4;
   static_assert(NCH >= 1 && EPL * ES % 8 == 0, "unsupported head dim");
 
-  constexpr int kPart = max_partition(G);
+  constexpr int kPart = max_partition(G, DT, D);
   constexpr int kScores = kPart * G + kWave;  // the tail absorbs discarded writes
   constexpr int kRed = kDecWaves * G * D;
+  constexpr bool kFlash = one_pass(G, DT, D);                                                  // one pass
+  constexpr int kSRow = D * ES + 32;  // staging row stride: four consecutive rows start 32 bytes apart in the banks
+  constexpr int kStageBytes = kDecWaves * 16 * kSRow;
+  constexpr int kBuf = kFlash ? (kStageBytes / 4 > kRed ? kStageBytes / 4 : kRed) : (kScores > kRed ? kScores : kRed);
   __shared__ int32_t s_tab[kPart / 8];
-  // [token][head]: scaled scores, then probabilities; after the last probability is read, the
-  // same words hold the per-wave partial outputs, so LDS stays within four workgroups per CU.
-  __shared__ float s_buf[kScores > kRed ? kScores : kRed];
+  // Three-phase kernel: [token][head] scaled scores, then probabilities. One-pass kernel: the
+  // waves' V staging tiles. After the last of either is read, the same words hold the per-wave
+  // partial outputs.
+  __shared__ __align__(16) float s_buf[kBuf];
+  __shared__ float s_wm[kFlash ? kDecWaves * G : 1];  // one-pass: per-wave running max and sum
+  __shared__ float s_wl[kFlash ? kDecWaves * G : 1];
+  unsigned char* const s_stage = reinterpret_cast<unsigned char*>(s_buf);
   float* const s_p = s_buf;
   float* const s_red = s_buf;
   __shared__ float s_m[G];
@@ -258,18 +310,17 @@ __global__ __launch_bounds__(kDecThreads, PKV_DECODE_MIN_WG) void paged_decode_k
     s_tab[i] = b;
   }
 
-  // Query slices of the G heads in the score mapping (VALU path), or the query as the MFMA B
-  // operand: lane (head column hc, group gg) holds dims 32·ks + 8·gg .. +7 of head hc for k-step
-  // ks, zero for the columns past G.
-  constexpr bool kMfma = PKV_DECODE_MFMA_SCORES && DT != DT_F32 && G == 8;
+  // Query slices of the G heads in the score mapping (three-phase kernel), or the query as the B
+  // operand of S = K·Qᵀ (one-pass kernel): lane (head column hc, group gg) holds dims
+  // 32·ks + 8·gg .. +7 of head hc for k-step ks, zero for the columns past G.
   constexpr int KS = D / 32;
   const int c = lane & 7;   // 16-byte chunk column
   const int r = lane >> 3;  // token row within a unit
   const int hc = lane & 15;  // MFMA mapping: token row (K operand) / head column (Q operand)
   const int gg = lane >> 4;  // MFMA mapping: 8-dim group of a k-step
-  u32x4 qr[kMfma ? 1 : G][kMfma ? 1 : NCH];
-  u32x4 qm[kMfma ? KS : 1];
-  if constexpr (kMfma) {
+  u32x4 qr[kFlash ? 1 : G][kFlash ? 1 : NCH];
+  u32x4 qm[kFlash ? KS : 1];
+  if constexpr (kFlash) {
     const T* qp = static_cast<const T*>(a.q) + ((size_t)row * a.hq + (size_t)kvh * G + min(hc, G - 1)) * D + 8 * gg;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
@@ -327,162 +378,263 @@ __global__ __launch_bounds__(kDecThreads, PKV_DECODE_MIN_WG) void paged_decode_k
     }
   };
 
-  // ---- phase 1: scores, PF units in flight per wave ---------------------------------------------
-  // Loads are unconditional (indices past the wave's last unit are clamped to it) so the wait
-  // counts inside the unrolled ring are static; results of padding iterations are discarded.
-  const int last = wave + kDecWaves * (nw > 0 ? nw - 1 : 0);
-  auto unit_of = [&](int i) { return min(wave + kDecWaves * i, last); };
-  const int nw_pad = (nw + PF - 1) / PF * PF;
-  Words<NWORDS> vb[PF][2];
-  if constexpr (kMfma) {
-    // Units of 16 tokens, unit v to wave v mod 4, two units of loads in flight. Lane (token hc,
-    // group gg) loads dims 32·ks + 8·gg .. +7 of its token's K row (the A operand of k-step ks);
-    // a token past the partition reads the last one (a written row) and its score is dropped.
-    // Scores go to LDS only for real heads and tokens; softmax reads no other entries.
-    constexpr int PF2 = 2;
-    const int nu16 = (n + 15) >> 4;
-    const int nw16 = nu16 > wave ? (nu16 - wave + kDecWaves - 1) / kDecWaves : 0;
-    const int last16 = wave + kDecWaves * (nw16 > 0 ? nw16 - 1 : 0);
-    auto unit16 = [&](int i) { return min(wave + kDecWaves * i, last16); };
-    auto load_k16 = [&](int v, u32x4 (&dst)[KS]) {
-      const int tk = min(16 * v + hc, n - 1);
+  // One-pass kernel: 16-token units, unit v to wave v mod 4. A token past the partition reads the
+  // last one (a written row); its score is dropped and its probability is 0.
+  const int nu16 = (n + 15) >> 4;
+  const int nw16 = nu16 > wave ? (nu16 - wave + kDecWaves - 1) / kDecWaves : 0;
+  const int last16 = wave + kDecWaves * (nw16 > 0 ? nw16 - 1 : 0);
+  auto unit16 = [&](int i) { return min(wave + kDecWaves * i, last16); };
+  // V of a unit: lane (chunk cw, row rw) loads 16 bytes of rows p·RP + rw.
+  constexpr int CPR = D * ES / 16;  // 16-byte chunks per row
+  constexpr int RP = 64 / CPR;      // rows per pass
+  constexpr int NPV = 16 / RP;      // passes per 16-token unit
+  const int cw = lane % CPR;
+  const int rw = lane / CPR;
+  auto load_v16 = [&](int v, u32x4 (&dst)[NPV]) {
+#pragma unroll
+    for (int ps = 0; ps < NPV; ++ps) {
+      const int tk = min(16 * v + ps * RP + rw, n - 1);
       const int phys = s_tab[tk >> a.log2_bs];
-      const T* p = kbase + ((size_t)phys * tile_rows + head_rows) * D + (size_t)(tk & (a.bs - 1)) * row_stride + 8 * gg;
+      const T* q = vbase + ((size_t)phys * tile_rows + head_rows) * D + (size_t)(tk & (a.bs - 1)) * row_stride + cw * VEC;
       if (v == (tn >> 4) && tn >= 0) {  // uniform: the unit holding the new token
-        if (tk == tn) p = knew + 8 * gg;
+        if (tk == tn) q = vnew + cw * VEC;
       }
+      dst[ps] = load_tile(reinterpret_cast<const u32x4*>(q));
+    }
+  };
+
+  // K of a unit as the A operand of S = K·Qᵀ: lane (token hc, group gg) loads dims 32·ks + 8·gg ..
+  // +7 of its token's row for k-step ks.
+  auto load_k16 = [&](int v, u32x4 (&dst)[KS]) {
+    const int tk = min(16 * v + hc, n - 1);
+    const int phys = s_tab[tk >> a.log2_bs];
+    const T* p = kbase + ((size_t)phys * tile_rows + head_rows) * D + (size_t)(tk & (a.bs - 1)) * row_stride + 8 * gg;
+    if (v == (tn >> 4) && tn >= 0) {  // uniform: the unit holding the new token
+      if (tk == tn) p = knew + 8 * gg;
+    }
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) dst[ks] = load_tile(reinterpret_cast<const u32x4*>(p + 32 * ks));
-    };
+    for (int ks = 0; ks < KS; ++ks) dst[ks] = load_tile(reinterpret_cast<const u32x4*>(p + 32 * ks));
+  };
+
+  if constexpr (kFlash) {
+    // ---- one pass: each wave streams its units' K and V together, with a running softmax -------
+    // Scores S = K·Qᵀ of a unit leave lane (head hc, group gg) with tokens 4·gg .. +3 of head hc,
+    // which is the B-operand layout of Oᵀ = Vᵀ·Pᵀ when K = 32 pairs the four tokens' rounded P
+    // (k 8·gg .. +3) with their rounded remainders (k 8·gg + 4 .. +7), and the A operand repeats
+    // the same four staged V rows in both halves: no probability leaves its lane and no score
+    // goes through LDS. Each wave keeps its own running max, sum and Oᵀ; the maximum is raised
+    // lazily (only when a unit's exceeds it by more than 2^8, so P ≤ 256 between rescales), and
+    // the four waves are combined with log-sum-exp weights at the end.
+    constexpr int NT = D / 16;
+    constexpr int PFF = PKV_DECODE_FLASH_PF;
+    constexpr float kLazy = 8.f;
+    dec_f32x4 oacc[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) oacc[t] = dec_f32x4{0.f, 0.f, 0.f, 0.f};
+    float m_run = -INFINITY, l_run = 0.f;
+    unsigned char* const stg = s_stage + wave * 16 * kSRow;
+    // Transposing read of tile t: lane (i, group gg) gives staged row 4·gg + i / 4, columns
+    // 16·t + 4·(i % 4) .. +3, and receives rows 4·gg .. +3 of column 16·t + i.
+    const unsigned char* const trp = stg + (4 * gg + (hc >> 2)) * kSRow + 4 * (hc & 3) * ES;
     if (nw16 > 0) {
-      u32x4 kb16[PF2][KS];
+      u32x4 kf[PFF][KS];
+      u32x4 vf[PFF][NPV];
 #pragma unroll
-      for (int j = 0; j < PF2; ++j) load_k16(unit16(j), kb16[j]);
-      const int nw16_pad = (nw16 + PF2 - 1) / PF2 * PF2;
-      for (int i0 = 0; i0 < nw16_pad; i0 += PF2) {
+      for (int j = 0; j < PFF; ++j) {
+        load_k16(unit16(j), kf[j]);
+        load_v16(unit16(j), vf[j]);
+      }
+      const int nwf_pad = (nw16 + PFF - 1) / PFF * PFF;
+      for (int i0 = 0; i0 < nwf_pad; i0 += PFF) {
 #pragma unroll
-        for (int j = 0; j < PF2; ++j) {
+        for (int j = 0; j < PFF; ++j) {
           const int i = i0 + j;
           const int v = unit16(i);
+          const bool live = i < nw16;  // uniform over the wave
           dec_f32x4 sacc = dec_f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int ks = 0; ks < KS; ++ks) sacc = score_mfma<DT>(kb16[j][ks], qm[ks], sacc);
-          load_k16(unit16(i + PF2), kb16[j]);
-          // lane holds tokens 16v + 4gg .. +3 of head column hc
+          for (int ks = 0; ks < KS; ++ks) sacc = mfma16x32<DT>(kf[j][ks], qm[ks], sacc);
+          if (live) {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int tok = 16 * v + 4 * gg + e;
-            const int dst = (hc < G && i < nw16 && tok < n) ? tok * G + hc : kPart * G + lane;
-            s_p[dst] = sacc[e] * a.scale_log2;
+            for (int ps = 0; ps < NPV; ++ps)
+              *reinterpret_cast<u32x4*>(stg + (ps * RP + rw) * kSRow + cw * 16) = vf[j][ps];
+          }
+          load_k16(unit16(i + PFF), kf[j]);
+          load_v16(unit16(i + PFF), vf[j]);
+          if (live) {
+            float sv[4];
+            float mx = -INFINITY;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              sv[e] = 16 * v + 4 * gg + e < n ? sacc[e] * a.scale_log2 : -INFINITY;
+              mx = fmaxf(mx, sv[e]);
+            }
+            mx = max_rows4(mx);  // over the unit's 16 tokens
+            const float mc = fmaxf(m_run, mx);
+            const bool need = mc > m_run + kLazy;  // always on the first unit (m_run = -inf)
+            if (__ballot(need) != 0) {
+              const float mn = need ? mc : m_run;
+              const float al = fast_exp2(m_run - mn);
+#pragma unroll
+              for (int t = 0; t < NT; ++t) oacc[t] *= al;
+              l_run *= al;
+              m_run = mn;
+            }
+            dec_f32x4 pv;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              pv[e] = fast_exp2(sv[e] - m_run);
+              l_run += pv[e];
+            }
+            const u32x4 pb = p_operand<DT>(pv);
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+              const u32x2 x = lds_read_tr16<DT>(trp + 32 * t);
+              oacc[t] = mfma16x32<DT>(u32x4{x[0], x[1], x[0], x[1]}, pb, oacc[t]);
+            }
           }
         }
       }
     }
+    // ---- the four waves: log-sum-exp weights against the largest running max ------------------
+    l_run = sum_rows4(l_run);  // the head's four lane groups
+    if (gg == 0 && hc < G) {
+      s_wm[wave * G + hc] = m_run;
+      s_wl[wave * G + hc] = l_run;
+    }
+    __syncthreads();  // staging tiles are dead; the waves' maxima and sums are visible
+    float mall = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kDecWaves; ++w) mall = fmaxf(mall, s_wm[w * G + (hc & (G - 1))]);
+    const float wt = m_run == -INFINITY ? 0.f : fast_exp2(m_run - mall);  // a wave without units
+    if (hc < G) {
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+        *reinterpret_cast<dec_f32x4*>(&s_red[(wave * G + hc) * D + 16 * t + 4 * gg]) = oacc[t] * wt;
+    }
+    if (tid < G) {
+      float l = 0.f;
+#pragma unroll
+      for (int w = 0; w < kDecWaves; ++w) {
+        const float mw = s_wm[w * G + tid];
+        l += mw == -INFINITY ? 0.f : fast_exp2(mw - mall) * s_wl[w * G + tid];
+      }
+      s_m[tid] = mall;
+      s_l[tid] = l;
+    }
+    __syncthreads();
+  } else {
+    // ---- phase 1: scores, PF units in flight per wave -------------------------------------------
+    // Loads are unconditional (indices past the wave's last unit are clamped to it) so the wait
+    // counts inside the unrolled ring are static; results of padding iterations are discarded.
+    const int last = wave + kDecWaves * (nw > 0 ? nw - 1 : 0);
+    auto unit_of = [&](int i) { return min(wave + kDecWaves * i, last); };
+    const int nw_pad = (nw + PF - 1) / PF * PF;
+    Words<NWORDS> vb[PF][2];
+    if (nw > 0) {
+      u32x4 kb[PF][NCH];
+#pragma unroll
+      for (int j = 0; j < PF; ++j) load_k(unit_of(j), kb[j]);
+      for (int i0 = 0; i0 < nw_pad; i0 += PF) {
+#pragma unroll
+        for (int j = 0; j < PF; ++j) {
+          const int i = i0 + j;
+          const int u = unit_of(i);
+          float sc[G];
+#pragma unroll
+          for (int g = 0; g < G; ++g) {
+            float acc = 0.f;
+#pragma unroll
+            for (int ch = 0; ch < NCH; ++ch) acc = dot16B<DT>(qr[g][ch], kb[j][ch], acc);
+            sc[g] = sum8(acc);
+          }
+          load_k(unit_of(i + PF), kb[j]);
+          const int tl = u * 8 + r;
+          float mine = sc[0];
+#pragma unroll
+          for (int g = 1; g < G; ++g) mine = (c == g) ? sc[g] : mine;
+          // Branch-free store: lanes with nothing to keep write into the discard tail.
+          const int dst = (c < G && i < nw) ? tl * G + c : kPart * G + lane;
+          s_p[dst] = tl < n ? mine * a.scale_log2 : -INFINITY;
+        }
+      }
+    }
+    // Value loads of the first units go out before the softmax so they overlap it.
     if (nw > 0) {
 #pragma unroll
       for (int j = 0; j < PF; ++j) load_v(unit_of(j), vb[j]);
     }
-  } else if (nw > 0) {
-    u32x4 kb[PF][NCH];
-#pragma unroll
-    for (int j = 0; j < PF; ++j) load_k(unit_of(j), kb[j]);
-    for (int i0 = 0; i0 < nw_pad; i0 += PF) {
-#pragma unroll
-      for (int j = 0; j < PF; ++j) {
-        const int i = i0 + j;
-        const int u = unit_of(i);
-        float sc[G];
-#pragma unroll
-        for (int g = 0; g < G; ++g) {
-          float acc = 0.f;
-#pragma unroll
-          for (int ch = 0; ch < NCH; ++ch) acc = dot16B<DT>(qr[g][ch], kb[j][ch], acc);
-          sc[g] = sum8(acc);
-        }
-        load_k(unit_of(i + PF), kb[j]);
-        const int tl = u * 8 + r;
-        float mine = sc[0];
-#pragma unroll
-        for (int g = 1; g < G; ++g) mine = (c == g) ? sc[g] : mine;
-        // Branch-free store: lanes with nothing to keep write into the discard tail.
-        const int dst = (c < G && i < nw) ? tl * G + c : kPart * G + lane;
-        s_p[dst] = tl < n ? mine * a.scale_log2 : -INFINITY;
+    __syncthreads();
+
+    // ---- softmax over the partition, one wave per head ---------------------------------------
+    for (int g = wave; g < G; g += kDecWaves) {
+      float m = -INFINITY;
+      for (int i = lane; i < n; i += kWave) m = fmaxf(m, s_p[i * G + g]);
+      m = wave_max(m);
+      float l = 0.f;
+      for (int i = lane; i < nunits * 8; i += kWave) {
+        const float p = i < n ? fast_exp2(s_p[i * G + g] - m) : 0.f;
+        s_p[i * G + g] = p;
+        l += p;
+      }
+      l = wave_sum(l);
+      if (lane == 0) {
+        s_m[g] = m;
+        s_l[g] = l;
       }
     }
-    // Value loads of the first units go out before the softmax so they overlap it.
-#pragma unroll
-    for (int j = 0; j < PF; ++j) load_v(unit_of(j), vb[j]);
-  }
-  __syncthreads();
+    __syncthreads();
 
-  // ---- softmax over the partition, one wave per head -----------------------------------------
-  for (int g = wave; g < G; g += kDecWaves) {
-    float m = -INFINITY;
-    for (int i = lane; i < n; i += kWave) m = fmaxf(m, s_p[i * G + g]);
-    m = wave_max(m);
-    float l = 0.f;
-    for (int i = lane; i < nunits * 8; i += kWave) {
-      const float p = i < n ? fast_exp2(s_p[i * G + g] - m) : 0.f;
-      s_p[i * G + g] = p;
-      l += p;
-    }
-    l = wave_sum(l);
-    if (lane == 0) {
-      s_m[g] = m;
-      s_l[g] = l;
-    }
-  }
-  __syncthreads();
-
-  // ---- phase 2: probability-weighted values, PF units in flight per wave ----------------------
-  float acc[G][EPL];
+    // ---- phase 2: probability-weighted values, PF units in flight per wave --------------------
+    float acc[G][EPL];
 #pragma unroll
-  for (int g = 0; g < G; ++g)
+    for (int g = 0; g < G; ++g)
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) acc[g][e] = 0.f;
-  if (nw > 0) {
-    for (int i0 = 0; i0 < nw_pad; i0 += PF) {
+      for (int e = 0; e < EPL; ++e) acc[g][e] = 0.f;
+    if (nw > 0) {
+      for (int i0 = 0; i0 < nw_pad; i0 += PF) {
 #pragma unroll
-      for (int j = 0; j < PF; ++j) {
-        const int i = i0 + j;
-        const int u = unit_of(i);
-        float vf[2][EPL];
-        words_to_f32<DT, NWORDS, EPL>(vb[j][0], vf[0]);
-        words_to_f32<DT, NWORDS, EPL>(vb[j][1], vf[1]);
-        load_v(unit_of(i + PF), vb[j]);
+        for (int j = 0; j < PF; ++j) {
+          const int i = i0 + j;
+          const int u = unit_of(i);
+          float vf[2][EPL];
+          words_to_f32<DT, NWORDS, EPL>(vb[j][0], vf[0]);
+          words_to_f32<DT, NWORDS, EPL>(vb[j][1], vf[1]);
+          load_v(unit_of(i + PF), vb[j]);
 #pragma unroll
-        for (int ps = 0; ps < 2; ++ps) {
-          const int tl = u * 8 + ps * 4 + rv;
-          const bool valid = i < nw && tl < n;
-          float pg[G];
+          for (int ps = 0; ps < 2; ++ps) {
+            const int tl = u * 8 + ps * 4 + rv;
+            const bool valid = i < nw && tl < n;
+            float pg[G];
 #pragma unroll
-          for (int g = 0; g < G; ++g) pg[g] = s_p[tl * G + g];  // 0 past the context
+            for (int g = 0; g < G; ++g) pg[g] = s_p[tl * G + g];  // 0 past the context
 #pragma unroll
-          for (int e = 0; e < EPL; ++e) {
-            const float x = valid ? vf[ps][e] : 0.f;  // unwritten slots may hold anything
+            for (int e = 0; e < EPL; ++e) {
+              const float x = valid ? vf[ps][e] : 0.f;  // unwritten slots may hold anything
 #pragma unroll
-            for (int g = 0; g < G; ++g) acc[g][e] = __builtin_fmaf(pg[g], x, acc[g][e]);
+              for (int g = 0; g < G; ++g) acc[g][e] = __builtin_fmaf(pg[g], x, acc[g][e]);
+            }
           }
         }
       }
     }
-  }
 
-  // ---- merge the four token rows of each wave, then the four waves ------------------------------
-#pragma unroll
-  for (int g = 0; g < G; ++g)
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) {
-      acc[g][e] = sum_rows4(acc[g][e]);
-    }
-  __syncthreads();  // every wave is done reading probabilities before s_red overwrites them
-  if (rv == 0) {
+    // ---- merge the four token rows of each wave, then the four waves --------------------------
 #pragma unroll
     for (int g = 0; g < G; ++g)
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) s_red[(wave * G + g) * D + cv * EPL + e] = acc[g][e];
-  }
-  __syncthreads();
+      for (int e = 0; e < EPL; ++e) {
+        acc[g][e] = sum_rows4(acc[g][e]);
+      }
+    __syncthreads();  // every wave is done reading probabilities before s_red overwrites them
+    if (rv == 0) {
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) s_red[(wave * G + g) * D + cv * EPL + e] = acc[g][e];
+    }
+    __syncthreads();
+  }  // three-phase kernel
 
   // The new token's rows into the pool (the fused cache write): nothing in this launch reads them.
   if (new_slot >= 0) {
@@ -701,7 +853,7 @@ static hipError_t launch_decode_dt(const DecodeLaunch& L, hipStream_t stream) {
 
 hipError_t launch_decode(const DecodeLaunch& L, hipStream_t stream) {
   const int g = L.num_kv_heads > 0 ? L.num_q_heads / L.num_kv_heads : 0;
-  if (g < 1 || L.partition > max_partition(g) || L.partition % 64 != 0) return hipErrorInvalidConfiguration;
+  if (g < 1 || L.partition > max_partition(g, L.dt, L.head_dim) || L.partition % 64 != 0) return hipErrorInvalidConfiguration;
   switch (L.dt) {
     case DT_F32: return launch_decode_dt<DT_F32>(L, stream);
     case DT_F16: return launch_decode_dt<DT_F16>(L, stream);

@@ -11,13 +11,34 @@
 #define PKV_DECODE_PREFETCH 3
 #endif
 
+// Query-head groupings (bit g set: g query heads per kv head) whose decode over 16-bit pools runs
+// the one-pass kernel, at head_dim 128 and at head_dim 64; the others, and f32 pools, run the
+// three-phase kernel. Chosen by measurement (bf16, block size 16, GQA lengths): the one-pass kernel
+// is ahead at eight heads per kv head (both head sizes) and at four with head_dim 64, behind at
+// four with head_dim 128 (-1 %) and at one or two (-2 to -4 %).
+#ifndef PKV_DECODE_FLASH
+#define PKV_DECODE_FLASH (1 << 8)
+#endif
+#ifndef PKV_DECODE_FLASH_D64
+#define PKV_DECODE_FLASH_D64 ((1 << 8) | (1 << 4))
+#endif
+// Largest partition of the one-pass kernel (it holds no scores, so LDS does not bound it).
+#ifndef PKV_FLASH_PARTITION
+#define PKV_FLASH_PARTITION 4096
+#endif
+
 namespace pkv {
 
-// Scores a decode workgroup holds in LDS: partition tokens x query heads per kv head (32 KiB, which
-// keeps four 256-thread workgroups per CU for every head grouping).
+// Scores a three-phase decode workgroup holds in LDS: partition tokens x query heads per kv head
+// (32 KiB, which keeps four 256-thread workgroups per CU for every head grouping).
 constexpr int kScoreFloats = PKV_SCORE_FLOATS;
-// Largest decode partition in tokens for g query heads per kv head.
-constexpr int max_partition(int g) { return kScoreFloats / g; }
+// Whether g query heads per kv head over a pool of element type dt (0 = f32, 1 = f16, 2 = bf16) and
+// head_dim d run the one-pass decode kernel.
+constexpr bool one_pass(int g, int dt, int d) {
+  return dt != 0 && g >= 1 && g <= 16 && (((d == 64 ? PKV_DECODE_FLASH_D64 : PKV_DECODE_FLASH) >> g) & 1) != 0;
+}
+// Largest decode partition in tokens for that kernel choice.
+constexpr int max_partition(int g, int dt, int d) { return one_pass(g, dt, d) ? PKV_FLASH_PARTITION : kScoreFloats / g; }
 
 inline int ilog2(int x) {
   int r = 0;

@@ -98,6 +98,7 @@ _SIGS = {
     "pkv_swap_blocks": (_I32, [_P, _P, _P, _P, _P, _I32, _DESC, _P]),
     "pkv_decode_workspace_bytes": (_SZ, [_I32, _I32, _I32, _DESC]),
     "pkv_decode_workspace_bytes_ex": (_SZ, [_I32, _I32, _I32, _DESC, _I32]),
+    "pkv_decode_max_partition": (_I32, [_I32, _DESC]),
     "pkv_decode_partition_size": (_I32, [_I32, _I32, _I32, _DESC]),
     "pkv_paged_attention_decode": (_I32, [_P, _I32, _P, _P, _P, _P, _I32, _P, _I32, _I32, ctypes.c_float,
                                           _I32, _DESC, _P, _SZ, _P]),
@@ -277,6 +278,10 @@ def decode_workspace_bytes(num_seqs: int, num_q_heads: int, max_context_len: int
                            partition_size: int = 0) -> int:
     return int(_lib.pkv_decode_workspace_bytes_ex(num_seqs, num_q_heads, max_context_len,
                                                   ctypes.byref(desc), partition_size))
+
+
+def decode_max_partition(num_q_heads: int, desc: CacheDesc) -> int:
+    return int(_lib.pkv_decode_max_partition(num_q_heads, ctypes.byref(desc)))
 
 
 def decode_partition_size(num_seqs: int, num_q_heads: int, max_context_len: int, desc: CacheDesc) -> int:

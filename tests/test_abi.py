@@ -88,9 +88,26 @@ def test_decode_workspace_validation():
     assert decode(c, part=100) == -1      # not a multiple of 64
     assert decode(c, part=8192 + 64) == -1            # too large for 1 query head per kv head
     assert decode(c, hq=8, part=4096 + 64) == -1      # 2 per kv head
-    assert decode(c, hq=16, part=2048 + 64) == -1     # 4 per kv head
-    assert decode(c, hq=32, part=1024 + 64) == -1     # 8 per kv head
-    assert L.pkv_decode_workspace_bytes_ex(2, 32, 5000, ctypes.byref(c), 2048) == 0  # invalid: 0
+    assert decode(c, hq=16, part=4096 + 64) == -1     # 4 per kv head at head_dim 64: the one-pass kernel
+    assert decode(desc(head_dim=128), hq=16, part=2048 + 64) == -1  # 4 per kv head at 128: three-phase
+    assert decode(c, hq=32, part=4096 + 64) == -1     # 8 per kv head, 16-bit pool: the one-pass kernel
+    assert decode(desc(dtype=pk.F32), hq=32, part=1024 + 64) == -1  # 8 per kv head over f32: three-phase
+    assert L.pkv_decode_workspace_bytes_ex(2, 32, 5000, ctypes.byref(c), 4096 + 64) == 0  # invalid: 0
+
+
+@pytest.mark.parametrize("dtype,head_dim,g,largest", [
+    (pk.F16, 64, 1, 8192), (pk.F16, 64, 2, 4096), (pk.F16, 64, 4, 4096), (pk.F16, 64, 8, 4096),
+    (pk.BF16, 128, 1, 8192), (pk.BF16, 128, 2, 4096), (pk.BF16, 128, 4, 2048), (pk.BF16, 128, 8, 4096),
+    (pk.F32, 64, 4, 2048), (pk.F32, 128, 8, 1024),
+])
+def test_decode_max_partition(dtype, head_dim, g, largest):
+    """Largest partition per kernel choice: 4096 for the one-pass kernel (16-bit pools at eight
+    query heads per kv head, and at four with head_dim 64), 8192 / g for the three-phase kernel."""
+    c = desc(dtype=dtype, head_dim=head_dim)
+    assert L.pkv_decode_max_partition(4 * g, ctypes.byref(c)) == largest
+    assert pk.decode_max_partition(4 * g, c) == largest
+    assert decode(c, hq=4 * g, part=largest + 64) == -1
+    assert L.pkv_decode_max_partition(6, ctypes.byref(c)) == -1  # 6 query heads over 4 kv heads
 
 
 def test_partition_size_rule():
@@ -104,8 +121,8 @@ def test_partition_size_rule():
     assert size(512, 4, 10000) == 4096
     assert size(512, 8, 5000) == 4096
     assert size(512, 16, 1000) == 1024
-    assert size(512, 16, 5000) == 2048
-    assert size(512, 32, 5000) == 1024
+    assert size(512, 16, 5000) == 4096    # one-pass kernel (f16, 4 per kv head, head_dim 64)
+    assert size(512, 32, 5000) == 4096    # one-pass kernel (f16, 8 per kv head)
     # fewer than 512 workgroups: halved, not below 256
     assert size(8, 16, 32768) == 2048     # 8 x 4 x 16 = 512
     assert size(4, 16, 32768) == 1024     # 4 x 4 x 32 = 512
@@ -129,7 +146,7 @@ def test_auto_workspace_covers_smaller_calls(g, hkv, S, ctx, fs, fc):
     bound = L.pkv_decode_workspace_bytes(S, hq, ctx, ctypes.byref(c))
     for s_, c_ in ((S, ctx), (S2, ctx), (S, ctx2), (S2, ctx2)):
         p = L.pkv_decode_partition_size(s_, hq, c_, ctypes.byref(c))
-        assert p >= 64 and p % 64 == 0 and p <= min(8192 // g, 4096)
+        assert p >= 64 and p % 64 == 0 and p <= min(L.pkv_decode_max_partition(hq, ctypes.byref(c)), 4096)
         need = L.pkv_decode_workspace_bytes_ex(s_, hq, c_, ctypes.byref(c), p)
         assert need <= bound, (s_, c_, p, need, bound)
 

@@ -105,17 +105,22 @@ def test_split_context_equals_oracle(partition):
     _check_attention(w, out, ref)
 
 
-@pytest.mark.parametrize("g,dt", [(1, "f16"), (2, "bf16"), (4, "bf16"), (8, "f32")])
-def test_largest_partition_per_head_grouping(g, dt):
-    """The largest partition for g query heads per kv head (8192 / g tokens, the LDS score buffer
-    full) on contexts that fill one, span two with a ragged tail, fall just short of one, and hold
-    a single token; then the automatic size, which for four sequences is the smallest (too few
-    workgroups otherwise)."""
-    cap = 8192 // g
+@pytest.mark.parametrize("g,dt,d", [(1, "f16", 128), (2, "bf16", 128), (4, "bf16", 128), (8, "f32", 128),
+                                    (8, "bf16", 128), (4, "f16", 64), (8, "bf16", 64)])
+def test_largest_partition_per_head_grouping(g, dt, d):
+    """The largest partition for g query heads per kv head (8192 / g tokens for the three-phase
+    kernel, its LDS score buffer full; 4096 for the one-pass kernel) on contexts that fill one,
+    span two with a ragged tail, fall just short of one, and hold a single token; then the
+    automatic size, which for four sequences is the smallest (too few workgroups otherwise)."""
+    from paged_kv_cache_323_amd import native as pk
+    one_pass = dt != "f32" and (g == 8 or (g == 4 and d == 64))
+    cap = 4096 if one_pass else 8192 // g
     ctx = [cap, 2 * cap + 37, cap - 5, 1]
-    w = make_decode_workload(70 + g, ctx, 2 * g, 2, 128, dt, 16, name=f"largest-partition-g{g}")
-    _announce(f"decode largest partition g={g} {dt} ctx={ctx}")
+    w = make_decode_workload(70 + g + d, ctx, 2 * g, 2, d, dt, 16, name=f"largest-partition-g{g}-d{d}")
+    _announce(f"decode largest partition g={g} {dt} d={d} ctx={ctx}")
     R = _runner()
+    desc = pk.CacheDesc.make(w.num_blocks, w.block_size, w.num_kv_heads, w.head_dim, dt)
+    assert pk.decode_max_partition(w.num_q_heads, desc) == cap
     _, ref = oracle.run_workload(w)
     st = R.play_script(w)
     for part in (cap, 0):
