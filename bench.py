@@ -978,9 +978,14 @@ def prefill_only(dtype: str = "bf16", reps: int = 20, warm: int = 50, prompts=No
     return res
 
 
-def profile_prefill(dtype: str = "bf16"):
-    """Profiling target for the prefill kernel (see prefill_only); prints one JSON line."""
-    print(json.dumps(prefill_only(dtype)))
+def profile_prefill(dtype: str = "bf16", prompts: str = ""):
+    """Profiling target for the prefill kernel (see prefill_only); prints one JSON line. prompts:
+    "LENxCOUNT" (e.g. 8192x4) instead of the 13B-shaped step's prompts."""
+    if prompts:
+        n, c = (int(x) for x in prompts.lower().split("x"))
+        print(json.dumps(prefill_only(dtype, reps=8, warm=5, prompts=[n] * c)))
+    else:
+        print(json.dumps(prefill_only(dtype)))
 
 
 HOST_LINK_GBS = 64.0  # PCIe 5.0 x16 per direction, the swap path's link
@@ -1066,6 +1071,8 @@ def main():
                     help="only run the prefill kernel on the 13B-shaped step's prompts (profiling target)")
     ap.add_argument("--prefill-dtype", default="bf16", choices=("bf16", "f16"),
                     help="pool dtype of --profile-prefill")
+    ap.add_argument("--prefill-prompts", default="",
+                    help="LENxCOUNT prompts for --profile-prefill (default: the 13B-shaped step's)")
     ap.add_argument("--profile-copy", action="store_true",
                     help="only run the copy kernel used to calibrate HBM byte counters")
     ap.add_argument("--profile-write", action="store_true",
@@ -1097,7 +1104,7 @@ def main():
         profile_swap()
         return
     if args.profile_prefill:
-        profile_prefill(args.prefill_dtype)
+        profile_prefill(args.prefill_dtype, args.prefill_prompts)
         return
     h = run_headline(args)
     w = h["w"]

@@ -97,6 +97,9 @@ constexpr int kPfTab = 1024;  // block-table entries cached in LDS at a time
 #ifndef PF_SCHED
 #define PF_SCHED 1
 #endif
+#ifndef PF_LDS_EPILOGUE
+#define PF_LDS_EPILOGUE 1
+#endif
 constexpr int kPfLookahead = PF_LOOKAHEAD;  // MFMA operand reads issued this many steps ahead
 
 
@@ -551,7 +554,49 @@ __global__ __launch_bounds__(kPfThreads, 2) void ragged_prefill_kernel(PrefillAr
     if (__syncthreads_or((int)bad)) run_keys(std::true_type{});  // uniform over the workgroup
   }
 
-  // ---- normalise and store: lane writes dims 16*dt + 4*g .. +3 of its row ----------------------
+  // ---- normalise and store ----------------------------------------------------------------------
+#if PF_LDS_EPILOGUE
+  if (a.out_dt != DT_F32) {
+    // 16-bit output: the wave's 32 rows go through its share of the (now idle) K buffers as whole
+    // rows, and leave as 16-byte stores, a row's 256 or 128 bytes contiguous.
+    __syncthreads();  // every wave is done reading the K/V buffers
+    constexpr int ORS = D + 8;  // LDS row stride (elements): rows start 16 bytes apart in the banks
+    uint16_t* ot = sK + wave * 32 * ORS;
+    static_assert(kPfRows * ORS <= 2 * KBUF, "output tile fits the K buffers");
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      const float l = lacc[nt][0];
+      const float inv = l > 0.f ? 1.f / l : 0.f;
+#pragma unroll
+      for (int dt = 0; dt < DT16; ++dt) {
+        const f32x4 v = oacc[dt][nt] * inv;
+        uint32_t w0, w1;
+        if (a.out_dt == DT_F16) {
+          w0 = pack_f16(v[0], v[1]);
+          w1 = pack_f16(v[2], v[3]);
+        } else {
+          w0 = f32_to_bf16_bits(v[0]) | ((uint32_t)f32_to_bf16_bits(v[1]) << 16);
+          w1 = f32_to_bf16_bits(v[2]) | ((uint32_t)f32_to_bf16_bits(v[3]) << 16);
+        }
+        *reinterpret_cast<u32x2*>(&ot[(nt * 16 + lr) * ORS + 16 * dt + 4 * g]) = u32x2{w0, w1};
+      }
+    }
+    // Lane (chunk c, row r): 16-byte chunk c of row r; CPR chunks per row, 64 / CPR rows per pass.
+    constexpr int RPP = kWave / CPR;
+#pragma unroll
+    for (int pass = 0; pass < 32 / RPP; ++pass) {
+      const int r = pass * RPP + lane / CPR;
+      const int c = lane % CPR;
+      const int row = wave * 32 + r;
+      if (row < nrows) {
+        const u32x4 x = *reinterpret_cast<const u32x4*>(&ot[r * ORS + 8 * c]);
+        *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(a.out) + ((size_t)(q0 + row0 + row) * a.hq + h) * D + 8 * c) = x;
+      }
+    }
+    return;
+  }
+#endif
+  // lane writes dims 16*dt + 4*g .. +3 of its row
 #pragma unroll
   for (int nt = 0; nt < 2; ++nt) {
     const float l = lacc[nt][0];
