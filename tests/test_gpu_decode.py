@@ -205,6 +205,28 @@ def test_decode_shape_sweep(dt, B, d, hq, hkv):
         assert np.array_equal(got[1].astype(np.float64), v1[np.arange(hq) // (hq // hkv)])
 
 
+@pytest.mark.parametrize("dt,d,hq,hkv", [("bf16", 128, 16, 2), ("bf16", 64, 16, 2), ("f16", 64, 8, 2),
+                                          ("bf16", 128, 8, 2), ("f16", 128, 2, 2)])
+def test_decode_sharp_scores(dt, d, hq, hkv):
+    """Scores scaled by 4.0 instead of 1/sqrt(d): a spread of about 65 in log2 units, so a running
+    maximum keeps rising by more than 2^8 from unit to unit (the one-pass kernel rescales its
+    accumulators many times per partition) and attention is close to one-hot, where the precision
+    of the probability operand shows. One-pass (8 and 4 query heads per kv head at d 64, 8 at
+    d 128) and three-phase shapes, automatic and 64-token partitions."""
+    import dataclasses
+    seed = zlib.crc32(f"sharp-{dt}-{d}-{hq}-{hkv}".encode()) % 10000
+    w = make_decode_workload(seed, [1, 17, 300, 2333, 5000], hq, hkv, d, dt, 16, name=f"sharp-{dt}-d{d}-{hq}/{hkv}")
+    w = dataclasses.replace(w, scale=4.0)
+    _announce(w.name)
+    R = _runner()
+    _, ref = oracle.run_workload(w)
+    st = R.play_script(w)
+    for part in (0, 64):
+        out, _ = R.attention(w, st, "f32", partition_size=part)
+        err = _check_attention(w, out, ref)
+        print(f"  partition {part}: max abs err {err:.3g}")
+
+
 def st_v_row(R, st, w, seq):
     tab = st.bm.block_table(seq)
     pool = device_pool_to_oracle_layout(R.to_host_storage(st.v_cache, w.dtype), w.num_blocks, w.block_size,

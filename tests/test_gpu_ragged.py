@@ -83,6 +83,20 @@ def test_ragged_shapes(case):
     _check(w, out, ref)
 
 
+@pytest.mark.parametrize("dt", ["bf16", "f16"])
+def test_ragged_sharp_scores(dt):
+    """Scores scaled by 4.0 instead of 1/sqrt(d): along a prefill row the maximum keeps rising by
+    more than the kernel's 2^8 lazy-rescale threshold, and attention is close to one-hot."""
+    import dataclasses
+    w = make_ragged_workload(51, [300, 1, 257, 2], [300, 2000, 600, 40], 8, 4, 128, dt, 16, name=f"ragged-sharp-{dt}")
+    w = dataclasses.replace(w, scale=4.0)
+    _announce(w.name)
+    _, ref = oracle.run_workload(w)
+    _, out = _run(w)
+    err = _check(w, out, ref)
+    print(f"  max abs err {err:.3g}")
+
+
 def test_ragged_native_out_dtype():
     w = make_workload("mixed", "small")
     _announce("mixed native out")
