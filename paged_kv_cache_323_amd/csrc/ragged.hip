@@ -97,6 +97,12 @@ constexpr int kPfTab = 1024;  // block-table entries cached in LDS at a time
 #ifndef PF_SCHED
 #define PF_SCHED 1
 #endif
+// Wave priority during the MFMA phases (Sᵀ and Oᵀ), back to 0 for softmax and staging: when the
+// two waves sharing a SIMD want to issue at once, the one feeding the matrix core goes first and
+// the other fills its gaps (+2.5 % on the 13B-shaped and on long prompts).
+#ifndef PF_SETPRIO
+#define PF_SETPRIO 1
+#endif
 #ifndef PF_LDS_EPILOGUE
 #define PF_LDS_EPILOGUE 1
 #endif
@@ -369,6 +375,9 @@ __global__ __launch_bounds__(kPfThreads, 2) void ragged_prefill_kernel(PrefillAr
       const uint16_t* cK = sK + (kt & 1) * KBUF;
       const uint16_t* cV = sVt + (kt & 1) * VBUF;
 
+#if PF_SETPRIO
+      __builtin_amdgcn_s_setprio(PF_SETPRIO);  // MFMA phase: issue first, the other wave fills the gaps
+#endif
       // ---- Sᵀ = K·Qᵀ: 4 key tiles x 2 row tiles -------------------------------------------------
       // Step st = (mt, ks) reads one K operand and feeds two MFMAs; operand reads run kPfLookahead
       // steps ahead of their MFMAs so that LDS latency overlaps matrix work.
@@ -404,6 +413,9 @@ __global__ __launch_bounds__(kPfThreads, 2) void ragged_prefill_kernel(PrefillAr
       // ---- causal mask and online softmax (per query row = per lane column) ----------------------
       // Scores stay unscaled here; exp2((s - m)·scale·log2 e) is one FMA per score. Only tiles that
       // reach past a wave's first row need the causal mask (a wave-uniform test).
+#if PF_SETPRIO
+      __builtin_amdgcn_s_setprio(0);
+#endif
       const bool need_mask = k0 + kPfKeys - 1 > pos0 + wave * 32;
       // P operands [row tile][k-step of 32 keys]: the only part (f16) or the high part and the
       // remainder (bf16)
@@ -479,6 +491,9 @@ __global__ __launch_bounds__(kPfThreads, 2) void ragged_prefill_kernel(PrefillAr
         }
       }
 
+#if PF_SETPRIO
+      __builtin_amdgcn_s_setprio(PF_SETPRIO);
+#endif
       // ---- Oᵀ += Vᵀ·Pᵀ with the same key order in both operands ---------------------------------
       // Step st = (dt, j) reads one V operand and feeds two MFMAs per row tile with a split P (one
       // otherwise); reads run ahead as above.
@@ -523,6 +538,9 @@ __global__ __launch_bounds__(kPfThreads, 2) void ragged_prefill_kernel(PrefillAr
         }
 #endif
       }
+#if PF_SETPRIO
+      __builtin_amdgcn_s_setprio(0);
+#endif
       __syncthreads();  // buffer kt&1 is free for tile kt+2; buffer (kt+1)&1 is complete
     }
     // The masked tiles: no products or softmax, only this wave's share of the staging and the
