@@ -29,6 +29,7 @@ long prompts), each row beside the ceiling that bounds it.
 from __future__ import annotations
 
 import argparse
+import collections
 import json
 import os
 import sys
@@ -62,6 +63,9 @@ def decode_algorithmic_bytes(ctx_lens, w, out_bytes_per_el):
 class DecodeLoop:
     """Steady-state decode steps over a resident workload (state advances every step)."""
 
+    RING = 8
+    MARK_EVERY = 4
+
     def __init__(self, w, steps_total, device="cuda", work_list=True, partition=0):
         import torch
         from paged_kv_cache_323_amd import native as pk
@@ -84,17 +88,18 @@ class DecodeLoop:
         # longest context in every sequence).
         self.work_list = work_list
         self.max_items = self.S * -(-self.max_ctx_final // self.partition)
-        self.n_items = [0, 0]
-        # one pinned staging area per parity of the step: [slots S | ctx S | tables S*MB | items]
-        # Two staging sets (host pinned + device) so that the upload of step k+1 runs on a copy
-        # stream while step k's kernels still read their own device copy.
+        # A ring of staging sets (pinned host + device), each [slots S | ctx S | tables S*MB | items]:
+        # step k fills set k % RING on the host and uploads it on a copy stream while earlier steps'
+        # kernels still read their own sets. Set reuse is guarded by sparse markers on the launch
+        # stream (one event every MARK_EVERY steps) that the host waits on: an event recorded on the
+        # launch stream every step delays the next step's launch by several microseconds.
+        self.n_items = [0] * self.RING
         self.items_off = 2 * self.S + self.S * self.max_blocks
         n = self.items_off + self.max_items
-        self.host = [torch.empty(n, dtype=torch.int32).pin_memory() for _ in range(2)]
+        self.host = [torch.empty(n, dtype=torch.int32).pin_memory() for _ in range(self.RING)]
         self.host_np = [h.numpy() for h in self.host]
-        self.dev = [torch.empty(n, dtype=torch.int32, device=device) for _ in range(2)]
-        self.uploaded = [None, None]      # copy-stream event: upload of set i finished
-        self.consumed = [None, None]      # main-stream event: kernels reading set i finished
+        self.dev = [torch.empty(n, dtype=torch.int32, device=device) for _ in range(self.RING)]
+        self.marks = collections.deque()  # (step index, launch-stream event recorded after that step)
         self.copy_stream = torch.cuda.Stream()
         self._views(0)
         self.q = R.to_device(w.queries(), w.dtype, device)
@@ -139,11 +144,20 @@ class DecodeLoop:
             for _ in self.attention():
                 pass
 
+    def _wait_step_done(self, j):
+        """Block the host until the kernels of step j (and so its upload) have finished."""
+        if j < 0:
+            return
+        while self.marks and self.marks[0][0] < j:
+            self.marks.popleft()
+        # markers come every MARK_EVERY <= RING steps, so one at or after step j exists
+        self.marks[0][1].synchronize()
+
     def step(self, ev=None):
         torch, pk, w = self.torch, self.pk, self.w
-        buf = self.step_idx & 1
-        if self.uploaded[buf] is not None:
-            self.uploaded[buf].synchronize()       # the H2D that last read this host buffer is done
+        buf = self.step_idx % self.RING
+        # step idx - RING last read this set (host buffer by its upload, device buffer by its kernels)
+        self._wait_step_done(self.step_idx - self.RING)
         hn = self.host_np[buf]
         slots, pairs = self.st.bm.append(self.seqs, np.ones(self.S, dtype=np.int32))
         hn[: self.S] = slots
@@ -154,12 +168,9 @@ class DecodeLoop:
                                                      hn[self.items_off: self.items_off + self.max_items])
         main = torch.cuda.current_stream()
         with torch.cuda.stream(self.copy_stream):
-            if self.consumed[buf] is not None:
-                self.copy_stream.wait_event(self.consumed[buf])
             self.dev[buf].copy_(self.host[buf], non_blocking=True)
             e = torch.cuda.Event()
             e.record(self.copy_stream)
-        self.uploaded[buf] = e
         main.wait_event(e)
         self._views(buf)
         if len(pairs):
@@ -187,9 +198,10 @@ class DecodeLoop:
         self._finish_step(buf, hn, main)
 
     def _finish_step(self, buf, hn, main):
-        done = self.torch.cuda.Event()
-        done.record(main)
-        self.consumed[buf] = done
+        if self.step_idx % self.MARK_EVERY == self.MARK_EVERY - 1:
+            done = self.torch.cuda.Event()
+            done.record(main)
+            self.marks.append((self.step_idx, done))
         self.ctx_history.append(hn[self.S: 2 * self.S].copy())
         self.step_idx += 1
 
