@@ -106,6 +106,12 @@ constexpr int kPfTab = 1024;  // block-table entries cached in LDS at a time
 #ifndef PF_LDS_EPILOGUE
 #define PF_LDS_EPILOGUE 1
 #endif
+// Order of the MFMA steps: 1 runs the k-steps outermost (Sᵀ: every key tile's first k-step, then
+// every second one; Oᵀ: every head-dim tile against keys 0..31, then against 32..63), so an MFMA's
+// accumulator was last written 8 or 16 MFMAs earlier instead of 2: 1-2 % faster than 0.
+#ifndef PF_ACC_ORDER
+#define PF_ACC_ORDER 1
+#endif
 constexpr int kPfLookahead = PF_LOOKAHEAD;  // MFMA operand reads issued this many steps ahead
 
 
@@ -380,11 +386,13 @@ __global__ __launch_bounds__(kPfThreads, 2) void ragged_prefill_kernel(PrefillAr
 #endif
       // ---- Sᵀ = K·Qᵀ: 4 key tiles x 2 row tiles -------------------------------------------------
       // Step st = (mt, ks) reads one K operand and feeds two MFMAs; operand reads run kPfLookahead
-      // steps ahead of their MFMAs so that LDS latency overlaps matrix work.
+      // steps ahead of their MFMAs so that LDS latency overlaps matrix work. The steps go ks-major
+      // (PF_ACC_ORDER).
       constexpr int NQK = 4 * KS;
       auto kread = [&](int st) {
+        const int mt = PF_ACC_ORDER ? st % 4 : st / KS, ks = PF_ACC_ORDER ? st / 4 : st % KS;
         return __builtin_bit_cast(
-            V8, *reinterpret_cast<const u32x4*>(&cK[(16 * (st / KS) + lr) * KLD + 32 * (st % KS) + 8 * g]));
+            V8, *reinterpret_cast<const u32x4*>(&cK[(16 * mt + lr) * KLD + 32 * ks + 8 * g]));
       };
       f32x4 sacc[4][2];
       {
@@ -394,7 +402,7 @@ __global__ __launch_bounds__(kPfThreads, 2) void ragged_prefill_kernel(PrefillAr
 #pragma unroll
         for (int st = 0; st < NQK; ++st) {
           if (st + kPfLookahead < NQK) kop[(st + kPfLookahead) % (kPfLookahead + 1)] = kread(st + kPfLookahead);
-          const int mt = st / KS, ks = st % KS;
+          const int mt = PF_ACC_ORDER ? st % 4 : st / KS, ks = PF_ACC_ORDER ? st / 4 : st % KS;
           const V8 ka = kop[st % (kPfLookahead + 1)];
 #pragma unroll
           for (int nt = 0; nt < 2; ++nt)
@@ -496,11 +504,12 @@ __global__ __launch_bounds__(kPfThreads, 2) void ragged_prefill_kernel(PrefillAr
 #endif
       // ---- Oᵀ += Vᵀ·Pᵀ with the same key order in both operands ---------------------------------
       // Step st = (dt, j) reads one V operand and feeds two MFMAs per row tile with a split P (one
-      // otherwise); reads run ahead as above.
+      // otherwise); reads run ahead as above. The steps go j-major (PF_ACC_ORDER).
       {
         constexpr int NPV = DT16 * 2;
         auto vread = [&](int st) {
-          const uint16_t* vrow = &cV[(16 * (st / 2) + lr) * VLD + 32 * (st % 2) + 4 * g];
+          const int dt = PF_ACC_ORDER ? st % DT16 : st / 2, j = PF_ACC_ORDER ? st / DT16 : st % 2;
+          const uint16_t* vrow = &cV[(16 * dt + lr) * VLD + 32 * j + 4 * g];
           const u32x2 x0 = *reinterpret_cast<const u32x2*>(vrow);
           const u32x2 x1 = *reinterpret_cast<const u32x2*>(vrow + 16);
           return __builtin_bit_cast(PV8, u32x4{x0[0], x0[1], x1[0], x1[1]});
@@ -511,7 +520,7 @@ __global__ __launch_bounds__(kPfThreads, 2) void ragged_prefill_kernel(PrefillAr
 #pragma unroll
         for (int st = 0; st < NPV; ++st) {
           if (st + kPfLookahead < NPV) vop[(st + kPfLookahead) % (kPfLookahead + 1)] = vread(st + kPfLookahead);
-          const int dt = st / 2, j = st % 2;
+          const int dt = PF_ACC_ORDER ? st % DT16 : st / 2, j = PF_ACC_ORDER ? st / DT16 : st % 2;
           const PV8 va = vop[st % (kPfLookahead + 1)];
 #pragma unroll
           for (int nt = 0; nt < 2; ++nt) {
