@@ -73,6 +73,9 @@ class EngineStats:
 
 
 class Engine:
+    STAGE_RING = 8    # staging sets (pinned host + device) for the per-step index upload
+    MARK_EVERY = 4    # a launch-stream marker every this many steps guards their reuse
+
     def __init__(self, num_blocks: int, block_size: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
                  dtype: str, max_num_seqs: int = 64, max_step_tokens: int = 8192, num_host_blocks: int = 0,
                  seed: int = 0, values=None, keep_outputs: bool = False, device: str = "cuda"):
@@ -109,11 +112,15 @@ class Engine:
         self.ws = torch.zeros(1, dtype=torch.uint8, device=device)
         self.scale = float(np.float32(1.0 / np.sqrt(head_dim)))
         # Per-step index data (slots, cu_seqlens, lengths, tables) goes up in one asynchronous copy
-        # from one of two pinned staging buffers, so the host prepares step k+1 while the GPU
-        # runs step k; a buffer is rewritten only after the copy that last read it has run.
-        self._stage_host = [None, None]
-        self._stage_done = [None, None]
-        self._stage_dev = None
+        # on a copy stream from a ring of staging sets (pinned host buffer + device buffer), so the
+        # host prepares later steps while the GPU runs earlier ones and the copy does not sit
+        # between the kernels. Step k uses set k mod STAGE_RING; before refilling it the host waits
+        # on a launch-stream marker at or after step k - STAGE_RING (markers every MARK_EVERY
+        # steps: an event recorded on the launch stream every step delays the next launch).
+        self._stage_host: List[Optional[torch.Tensor]] = [None] * self.STAGE_RING
+        self._stage_dev: List[Optional[torch.Tensor]] = [None] * self.STAGE_RING
+        self._marks: Deque = deque()      # (step index, launch-stream event after that step)
+        self._copy_stream = torch.cuda.Stream(device=device)
         self.max_len = 0                  # longest context any request can reach (sizes tables)
 
     # ---- requests -------------------------------------------------------------------------------
@@ -256,30 +263,44 @@ class Engine:
         host = torch.from_numpy(np.ascontiguousarray(pairs, dtype=np.int32)).pin_memory()
         return host.to(self.device, non_blocking=True)
 
+    def _wait_step_done(self, j: int) -> None:
+        """Block the host until the kernels of step j (and so its upload) have finished."""
+        if j < 0:
+            return
+        while self._marks and self._marks[0][0] < j:
+            self._marks.popleft()
+        if self._marks:  # markers come every MARK_EVERY <= STAGE_RING steps, so one is there
+            self._marks[0][1].synchronize()
+        else:
+            torch.cuda.synchronize(self.device)
+
     def _staging(self, n: int) -> np.ndarray:
-        """An int32 view of n elements of the pinned staging buffer for this step."""
-        i = self.step_idx & 1
-        if self._stage_done[i] is not None:
-            self._stage_done[i].synchronize()   # the upload that last read this buffer has run
+        """An int32 view of n elements of this step's pinned staging buffer."""
+        i = self.step_idx % self.STAGE_RING
+        # step_idx - STAGE_RING last used this set: its upload read the host buffer and its
+        # kernels read the device buffer
+        self._wait_step_done(self.step_idx - self.STAGE_RING)
         buf = self._stage_host[i]
         if buf is None or buf.numel() < n:
-            buf = torch.empty(max(n, 2 * (buf.numel() if buf is not None else 0), 1 << 16),
-                              dtype=torch.int32).pin_memory()
-            self._stage_host[i] = buf
-        return buf.numpy()[:n]
+            m = max(n, 2 * (buf.numel() if buf is not None else 0), 1 << 16)
+            if buf is not None:
+                torch.cuda.synchronize(self.device)  # rare: nothing in flight uses the old pair
+            self._stage_host[i] = torch.empty(m, dtype=torch.int32).pin_memory()
+            self._stage_dev[i] = torch.empty(m, dtype=torch.int32, device=self.device)
+        return self._stage_host[i].numpy()[:n]
 
     def _upload(self, host: np.ndarray) -> torch.Tensor:
-        """Copy this step's staging contents to the device (asynchronously, on the current stream)."""
-        i = self.step_idx & 1
+        """Copy this step's staging contents to the device on the copy stream; the launch stream
+        waits for the copy."""
+        i = self.step_idx % self.STAGE_RING
         n = len(host)
-        if self._stage_dev is None or self._stage_dev.numel() < n:
-            self._stage_dev = torch.empty(max(n, 1 << 16, 2 * (self._stage_dev.numel() if self._stage_dev is not None
-                                                                else 0)), dtype=torch.int32, device=self.device)
-        dev = self._stage_dev[:n]
-        dev.copy_(self._stage_host[i][:n], non_blocking=True)
-        ev = torch.cuda.Event()
-        ev.record()
-        self._stage_done[i] = ev
+        dev = self._stage_dev[i][:n]
+        main = torch.cuda.current_stream(self.device)
+        with torch.cuda.stream(self._copy_stream):
+            dev.copy_(self._stage_host[i][:n], non_blocking=True)
+            ev = torch.cuda.Event()
+            ev.record(self._copy_stream)
+        main.wait_event(ev)
         return dev
 
     # ---- one model step -------------------------------------------------------------------------
@@ -336,5 +357,9 @@ class Engine:
                 self.finished.append(s)
                 self.stats.finished += 1
         self.stats.steps += 1
+        if self.step_idx % self.MARK_EVERY == self.MARK_EVERY - 1:
+            ev = torch.cuda.Event()
+            ev.record(torch.cuda.current_stream(self.device))
+            self._marks.append((self.step_idx, ev))
         self.step_idx += 1
         return rec
