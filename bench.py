@@ -689,9 +689,10 @@ def run_mixed():
     T_p = int(w.cu_seqlens()[n_pre])
     ql_p, ctx_p = w.q_lens[:n_pre], list(lens[:n_pre])
     mx_p = int(max(ctx_p))
+    # (its shortest prompt as the lower bound on q_len: no decode-row launches)
     pre_us, _ = _time_events(lambda: pk.paged_attention_ragged(out[:T_p], q[:T_p], cu_p, cl[:n_pre], st.k_cache,
                                                                st.v_cache, bt[:n_pre], w.scale, mq, mx_p, st.desc,
-                                                               ws), reps=20)
+                                                               ws, min_q_len=min(ql_p)), reps=20)
     flops = prefill_flops(ql_p, ctx_p, w.num_q_heads, w.head_dim)
     dec_kv = int(sum(int(c) for c, ql in zip(lens, w.q_lens) if ql == 1)) * w.kv_bytes_per_token()
     write_bytes = 2 * 2 * int(q.shape[0]) * w.num_kv_heads * w.head_dim * 2
@@ -980,7 +981,8 @@ def prefill_only(dtype: str = "bf16", reps: int = 20, warm: int = 50, prompts=No
     ws = torch.zeros(max(pk.ragged_workspace_bytes(len(lens), q.shape[0], w.num_q_heads, mx, mx, st.desc), 1),
                      dtype=torch.uint8, device="cuda")
     med, _ = _time_events(lambda: pk.paged_attention_ragged(out, q, cu, cl, st.k_cache, st.v_cache, bt, w.scale,
-                                                            mx, mx, st.desc, ws), reps=reps, warm=warm)
+                                                            mx, mx, st.desc, ws, min_q_len=min(pre)),
+                          reps=reps, warm=warm)
     flops = prefill_flops(pre, pre, w.num_q_heads, w.head_dim)
     res = {"dtype": dtype, "prefill_rows": int(sum(pre)), "sequences": len(pre), "launches": reps + warm,
            "gflop_per_launch": round(flops / 1e9, 2), "median_us": round(med, 1),

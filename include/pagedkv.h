@@ -371,6 +371,26 @@ int32_t pkv_paged_attention_ragged(void* out, int32_t out_dtype, const void* q,
                                    size_t workspace_bytes, void* stream);
 
 /*
+ * paged_attention_ragged_ex — pkv_paged_attention_ragged with a host lower bound min_q_len on
+ *   every sequence's q_len beside the upper bound max_q_len (same step, same layouts). A batch of
+ *   prefill chunks only (min_q_len >= 2) needs neither the decode-row launch nor its merge: both
+ *   are skipped, and if a sequence has a single row after all it is computed by the prefill
+ *   kernel, whose one-row tile attends the same keys, so a wrong bound costs time, not results.
+ *   min_q_len == 1 is pkv_paged_attention_ragged exactly (bit-identical outputs). In causal-rows
+ *   mode (see above) min_q_len has no effect.
+ *   Errors: min_q_len < 1, or min_q_len > 1 and above max_q_len: PKV_EINVAL (nothing enqueued);
+ *   otherwise as pkv_paged_attention_ragged. The workspace size is the same.
+ */
+int32_t pkv_paged_attention_ragged_ex(void* out, int32_t out_dtype, const void* q,
+                                      const int32_t* cu_seqlens_q, const int32_t* context_lens,
+                                      const void* k_cache, const void* v_cache,
+                                      const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                      int32_t num_seqs, int32_t num_tokens, int32_t num_q_heads,
+                                      float scale, int32_t min_q_len, int32_t max_q_len,
+                                      int32_t max_context_len, const pkv_cache_desc* cache,
+                                      void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * swap_blocks — move whole blocks between a GPU pool and a host swap pool for preemption and
  *   restore (「PagedAttention原理」 §抢占与恢复 / §swap). For each pair i: block dst_i of
  *   (dst_k, dst_v) <- block src_i of (src_k, src_v), all B slots, all kv heads, bit for bit.

@@ -468,12 +468,12 @@ size_t pkv_ragged_workspace_bytes(int32_t num_seqs, int32_t num_tokens, int32_t 
   return pkv_decode_workspace_bytes_ex(items, num_q_heads, max_context_len, c, 0);
 }
 
-int32_t pkv_paged_attention_ragged(void* out, int32_t out_dtype, const void* q, const int32_t* cu_seqlens_q,
-                                   const int32_t* context_lens, const void* k_cache, const void* v_cache,
-                                   const int32_t* block_tables, int32_t max_blocks_per_seq, int32_t num_seqs,
-                                   int32_t num_tokens, int32_t num_q_heads, float scale, int32_t max_q_len,
-                                   int32_t max_context_len, const pkv_cache_desc* c, void* workspace,
-                                   size_t workspace_bytes, void* stream) {
+int32_t pkv_paged_attention_ragged_ex(void* out, int32_t out_dtype, const void* q, const int32_t* cu_seqlens_q,
+                                      const int32_t* context_lens, const void* k_cache, const void* v_cache,
+                                      const int32_t* block_tables, int32_t max_blocks_per_seq, int32_t num_seqs,
+                                      int32_t num_tokens, int32_t num_q_heads, float scale, int32_t min_q_len,
+                                      int32_t max_q_len, int32_t max_context_len, const pkv_cache_desc* c,
+                                      void* workspace, size_t workspace_bytes, void* stream) {
   int32_t st = check_cache(c);
   if (st != PKV_OK) return st;
   if ((st = check_heads(num_q_heads, c)) != PKV_OK) return st;
@@ -482,6 +482,7 @@ int32_t pkv_paged_attention_ragged(void* out, int32_t out_dtype, const void* q, 
     return PKV_EINVAL;
   if (num_seqs == 0 || num_tokens == 0) return PKV_OK;
   if (max_q_len > max_context_len || max_q_len > num_tokens) return PKV_EINVAL;
+  if (min_q_len < 1 || (min_q_len > 1 && min_q_len > max_q_len)) return PKV_EINVAL;
   if (!out || !q || !cu_seqlens_q || !context_lens || !k_cache || !v_cache || !block_tables) return PKV_EINVAL;
   // Every row through the decode kernels, one item per query row attending keys up to its own
   // position (fp32 throughout), when ragged_rows_mode says so; else decode rows there and
@@ -490,11 +491,16 @@ int32_t pkv_paged_attention_ragged(void* out, int32_t out_dtype, const void* q, 
     return decode_common_cu(out, out_dtype, q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens,
                             num_seqs, num_q_heads, scale, max_context_len, c, 0, workspace, workspace_bytes, stream,
                             cu_seqlens_q, 0, num_tokens, nullptr, 0, true);
-  // decode rows (q_len == 1) through the decode kernels with row indirection
-  st = decode_common_cu(out, out_dtype, q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens,
-                        num_seqs, num_q_heads, scale, max_context_len, c, 0, workspace, workspace_bytes, stream,
-                        cu_seqlens_q, 0, num_tokens);
-  if (st != PKV_OK || max_q_len <= 1) return st;
+  // Decode rows (q_len == 1) through the decode kernels with row indirection, unless the caller
+  // states that no sequence has a single row: then the two decode launches are skipped and any
+  // single-row sequence there is after all gets a row tile of the prefill kernel.
+  const bool decode_rows = min_q_len == 1;
+  if (decode_rows) {
+    st = decode_common_cu(out, out_dtype, q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens,
+                          num_seqs, num_q_heads, scale, max_context_len, c, 0, workspace, workspace_bytes, stream,
+                          cu_seqlens_q, 0, num_tokens);
+    if (st != PKV_OK || max_q_len <= 1) return st;
+  }
   pkv::PrefillLaunch P;
   P.out = out;
   P.out_dt = out_dtype;
@@ -514,7 +520,20 @@ int32_t pkv_paged_attention_ragged(void* out, int32_t out_dtype, const void* q, 
   P.dt = c->dtype;
   P.scale = scale;
   P.num_blocks = c->num_blocks;
+  P.min_rows = decode_rows ? 2 : 1;
   return launched(pkv::launch_ragged_prefill(P, (hipStream_t)stream));
+}
+
+int32_t pkv_paged_attention_ragged(void* out, int32_t out_dtype, const void* q, const int32_t* cu_seqlens_q,
+                                   const int32_t* context_lens, const void* k_cache, const void* v_cache,
+                                   const int32_t* block_tables, int32_t max_blocks_per_seq, int32_t num_seqs,
+                                   int32_t num_tokens, int32_t num_q_heads, float scale, int32_t max_q_len,
+                                   int32_t max_context_len, const pkv_cache_desc* c, void* workspace,
+                                   size_t workspace_bytes, void* stream) {
+  return pkv_paged_attention_ragged_ex(out, out_dtype, q, cu_seqlens_q, context_lens, k_cache, v_cache, block_tables,
+                                       max_blocks_per_seq, num_seqs, num_tokens, num_q_heads, scale,
+                                       1, max_q_len, max_context_len, c, workspace,
+                                       workspace_bytes, stream);
 }
 
 int32_t pkv_paged_attention_decode(void* out, int32_t out_dtype, const void* q, const void* k_cache,

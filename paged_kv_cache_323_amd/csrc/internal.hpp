@@ -139,10 +139,11 @@ struct PrefillLaunch {
   int dt;
   float scale;
   int num_blocks;  // pool blocks (debug builds check table entries against it)
+  int min_rows;    // sequences with at least this many query rows (1 or 2) get row tiles
 };
 
-// Causal attention of every multi-row (prefill) sequence of a ragged batch; rows of
-// single-row sequences are left untouched.
+// Causal attention of every sequence of a ragged batch with at least min_rows query rows (2:
+// the prefill sequences; rows of single-row sequences are left untouched. 1: every sequence).
 hipError_t launch_ragged_prefill(const PrefillLaunch& a, hipStream_t stream);
 
 }  // namespace pkv

@@ -87,6 +87,7 @@ struct PrefillArgs {
   float scale_log2;
   int num_tokens;  // rows of q / out (debug builds check cu_seqlens against it)
   int num_blocks;  // pool blocks (debug builds check table entries)
+  int min_rows;    // a sequence with at least this many query rows (1 or 2) gets row tiles
 };
 
 constexpr int kPfTab = 1024;  // block-table entries cached in LDS at a time
@@ -152,7 +153,7 @@ __global__ __launch_bounds__(kPfThreads, 2) void ragged_prefill_kernel(PrefillAr
   // sequence per thread: a wave prefix sum of the row-tile counts and the four wave totals give
   // each sequence's running count, and the thread whose sequence holds the slot publishes it with
   // its row offset, row count and context length (read in the same pass). Decode rows (one query
-  // row) have no row tiles. Debug builds reject row offsets that are negative, decreasing or past
+  // row) have no row tiles unless min_rows is 1 (the call runs no decode launch). Debug builds reject row offsets that are negative, decreasing or past
   // the batch, and treat such a sequence as empty.
   if (tid == 0) s_seq = -1;
   {
@@ -169,7 +170,7 @@ __global__ __launch_bounds__(kPfThreads, 2) void ragged_prefill_kernel(PrefillAr
           debug_flag(DBG_RAGGED);
         } else {
           cql = c1 - cq0;
-          nt = cql > 1 ? (cql + kPfRows - 1) / kPfRows : 0;
+          nt = cql >= a.min_rows ? (cql + kPfRows - 1) / kPfRows : 0;
         }
       }
       int incl = nt;
@@ -655,13 +656,15 @@ static hipError_t launch_prefill_dt(const PrefillLaunch& L, hipStream_t stream) 
   a.scale_log2 = L.scale * 1.4426950408889634f;
   a.num_tokens = L.num_tokens;
   a.num_blocks = L.num_blocks;
-  // Row tiles: sum over sequences of ceil(q_len / 128) <= T / 128 + (number of prefill
-  // sequences); slots past the real count exit at once.
-  const long long slots = (L.num_tokens + kPfRows - 1) / kPfRows + (L.num_seqs < L.num_tokens / 2 ? L.num_seqs : L.num_tokens / 2);
+  a.min_rows = L.min_rows;
+  // Row tiles: sum over sequences of ceil(q_len / 128) <= T / 128 + (number of sequences with
+  // at least min_rows rows, at most T / min_rows); slots past the real count exit at once.
+  const int with_tiles = L.num_tokens / L.min_rows;
+  const long long slots = (L.num_tokens + kPfRows - 1) / kPfRows + (L.num_seqs < with_tiles ? L.num_seqs : with_tiles);
   if (slots <= 0) return hipSuccess;
   // Heads are the fast grid dimension so the heaviest row tiles of every head go out first. Slots
   // run over y, then z (slot = y + z * gridDim.y keeps the dispatch order), so there is no limit
-  // below the 2^31 row offsets: slots < T/128 + T/2 + 1 < 65535^2.
+  // below the 2^31 row offsets: slots < T/128 + T + 1 < 65535^2.
   const unsigned gy = slots > 65535 ? 65535u : (unsigned)slots;
   const unsigned gz = (unsigned)((slots + gy - 1) / gy);
   const dim3 grid(L.num_q_heads, gy, gz);
@@ -670,6 +673,7 @@ static hipError_t launch_prefill_dt(const PrefillLaunch& L, hipStream_t stream) 
 }
 
 hipError_t launch_ragged_prefill(const PrefillLaunch& L, hipStream_t stream) {
+  if (L.min_rows != 1 && L.min_rows != 2) return hipErrorInvalidValue;
   if (L.dt == DT_BF16) return launch_prefill_dt<DT_BF16>(L, stream);
   if (L.dt == DT_F16) return launch_prefill_dt<DT_F16>(L, stream);
   return hipErrorInvalidConfiguration;

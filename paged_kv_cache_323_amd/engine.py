@@ -336,8 +336,10 @@ class Engine:
         nbytes = pk.ragged_workspace_bytes(S, int(cu[-1]), self.hq, max_q, max_ctx, self.desc)
         if self.ws.numel() < nbytes:
             self.ws = torch.zeros(nbytes, dtype=torch.uint8, device=self.device)
+        # the step's shortest chunk bounds q_len from below: a step of prefill chunks only runs
+        # no decode-row launches
         pk.paged_attention_ragged(out, q, cu_d, lens_d, self.k_cache, self.v_cache, tab_d, self.scale,
-                                  max_q, max_ctx, self.desc, self.ws)
+                                  max_q, max_ctx, self.desc, self.ws, min_q_len=int(min(ns)))
         rec = StepRecord(self.step_idx, list(seqs), list(ns), lens.tolist(), len(self.ops),
                          out if self.keep_outputs else None)
         self.records.append(rec)

@@ -119,6 +119,8 @@ _SIGS = {
     "pkv_ragged_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32, _I32, _DESC]),
     "pkv_paged_attention_ragged": (_I32, [_P, _I32, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32,
                                           ctypes.c_float, _I32, _I32, _DESC, _P, _SZ, _P]),
+    "pkv_paged_attention_ragged_ex": (_I32, [_P, _I32, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32,
+                                             ctypes.c_float, _I32, _I32, _I32, _DESC, _P, _SZ, _P]),
     "pkv_bm_create": (_P, [_I32, _I32, _I32P]),
     "pkv_bm_destroy": (None, [_P]),
     "pkv_bm_clone": (_P, [_P]),
@@ -407,8 +409,12 @@ def ragged_workspace_bytes(num_seqs: int, num_tokens: int, num_q_heads: int, max
 
 def paged_attention_ragged(out, q, cu_seqlens_q, context_lens, k_cache, v_cache, block_tables, scale: float,
                            max_q_len: int, max_context_len: int, desc: CacheDesc, workspace=None,
-                           stream=None) -> None:
-    """Selective-batching attention over a flattened ragged batch (see include/pagedkv.h)."""
+                           stream=None, min_q_len: Optional[int] = None) -> None:
+    """Selective-batching attention over a flattened ragged batch (see include/pagedkv.h).
+
+    ``min_q_len`` (a host lower bound on every sequence's query rows) selects
+    pkv_paged_attention_ragged_ex; with 2 or more the decode-row launches are skipped.
+    """
     torch = _torch()
     T, hq, d = q.shape
     S = int(context_lens.shape[0])
@@ -416,11 +422,14 @@ def paged_attention_ragged(out, q, cu_seqlens_q, context_lens, k_cache, v_cache,
         raise ValueError("shape mismatch")
     ws = _dev(workspace, "workspace") if workspace is not None else None
     wsb = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    st = _lib.pkv_paged_attention_ragged(
-        _dev(out, "out"), _tdtype_code(out), _dev(q, "q"), _dev(cu_seqlens_q, "cu_seqlens_q", torch.int32),
-        _dev(context_lens, "context_lens", torch.int32), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
-        _dev(block_tables, "block_tables", torch.int32), int(block_tables.shape[1]), S, T, hq, float(scale),
-        int(max_q_len), int(max_context_len), ctypes.byref(desc), ws, wsb, _stream(stream))
+    head = (_dev(out, "out"), _tdtype_code(out), _dev(q, "q"), _dev(cu_seqlens_q, "cu_seqlens_q", torch.int32),
+            _dev(context_lens, "context_lens", torch.int32), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
+            _dev(block_tables, "block_tables", torch.int32), int(block_tables.shape[1]), S, T, hq, float(scale))
+    tail = (int(max_q_len), int(max_context_len), ctypes.byref(desc), ws, wsb, _stream(stream))
+    if min_q_len is None:
+        st = _lib.pkv_paged_attention_ragged(*head, *tail)
+    else:
+        st = _lib.pkv_paged_attention_ragged_ex(*head, int(min_q_len), *tail)
     _check(st, "paged_attention_ragged")
 
 

@@ -196,6 +196,23 @@ def test_ragged_validation():
     assert ragged(desc(), S=0) == 0 and ragged(desc(), T=0) == 0
 
 
+def ragged_ex(c, min_q, hq=4, S=2, T=5, max_q=3, max_ctx=100, mb=8):
+    p = ctypes.c_void_p(1)
+    return L.pkv_paged_attention_ragged_ex(p, c.dtype, p, p, p, p, p, p, mb, S, T, hq, 0.125, min_q, max_q, max_ctx,
+                                           ctypes.byref(c), NULL, 0, NULL)
+
+
+def test_ragged_ex_validation():
+    # the lower bound on q_len: at least 1, and above 1 no more than the upper bound
+    assert ragged_ex(desc(), 0) == -1
+    assert ragged_ex(desc(), -2) == -1
+    assert ragged_ex(desc(), 4, max_q=3) == -1
+    # the other checks come first, as in pkv_paged_attention_ragged
+    assert ragged_ex(desc(), 2, hq=6) == -3
+    assert ragged_ex(desc(), 2, max_q=6, T=5) == -1
+    assert ragged_ex(desc(), 0, S=0) == 0 and ragged_ex(desc(), 0, T=0) == 0  # nothing to do
+
+
 def test_single_hip_runtime_when_binding_is_imported_before_torch():
     # Loaded before torch, the library would bind to a second libamdhip64 that may not see
     # the device; the binding imports torch first so every HIP call shares torch's runtime.

@@ -83,6 +83,44 @@ def test_ragged_shapes(case):
     _check(w, out, ref)
 
 
+HINT_CASES = [
+    # (dtype, B, d, hq, hkv, q_lens, ctx, min_q_len)
+    ("bf16", 16, 128, 4, 4, [130, 2, 257], [130, 40, 300], 2),            # prefill only: no decode launches
+    ("f16", 32, 64, 8, 2, [65, 200, 17], [65, 450, 17], 17),              # GQA; the bound is the shortest chunk
+    # a bound that is wrong: the single rows run on the prefill kernel (one-row tiles)
+    ("bf16", 16, 128, 4, 4, [1, 130, 1, 2, 257, 1], [90, 130, 1, 40, 300, 700], 2),
+    ("f16", 8, 128, 8, 2, [1, 65, 0, 1], [33, 65, 5, 4000], 2),            # and an empty sequence
+]
+
+
+@pytest.mark.parametrize("case", HINT_CASES, ids=lambda c: f"{c[0]}-{len(c[5])}seqs-min{c[7]}")
+def test_ragged_min_q_len_hint(case):
+    """pkv_paged_attention_ragged_ex with a lower bound on q_len: the oracle's outputs within the
+    tolerance, and every row of a multi-row sequence bit-identical to the call without the bound
+    (the same prefill kernel computes it)."""
+    import torch
+    from paged_kv_cache_323_amd import native as pk
+    from paged_kv_cache_323_amd import runner as R
+    dt, B, d, hq, hkv, ql, ctx, min_q = case
+    seed = zlib.crc32(repr(case).encode()) % 10000
+    w = make_ragged_workload(seed, ql, ctx, hq, hkv, d, dt, B, name=f"ragged-hint-{dt}-B{B}-d{d}")
+    _announce(f"{w.name} q_lens={ql} ctx={ctx} min_q_len={min_q}")
+    _, ref = oracle.run_workload(w)
+    st = R.play_script(w, threads=16)
+    out, inp = R.attention(w, st, "f32")
+    cu = torch.from_numpy(w.cu_seqlens()).cuda()
+    hinted = torch.full_like(out, float("nan"))
+    pk.paged_attention_ragged(hinted, inp["q"], cu, inp["context_lens"], st.k_cache, st.v_cache, inp["block_tables"],
+                              w.scale, int(max(ql)), int(inp["lens_host"].max()), st.desc, inp["workspace"],
+                              min_q_len=min_q)
+    torch.cuda.synchronize()
+    err = _check(w, hinted, ref)
+    cuh = w.cu_seqlens()
+    multi = np.concatenate([np.arange(cuh[i], cuh[i + 1]) for i in range(len(ql)) if ql[i] >= 2])
+    assert torch.equal(hinted[multi].view(torch.int32), out[multi].view(torch.int32)), "prefill rows differ"
+    print(f"  max abs err {err:.3g}")
+
+
 @pytest.mark.parametrize("dt", ["bf16", "f16"])
 def test_ragged_sharp_scores(dt):
     """Scores scaled by 4.0 instead of 1/sqrt(d): along a prefill row the maximum keeps rising by
