@@ -363,13 +363,13 @@ def measured_gather_peak(loop):
     """Tile-gather probe (libpkv_probe.so) over the headline's own pools: every (block, kv head)
     tile of the current step's contexts, listed per (sequence, kv head) in table order, read from
     the K pool and then the V pool, with no arithmetic; the best of 16, 32, 64 and 128 tiles per
-    workgroup, median of 20 each. The attainable rate of the decode kernel's access pattern (None
-    for tiles smaller than 4 KiB)."""
+    workgroup, median of 20 each. The attainable rate of the decode kernel's access pattern (tiles
+    of 1 or 2 KiB, or a multiple of 4 KiB; None otherwise)."""
     import ctypes
     import torch
     w = loop.w
     tile_bytes = w.block_size * w.head_dim * {"f32": 4, "f16": 2, "bf16": 2}[w.dtype]
-    if tile_bytes % 4096:
+    if tile_bytes % 4096 and tile_bytes not in (1024, 2048):
         return None
     lib = ctypes.CDLL(os.path.join(ROOT, "paged_kv_cache_323_amd", "libpkv_probe.so"))
     lib.pkvprobe_gather_read.restype = ctypes.c_int32
@@ -503,11 +503,17 @@ def run_head_shapes(shapes=HEAD_SHAPES, K=20):
         _, kern_ms, merge_ms = _timed_windows(loop, K, 0.05, 3, 20, ev=True)
         kv = sum(decode_algorithmic_bytes(c, w, 2)[0] for c in loop.ctx_history) / len(loop.ctx_history)
         k_us, m_us = float(np.mean(kern_ms)) * 1e3, float(np.mean(merge_ms)) * 1e3
-        res[f"{hq}/{hkv}/d{d}"] = {"partition": loop.partition, "partition_launch_us": round(k_us, 1),
-                                   "merge_launch_us": round(m_us, 1),
-                                   "kv_gbs": round(kv / (k_us + m_us) / 1e3, 1),
-                                   "pct_hbm": round(100 * kv / (k_us + m_us) / 1e3 / HBM_PEAK_GBS, 1),
-                                   "kv_gbs_partition_launch": round(kv / k_us / 1e3, 1)}
+        row = {"partition": loop.partition, "partition_launch_us": round(k_us, 1),
+               "merge_launch_us": round(m_us, 1),
+               "kv_gbs": round(kv / (k_us + m_us) / 1e3, 1),
+               "pct_hbm": round(100 * kv / (k_us + m_us) / 1e3 / HBM_PEAK_GBS, 1),
+               "kv_gbs_partition_launch": round(kv / k_us / 1e3, 1)}
+        # the same (block, kv head) tiles gathered with no arithmetic: the access pattern's ceiling
+        gather = measured_gather_peak(loop)
+        if gather:
+            row["gather_ceiling_gbs"] = round(gather, 1)
+            row["partition_launch_frac_of_gather"] = round(kv / k_us / 1e3 / gather, 4)
+        res[f"{hq}/{hkv}/d{d}"] = row
         del loop
         torch.cuda.empty_cache()
     return res

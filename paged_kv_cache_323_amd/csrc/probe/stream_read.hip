@@ -48,7 +48,8 @@ extern "C" int32_t pkvprobe_stream_read(const void* buf, size_t bytes, uint32_t*
 //                                uint32_t* sink, void* stream)
 // pool_k, pool_v: device memory, 16-byte aligned; tiles: device list of tile indices (tile i is
 // bytes [i * tile_bytes, (i + 1) * tile_bytes) of each pool; the caller keeps every index inside
-// both pools); tile_bytes: a positive multiple of 4096; per_wg: list entries per workgroup.
+// both pools); tile_bytes: 1024, 2048 or a positive multiple of 4096; per_wg: list entries per
+// workgroup.
 // Returns 0, -1 on bad arguments, or the hipError_t of the launch.
 __global__ __launch_bounds__(256) void gather_read_kernel(const u32x4* __restrict__ pk, const u32x4* __restrict__ pv,
                                                           const uint32_t* __restrict__ tiles, int32_t n,
@@ -79,16 +80,60 @@ __global__ __launch_bounds__(256) void gather_read_kernel(const u32x4* __restric
   if (acc == 0x12345679u) sink[0] = acc;
 }
 
+// Tiles of 1 or 2 KiB (head_dim 64, or 8-token blocks, at 16 bits): every 256-thread step reads
+// 4096 / tile_bytes consecutive list entries, tile_bytes / 16 threads per tile; the last step of a
+// workgroup's range loads only the entries inside it.
+__global__ __launch_bounds__(256) void gather_read_small_kernel(const u32x4* __restrict__ pk,
+                                                                const u32x4* __restrict__ pv,
+                                                                const uint32_t* __restrict__ tiles, int32_t n,
+                                                                int32_t per_wg, int32_t lanes,
+                                                                uint32_t* __restrict__ sink) {
+  constexpr int U = 8;
+  const int per_step = 256 / lanes;
+  const long long t0 = (long long)blockIdx.x * per_wg;
+  const long long t1 = min((long long)n, t0 + per_wg);
+  const int sub = threadIdx.x / lanes, off = threadIdx.x % lanes;
+  uint32_t acc = 0;
+  for (int pass = 0; pass < 2; ++pass) {
+    const u32x4* pool = pass ? pv : pk;
+    long long t = t0;
+    for (; t + (long long)U * per_step <= t1; t += (long long)U * per_step) {
+      u32x4 v[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        v[u] = __builtin_nontemporal_load(pool + (size_t)tiles[t + u * per_step + sub] * lanes + off);
+#pragma unroll
+      for (int u = 0; u < U; ++u) acc ^= v[u][0] ^ v[u][1] ^ v[u][2] ^ v[u][3];
+    }
+    for (; t < t1; t += per_step) {
+      const long long e = t + sub;
+      if (e < t1) {
+        const u32x4 v = __builtin_nontemporal_load(pool + (size_t)tiles[e] * lanes + off);
+        acc ^= v[0] ^ v[1] ^ v[2] ^ v[3];
+      }
+    }
+  }
+  if (acc == 0x12345679u) sink[0] = acc;
+}
+
 extern "C" int32_t pkvprobe_gather_read(const void* pool_k, const void* pool_v, const uint32_t* tiles,
                                         int32_t num_tiles, int32_t tile_bytes, int32_t per_wg, uint32_t* sink,
                                         void* stream) {
   if (!pool_k || !pool_v || !tiles || !sink || (uintptr_t)pool_k % 16 || (uintptr_t)pool_v % 16) return -1;
-  if (num_tiles < 1 || tile_bytes < 4096 || tile_bytes % 4096 || per_wg < 1) return -1;
+  const bool small = tile_bytes == 1024 || tile_bytes == 2048;
+  if (num_tiles < 1 || per_wg < 1 || (!small && (tile_bytes < 4096 || tile_bytes % 4096))) return -1;
   const long long grid = ((long long)num_tiles + per_wg - 1) / per_wg;
   if (grid > 0x7fffffff) return -1;
   const u32x4* pk = static_cast<const u32x4*>(pool_k);
   const u32x4* pv = static_cast<const u32x4*>(pool_v);
-  int32_t n = num_tiles, chunks = tile_bytes / 4096;
+  int32_t n = num_tiles;
+  if (small) {
+    int32_t lanes = tile_bytes / 16;
+    void* args[] = {&pk, &pv, &tiles, &n, &per_wg, &lanes, &sink};
+    return (int32_t)hipLaunchKernel(reinterpret_cast<const void*>(&gather_read_small_kernel), dim3((unsigned)grid),
+                                    dim3(256), args, 0, (hipStream_t)stream);
+  }
+  int32_t chunks = tile_bytes / 4096;
   void* args[] = {&pk, &pv, &tiles, &n, &per_wg, &chunks, &sink};
   return (int32_t)hipLaunchKernel(reinterpret_cast<const void*>(&gather_read_kernel), dim3((unsigned)grid), dim3(256),
                                   args, 0, (hipStream_t)stream);

@@ -25,7 +25,7 @@ def _lib():
     return lib
 
 
-@pytest.mark.parametrize("tile_bytes", [4096, 8192])
+@pytest.mark.parametrize("tile_bytes", [1024, 2048, 4096, 8192])
 def test_gather_probe_reads_listed_tiles(tile_bytes):
     import torch
     print(f"[case] gather probe tile_bytes={tile_bytes}", flush=True)
@@ -36,11 +36,15 @@ def test_gather_probe_reads_listed_tiles(tile_bytes):
     pv = torch.zeros_like(pk)
     pk[marked * words] = MARK  # thread 0's first chunk of tile `marked` in the K pool
     stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
-    for listed, expect in (([5, 9, marked], MARK), ([5, 9, 11], 0), ([marked, 2, 3, 4], MARK)):
+    # (list, entries per workgroup, expected sink): a range's last entry, a list without the tile,
+    # its first entry, and a list split over workgroups with the tile in the last one's short tail
+    cases = (([5, 9, marked], 3, MARK), ([5, 9, 11], 3, 0), ([marked, 2, 3, 4], 4, MARK),
+             (list(range(20)) + [marked], 4, MARK), (list(range(21)), 4, 0))
+    for listed, per_wg, expect in cases:
         sink = torch.zeros(1, dtype=torch.int32, device="cuda")
         tiles = torch.tensor(listed, dtype=torch.int32, device="cuda")
         st = lib.pkvprobe_gather_read(pk.data_ptr(), pv.data_ptr(), tiles.data_ptr(), len(listed), tile_bytes,
-                                      len(listed), sink.data_ptr(), stream)
+                                      per_wg, sink.data_ptr(), stream)
         assert st == 0
         torch.cuda.synchronize()
         assert int(sink.item()) == expect, (listed, int(sink.item()))
@@ -54,7 +58,9 @@ def test_gather_probe_reads_listed_tiles(tile_bytes):
     torch.cuda.synchronize()
     assert int(sink.item()) == MARK
     # bad arguments are rejected before any launch
-    assert lib.pkvprobe_gather_read(pk.data_ptr(), pv.data_ptr(), tiles.data_ptr(), 1, 2048, 1, sink.data_ptr(),
+    assert lib.pkvprobe_gather_read(pk.data_ptr(), pv.data_ptr(), tiles.data_ptr(), 1, 3072, 1, sink.data_ptr(),
+                                    stream) == -1
+    assert lib.pkvprobe_gather_read(pk.data_ptr(), pv.data_ptr(), tiles.data_ptr(), 1, 512, 1, sink.data_ptr(),
                                     stream) == -1
     assert lib.pkvprobe_gather_read(pk.data_ptr(), pv.data_ptr(), tiles.data_ptr(), 0, 4096, 1, sink.data_ptr(),
                                     stream) == -1
