@@ -113,6 +113,9 @@ constexpr int kPfTab = 1024;  // block-table entries cached in LDS at a time
 #ifndef PF_ACC_ORDER
 #define PF_ACC_ORDER 1
 #endif
+#ifndef PF_XCD
+#define PF_XCD 1
+#endif
 constexpr int kPfLookahead = PF_LOOKAHEAD;  // MFMA operand reads issued this many steps ahead
 
 
@@ -143,9 +146,19 @@ __global__ __launch_bounds__(kPfThreads, 2) void ragged_prefill_kernel(PrefillAr
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar branches on it
-  const int h = blockIdx.x;
+  // Workgroups go to the eight XCDs (each with its own L2) in turn, so with a multiple of 8 heads
+  // blockIdx.x mod 8 picks the XCD. With PF_XCD and several query heads per kv head (kv heads a
+  // multiple of 8), blockIdx.x = 8t + r serves a query head of kv head r + 8 (t / g): all query
+  // heads of a kv head, which read the same keys and values, share one XCD's L2.
+  const int gq = a.hq / a.hkv;
+  int hx = blockIdx.x;
+  if (PF_XCD && gq > 1 && a.hkv % 8 == 0) {
+    const int r = hx & 7, t = hx >> 3;
+    hx = (r + 8 * (t / gq)) * gq + t % gq;
+  }
+  const int h = __builtin_amdgcn_readfirstlane(hx);
   // uniform (the integer division would otherwise leave it, and what depends on it, in VGPRs)
-  const int kvh = __builtin_amdgcn_readfirstlane(h / (a.hq / a.hkv));
+  const int kvh = __builtin_amdgcn_readfirstlane(h / gq);
   // ---- which (sequence, row tile) this workgroup owns ----------------------------------------
   // Slot y is the y-th row tile counted back from the last tile of the last sequence: the last
   // row tiles of the last sequences (the longest causal rows, hence the most key tiles) are
