@@ -460,8 +460,7 @@ __global__ __launch_bounds__(kPfThreads, 2) void ragged_prefill_kernel(PrefillAr
         mx = max_rows4(mx);
         // Lazy rescaling: the reference max m_run only moves when some row's tile max exceeds it by
         // more than 2^8 in probability terms; until then probabilities may reach 2^8, which fp32
-        // sums and the 16-bit split represent as well as values below 1. A row with no visible key
-        // yet keeps m_run = -inf (its probabilities are exactly 0).
+        // sums and the 16-bit split represent as well as values below 1.
         // The wave's first tile sets the reference max directly (the accumulators are still zero;
         // every row sees key 0, so the max is finite).
         const bool grow = mx > m_run[nt] + lazy_thr;
@@ -469,13 +468,15 @@ __global__ __launch_bounds__(kPfThreads, 2) void ragged_prefill_kernel(PrefillAr
           m_run[nt] = mx;
         } else if (__builtin_amdgcn_read_exec() & __ballot(grow)) {  // wave-uniform
           const float m_new = fmaxf(m_run[nt], mx);
-          const float alpha = m_run[nt] == -INFINITY ? 0.f : fast_exp2((m_run[nt] - m_new) * a.scale_log2);
+          const float alpha = fast_exp2((m_run[nt] - m_new) * a.scale_log2);
           m_run[nt] = m_new;
           lacc[nt] *= alpha;
 #pragma unroll
           for (int dt = 0; dt < DT16; ++dt) oacc[dt][nt] *= alpha;
         }
-        const float off = -(m_run[nt] == -INFINITY ? 0.f : m_run[nt]) * a.scale_log2;
+        // From the wave's first computed tile on, m_run is finite (every row, padding rows included,
+        // sees key 0), so the offset and the rescale factor need no -inf case.
+        const float off = -m_run[nt] * a.scale_log2;
         float p[4][4];
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt)
