@@ -150,8 +150,10 @@ class DecodeLoop:
             return
         while self.marks and self.marks[0][0] < j:
             self.marks.popleft()
-        # markers come every MARK_EVERY <= RING steps, so one at or after step j exists
-        self.marks[0][1].synchronize()
+        if self.marks:  # markers come every MARK_EVERY <= RING steps, so one at or after step j exists
+            self.marks[0][1].synchronize()
+        else:
+            self.torch.cuda.synchronize()
 
     def step(self, ev=None):
         torch, pk, w = self.torch, self.pk, self.w
