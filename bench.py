@@ -551,6 +551,27 @@ def run_head_shapes(shapes=HEAD_SHAPES, K=20):
     return res
 
 
+def profile_heads(shape: str, K=20):
+    """One decode head shape ("QH/KVH/D") at the GQA configuration's lengths (bf16, B 16, automatic
+    partition): two event-timed K-step windows from a saved state after 50 repeats, for counter
+    runs; prints the partition launch's mean event time."""
+    import torch
+    from workloads import make_decode_workload, make_workload
+    hq, hkv, d = (int(x) for x in shape.split("/"))
+    ctx = list(make_workload("gqa", "full").context_lens)
+    w = make_decode_workload(3, ctx, hq, hkv, d, "bf16", 16, name=f"heads-{hq}-{hkv}-d{d}")
+    loop = DecodeLoop(w, 5 + K + 5)
+    for _ in range(5):
+        loop.step()
+    torch.cuda.synchronize()
+    loop.snapshot = loop.st.bm.clone()
+    loop.repeat_attention(50)
+    torch.cuda.synchronize()
+    _, kern_ms, _ = _timed_windows(loop, K, 0.0, 2, 2, ev=True)
+    print(json.dumps({"shape": shape, "partition": loop.partition,
+                      "partition_launch_us": round(float(np.mean(kern_ms)) * 1e3, 1)}), flush=True)
+
+
 def run_shared_prefix():
     """Copy-on-write copies at the first generated token and decode over shared blocks."""
     import torch
@@ -1133,6 +1154,9 @@ def main():
                     help="GQA decode and cache write with the library PAGEDKV_LIB names, pools in this layout")
     ap.add_argument("--profile-swap", action="store_true",
                     help="only run swap-out then swap-in of 4096 blocks (counter target)")
+    ap.add_argument("--profile-heads", default="",
+                    help="only run one decode head shape QH/KVH/D (GQA lengths, bf16, B 16): two "
+                         "event-timed 20-step windows (counter target)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the path has no "
@@ -1157,6 +1181,9 @@ def main():
         return
     if args.profile_prefill:
         profile_prefill(args.prefill_dtype, args.prefill_prompts)
+        return
+    if args.profile_heads:
+        profile_heads(args.profile_heads)
         return
     h = run_headline(args)
     w = h["w"]
