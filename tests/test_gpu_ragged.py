@@ -90,6 +90,10 @@ HINT_CASES = [
     # a bound that is wrong: the single rows run on the prefill kernel (one-row tiles)
     ("bf16", 16, 128, 4, 4, [1, 130, 1, 2, 257, 1], [90, 130, 1, 40, 300, 700], 2),
     ("f16", 8, 128, 8, 2, [1, 65, 0, 1], [33, 65, 5, 4000], 2),            # and an empty sequence
+    ("bf16", 16, 64, 4, 4, [40, 40, 40], [40, 900, 3000], 40),            # the bound equals max_q_len
+    # causal-rows mode (an f32 pool; 16-bit chunks of at most g rows): the bound has no effect
+    ("f32", 16, 128, 4, 4, [1, 130, 2, 257], [90, 130, 40, 300], 2),
+    ("bf16", 16, 128, 32, 8, [2, 4, 3], [1500, 40, 3], 2),
 ]
 
 
@@ -118,6 +122,8 @@ def test_ragged_min_q_len_hint(case):
     cuh = w.cu_seqlens()
     multi = np.concatenate([np.arange(cuh[i], cuh[i + 1]) for i in range(len(ql)) if ql[i] >= 2])
     assert torch.equal(hinted[multi].view(torch.int32), out[multi].view(torch.int32)), "prefill rows differ"
+    if dt == "f32" or max(ql) <= hq // hkv:  # causal-rows mode: every row, bit for bit
+        assert torch.equal(hinted.view(torch.int32), out.view(torch.int32)), "rows mode must ignore the bound"
     print(f"  max abs err {err:.3g}")
 
 
