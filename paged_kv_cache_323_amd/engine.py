@@ -290,17 +290,17 @@ class Engine:
         return self._stage_host[i].numpy()[:n]
 
     def _upload(self, host: np.ndarray) -> torch.Tensor:
-        """Copy this step's staging contents to the device on the copy stream; the launch stream
-        waits for the copy."""
+        """Copy this step's staging contents to the device on the copy stream and wait for it on
+        the host (the copy waits on nothing on the device), so the launch stream's queue holds no
+        cross-stream wait between the previous step's kernels and this step's."""
         i = self.step_idx % self.STAGE_RING
         n = len(host)
         dev = self._stage_dev[i][:n]
-        main = torch.cuda.current_stream(self.device)
         with torch.cuda.stream(self._copy_stream):
             dev.copy_(self._stage_host[i][:n], non_blocking=True)
             ev = torch.cuda.Event()
             ev.record(self._copy_stream)
-        main.wait_event(ev)
+        ev.synchronize()
         return dev
 
     # ---- one model step -------------------------------------------------------------------------
