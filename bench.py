@@ -164,7 +164,9 @@ class DecodeLoop:
         slots, pairs = self.st.bm.append(self.seqs, np.ones(self.S, dtype=np.int32))
         hn[: self.S] = slots
         tab = hn[2 * self.S: self.items_off].reshape(self.S, self.max_blocks)
-        self.st.bm.block_tables(self.seqs, self.max_blocks, out=tab, ctx_out=hn[self.S: 2 * self.S])
+        # only the live entries of each row: the kernels read no further, and the rest of the
+        # staging row (an earlier step's shorter table, or never written) is not padding to redo
+        self.st.bm.block_tables(self.seqs, self.max_blocks, out=tab, ctx_out=hn[self.S: 2 * self.S], pad=False)
         if self.work_list:
             self.n_items[buf] = pk.decode_items_into(hn[self.S: 2 * self.S], self.partition,
                                                      hn[self.items_off: self.items_off + self.max_items])

@@ -471,6 +471,13 @@ int32_t pkv_bm_append(pkv_bm* bm, const int64_t* seq_ids, const int32_t* n_token
 int32_t pkv_bm_block_tables(const pkv_bm* bm, const int64_t* seq_ids, int32_t n, int32_t max_blocks,
                             int32_t* tables_out, int32_t* ctx_out);
 
+/* As pkv_bm_block_tables, with pad == 0 writing only each row's first ceil(len / B) entries (the
+ * ones a kernel reads for that context) and leaving the rest of the row as it was: a serving loop
+ * that refills the same staging rows every step saves rewriting the padding. pad != 0 is
+ * pkv_bm_block_tables. Errors and validation are the same (nothing is written on an error). */
+int32_t pkv_bm_block_tables_ex(const pkv_bm* bm, const int64_t* seq_ids, int32_t n, int32_t max_blocks,
+                               int32_t* tables_out, int32_t* ctx_out, int32_t pad);
+
 /* Table of one sequence: writes up to cap entries, returns its length in blocks (or error). */
 int32_t pkv_bm_seq_table(const pkv_bm* bm, int64_t seq_id, int32_t* table_out, int32_t cap);
 int32_t pkv_bm_context_len(const pkv_bm* bm, int64_t seq_id);

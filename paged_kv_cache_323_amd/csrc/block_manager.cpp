@@ -282,6 +282,11 @@ int32_t pkv_bm_append(pkv_bm* bm, const int64_t* ids, const int32_t* n, int32_t 
 
 int32_t pkv_bm_block_tables(const pkv_bm* bm, const int64_t* ids, int32_t count, int32_t max_blocks,
                             int32_t* tables_out, int32_t* ctx_out) {
+  return pkv_bm_block_tables_ex(bm, ids, count, max_blocks, tables_out, ctx_out, 1);
+}
+
+int32_t pkv_bm_block_tables_ex(const pkv_bm* bm, const int64_t* ids, int32_t count, int32_t max_blocks,
+                               int32_t* tables_out, int32_t* ctx_out, int32_t pad) {
   if (!bm || count < 0 || max_blocks < 0 || (count > 0 && (!ids || !tables_out))) return PKV_EINVAL;
   for (int32_t i = 0; i < count; ++i) {
     auto it = bm->seqs.find(ids[i]);
@@ -294,7 +299,7 @@ int32_t pkv_bm_block_tables(const pkv_bm* bm, const int64_t* ids, int32_t count,
     int32_t* row = tables_out + (int64_t)i * max_blocks;
     const int32_t nt = (int32_t)sq.table.size();
     std::copy(sq.table.begin(), sq.table.end(), row);
-    std::fill(row + nt, row + max_blocks, -1);
+    if (pad) std::fill(row + nt, row + max_blocks, -1);
     if (ctx_out) ctx_out[i] = sq.len;
   }
   return PKV_OK;

@@ -130,6 +130,7 @@ _SIGS = {
     "pkv_bm_blocks_needed": (_I64, [_P, _I64P, _I32P, _I32]),
     "pkv_bm_append": (_I32, [_P, _I64P, _I32P, _I32, _I32P, _I32P, _I32, _I32P]),
     "pkv_bm_block_tables": (_I32, [_P, _I64P, _I32, _I32, _I32P, _I32P]),
+    "pkv_bm_block_tables_ex": (_I32, [_P, _I64P, _I32, _I32, _I32P, _I32P, _I32]),
     "pkv_bm_seq_table": (_I32, [_P, _I64, _I32P, _I32]),
     "pkv_bm_context_len": (_I32, [_P, _I64]),
     "pkv_bm_refcount": (_I32, [_P, _I32]),
@@ -507,12 +508,14 @@ class BlockManager:
         return slots[: int(n.sum())], pairs[: np_out.value]
 
     def block_tables(self, seqs, max_blocks: int, out: Optional[np.ndarray] = None,
-                     ctx_out: Optional[np.ndarray] = None):
+                     ctx_out: Optional[np.ndarray] = None, pad: bool = True):
+        """Tables [n][max_blocks] and lengths of resident sequences; with ``pad=False`` only each
+        row's live entries are written (into ``out``) and the rest of the row is left as it was."""
         ids = np.ascontiguousarray(seqs, dtype=np.int64)
         tab = out if out is not None else np.empty((len(ids), max_blocks), dtype=np.int32)
         ctx = ctx_out if ctx_out is not None else np.empty(len(ids), dtype=np.int32)
-        _check(_lib.pkv_bm_block_tables(self._h, _i64p(ids), len(ids), int(max_blocks), _i32p(tab), _i32p(ctx)),
-               "bm_block_tables")
+        _check(_lib.pkv_bm_block_tables_ex(self._h, _i64p(ids), len(ids), int(max_blocks), _i32p(tab), _i32p(ctx),
+                                           1 if pad else 0), "bm_block_tables")
         return tab, ctx
 
     def block_table(self, seq: int):

@@ -275,3 +275,29 @@ def test_native_clone_is_independent():
     del bm                                                # destroying one leaves the other usable
     c.append([0], [1])
     assert c.context_len(0) == 7
+
+
+def test_native_block_tables_without_padding():
+    """pkv_bm_block_tables_ex with pad = 0 writes each row's live entries (the sequence's table,
+    ceil(len / B) blocks) exactly as the padded export does and leaves the rest of the row as it
+    was; its errors are the padded export's, with nothing written."""
+    bm = pk.BlockManager(64, 4, np.random.default_rng(5).permutation(64).astype(np.int32))
+    for s in range(3):
+        bm.add_seq(s)
+    bm.append([0, 1, 2], [5, 12, 1])
+    padded, ctx = bm.block_tables([0, 1, 2], 6)
+    assert ctx.tolist() == [5, 12, 1]
+    sentinel = np.int32(-12345)
+    out = np.full((3, 6), sentinel, dtype=np.int32)
+    ctx2 = np.zeros(3, dtype=np.int32)
+    bm.block_tables([0, 1, 2], 6, out=out, ctx_out=ctx2, pad=False)
+    assert ctx2.tolist() == ctx.tolist()
+    for r, n in enumerate((2, 3, 1)):                     # ceil(5/4), ceil(12/4), ceil(1/4)
+        assert out[r, :n].tolist() == padded[r, :n].tolist() == bm.block_table(r)
+        assert (out[r, n:] == sentinel).all() and (padded[r, n:] == -1).all()
+    # a table longer than max_blocks is rejected before anything is written
+    out[:] = sentinel
+    with pytest.raises(pk.PagedKVError):
+        bm.block_tables([0, 1, 2], 2, out=out[:, :2].copy(), pad=False)
+    with pytest.raises(pk.PagedKVError):
+        bm.block_tables([0, 7], 6, out=out[:2], pad=False)  # unknown sequence
