@@ -494,6 +494,9 @@ def run_decode_config(name, block_size=None, steps=30, warmup=5, partition=0):
     util = kv_utilisation(w, loop.st.bm, MAX_LEN[name])
     for _ in range(warmup):
         loop.step()
+    # clocks up before the timed steps, as in the headline: the last step's attention repeated
+    # (the state does not advance)
+    loop.repeat_attention(200)
     torch.cuda.synchronize()
     loop.ctx_history.clear()
     evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(steps)]
@@ -511,6 +514,11 @@ def run_decode_config(name, block_size=None, steps=30, warmup=5, partition=0):
            "kv_gbs_partition_launch": round(kv / kern / 1e9, 1),
            "pct_hbm_partition_launch": round(100 * kv / kern / 1e9 / HBM_PEAK_GBS, 1),
            "kv_memory_utilisation": util}
+    # the same (block, kv head) tiles gathered with no arithmetic: this block size's pattern ceiling
+    gather = measured_gather_peak(loop)
+    if gather:
+        res["gather_ceiling_gbs"] = round(gather, 1)
+        res["partition_launch_frac_of_gather"] = round(kv / kern / 1e9 / gather, 4)
     del loop
     torch.cuda.empty_cache()
     return res
