@@ -299,6 +299,7 @@ def run_headline(args):
         achieved=achieved, alg_per_launch=alg_per_launch, kv_per_step=kv_per_step,
         kern_kv_gbs=kv_per_step / kern_avg_s / 1e9, partition=loop.partition,
         mean_ctx=float(np.mean([c.mean() for c in ctx_hist])), util=util,
+        split_seqs=split_seqs(ctx_hist, loop.partition),
         merge_avg_us=float(np.mean(merge_ms)) * 1e3, kern_launches=len(kern_ms),
         windows={"count": len(win_s), "steps_each": K, "total_s": round(sum(win_s), 4),
                  "step_us_median": round(step_s * 1e6, 2),
@@ -480,9 +481,15 @@ def kv_utilisation(w, bm, max_len, stored_tokens=None):
     every sequence reserves max_len slots and shares nothing."""
     used = w.num_blocks - bm.num_free()
     tokens = int(sum(w.context_lens)) if stored_tokens is None else int(stored_tokens)
+    # the empty slots of each sequence's last block: for lengths spread evenly over a block's
+    # residues their mean is (B - 1) / 2 slots
+    lens = np.asarray(w.context_lens, dtype=np.int64)
+    waste = -(-lens // w.block_size) * w.block_size - lens
     return {"paged": round(tokens / (used * w.block_size), 4),
             "max_len_prealloc": round(int(sum(w.context_lens)) / (len(w.context_lens) * max_len), 4),
-            "max_len": max_len, "blocks_in_use": int(used)}
+            "max_len": max_len, "blocks_in_use": int(used),
+            "last_block_empty_slots_mean": round(float(waste.mean()), 2),
+            "last_block_empty_slots_even_residues": (w.block_size - 1) / 2}
 
 
 def run_decode_config(name, block_size=None, steps=30, warmup=5, partition=0):
@@ -508,7 +515,8 @@ def run_decode_config(name, block_size=None, steps=30, warmup=5, partition=0):
     kern = float(np.mean([a.elapsed_time(b) for a, b, _ in evs])) * 1e-3
     merge = float(np.mean([b.elapsed_time(c) for _, b, c in evs])) * 1e-3
     kv = float(np.mean([decode_algorithmic_bytes(c, w, 2)[0] for c in loop.ctx_history]))
-    res = {"workload": w.name, "seqs": len(w.query_seqs), "partition": loop.partition, "step_us": round(el * 1e6, 1),
+    res = {"workload": w.name, "seqs": len(w.query_seqs), "partition": loop.partition,
+           "split_seqs": split_seqs(loop.ctx_history, loop.partition), "step_us": round(el * 1e6, 1),
            "seqs_per_s": round(len(w.query_seqs) / el, 1), "kv_gbs_step": round(kv / el / 1e9, 1),
            "partition_launch_us": round(kern * 1e6, 1), "merge_launch_us": round(merge * 1e6, 1),
            "kv_gbs_partition_launch": round(kv / kern / 1e9, 1),
@@ -522,6 +530,12 @@ def run_decode_config(name, block_size=None, steps=30, warmup=5, partition=0):
     del loop
     torch.cuda.empty_cache()
     return res
+
+
+def split_seqs(ctx_history, partition):
+    """Mean count per step of sequences whose context spans more than one partition (the ones the
+    merge launch combines; the others take one partition's result as it stands)."""
+    return round(float(np.mean([int((np.asarray(c) > partition).sum()) for c in ctx_history])), 1)
 
 
 HEAD_SHAPES = ((64, 8, 128), (64, 8, 64), (32, 8, 64), (16, 8, 128), (32, 32, 128))
@@ -641,6 +655,53 @@ def run_shared_prefix():
     med, _ = _time_events(lambda: pk.copy_blocks(kc, vc, seq, desc), reps=20)
     res["copy_4096_sequential_pairs_gbs"] = round(2 * 2 * 4096 * blk_bytes / med / 1e3, 1)
     del kc, vc
+    torch.cuda.empty_cache()
+    return res
+
+
+def run_tiny():
+    """The tiny configuration (4 sequences of 5-100 tokens, 4 heads, head_dim 64, f32): a launch-
+    latency case. The step's fused cache write and decode, the decode alone, and the 4-token cache
+    write alone, each timed with HIP events (10 warm-ups, median of 50) with the caches flushed
+    before every call: the flush keeps the stream busy, so each call's launch is queued before its
+    start event fires. The fused step is timed once more without the flush, so the host paces
+    every call and the event pair includes the call's host overhead."""
+    import torch
+    from paged_kv_cache_323_amd import native as pk
+    from paged_kv_cache_323_amd import runner as R
+    from workloads import make_workload
+    w = make_workload("tiny", "full")
+    st = R.play_script(w)
+    op = w.ops[-1]  # the step: one new token per sequence, written before the decode reads it
+    if list(op.seqs) != list(w.query_seqs) or any(n != 1 for n in op.n_tokens):
+        raise RuntimeError("the tiny script's last append is not one token per query sequence")
+    k, v = w.append_values(op)
+    kd = R.to_device(k, w.dtype).contiguous()
+    vd = R.to_device(v, w.dtype).contiguous()
+    slots = torch.from_numpy(np.ascontiguousarray(st.slots_per_append[-1])).cuda()
+    out, inp = R.attention(w, st, w.dtype)
+    bt, cl, q, ws = inp["block_tables"], inp["context_lens"], inp["q"], inp["workspace"]
+    mx = int(inp["lens_host"].max())
+
+    def step():
+        pk.paged_attention_decode_append(out, q, kd, vd, slots, st.k_cache, st.v_cache, bt, cl, w.scale, mx,
+                                         st.desc, ws)
+
+    res = {"workload": w.name, "seqs": len(w.query_seqs), "context_lens": [int(x) for x in inp["lens_host"]],
+           "timing": "HIP events, 10 warm-ups, median of 50; caches flushed before each timed call"}
+    res["step_us"], _ = _time_events(step, reps=50, warm=10, evict=True)
+    res["step_us_host_paced"], _ = _time_events(step, reps=50, warm=10)
+    res["decode_us"], _ = _time_events(
+        lambda: pk.paged_attention_decode(out, q, st.k_cache, st.v_cache, bt, cl, w.scale, mx, st.desc, ws),
+        reps=50, warm=10, evict=True)
+    res["kv_cache_write_us"], _ = _time_events(
+        lambda: pk.kv_cache_write(kd, vd, st.k_cache, st.v_cache, slots, st.desc), reps=50, warm=10, evict=True)
+    _, empty = _time_events(lambda: None, reps=50, warm=10)
+    res["event_pair_us"] = round(empty, 2)  # an event pair around no launch
+    for key in ("step_us", "step_us_host_paced", "decode_us", "kv_cache_write_us"):
+        res[key] = round(res[key], 2)
+    res["kv_memory_utilisation"] = kv_utilisation(w, st.bm, max(w.context_lens))
+    del st
     torch.cuda.empty_cache()
     return res
 
@@ -1129,6 +1190,10 @@ def row_rooflines(result, extra, read_peak, copy_peak, copy_traffic=None):
         if "copy_blocks" in copy_traffic:
             rows["a3_copy_blocks_4096_pairs"]["traffic_over_algorithmic"] = copy_traffic["copy_blocks"]
         rows["a3_copy_blocks_48_pairs"] = {"us": sp["copy_us"], "bound": "launch latency (24 MiB)"}
+    tn = extra.get("tiny", {})
+    if "step_us" in tn:
+        rows["a4_a5_tiny_step"] = {"us": tn["step_us"], "decode_us": tn["decode_us"],
+                                   "bound": "launch latency (315 KB of KV)"}
     sw = extra.get("swap", {})
     if "swap_out_gbs" in sw:
         rows["swap"] = {"out_gbs": sw["swap_out_gbs"], "in_gbs": sw["swap_in_gbs"], "link_gbs": HOST_LINK_GBS,
@@ -1221,6 +1286,7 @@ def main():
                    "seqs": len(w.query_seqs), "block_size": w.block_size,
                    "sum_ctx_first_step": int(sum(w.context_lens)) + len(w.context_lens),
                    "partition_tokens": h["partition"], "mean_ctx_timed": round(h["mean_ctx"], 1),
+                   "split_seqs": h["split_seqs"],
                    "partition_launch": "dense grid" if args.dense_grid else "host-built work list"},
         "seqs_per_s": round(h["seqs_per_s"], 1),
         "kv_memory_utilisation": h["util"],
@@ -1265,6 +1331,9 @@ def main():
     if not args.no_extra:
         extra = {}
         for key, fn in (("head_shapes", run_head_shapes),
+                        ("tiny", run_tiny),
+                        ("gqa_partition_1024", lambda: run_decode_config("gqa", partition=1024)),
+                        ("gqa_partition_512", lambda: run_decode_config("gqa", partition=512)),
                         ("gqa_B32", lambda: run_decode_config("gqa", 32)),
                         ("gqa_B8", lambda: run_decode_config("gqa", 8)),
                         ("llama7b", lambda: run_decode_config("llama7b")),

@@ -51,3 +51,39 @@ def test_headline_kv_bytes_per_token():
     w = make_workload("gqa", "full")
     assert (w.num_kv_heads, w.head_dim, w.dtype) == (8, 128, "bf16")
     assert w.kv_bytes_per_token() == 4096
+
+
+class _Pool:
+    def __init__(self, free):
+        self.free = free
+
+    def num_free(self):
+        return self.free
+
+
+class _W:
+    def __init__(self, lens, block_size, num_blocks):
+        self.context_lens, self.block_size, self.num_blocks = lens, block_size, num_blocks
+
+
+@pytest.mark.parametrize("B", [8, 16, 32])
+def test_last_block_waste_over_a_full_period(B):
+    # lengths 1..kB cover every residue of B k times: the mean of the empty slots is (B - 1) / 2
+    lens = list(range(1, 3 * B + 1))
+    used = sum(-(-L // B) for L in lens)
+    u = bench.kv_utilisation(_W(lens, B, used + 5), _Pool(5), 3 * B)
+    assert u["last_block_empty_slots_mean"] == (B - 1) / 2 == u["last_block_empty_slots_even_residues"]
+    assert u["blocks_in_use"] == used
+    assert u["paged"] == round(sum(lens) / (used * B), 4)
+
+
+def test_last_block_waste_by_hand():
+    u = bench.kv_utilisation(_W([1, 16, 17, 100], 16, 20), _Pool(9), 128)
+    assert u["last_block_empty_slots_mean"] == (15 + 0 + 15 + 12) / 4
+    assert u["blocks_in_use"] == 11 and u["max_len_prealloc"] == round(134 / 512, 4)
+
+
+def test_split_seqs_counts_contexts_beyond_one_partition():
+    hist = [np.array([100, 2048, 2049, 9000]), np.array([2049, 1, 5000, 2048])]
+    assert bench.split_seqs(hist, 2048) == 2.0
+    assert bench.split_seqs(hist, 1024) == 3.0
