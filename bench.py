@@ -846,6 +846,11 @@ def run_mixed():
                            evict=True)
     res["kv_cache_write_cold_us"] = round(w_us, 1)
     res["kv_cache_write_cold_gbs"] = round(write_bytes / w_us / 1e3, 1)
+    # The same rows into consecutive slots of the same pool (blocks 0, 1, 2, ... in order): the write
+    # without the scatter of a paged pool's blocks. It overwrites those blocks, so it comes last.
+    seq_slots = torch.arange(int(slots.numel()), dtype=torch.int32, device="cuda")
+    w_us, _ = _time_events(lambda: pk.kv_cache_write(kd, vd, st.k_cache, st.v_cache, seq_slots, st.desc), reps=20)
+    res["kv_cache_write_sequential_slots_gbs"] = round(write_bytes / w_us / 1e3, 1)
     del st
     torch.cuda.empty_cache()
     return res
@@ -1166,6 +1171,11 @@ def row_rooflines(result, extra, read_peak, copy_peak, copy_traffic=None):
         if "kv_cache_write_cold_gbs" in m:
             rows["a4_kv_cache_write"]["cold_caches_gbs"] = m["kv_cache_write_cold_gbs"]
             rows["a4_kv_cache_write"]["cold_frac_of_measured"] = round(m["kv_cache_write_cold_gbs"] / copy_peak, 4)
+        if "kv_cache_write_sequential_slots_gbs" in m:
+            # the same write into consecutive slots: the kernel without the pool's scatter
+            rows["a4_kv_cache_write"]["sequential_slots_gbs"] = m["kv_cache_write_sequential_slots_gbs"]
+            rows["a4_kv_cache_write"]["sequential_frac_of_measured"] = round(
+                m["kv_cache_write_sequential_slots_gbs"] / copy_peak, 4)
         if "kv_cache_write" in copy_traffic:
             rows["a4_kv_cache_write"]["traffic_over_algorithmic"] = copy_traffic["kv_cache_write"]
     if "prefill_tflops" in m:
