@@ -761,6 +761,9 @@ def run_engine(n_requests=512, max_steps=400):
            "finished_per_s": round((st.finished - s0.finished) / el, 1),
            "decode_tokens_per_s": round((st.decode_tokens - s0.decode_tokens) / el, 1),
            "prefill_tokens_per_s": round((st.prefill_tokens - s0.prefill_tokens) / el, 1),
+           # KV the decode rows read (every cached token of theirs, K and V), over the whole step
+           "decode_kv_gbs_step": round((st.decode_kv_tokens - s0.decode_kv_tokens) * 2 * eng.hkv * eng.d
+                                       * 2 / el / 1e9, 1),
            "preemptions": st.preemptions, "resumptions": st.resumptions, "finished_total": st.finished}
     del eng
     torch.cuda.empty_cache()

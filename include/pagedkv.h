@@ -391,6 +391,45 @@ int32_t pkv_paged_attention_ragged_ex(void* out, int32_t out_dtype, const void* 
                                       void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * paged_attention_ragged_items — pkv_paged_attention_ragged_ex with the decode rows run from a
+ *   work list, for callers that know the context lengths on the host (a serving loop's block
+ *   manager does; the selective-batching step of 「Paged Attention&Orca Paper笔记与解读」
+ *   §Orca的Solution). The decode-row launch then has one workgroup per (kv head, item), in the
+ *   items' order, instead of a grid sized for max_context_len in every sequence: with
+ *   pkv_decode_items the longest partitions go first and the shortest fill the launch's tail.
+ *   partition_size  > 0, the size the items were built with (a multiple of 64 and of the block
+ *                 size, at most pkv_decode_max_partition); pkv_decode_partition_size gives the
+ *                 automatic one.
+ *   items, num_items  device int32 [num_items] as from pkv_decode_items over the host context
+ *                 lengths: every partition of every decode-row (q_len == 1) sequence listed once.
+ *                 Items of sequences with more than one row do nothing (those rows go to the
+ *                 prefill kernel as always), so the list of every sequence serves. An item for
+ *                 a partition that does not exist, or for a sequence >= num_seqs, does nothing.
+ *                 num_items may be 0 when no sequence has a single row.
+ *   workspace     at least pkv_ragged_workspace_bytes(...) and at least
+ *                 pkv_decode_workspace_bytes_ex(num_seqs, num_q_heads, max_context_len, cache,
+ *                 partition_size) bytes; 16-byte aligned.
+ *   With every such item listed and partition_size the automatic size, the outputs equal those
+ *   of pkv_paged_attention_ragged_ex bit for bit (the same partitions, merged the same way); at
+ *   another size the decode rows are split at that size. In causal-rows mode (see
+ *   pkv_paged_attention_ragged) and when min_q_len >= 2 the work list is not used and the call is
+ *   pkv_paged_attention_ragged_ex.
+ *   Errors: as pkv_paged_attention_ragged_ex; PKV_EINVAL also for partition_size <= 0,
+ *   num_items < 0 or a null items with num_items > 0, and, when the work list is used, for a
+ *   partition size the decode kernel does not take (all before anything is enqueued).
+ */
+int32_t pkv_paged_attention_ragged_items(void* out, int32_t out_dtype, const void* q,
+                                         const int32_t* cu_seqlens_q, const int32_t* context_lens,
+                                         const void* k_cache, const void* v_cache,
+                                         const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                         int32_t num_seqs, int32_t num_tokens, int32_t num_q_heads,
+                                         float scale, int32_t min_q_len, int32_t max_q_len,
+                                         int32_t max_context_len, const pkv_cache_desc* cache,
+                                         int32_t partition_size, const int32_t* items,
+                                         int32_t num_items, void* workspace, size_t workspace_bytes,
+                                         void* stream);
+
+/*
  * swap_blocks — move whole blocks between a GPU pool and a host swap pool for preemption and
  *   restore (「PagedAttention原理」 §抢占与恢复 / §swap). For each pair i: block dst_i of
  *   (dst_k, dst_v) <- block src_i of (src_k, src_v), all B slots, all kv heads, bit for bit.

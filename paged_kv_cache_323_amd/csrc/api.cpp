@@ -468,12 +468,15 @@ size_t pkv_ragged_workspace_bytes(int32_t num_seqs, int32_t num_tokens, int32_t 
   return pkv_decode_workspace_bytes_ex(items, num_q_heads, max_context_len, c, 0);
 }
 
-int32_t pkv_paged_attention_ragged_ex(void* out, int32_t out_dtype, const void* q, const int32_t* cu_seqlens_q,
-                                      const int32_t* context_lens, const void* k_cache, const void* v_cache,
-                                      const int32_t* block_tables, int32_t max_blocks_per_seq, int32_t num_seqs,
-                                      int32_t num_tokens, int32_t num_q_heads, float scale, int32_t min_q_len,
-                                      int32_t max_q_len, int32_t max_context_len, const pkv_cache_desc* c,
-                                      void* workspace, size_t workspace_bytes, void* stream) {
+// The ragged step; decode rows through the dense partition grid (items == nullptr, partition_size
+// 0: automatic) or through the caller's work list at partition_size.
+static int32_t ragged_common(void* out, int32_t out_dtype, const void* q, const int32_t* cu_seqlens_q,
+                             const int32_t* context_lens, const void* k_cache, const void* v_cache,
+                             const int32_t* block_tables, int32_t max_blocks_per_seq, int32_t num_seqs,
+                             int32_t num_tokens, int32_t num_q_heads, float scale, int32_t min_q_len,
+                             int32_t max_q_len, int32_t max_context_len, const pkv_cache_desc* c,
+                             int32_t partition_size, const int32_t* items, int32_t num_items, void* workspace,
+                             size_t workspace_bytes, void* stream) {
   int32_t st = check_cache(c);
   if (st != PKV_OK) return st;
   if ((st = check_heads(num_q_heads, c)) != PKV_OK) return st;
@@ -497,8 +500,8 @@ int32_t pkv_paged_attention_ragged_ex(void* out, int32_t out_dtype, const void* 
   const bool decode_rows = min_q_len == 1;
   if (decode_rows) {
     st = decode_common_cu(out, out_dtype, q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens,
-                          num_seqs, num_q_heads, scale, max_context_len, c, 0, workspace, workspace_bytes, stream,
-                          cu_seqlens_q, 0, num_tokens);
+                          num_seqs, num_q_heads, scale, max_context_len, c, partition_size, workspace,
+                          workspace_bytes, stream, cu_seqlens_q, 0, num_tokens, items, num_items);
     if (st != PKV_OK || max_q_len <= 1) return st;
   }
   pkv::PrefillLaunch P;
@@ -522,6 +525,30 @@ int32_t pkv_paged_attention_ragged_ex(void* out, int32_t out_dtype, const void* 
   P.num_blocks = c->num_blocks;
   P.min_rows = decode_rows ? 2 : 1;
   return launched(pkv::launch_ragged_prefill(P, (hipStream_t)stream));
+}
+
+int32_t pkv_paged_attention_ragged_ex(void* out, int32_t out_dtype, const void* q, const int32_t* cu_seqlens_q,
+                                      const int32_t* context_lens, const void* k_cache, const void* v_cache,
+                                      const int32_t* block_tables, int32_t max_blocks_per_seq, int32_t num_seqs,
+                                      int32_t num_tokens, int32_t num_q_heads, float scale, int32_t min_q_len,
+                                      int32_t max_q_len, int32_t max_context_len, const pkv_cache_desc* c,
+                                      void* workspace, size_t workspace_bytes, void* stream) {
+  return ragged_common(out, out_dtype, q, cu_seqlens_q, context_lens, k_cache, v_cache, block_tables,
+                       max_blocks_per_seq, num_seqs, num_tokens, num_q_heads, scale, min_q_len, max_q_len,
+                       max_context_len, c, 0, nullptr, 0, workspace, workspace_bytes, stream);
+}
+
+int32_t pkv_paged_attention_ragged_items(void* out, int32_t out_dtype, const void* q, const int32_t* cu_seqlens_q,
+                                         const int32_t* context_lens, const void* k_cache, const void* v_cache,
+                                         const int32_t* block_tables, int32_t max_blocks_per_seq, int32_t num_seqs,
+                                         int32_t num_tokens, int32_t num_q_heads, float scale, int32_t min_q_len,
+                                         int32_t max_q_len, int32_t max_context_len, const pkv_cache_desc* c,
+                                         int32_t partition_size, const int32_t* items, int32_t num_items,
+                                         void* workspace, size_t workspace_bytes, void* stream) {
+  if (partition_size <= 0 || num_items < 0 || (num_items > 0 && !items)) return PKV_EINVAL;
+  return ragged_common(out, out_dtype, q, cu_seqlens_q, context_lens, k_cache, v_cache, block_tables,
+                       max_blocks_per_seq, num_seqs, num_tokens, num_q_heads, scale, min_q_len, max_q_len,
+                       max_context_len, c, partition_size, items, num_items, workspace, workspace_bytes, stream);
 }
 
 int32_t pkv_paged_attention_ragged(void* out, int32_t out_dtype, const void* q, const int32_t* cu_seqlens_q,

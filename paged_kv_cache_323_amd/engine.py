@@ -67,6 +67,7 @@ class EngineStats:
     steps: int = 0
     prefill_tokens: int = 0
     decode_tokens: int = 0
+    decode_kv_tokens: int = 0     # cached tokens the decode rows attended (each read in full)
     finished: int = 0
     preemptions: int = 0
     resumptions: int = 0
@@ -317,40 +318,55 @@ class Engine:
         k, v = self._kv(seqs, ns, tag)
         S, T = len(seqs), len(slots)
         max_blocks = -(-self.max_len // self.B)
-        host = self._staging(T + 2 * S + 1 + S * max_blocks)
+        # work-list capacity: the automatic partition is at least 256 tokens whenever a context
+        # needs more than one
+        max_parts = -(-self.max_len // 256)
+        tab0 = T + 2 * S + 1
+        items0 = tab0 + S * max_blocks
+        host = self._staging(items0 + S * max_parts)
         host[:T] = slots
         cu = host[T: T + S + 1]
         cu[0] = 0
         np.cumsum(ns, out=cu[1:])
-        lens = host[T + S + 1: T + 2 * S + 1]
-        tables = host[T + 2 * S + 1: T + 2 * S + 1 + S * max_blocks].reshape(S, max_blocks)
+        lens = host[T + S + 1: tab0]
+        tables = host[tab0: items0].reshape(S, max_blocks)
         self.bm.block_tables(seqs, max_blocks, out=tables, ctx_out=lens)
-        dev = self._upload(host)
+        max_ctx, max_q, min_q = int(lens.max()), int(max(ns)), int(min(ns))
+        # The decode rows run from a work list, longest partitions first (built from the host
+        # lengths, uploaded with the rest); a step of prefill chunks only has none.
+        n_items, part = 0, 0
+        if min_q == 1:
+            part = pk.decode_partition_size(S, self.hq, max_ctx, self.desc)
+            n_items = pk.decode_items_into(lens, part, host[items0:])
+        dev = self._upload(host[:items0 + n_items])
         sd, cu_d = dev[:T], dev[T: T + S + 1]
-        lens_d = dev[T + S + 1: T + 2 * S + 1]
-        tab_d = dev[T + 2 * S + 1: T + 2 * S + 1 + S * max_blocks].view(S, max_blocks)
+        lens_d = dev[T + S + 1: tab0]
+        tab_d = dev[tab0: items0].view(S, max_blocks)
+        items_d = dev[items0: items0 + n_items] if min_q == 1 else None
         pk.kv_cache_write(k, v, self.k_cache, self.v_cache, sd, self.desc)
         q = self._q(seqs, ns)
         out = torch.empty(q.shape, dtype=torch.float32 if self.keep_outputs else q.dtype, device=self.device)
-        max_ctx, max_q = int(lens.max()), int(max(ns))
         nbytes = pk.ragged_workspace_bytes(S, int(cu[-1]), self.hq, max_q, max_ctx, self.desc)
         if self.ws.numel() < nbytes:
             self.ws = torch.zeros(nbytes, dtype=torch.uint8, device=self.device)
         # the step's shortest chunk bounds q_len from below: a step of prefill chunks only runs
         # no decode-row launches
         pk.paged_attention_ragged(out, q, cu_d, lens_d, self.k_cache, self.v_cache, tab_d, self.scale,
-                                  max_q, max_ctx, self.desc, self.ws, min_q_len=int(min(ns)))
-        rec = StepRecord(self.step_idx, list(seqs), list(ns), lens.tolist(), len(self.ops),
+                                  max_q, max_ctx, self.desc, self.ws, min_q_len=min_q, partition_size=part,
+                                  items=items_d)
+        lens_list = lens.tolist()
+        rec = StepRecord(self.step_idx, list(seqs), list(ns), lens_list, len(self.ops),
                          out if self.keep_outputs else None)
         self.records.append(rec)
         # every row group yields one generated token (the prompt's last row, or the decode row)
-        for s, n in zip(seqs, ns):
+        for s, n, ctx in zip(seqs, ns, lens_list):
             req = self.requests[s]
             if req.state == PREFILL:
                 self.stats.prefill_tokens += n
                 req.state = DECODING
             else:
                 self.stats.decode_tokens += 1
+                self.stats.decode_kv_tokens += ctx
             req.generated += 1
             if req.generated >= req.max_new_tokens:
                 req.state = FINISHED

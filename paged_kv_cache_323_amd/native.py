@@ -121,6 +121,9 @@ _SIGS = {
                                           ctypes.c_float, _I32, _I32, _DESC, _P, _SZ, _P]),
     "pkv_paged_attention_ragged_ex": (_I32, [_P, _I32, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32,
                                              ctypes.c_float, _I32, _I32, _I32, _DESC, _P, _SZ, _P]),
+    "pkv_paged_attention_ragged_items": (_I32, [_P, _I32, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32,
+                                                ctypes.c_float, _I32, _I32, _I32, _DESC, _I32, _P, _I32, _P,
+                                                _SZ, _P]),
     "pkv_bm_create": (_P, [_I32, _I32, _I32P]),
     "pkv_bm_destroy": (None, [_P]),
     "pkv_bm_clone": (_P, [_P]),
@@ -410,11 +413,15 @@ def ragged_workspace_bytes(num_seqs: int, num_tokens: int, num_q_heads: int, max
 
 def paged_attention_ragged(out, q, cu_seqlens_q, context_lens, k_cache, v_cache, block_tables, scale: float,
                            max_q_len: int, max_context_len: int, desc: CacheDesc, workspace=None,
-                           stream=None, min_q_len: Optional[int] = None) -> None:
+                           stream=None, min_q_len: Optional[int] = None, partition_size: int = 0,
+                           items=None, num_items: Optional[int] = None) -> None:
     """Selective-batching attention over a flattened ragged batch (see include/pagedkv.h).
 
     ``min_q_len`` (a host lower bound on every sequence's query rows) selects
     pkv_paged_attention_ragged_ex; with 2 or more the decode-row launches are skipped.
+    ``items`` (device int32, from decode_items at ``partition_size``) selects
+    pkv_paged_attention_ragged_items: the decode rows run from that work list; ``num_items``
+    defaults to its length.
     """
     torch = _torch()
     T, hq, d = q.shape
@@ -427,7 +434,14 @@ def paged_attention_ragged(out, q, cu_seqlens_q, context_lens, k_cache, v_cache,
             _dev(context_lens, "context_lens", torch.int32), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
             _dev(block_tables, "block_tables", torch.int32), int(block_tables.shape[1]), S, T, hq, float(scale))
     tail = (int(max_q_len), int(max_context_len), ctypes.byref(desc), ws, wsb, _stream(stream))
-    if min_q_len is None:
+    if items is not None:
+        n = int(items.numel()) if num_items is None else int(num_items)
+        if n > items.numel():
+            raise ValueError("num_items exceeds the items tensor")
+        st = _lib.pkv_paged_attention_ragged_items(
+            *head, int(1 if min_q_len is None else min_q_len), *tail[:3], int(partition_size),
+            _dev(items, "items", torch.int32), n, *tail[3:])
+    elif min_q_len is None:
         st = _lib.pkv_paged_attention_ragged(*head, *tail)
     else:
         st = _lib.pkv_paged_attention_ragged_ex(*head, int(min_q_len), *tail)

@@ -213,6 +213,31 @@ def test_ragged_ex_validation():
     assert ragged_ex(desc(), 0, S=0) == 0 and ragged_ex(desc(), 0, T=0) == 0  # nothing to do
 
 
+def ragged_items(c, min_q, part, items, n, hq=4, S=2, T=5, max_q=3, max_ctx=100, mb=8):
+    p = ctypes.c_void_p(1)
+    return L.pkv_paged_attention_ragged_items(p, c.dtype, p, p, p, p, p, p, mb, S, T, hq, 0.125, min_q, max_q,
+                                              max_ctx, ctypes.byref(c), part, items, n, NULL, 0, NULL)
+
+
+def test_ragged_items_validation():
+    p = ctypes.c_void_p(1)
+    # the work list's own arguments: a positive partition size, a count >= 0, items when counted
+    assert ragged_items(desc(), 1, 0, p, 1) == -1
+    assert ragged_items(desc(), 1, -64, p, 1) == -1
+    assert ragged_items(desc(), 1, 256, p, -1) == -1
+    assert ragged_items(desc(), 1, 256, NULL, 3) == -1
+    # then the checks of pkv_paged_attention_ragged_ex
+    assert ragged_items(desc(), 0, 256, p, 1) == -1
+    assert ragged_items(desc(), 4, 256, p, 1, max_q=3) == -1
+    assert ragged_items(desc(), 1, 256, p, 1, hq=6) == -3
+    assert ragged_items(desc(), 1, 256, p, 1, S=0) == 0 and ragged_items(desc(), 1, 256, NULL, 0, T=0) == 0
+    # a partition size the decode kernel does not take (not a multiple of 64; beyond the largest
+    # partition for these heads), rejected before the decode-row launch (f16, one query head per kv
+    # head, max_q_len 3: not causal-rows mode)
+    assert ragged_items(desc(), 1, 100, p, 1) == -1
+    assert ragged_items(desc(), 1, 16384, p, 1, max_ctx=100, mb=1024) == -1
+
+
 def test_single_hip_runtime_when_binding_is_imported_before_torch():
     # Loaded before torch, the library would bind to a second libamdhip64 that may not see
     # the device; the binding imports torch first so every HIP call shares torch's runtime.

@@ -127,6 +127,53 @@ def test_ragged_min_q_len_hint(case):
     print(f"  max abs err {err:.3g}")
 
 
+ITEM_CASES = [
+    # (dtype, B, d, hq, hkv, q_lens, ctx)
+    ("bf16", 16, 128, 4, 4, [1, 130, 1, 1, 257, 1], [900, 130, 5000, 1, 300, 2100]),  # long decodes split
+    ("f16", 16, 128, 32, 8, [1, 1, 65, 1], [3000, 40, 65, 9000]),        # four query heads per kv head
+    ("bf16", 32, 64, 64, 8, [1, 200, 1], [4500, 200, 77]),               # eight: the one-pass kernel
+    ("bf16", 16, 128, 40, 40, [1] * 6, [300, 1200, 17, 640, 1280, 5]),   # decode rows only
+    ("bf16", 16, 128, 32, 8, [2, 4, 3], [1500, 40, 3]),                  # causal-rows mode: list unused
+]
+
+
+@pytest.mark.parametrize("case", ITEM_CASES, ids=lambda c: f"{c[0]}-{c[3]}q{c[4]}kv-d{c[2]}-{len(c[5])}seqs")
+def test_ragged_work_list(case):
+    """pkv_paged_attention_ragged_items: at the automatic partition size every output row equals
+    the dense-grid call bit for bit, whatever the order of the work list; at a smaller partition
+    size the oracle's outputs within the tolerance."""
+    import torch
+    from paged_kv_cache_323_amd import native as pk
+    from paged_kv_cache_323_amd import runner as R
+    dt, B, d, hq, hkv, ql, ctx = case
+    seed = zlib.crc32(repr(case).encode()) % 10000
+    w = make_ragged_workload(seed, ql, ctx, hq, hkv, d, dt, B, name=f"ragged-items-{dt}-B{B}-d{d}")
+    _announce(f"{w.name} q_lens={ql} ctx={ctx}")
+    _, ref = oracle.run_workload(w)
+    st = R.play_script(w, threads=16)
+    out, inp = R.attention(w, st, "f32")
+    cu = torch.from_numpy(w.cu_seqlens()).cuda()
+    lens = inp["lens_host"]
+    S, mx, mq = len(ql), int(lens.max()), int(max(ql))
+    p_auto = pk.decode_partition_size(S, hq, mx, st.desc)
+    for p in (p_auto, 256):
+        host_items = pk.decode_items(lens, p)
+        ws = torch.zeros(max(pk.ragged_workspace_bytes(S, int(inp["q"].shape[0]), hq, mq, mx, st.desc),
+                             pk.decode_workspace_bytes(S, hq, mx, st.desc, p), 1), dtype=torch.uint8, device="cuda")
+        for order in ("longest first", "reversed"):
+            it = host_items if order == "longest first" else host_items[::-1].copy()
+            items = torch.from_numpy(np.ascontiguousarray(it)).cuda()
+            got = torch.full_like(out, float("nan"))
+            pk.paged_attention_ragged(got, inp["q"], cu, inp["context_lens"], st.k_cache, st.v_cache,
+                                      inp["block_tables"], w.scale, mq, mx, st.desc, ws, min_q_len=int(min(ql)),
+                                      partition_size=p, items=items)
+            torch.cuda.synchronize()
+            err = _check(w, got, ref)
+            if p == p_auto:
+                assert torch.equal(got.view(torch.int32), out.view(torch.int32)), f"partition {p}, {order}"
+            print(f"  partition {p} ({len(it)} items, {order}): max abs err {err:.3g}")
+
+
 @pytest.mark.parametrize("dt", ["bf16", "f16"])
 def test_ragged_sharp_scores(dt):
     """Scores scaled by 4.0 instead of 1/sqrt(d): along a prefill row the maximum keeps rising by
