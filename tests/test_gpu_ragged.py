@@ -210,16 +210,29 @@ def test_ragged_short_rows_precision():
 
 
 def test_mixed_full_every_row():
-    """The full 13B-shaped mixed step (8 prefills + 248 decodes, 40 heads, bf16) in the launch
-    configuration the benchmark uses: every row of every prompt and every decode row against the
-    oracle, every append's slots, and both full pools bit for bit after the setup writes and the
-    step's own cache write (about 548 k tokens, the cache write's grid-stride path)."""
+    """The full 13B-shaped mixed step (8 prefills + 248 decodes, 40 heads, bf16): every row of every
+    prompt and every decode row against the oracle, every append's slots, and both full pools bit
+    for bit after the setup writes and the step's own cache write (about 548 k tokens, the cache
+    write's grid-stride path); the benchmark's work-list call bit for bit equal to the dense one."""
     from paged_kv_cache_323_amd import runner as R
     from support import compare_pool_bits, oracle_attention_threaded
     w = make_workload("mixed", "full")
     _announce(f"{w.name}: {len(w.query_seqs)} seqs, {sum(w.q_lens)} rows, sum ctx {sum(w.context_lens)}")
     st = R.play_script(w, threads=16)
-    out, _ = R.attention(w, st, "f32")
+    out, inp = R.attention(w, st, "f32")
+    # the benchmark's call: decode rows from the longest-first work list, bit for bit the same
+    import torch
+    from paged_kv_cache_323_amd import native as pk
+    lens = inp["lens_host"]
+    p = pk.decode_partition_size(len(lens), w.num_q_heads, int(lens.max()), st.desc)
+    items = torch.from_numpy(pk.decode_items(lens, p)).cuda()
+    got_items = torch.full_like(out, float("nan"))
+    pk.paged_attention_ragged(got_items, inp["q"], torch.from_numpy(w.cu_seqlens()).cuda(), inp["context_lens"],
+                              st.k_cache, st.v_cache, inp["block_tables"], w.scale, int(max(w.q_lens)),
+                              int(lens.max()), st.desc, inp["workspace"], min_q_len=1, partition_size=p, items=items)
+    torch.cuda.synchronize()
+    assert torch.equal(got_items.view(torch.int32), out.view(torch.int32)), "work-list call differs"
+    del got_items, items
     got = out.cpu().numpy()
     st_or, _ = oracle.run_workload(w, attend=False, threads=16)
     for a, b in zip(st.slots_per_append, st_or.slots_per_append):
