@@ -79,7 +79,8 @@ class Engine:
 
     def __init__(self, num_blocks: int, block_size: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
                  dtype: str, max_num_seqs: int = 64, max_step_tokens: int = 8192, num_host_blocks: int = 0,
-                 seed: int = 0, values=None, keep_outputs: bool = False, device: str = "cuda"):
+                 seed: int = 0, values=None, keep_outputs: bool = False, device: str = "cuda",
+                 copy_stream=None):
         self.B, self.hq, self.hkv, self.d, self.dtype = block_size, num_q_heads, num_kv_heads, head_dim, dtype
         self.max_num_seqs, self.max_step_tokens = max_num_seqs, max_step_tokens
         self.seed, self.values, self.keep_outputs, self.device = seed, values, keep_outputs, device
@@ -121,7 +122,11 @@ class Engine:
         self._stage_host: List[Optional[torch.Tensor]] = [None] * self.STAGE_RING
         self._stage_dev: List[Optional[torch.Tensor]] = [None] * self.STAGE_RING
         self._marks: Deque = deque()      # (step index, launch-stream event after that step)
-        self._copy_stream = torch.cuda.Stream(device=device)
+        # The upload stream. HIP gives a stream a hardware queue when the stream first submits
+        # work, in turn over a few queues (four by default), so a process that keeps creating
+        # streams eventually puts one on the launch stream's queue, where its uploads wait behind
+        # the kernels; a caller running several engines can pass one stream for all of them.
+        self._copy_stream = copy_stream if copy_stream is not None else torch.cuda.Stream(device=device)
         self.max_len = 0                  # longest context any request can reach (sizes tables)
 
     # ---- requests -------------------------------------------------------------------------------
