@@ -1,6 +1,6 @@
 """Iteration-level continuous batching over the paged KV cache.
 
-A small driver, not a serving system: requests carry a prompt length and a number of tokens to
+A small step loop, not a serving system: requests carry a prompt length and a number of tokens to
 generate, there is no model, and the new tokens' q/k/v come from a value provider (the seeded
 generator for parity runs, device random numbers for throughput runs). What it exercises is the
 hot path as an engine drives it, step after step with changing tables:

@@ -1,4 +1,4 @@
-// Stress driver for the host block manager, built with AddressSanitizer and UBSan by
+// Stress program for the host block manager, built with AddressSanitizer and UBSan by
 // tests/test_bm_sanitize.py (host code only; no HIP).
 //
 // A seeded random script of add / fork / append (batches with repeated sequences) / free /
