@@ -7,6 +7,7 @@ import re
 import subprocess
 import sys
 
+import numpy as np
 import pytest
 from hypothesis import given, settings, strategies as st
 
@@ -131,6 +132,24 @@ def test_partition_size_rule():
     assert size(32, 4, 3000) == 768       # 3008 -> 1536 -> 768: 32 x 4 x 4 = 512
     assert size(6, 6, 5000) == -1         # 6 query heads over 4 kv heads
     assert size(-1, 4, 5000) == -1
+
+
+@settings(max_examples=300, derandomize=True, deadline=None, database=None)
+@given(st.sampled_from([1, 2, 4, 8]), st.sampled_from([1, 2, 8, 40]), st.integers(1, 600),
+       st.integers(1, 200_000), st.sampled_from([pk.F32, pk.F16, pk.BF16]), st.sampled_from([64, 128]))
+def test_auto_partition_splits_only_at_256_or_more(g, hkv, S, max_ctx, dt, d):
+    """What a caller sizing a work list ahead of time relies on (the engine's staging does): the
+    automatic partition is at least 256 tokens whenever the longest context needs more than one, so
+    no context up to max_context_len has more than max(1, ceil(max_context_len / 256)) items."""
+    c = desc(num_kv_heads=hkv, head_dim=d, dtype=dt)
+    p = L.pkv_decode_partition_size(S, g * hkv, max_ctx, ctypes.byref(c))
+    assert p > 0 and p % 64 == 0
+    if max_ctx > p:
+        assert p >= 256
+    n_longest = -(-max_ctx // p)
+    assert n_longest <= max(1, -(-max_ctx // 256))
+    items = pk.decode_items(np.array([max_ctx, max(1, max_ctx // 3), 1], dtype=np.int32), p)
+    assert len(items) <= 3 * max(1, -(-max_ctx // 256))
 
 
 @settings(max_examples=300, derandomize=True, deadline=None, database=None)
